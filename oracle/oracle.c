@@ -1,0 +1,295 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU reference for the fp8 KV-cache
+ * hot path: the e4m3 codec, quantise-on-write into the paged cache, and GQA
+ * decode attention over that cache in fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file: only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no code, header, table or constant with the HIP library.
+ *
+ * Citations name the source pages by title and section:
+ *   [VLLM]  "The State of FP8 KV-Cache and Attention Quantization in vLLM"
+ *           (vLLM project blog summary), keyed paragraphs such as
+ *           "ACCURACY AT LONG CONTEXT" and "DECODE COST".
+ *   [FLOPS] "ctx-fp8-kv-cache-long-context-accuracy" (arithmetic-intensity
+ *           record), sections "Arithmetic intensity", "Workarounds", "notes".
+ *   [CAP]   "FP8 KV Cache Quantization: Capacity Gains and Accuracy Risk"
+ *           (GPU Smith), sections named where cited.
+ *   [ACC]   "KV Cache Quantization: What FP8 and q8_0 Cost in Accuracy"
+ *           (Particula Tech), cited by paragraph topic.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - fp8 flavour is OCP E4M3 ("fn"): bias 7, no infinities, S.1111.111 = NaN,
+ *     largest finite 448 [CAP "What FP8 KV changes" / E4M3 vs E5M2].
+ *   - the element is divided by the per-tensor scale in IEEE f32 and then cast
+ *     once to e4m3 with round-to-nearest-even; magnitudes at or above 448 (and
+ *     infinities) saturate to 448; NaN keeps its sign [CAP "Scales and
+ *     calibration"]; rounding and saturation are not stated on the pages.
+ *   - decoding multiplies the code's value by the same scale.
+ *   - paged layout: key tiles are token-major  [block][kv_head][slot][dim],
+ *     value tiles are channel-major            [block][kv_head][dim][slot].
+ *     The pages fix only that the cache is held in fixed-size blocks
+ *     [CAP "Why the KV cache sets long-context capacity"].
+ *   - query head hq reads kv head hq / g, g = Hq / Hkv (contiguous groups);
+ *     the pages name only the group ratio g [FLOPS "Arithmetic intensity"].
+ *   - positions attended: [lo, L) with lo = max(0, L - W) for a window W > 0,
+ *     else 0; an empty range yields a zero output.
+ *   - softmax scale 1/sqrt(head_dim).
+ *
+ * Precision: all attention arithmetic in double; the only float operation is
+ * the quantiser's f32 division, which is the step being specified.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_CACHE_E4M3 0
+#define ORACLE_CACHE_BF16 1
+
+/* ---------------------------------------------------------------- bf16 --- */
+
+/* A bf16 value is the upper half of an IEEE binary32. */
+float oracle_bf16_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* ---------------------------------------------------------------- e4m3 --- */
+
+/*
+ * Value of an OCP E4M3 code [CAP "What FP8 KV changes" / E4M3 vs E5M2: three
+ * mantissa bits, largest normal 448].  Fields: sign s = bit 7, exponent
+ * E = bits 6..3 (bias 7), mantissa M = bits 2..0.
+ *   E = 15, M = 7   -> NaN (the only non-finite codes; there is no infinity)
+ *   E = 0           -> subnormal, M * 2^-9
+ *   otherwise       -> (1 + M/8) * 2^(E-7)
+ */
+double oracle_e4m3_decode(uint8_t c) {
+    int s = (c >> 7) & 1;
+    int E = (c >> 3) & 0xF;
+    int M = c & 0x7;
+    double mag;
+    if (E == 15 && M == 7) return s ? -NAN : NAN;
+    if (E == 0)
+        mag = ldexp((double)M, -9);
+    else
+        mag = ldexp(1.0 + (double)M / 8.0, E - 7);
+    return s ? -mag : mag;
+}
+
+/*
+ * Nearest E4M3 code to y, ties to even mantissa, saturating at 448.
+ * y is an f32 value carried in a double, so every step below is exact in
+ * double except the explicit rint() (round-half-even under the default
+ * rounding mode).
+ */
+uint8_t oracle_e4m3_encode(double y) {
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    double a = fabs(y);
+    if (isnan(y)) return (uint8_t)(sign | 0x7F);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);   /* saturate, +-inf too */
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal spacing 2^-9; m == 8 is the smallest normal, code 0x08 */
+        double m = rint(a * 512.0);
+        return (uint8_t)(sign | (uint8_t)m);
+    }
+    int e;
+    (void)frexp(a, &e);      /* a = f * 2^e, f in [0.5, 1) */
+    e -= 1;                  /* now a = f' * 2^e, f' in [1, 2) */
+    double m = rint((ldexp(a, -e) - 1.0) * 8.0);
+    if (m == 8.0) {          /* mantissa carried into the exponent */
+        m = 0.0;
+        e += 1;
+    }
+    /* a < 448 = 1.75 * 2^8 keeps (e, m) at or below (8, 6): never the NaN code */
+    return (uint8_t)(sign | (uint8_t)((e + 7) << 3) | (uint8_t)m);
+}
+
+/*
+ * Quantise one bf16 element with a per-tensor scale: divide in IEEE f32, then
+ * cast once to e4m3 [CAP "Scales and calibration": each K or V tensor is
+ * divided by its scale before the cast].
+ */
+uint8_t oracle_quantize(uint16_t x_bf16, float scale) {
+    float x = oracle_bf16_to_f32(x_bf16);
+    float y = x / scale;                 /* binary32 division, round-to-nearest-even */
+    return oracle_e4m3_encode((double)y);
+}
+
+/* Array helpers so callers can sweep whole domains in one call. */
+void oracle_e4m3_decode_n(const uint8_t* c, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(c[i]);
+}
+void oracle_e4m3_encode_n(const double* y, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(y[i]);
+}
+void oracle_quantize_n(const uint16_t* x, float scale, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_quantize(x[i], scale);
+}
+void oracle_div_f32_n(const float* x, float scale, float* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = x[i] / scale;
+}
+
+/* ------------------------------------------------------- paged layout --- */
+
+/* Byte/element offset of (block, kv_head, slot, dim) in a key cache. */
+static int64_t key_index(int64_t blk, int h, int off, int i, int Hkv, int bs, int D) {
+    return ((blk * Hkv + h) * (int64_t)bs + off) * (int64_t)D + i;
+}
+/* Offset of (block, kv_head, slot, dim) in a value cache (channel-major tile). */
+static int64_t value_index(int64_t blk, int h, int off, int i, int Hkv, int bs, int D) {
+    return ((blk * Hkv + h) * (int64_t)D + i) * (int64_t)bs + off;
+}
+
+/* --------------------------------------------------------- cache write --- */
+
+/*
+ * Quantise-on-write [CAP "Scales and calibration"] and scatter by slot into
+ * paged blocks [CAP "Why the KV cache sets long-context capacity"].
+ *   key, value    bf16 [T][Hkv][D]
+ *   key_cache     [NB][Hkv][bs][D], value_cache [NB][Hkv][D][bs], elements of
+ *                 cache_dtype (u8 e4m3 codes, or bf16 kept as-is: the native-
+ *                 dtype variant used for skipped sliding-window layers,
+ *                 [FLOPS "Workarounds"]; scales are not applied to it)
+ *   slot_mapping  int64 [T]: slot = block * bs + offset.  A slot outside
+ *                 [0, NB*bs) writes nothing.  Untouched bytes keep their value.
+ */
+void oracle_cache_write(const uint16_t* key, const uint16_t* value,
+                        void* key_cache, void* value_cache, int cache_dtype,
+                        const int64_t* slot_mapping, int T, int Hkv, int D,
+                        int bs, int NB, float k_scale, float v_scale) {
+    for (int t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= (int64_t)NB * bs) continue;
+        int64_t blk = slot / bs;
+        int off = (int)(slot % bs);
+        for (int h = 0; h < Hkv; ++h) {
+            for (int i = 0; i < D; ++i) {
+                uint16_t xk = key[((int64_t)t * Hkv + h) * D + i];
+                uint16_t xv = value[((int64_t)t * Hkv + h) * D + i];
+                int64_t ki = key_index(blk, h, off, i, Hkv, bs, D);
+                int64_t vi = value_index(blk, h, off, i, Hkv, bs, D);
+                if (cache_dtype == ORACLE_CACHE_E4M3) {
+                    ((uint8_t*)key_cache)[ki] = oracle_quantize(xk, k_scale);
+                    ((uint8_t*)value_cache)[vi] = oracle_quantize(xv, v_scale);
+                } else {
+                    ((uint16_t*)key_cache)[ki] = xk;
+                    ((uint16_t*)value_cache)[vi] = xv;
+                }
+            }
+        }
+    }
+}
+
+/* Dequantised cache element: e4m3 value times scale, or the bf16 value. */
+static double cache_value(const void* cache, int cache_dtype, int64_t idx, double scale) {
+    if (cache_dtype == ORACLE_CACHE_E4M3)
+        return oracle_e4m3_decode(((const uint8_t*)cache)[idx]) * scale;
+    return (double)oracle_bf16_to_f32(((const uint16_t*)cache)[idx]);
+}
+
+/* ---------------------------------------------------- decode attention --- */
+
+/*
+ * Softmax attention of one query vector over L_eff key/value rows, fp64:
+ *   s_j = (q . K_j) / sqrt(D);  w_j = exp(s_j - max s);  out = sum w_j V_j / sum w_j
+ * K and V are given already dequantised, row-major [n][D].  n = 0 -> zeros.
+ * This is the unpaged definition the paged walk below must agree with.
+ */
+void oracle_attention_rows(double* out, const double* q, const double* K,
+                           const double* V, int64_t n, int D) {
+    for (int i = 0; i < D; ++i) out[i] = 0.0;
+    if (n <= 0) return;
+    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int i = 0; i < D; ++i) dot += q[i] * K[j * D + i];
+        s[j] = dot / sqrt((double)D);
+        if (s[j] > m) m = s[j];
+    }
+    double Z = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        s[j] = exp(s[j] - m);
+        Z += s[j];
+    }
+    for (int64_t j = 0; j < n; ++j)
+        for (int i = 0; i < D; ++i) out[i] += s[j] * V[j * D + i];
+    for (int i = 0; i < D; ++i) out[i] /= Z;
+    free(s);
+}
+
+/*
+ * Decode attention for one (sequence b, query head hq) over the paged cache:
+ * GQA with group ratio g = Hq/Hkv [FLOPS "Arithmetic intensity"], K and V
+ * dequantised inside the attention [CAP "Attention backend interactions"],
+ * optional sliding window [CAP "Accuracy risks to test for"].
+ *   q             bf16 [B][Hq][D]
+ *   block_tables  int32 [B][max_blocks]; logical block n of sequence b lives
+ *                 in physical block block_tables[b][n]
+ *   context_lens  int32 [B]
+ *   out           double [D]
+ */
+void oracle_paged_decode_head(double* out, const uint16_t* q,
+                              const void* key_cache, const void* value_cache,
+                              int cache_dtype, const int32_t* block_tables,
+                              int max_blocks, const int32_t* context_lens,
+                              int Hq, int Hkv, int D, int bs,
+                              double k_scale, double v_scale, int window,
+                              int b, int hq) {
+    int g = Hq / Hkv;
+    int h = hq / g;
+    int64_t L = context_lens[b];
+    int64_t lo = (window > 0 && L > window) ? L - window : 0;
+    int64_t n = L > lo ? L - lo : 0;
+    double* qv = (double*)malloc(sizeof(double) * (size_t)D);
+    double* K = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
+    double* V = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
+    for (int i = 0; i < D; ++i)
+        qv[i] = (double)oracle_bf16_to_f32(q[((int64_t)b * Hq + hq) * D + i]);
+    for (int64_t j = lo; j < L; ++j) {
+        int64_t pb = block_tables[(int64_t)b * max_blocks + j / bs];
+        int off = (int)(j % bs);
+        for (int i = 0; i < D; ++i) {
+            K[(j - lo) * D + i] = cache_value(key_cache, cache_dtype,
+                                              key_index(pb, h, off, i, Hkv, bs, D), k_scale);
+            V[(j - lo) * D + i] = cache_value(value_cache, cache_dtype,
+                                              value_index(pb, h, off, i, Hkv, bs, D), v_scale);
+        }
+    }
+    oracle_attention_rows(out, qv, K, V, n, D);
+    free(qv);
+    free(K);
+    free(V);
+}
+
+/* All (b, hq) pairs: out double [B][Hq][D]. */
+void oracle_paged_decode(double* out, const uint16_t* q, const void* key_cache,
+                         const void* value_cache, int cache_dtype,
+                         const int32_t* block_tables, int max_blocks,
+                         const int32_t* context_lens, int B, int Hq, int Hkv,
+                         int D, int bs, double k_scale, double v_scale, int window) {
+    for (int b = 0; b < B; ++b)
+        for (int hq = 0; hq < Hq; ++hq)
+            oracle_paged_decode_head(out + ((int64_t)b * Hq + hq) * D, q, key_cache,
+                                     value_cache, cache_dtype, block_tables, max_blocks,
+                                     context_lens, Hq, Hkv, D, bs, k_scale, v_scale,
+                                     window, b, hq);
+}
+
+/* Selected (b, hq) pairs, pairs int32 [n][2]: out double [n][D]. */
+void oracle_paged_decode_pairs(double* out, const int32_t* pairs, int npairs,
+                               const uint16_t* q, const void* key_cache,
+                               const void* value_cache, int cache_dtype,
+                               const int32_t* block_tables, int max_blocks,
+                               const int32_t* context_lens, int Hq, int Hkv, int D,
+                               int bs, double k_scale, double v_scale, int window) {
+    for (int p = 0; p < npairs; ++p)
+        oracle_paged_decode_head(out + (int64_t)p * D, q, key_cache, value_cache,
+                                 cache_dtype, block_tables, max_blocks, context_lens,
+                                 Hq, Hkv, D, bs, k_scale, v_scale, window,
+                                 pairs[2 * p], pairs[2 * p + 1]);
+}

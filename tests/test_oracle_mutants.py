@@ -1,0 +1,76 @@
+"""The oracle's pins must catch plausible mistakes (CPU only).
+
+Each mutant is oracle.c with one deliberate error: a wrong rounding rule, a
+dropped term, a flipped sign, a wrong index or a transposed operand.  The
+mutant is compiled to a temporary library and the pin suites are run against
+it in a subprocess; every mutant must make at least one pin fail.  Mutants are
+chosen so that none writes outside its buffers.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+PINS = [os.path.join(ROOT, "tests", "test_oracle_codec.py"),
+        os.path.join(ROOT, "tests", "test_oracle_attention.py")]
+
+MUTANTS = {
+    "subnormal_ties_away": ("double m = rint(a * 512.0);", "double m = round(a * 512.0);"),
+    "normal_ties_up": ("double m = rint((ldexp(a, -e) - 1.0) * 8.0);",
+                       "double m = floor((ldexp(a, -e) - 1.0) * 8.0 + 0.5);"),
+    "saturate_to_nan": ("if (a >= 448.0) return (uint8_t)(sign | 0x7E);",
+                        "if (a >= 448.0) return (uint8_t)(sign | 0x7F);"),
+    "no_saturation_above_448": ("if (a >= 448.0) return", "if (a >= 480.0) return"),
+    "subnormal_step": ("mag = ldexp((double)M, -9);", "mag = ldexp((double)M, -8);"),
+    "exponent_bias": ("mag = ldexp(1.0 + (double)M / 8.0, E - 7);",
+                      "mag = ldexp(1.0 + (double)M / 8.0, E - 8);"),
+    "nan_loses_sign": ("if (isnan(y)) return (uint8_t)(sign | 0x7F);",
+                       "if (isnan(y)) return (uint8_t)0x7F;"),
+    "reciprocal_multiply": ("float y = x / scale;", "float y = x * (1.0f / scale);"),
+    "bf16_bits_misplaced": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    "no_softmax_scale": ("s[j] = dot / sqrt((double)D);", "s[j] = dot;"),
+    "exp_sign": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    "no_normalisation": ("for (int i = 0; i < D; ++i) out[i] /= Z;", "(void)Z;"),
+    "value_tile_token_major": (
+        "return ((blk * Hkv + h) * (int64_t)D + i) * (int64_t)bs + off;",
+        "return ((blk * Hkv + h) * (int64_t)bs + off) * (int64_t)D + i;"),
+    "key_tile_channel_major": (
+        "return ((blk * Hkv + h) * (int64_t)bs + off) * (int64_t)D + i;\n}\n/* Offset",
+        "return ((blk * Hkv + h) * (int64_t)D + i) * (int64_t)bs + off;\n}\n/* Offset"),
+    "gqa_interleaved_heads": ("int h = hq / g;", "int h = hq % Hkv;"),
+    "window_off_by_one": ("? L - window : 0;", "? L - window + 1 : 0;"),
+    "slot_offset_shift": ("int off = (int)(j % bs);", "int off = (int)((j + 1) % bs);"),
+    "k_scale_for_values": ("((uint8_t*)value_cache)[vi] = oracle_quantize(xv, v_scale);",
+                           "((uint8_t*)value_cache)[vi] = oracle_quantize(xv, k_scale);"),
+    "scale_dropped_in_decode": ("return oracle_e4m3_decode(((const uint8_t*)cache)[idx]) * scale;",
+                                "return oracle_e4m3_decode(((const uint8_t*)cache)[idx]);"),
+    "bf16_cache_bits_altered": ("((uint16_t*)key_cache)[ki] = xk;",
+                          "((uint16_t*)key_cache)[ki] = (uint16_t)(xk ^ 0x0001);"),
+}
+
+
+def test_mutant_table_applies_to_current_source():
+    src = open(SRC).read()
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) == 1, name
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    import oracle
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mutant.so"
+    subprocess.check_call(["gcc", *oracle.GCC_FLAGS, str(mutated), "-o", str(so), "-lm"],
+                          stderr=subprocess.DEVNULL)
+    env = dict(os.environ, FP8KV_ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        *PINS], cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout[-2000:]}"
