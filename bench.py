@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp8 paged-KV decode hot path on one MI355X.
+
+One step = one decode step of one attention layer for the whole batch: quantise-on-write of
+each sequence's new K/V token into the paged fp8 cache (fp8kv_cache_write), then GQA decode
+attention over the cache (fp8kv_paged_decode: split partials + log-sum-exp merge).  The
+default workload is the Llama-3.1-8B attention shape (32 query heads, 8 KV heads, head_dim
+128, 16-token blocks) at batch 1 and 131,072 tokens of context, the shape the pages' decode
+cost figures are quoted on ("The State of FP8 KV-Cache and Attention Quantization in vLLM",
+"DECODE COST").  Inputs are seeded synthetic bf16 N(0,1) values with 1% x8 key outlier
+channels and amax/448 scales, already resident in HBM; the cache is held in several rotated
+instances (>= 1 GiB together) so that repeated steps read HBM rather than the 256 MB
+Infinity Cache.
+
+Prints ONE JSON line.  `value` is algorithmic bytes per step / step time (GB/s): the bytes
+the method must move (fp8 K and V of every attended position, block-table entries, q, out,
+context lengths, and the step's K/V write), not what the kernels happen to fetch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published peak
+BLOCK = 16
+
+
+# ------------------------------------------------------------- byte counts ----
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """K and V bytes one cached token costs across all layers (2 x layers x heads x dim x bytes)."""
+    return 2 * num_layers * num_kv_heads * head_dim * elem_bytes
+
+
+def arithmetic_intensity(group: int, elem_bytes: int, head_dim: int = 128) -> float:
+    """Decode-attention flop per KV byte: (2gd for q.K + 2gd for p.V) over 2d*e bytes."""
+    return (4.0 * group * head_dim) / (2.0 * head_dim * elem_bytes)
+
+
+def attended(L: int, window: int):
+    lo = max(0, L - window) if window > 0 else 0
+    n = max(0, L - lo)
+    nblk = ((L + BLOCK - 1) // BLOCK - lo // BLOCK) if n > 0 else 0
+    return n, nblk
+
+
+def algorithmic_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                      elem_bytes: int, window: int = 0) -> dict:
+    """Bytes the method must move per decode step, split by kernel.
+
+    pass1 (partials): K and V of every attended position, one int32 block-table entry per
+      attended block, the bf16 query and the int32 context length of every sequence.
+    pass2 (merge): the bf16 output (plus the context length it re-reads).
+    write: the step's bf16 K/V rows in, their cache elements out, one int64 slot each.
+    """
+    p1 = p2 = 0
+    flops = 0
+    for L in context_lens:
+        n, nblk = attended(int(L), window)
+        p1 += 2 * n * num_kv_heads * head_dim * elem_bytes + 4 * nblk + 2 * num_q_heads * head_dim + 4
+        p2 += 2 * num_q_heads * head_dim + 4
+        flops += 4 * num_q_heads * head_dim * n
+    B = len(context_lens)
+    write = B * num_kv_heads * head_dim * (2 * 2 + 2 * elem_bytes) + 8 * B
+    return {"pass1": p1, "pass2": p2, "write": write, "step": p1 + p2 + write, "flops": flops}
+
+
+# ----------------------------------------------------------------- harness ----
+
+class DecodeBench:
+    """Device buffers for one workload layer and the calls of one decode step."""
+
+    def __init__(self, F, torch, w, layer, instances: int, num_splits: int):
+        self.F, self.torch, self.w, self.layer = F, torch, w, layer
+        dev = "cuda"
+        self.cdt = F.FP8KV_E4M3 if layer.cache_dtype == "e4m3" else F.FP8KV_BF16
+        self.ebytes = 1 if self.cdt == F.FP8KV_E4M3 else 2
+        B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+        n = w.num_blocks * Hkv * BLOCK * D
+        u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        cache_dtype = torch.uint8 if self.ebytes == 1 else torch.int16
+        self.q = u16(w.q)
+        self.bt = torch.from_numpy(w.block_tables).to(dev)
+        self.cl = torch.from_numpy(w.context_lens).to(dev)
+        self.stream = int(torch.cuda.current_stream().cuda_stream)
+        # the context before this step, written once into every rotated cache instance
+        prefix = w.prefix_token_rows()
+        kp, vp = u16(layer.k[prefix]), u16(layer.v[prefix])
+        sp = torch.from_numpy(w.slot_mapping[prefix]).to(dev)
+        self.kc, self.vc = [], []
+        for _ in range(instances):
+            kc = torch.zeros(n, dtype=cache_dtype, device=dev)
+            vc = torch.zeros(n, dtype=cache_dtype, device=dev)
+            F.fp8kv_cache_write(kp, vp, kc, vc, self.cdt, sp, len(prefix), Hkv, D, BLOCK,
+                                w.num_blocks, layer.k_scale, layer.v_scale, self.stream)
+            self.kc.append(kc)
+            self.vc.append(vc)
+        del kp, vp, sp
+        # the step's new token of every sequence
+        rows = w.step_token_rows()
+        self.k_new, self.v_new = u16(layer.k[rows]), u16(layer.v[rows])
+        self.slots_new = torch.from_numpy(w.slot_mapping[rows]).to(dev)
+        self.T_new = len(rows)
+        self.maxl = w.max_context_len
+        self.win = layer.sliding_window
+        self.splits = num_splits
+        self.nsplits = F.fp8kv_paged_decode_num_splits(B, Hkv, D, BLOCK, self.maxl, self.win, num_splits)
+        self.ws_bytes = F.fp8kv_paged_decode_workspace_size(B, Hq, Hkv, D, BLOCK, self.maxl,
+                                                            self.win, num_splits)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty(B * Hq * D, dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        self.bytes = algorithmic_bytes(w.context_lens, Hq, Hkv, D, self.ebytes, self.win)
+        self.footprint = 2 * n * self.ebytes
+
+    # -- the three kernels of a step, called through the C-ABI binding
+    def write(self, i):
+        w, L = self.w, self.layer
+        self.F.fp8kv_cache_write(self.k_new, self.v_new, self.kc[i], self.vc[i], self.cdt,
+                                 self.slots_new, self.T_new, w.num_kv_heads, w.head_dim, BLOCK,
+                                 w.num_blocks, L.k_scale, L.v_scale, self.stream)
+
+    def decode(self, i):
+        w, L = self.w, self.layer
+        self.F.fp8kv_paged_decode(self.out, self.F.FP8KV_BF16, self.q, self.kc[i], self.vc[i],
+                                  self.cdt, self.bt, w.max_blocks_per_seq, self.cl, self.maxl,
+                                  w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, BLOCK,
+                                  w.num_blocks, L.k_scale, L.v_scale, self.win, self.splits,
+                                  self.ws, self.ws_bytes, self.stream)
+
+    def partial(self, i):
+        w, L = self.w, self.layer
+        self.F.fp8kv_paged_decode_partial(self.q, self.kc[i], self.vc[i], self.cdt, self.bt,
+                                          w.max_blocks_per_seq, self.cl, self.maxl, w.num_seqs,
+                                          w.num_q_heads, w.num_kv_heads, w.head_dim, BLOCK,
+                                          w.num_blocks, L.k_scale, self.win, self.splits,
+                                          self.ws, self.ws_bytes, self.stream)
+
+    def merge(self):
+        w, L = self.w, self.layer
+        vs = L.v_scale if self.cdt == self.F.FP8KV_E4M3 else 1.0
+        self.F.fp8kv_paged_decode_merge(self.out, self.F.FP8KV_BF16, self.cl, self.maxl,
+                                        w.max_blocks_per_seq, w.num_seqs, w.num_q_heads,
+                                        w.num_kv_heads, w.head_dim, BLOCK, vs, self.win,
+                                        self.splits, self.ws, self.ws_bytes, self.stream)
+
+    def step(self, i):
+        self.write(i)
+        self.decode(i)
+
+    # -- timing
+    def time_steps(self, steps: int, warmup: int):
+        """Region A: `steps` whole steps bracketed by two events (no events inside)."""
+        torch = self.torch
+        R = len(self.kc)
+        for s in range(warmup):
+            self.step(s % R)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_cpu = time.perf_counter()
+        e0.record()
+        for s in range(steps):
+            self.step(s % R)
+        e1.record()
+        t_enq = time.perf_counter() - t_cpu
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, t_enq * 1e3 / steps
+
+    def time_kernels(self, steps: int):
+        """Region B: the same steps with events around each kernel of the step."""
+        torch = self.torch
+        R = len(self.kc)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for s in range(steps):
+            ev[s][0].record()
+            self.write(s % R)
+            ev[s][1].record()
+            self.partial(s % R)
+            ev[s][2].record()
+            if self.nsplits > 1:
+                self.merge()
+            ev[s][3].record()
+        torch.cuda.synchronize()
+        t = np.array([[ev[s][k].elapsed_time(ev[s][k + 1]) for k in range(3)] for s in range(steps)])
+        return {"write_ms": float(np.median(t[:, 0])), "pass1_ms": float(np.mean(t[:, 1])),
+                "pass1_median_ms": float(np.median(t[:, 1])), "merge_ms": float(np.median(t[:, 2]))}
+
+
+def cpu_baseline(w, layer, pairs_kv_heads: int = 2) -> dict:
+    """The oracle (plain C, fp64, single thread) on a bounded sample of the same workload:
+    every query head of the first `pairs_kv_heads` KV heads over the full context."""
+    import oracle
+    okc = np.zeros(w.num_blocks * w.num_kv_heads * BLOCK * w.head_dim, np.uint8)
+    ovc = np.zeros_like(okc)
+    oracle.cache_write(layer.k, layer.v, okc, ovc, oracle.CACHE_E4M3, w.slot_mapping, w.num_kv_heads,
+                       w.head_dim, BLOCK, w.num_blocks, layer.k_scale, layer.v_scale)
+    g = w.num_q_heads // w.num_kv_heads
+    pairs = np.array([(b, hq) for b in range(w.num_seqs) for hq in range(pairs_kv_heads * g)], np.int32)
+    t0 = time.perf_counter()
+    oracle.paged_decode_pairs(pairs, w.q, okc, ovc, oracle.CACHE_E4M3, w.block_tables, w.context_lens,
+                              w.num_q_heads, w.num_kv_heads, w.head_dim, BLOCK, layer.k_scale,
+                              layer.v_scale, layer.sliding_window)
+    dt = time.perf_counter() - t0
+    frac = pairs_kv_heads / w.num_kv_heads
+    sample_bytes = algorithmic_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, 1,
+                                     layer.sliding_window)["pass1"] * frac
+    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"fp64 C oracle decode of query heads 0..{len(pairs) - 1} (KV heads 0..{pairs_kv_heads - 1} "
+                      f"of {w.num_kv_heads}) over the full {int(w.context_lens[0])}-token context, single thread; "
+                      f"GB/s = the sample's algorithmic KV+q+table bytes / time"}
+
+
+WORKLOADS = {
+    "llama8b-b1-128k": lambda syn: syn.llama8b_long(131072, "amax"),
+    "llama8b-b8-16k-24k": lambda syn: syn.llama8b_batch("amax"),
+    "llama70b-b1-128k": lambda syn: syn.llama70b_needle(131072),
+    "gptoss-b8-20k": lambda syn: syn.gptoss_mixed(skip_sw=False),
+    "gptoss-b8-20k-skipsw": lambda syn: syn.gptoss_mixed(skip_sw=True),
+    "d256-b16-64k": lambda syn: syn.gemma_d256(),
+}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b-b1-128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--layer", type=int, default=0, help="layer of a mixed workload to time")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of rotated cache instances")
+    ap.add_argument("--no-bf16", action="store_true", help="skip the bf16-KV instantiation")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for a profiler: no bf16 variant, no CPU baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (for counter scaling)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this path runs on one GPU; --gpus must be 1 (multi-GPU sharding "
+                                   "of the decode is described in the design notes, not built)"}))
+        return 2
+
+    import torch
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return 0
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    import fp8_kv_cache_reshape_amd as F
+    import synthetic as syn
+
+    t0 = time.perf_counter()
+    w = WORKLOADS[args.workload](syn)
+    layer = w.layers[args.layer]
+    gen_s = time.perf_counter() - t0
+    one = 2 * w.num_blocks * w.num_kv_heads * BLOCK * w.head_dim * (1 if layer.cache_dtype == "e4m3" else 2)
+    R = max(1, math.ceil(args.rotate_bytes * (1 << 30) / one))
+    bench = DecodeBench(F, torch, w, layer, R, args.num_splits)
+    ms_step, ms_enqueue = bench.time_steps(args.steps, args.warmup)
+    kern = bench.time_kernels(min(args.steps, 100))
+    by = bench.bytes
+    value = by["step"] / (ms_step * 1e-3) / 1e9
+    achieved = by["pass1"] / (kern["pass1_ms"] * 1e-3) / 1e9
+
+    result = {
+        "metric": "FP8 paged decode attn: KV HBM GB/s (% of peak) + µs/step, 8B shape @128K",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_step": round(ms_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 KV -> bf16 MFMA, f32 accumulate" if bench.ebytes == 1 else "bf16 KV, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {w.name}, layer {layer.name} "
+                               f"({layer.cache_dtype} cache, window {layer.sliding_window})",
+                   "num_seqs": w.num_seqs, "context_lens": sorted(set(int(x) for x in w.context_lens))[:4],
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": BLOCK, "splits": bench.nsplits,
+                   "rotated_instances": R, "instance_bytes": one, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_partial_kernel", "bytes_per_launch": by["pass1"],
+                     "avg_launch_us": round(kern["pass1_ms"] * 1e3, 3)},
+        "kernels_us": {"cache_write": round(kern["write_ms"] * 1e3, 3),
+                       "decode_partial": round(kern["pass1_ms"] * 1e3, 3),
+                       "decode_merge": round(kern["merge_ms"] * 1e3, 3)},
+        "bytes_per_step": by["step"], "flops_per_step": by["flops"],
+        "enqueue_us_per_step": round(ms_enqueue * 1e3, 2), "input_gen_s": round(gen_s, 1),
+    }
+    del bench
+    torch.cuda.empty_cache()
+
+    if not (args.no_bf16 or args.profile) and layer.cache_dtype == "e4m3":
+        import dataclasses
+        bl = dataclasses.replace(layer, cache_dtype="bf16", k_scale=1.0, v_scale=1.0)
+        R2 = max(1, math.ceil(args.rotate_bytes * (1 << 30) / (2 * one)))
+        b2 = DecodeBench(F, torch, w, bl, R2, args.num_splits)
+        ms2, _ = b2.time_steps(args.steps, args.warmup)
+        k2 = b2.time_kernels(min(args.steps, 100))
+        result["bf16_kv"] = {"us_per_step": round(ms2 * 1e3, 2),
+                             "GBps": round(b2.bytes["step"] / (ms2 * 1e-3) / 1e9, 2),
+                             "decode_partial_us": round(k2["pass1_ms"] * 1e3, 3),
+                             "fp8_over_bf16_time": round(ms_step / ms2, 4)}
+        del b2
+        torch.cuda.empty_cache()
+
+    if not (args.no_cpu_baseline or args.profile) and layer.cache_dtype == "e4m3":
+        result["cpu_baseline"] = cpu_baseline(w, layer)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

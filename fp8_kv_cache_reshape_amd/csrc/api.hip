@@ -1,0 +1,301 @@
+// api.hip -- the extern "C" entry points of libfp8kv (declared in include/fp8kv.h):
+// host-side validation (before any HIP call), split planning, workspace layout, and the
+// kernel launches on the caller's stream.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fp8kv.h"
+#include "internal.h"
+
+namespace {
+
+using fp8kv::kBlockSize;
+using fp8kv::kMaxGroup;
+using fp8kv::kMaxSplits;
+
+constexpr int kTargetWorkgroups = 1024;   // about 4 decode workgroups per compute unit
+constexpr int kMinBlocksPerSplit = 16;    // one wave step (4 blocks) for each of 4 waves
+
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
+
+int check_decode_shape(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int block_size, int max_context_len, int sliding_window, int num_splits) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+        sliding_window < 0 || num_splits < 0)
+        return FP8KV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return FP8KV_ERR_SHAPE;
+    if (!head_dim_ok(head_dim) || block_size != kBlockSize) return FP8KV_ERR_UNSUPPORTED;
+    if (num_q_heads / num_kv_heads > kMaxGroup) return FP8KV_ERR_UNSUPPORTED;
+    if (num_splits > kMaxSplits) return FP8KV_ERR_UNSUPPORTED;
+    return FP8KV_OK;
+}
+
+// Longest block span any sequence can need: full context, or a window of W positions
+// that may straddle one extra block boundary.
+int max_window_blocks(int max_context_len, int sliding_window) {
+    if (max_context_len <= 0) return 0;
+    int nb = (max_context_len + kBlockSize - 1) / kBlockSize;
+    if (sliding_window > 0) {
+        const int wb = (sliding_window + kBlockSize - 1) / kBlockSize + 1;
+        if (wb < nb) nb = wb;
+    }
+    return nb;
+}
+
+struct Plan {
+    int splits;
+    int blocks_per_split;
+};
+
+Plan make_plan(int num_seqs, int num_kv_heads, int max_context_len, int sliding_window,
+               int num_splits) {
+    Plan pl;
+    const int nb = max_window_blocks(max_context_len, sliding_window);
+    if (nb == 0) {
+        pl.splits = 1;
+        pl.blocks_per_split = kMinBlocksPerSplit;
+        return pl;
+    }
+    int bps;
+    if (num_splits > 0) {
+        const int s = num_splits < nb ? num_splits : nb;
+        bps = (nb + s - 1) / s;
+    } else {
+        const long long units = (long long)(num_seqs > 0 ? num_seqs : 1) * num_kv_heads;
+        long long s = (kTargetWorkgroups + units - 1) / units;
+        if (s < 1) s = 1;
+        if (s > nb) s = nb;
+        bps = (int)((nb + s - 1) / s);
+        bps = (bps + kMinBlocksPerSplit - 1) / kMinBlocksPerSplit * kMinBlocksPerSplit;
+    }
+    if ((nb + bps - 1) / bps > kMaxSplits) bps = (nb + kMaxSplits - 1) / kMaxSplits;
+    pl.blocks_per_split = bps;
+    pl.splits = (nb + bps - 1) / bps;
+    return pl;
+}
+
+struct WorkspaceLayout {
+    size_t ml_bytes, acc_offset, total;
+};
+
+WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, int splits) {
+    WorkspaceLayout l;
+    const size_t rows = (size_t)num_seqs * num_q_heads * splits;
+    l.ml_bytes = rows * 2 * sizeof(float);
+    l.acc_offset = (l.ml_bytes + 255) / 256 * 256;
+    l.total = l.acc_offset + rows * (size_t)head_dim * sizeof(float);
+    return l;
+}
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return FP8KV_OK;
+    g_last_hip_error = e;
+    return FP8KV_ERR_HIP;
+}
+
+// Shared validation and parameter setup of the decode entry points.
+int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const void* key_cache,
+                 const void* value_cache, int cache_dtype, const int32_t* block_tables,
+                 int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                 int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                 int num_blocks, float k_scale, float v_scale, int sliding_window, int num_splits,
+                 void* workspace, size_t workspace_bytes, bool need_workspace_for_single) {
+    int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_context_len, sliding_window, num_splits);
+    if (st != FP8KV_OK) return st;
+    if (max_blocks_per_seq < 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
+    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
+    fp8 = cache_dtype == FP8KV_E4M3;
+    if (fp8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return FP8KV_ERR_SCALE;
+    if (num_seqs > 0) {
+        if (!query || !context_lens || !block_tables || !key_cache || !value_cache)
+            return FP8KV_ERR_NULL;
+        if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+            return FP8KV_ERR_SHAPE;
+        if (max_blocks_per_seq == 0 && max_context_len > 0) return FP8KV_ERR_SHAPE;
+    }
+    const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, sliding_window, num_splits);
+    const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits);
+    const bool single = pl.splits == 1 && !need_workspace_for_single;
+    if (!single && num_seqs > 0) {
+        if (!workspace || workspace_bytes < wl.total) return FP8KV_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP8KV_ERR_WORKSPACE;
+    }
+    p.query = static_cast<const uint16_t*>(query);
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_context_len = max_context_len;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.num_blocks = num_blocks;
+    p.sliding_window = sliding_window;
+    const double log2e = 1.4426950408889634;
+    p.score_scale = (float)((fp8 ? (double)k_scale : 1.0) * log2e / sqrt((double)head_dim));
+    p.v_scale = fp8 ? v_scale : 1.0f;
+    p.splits = pl.splits;
+    p.blocks_per_split = pl.blocks_per_split;
+    p.ws_ml = single ? nullptr : reinterpret_cast<float*>(workspace);
+    p.ws_acc = single ? nullptr
+                      : reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.acc_offset);
+    p.write_final = single ? 1 : 0;
+    p.out = nullptr;
+    p.out_f32 = 0;
+    return FP8KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8kv_status_string(int status) {
+    switch (status) {
+        case FP8KV_OK: return "ok";
+        case FP8KV_ERR_NULL: return "a required pointer is NULL";
+        case FP8KV_ERR_SHAPE: return "a size is negative or inconsistent, or a buffer is misaligned";
+        case FP8KV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, group ratio, split count or dtype";
+        case FP8KV_ERR_SCALE: return "an fp8 scale is not finite and positive";
+        case FP8KV_ERR_WORKSPACE: return "workspace is NULL, too small, or not 256-byte aligned";
+        case FP8KV_ERR_HIP: return "a HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int fp8kv_version(void) { return 100; }
+
+const char* fp8kv_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
+
+int fp8kv_cache_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                      int cache_dtype, const int64_t* slot_mapping, int num_tokens,
+                      int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                      float k_scale, float v_scale, void* stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
+    if (!head_dim_ok(head_dim) || block_size != kBlockSize) return FP8KV_ERR_UNSUPPORTED;
+    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
+    if (cache_dtype == FP8KV_E4M3 && (!scale_ok(k_scale) || !scale_ok(v_scale)))
+        return FP8KV_ERR_SCALE;
+    if (num_tokens == 0) return FP8KV_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping) return FP8KV_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+        return FP8KV_ERR_SHAPE;
+    fp8kv::CacheWriteParams p;
+    p.key = static_cast<const uint16_t*>(key);
+    p.value = static_cast<const uint16_t*>(value);
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.slot_mapping = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_kv_heads = num_kv_heads;
+    p.num_blocks = num_blocks;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    return hip_status(fp8kv::launch_cache_write(p, cache_dtype == FP8KV_E4M3, head_dim,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int fp8kv_paged_decode_num_splits(int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                                  int max_context_len, int sliding_window, int num_splits) {
+    int st = check_decode_shape(num_seqs, num_kv_heads, num_kv_heads, head_dim, block_size,
+                                max_context_len, sliding_window, num_splits);
+    if (st != FP8KV_OK) return st;
+    return make_plan(num_seqs, num_kv_heads, max_context_len, sliding_window, num_splits).splits;
+}
+
+size_t fp8kv_paged_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int block_size, int max_context_len,
+                                         int sliding_window, int num_splits) {
+    if (check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, sliding_window, num_splits) != FP8KV_OK)
+        return 0;
+    const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, sliding_window, num_splits);
+    return workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits).total;
+}
+
+int fp8kv_paged_decode(void* out, int out_dtype, const void* query, const void* key_cache,
+                       const void* value_cache, int cache_dtype, const int32_t* block_tables,
+                       int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int block_size, int num_blocks, float k_scale, float v_scale,
+                       int sliding_window, int num_splits, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    fp8kv::DecodeParams p;
+    bool fp8 = true;
+    int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
+                          max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, k_scale,
+                          v_scale, sliding_window, num_splits, workspace, workspace_bytes, false);
+    if (st != FP8KV_OK) return st;
+    if (num_seqs == 0) return FP8KV_OK;
+    if (!out) return FP8KV_ERR_NULL;
+    if (!aligned16(out)) return FP8KV_ERR_SHAPE;
+    p.out = out;
+    p.out_f32 = out_dtype == FP8KV_F32;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
+    if (st != FP8KV_OK || p.write_final) return st;
+    return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
+}
+
+int fp8kv_paged_decode_partial(const void* query, const void* key_cache, const void* value_cache,
+                               int cache_dtype, const int32_t* block_tables,
+                               int max_blocks_per_seq, const int32_t* context_lens,
+                               int max_context_len, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               float k_scale, int sliding_window, int num_splits, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    fp8kv::DecodeParams p;
+    bool fp8 = true;
+    int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
+                          max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, k_scale,
+                          1.0f, sliding_window, num_splits, workspace, workspace_bytes, true);
+    if (st != FP8KV_OK || num_seqs == 0) return st;
+    return hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int fp8kv_paged_decode_merge(void* out, int out_dtype, const int32_t* context_lens,
+                             int max_context_len, int max_blocks_per_seq, int num_seqs,
+                             int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                             float v_scale, int sliding_window, int num_splits,
+                             const void* workspace, size_t workspace_bytes, void* stream) {
+    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_context_len, sliding_window, num_splits);
+    if (st != FP8KV_OK) return st;
+    if (max_blocks_per_seq < 0) return FP8KV_ERR_SHAPE;
+    if (!scale_ok(v_scale)) return FP8KV_ERR_SCALE;
+    if (num_seqs == 0) return FP8KV_OK;
+    if (!out || !context_lens) return FP8KV_ERR_NULL;
+    if (!aligned16(out)) return FP8KV_ERR_SHAPE;
+    const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, sliding_window, num_splits);
+    const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits);
+    if (!workspace || workspace_bytes < wl.total) return FP8KV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP8KV_ERR_WORKSPACE;
+    fp8kv::DecodeParams p = {};
+    p.out = out;
+    p.out_f32 = out_dtype == FP8KV_F32;
+    p.context_lens = context_lens;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_context_len = max_context_len;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.sliding_window = sliding_window;
+    p.v_scale = v_scale;
+    p.splits = pl.splits;
+    p.blocks_per_split = pl.blocks_per_split;
+    p.ws_ml = reinterpret_cast<float*>(const_cast<void*>(workspace));
+    p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) + wl.acc_offset);
+    return hip_status(fp8kv::launch_decode_merge(p, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

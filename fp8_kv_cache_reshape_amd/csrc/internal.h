@@ -1,0 +1,86 @@
+// internal.h -- launch parameters and launcher declarations shared by the HIP sources of
+// libfp8kv.  Not part of the public ABI (that is include/fp8kv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8kv {
+
+constexpr int kBlockSize = 16;     // tokens per cache block (the only supported size)
+constexpr int kMaxGroup = 16;      // query heads per kv head: one MFMA column tile
+constexpr int kDecodeWaves = 4;    // waves per decode workgroup
+constexpr int kMaxSplits = 1024;   // upper bound on context splits per (seq, kv head)
+
+struct CacheWriteParams {
+    const uint16_t* key;           // bf16 [T][Hkv][D]
+    const uint16_t* value;
+    void* key_cache;               // [NB][Hkv][16][D]
+    void* value_cache;             // [NB][Hkv][D][16]
+    const int64_t* slot_mapping;   // [T]
+    int num_tokens;
+    int num_kv_heads;
+    int num_blocks;
+    float k_scale;
+    float v_scale;
+};
+
+struct DecodeParams {
+    void* out;                     // [B][Hq][D] bf16 or f32 (final output)
+    int out_f32;
+    const uint16_t* query;         // bf16 [B][Hq][D]
+    const void* key_cache;
+    const void* value_cache;
+    const int32_t* block_tables;   // [B][max_blocks]
+    const int32_t* context_lens;   // [B]
+    int max_blocks_per_seq;
+    int max_context_len;
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int num_blocks;
+    int sliding_window;
+    float score_scale;             // k_scale * log2(e) / sqrt(D): scores in base-2 units
+    float v_scale;
+    int splits;                    // grid extent over context splits
+    int blocks_per_split;
+    float* ws_ml;                  // [B][Hq][splits][2]  (m, l)
+    float* ws_acc;                 // [B][Hq][splits][D]
+    int write_final;               // single split: pass 1 normalises and stores `out`
+};
+
+// Context window of one sequence in blocks: positions [lo, L), blocks [blk0, blk0+nblk).
+struct SeqWindow {
+    int L, lo, blk0, nblk;
+};
+
+__host__ __device__ inline SeqWindow seq_window(int ctx_len, int max_context_len,
+                                                int max_blocks_per_seq, int sliding_window) {
+    SeqWindow w;
+    int L = ctx_len;
+    int cap = max_blocks_per_seq * kBlockSize;
+    if (L > max_context_len) L = max_context_len;
+    if (L > cap) L = cap;
+    if (L < 0) L = 0;
+    int lo = (sliding_window > 0 && L > sliding_window) ? L - sliding_window : 0;
+    w.L = L;
+    w.lo = lo;
+    w.blk0 = lo / kBlockSize;
+    w.nblk = (L > lo) ? (L + kBlockSize - 1) / kBlockSize - w.blk0 : 0;
+    return w;
+}
+
+// Launch a kernel whose only argument is a parameter struct and return the status of this
+// launch alone (hipGetLastError would also report errors other HIP users left behind).
+template <typename P>
+inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                                const P& p) {
+    void* args[] = {const_cast<P*>(&p)};
+    return hipLaunchKernel(fn, grid, block, args, lds, s);
+}
+
+hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, int head_dim, hipStream_t s);
+hipError_t launch_decode_partial(const DecodeParams& p, bool fp8, int head_dim, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t s);
+
+}  // namespace fp8kv

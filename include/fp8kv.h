@@ -1,0 +1,208 @@
+/*
+ * fp8kv.h -- C ABI of libfp8kv: an fp8 (OCP E4M3) paged KV cache and grouped-query
+ * decode attention over it, for AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, as the source pages frame the problem:
+ *   - quantise-on-write: each new K/V element is divided by its tensor's scale and
+ *     cast to E4M3, then stored into fixed-size cache blocks
+ *     (page "FP8 KV Cache Quantization: Capacity Gains and Accuracy Risk", sections
+ *     "Scales and calibration" and "Why the KV cache sets long-context capacity");
+ *   - decode attention softmax(q K^T / sqrt(d)) V that reads the fp8 blocks directly,
+ *     dequantising inside the kernel (same page, "Attention backend interactions"),
+ *     with GQA group ratio g = Hq / Hkv (page "ctx-fp8-kv-cache-long-context-accuracy",
+ *     "Arithmetic intensity"), an optional sliding window (first page, "Accuracy risks
+ *     to test for"), and fp32 partial results merged across context splits: the
+ *     two-level accumulation that keeps long contractions accurate (page "The State of
+ *     FP8 KV-Cache and Attention Quantization in vLLM", "ACCURACY AT LONG CONTEXT").
+ *   A bf16 cache variant of both calls keeps chosen layers in the native dtype (page
+ *   "ctx-fp8-kv-cache-long-context-accuracy", "Workarounds": skipping sliding-window
+ *   layers).
+ *
+ * Conventions for every call
+ *   - All pointers except the scalars are DEVICE pointers the caller owns.  The library
+ *     allocates nothing, keeps no state between calls, and is thread-safe.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns without synchronising.
+ *   - Arguments are validated on the host before any HIP call; a failed check returns a
+ *     negative status and enqueues nothing.  A failed launch returns FP8KV_ERR_HIP.
+ *   - Device-resident indices (slot_mapping, block_tables, context_lens) are not read by
+ *     the host.  Out-of-range values never cause an out-of-bounds access: a slot outside
+ *     [0, num_blocks*block_size) is skipped, a block id outside [0, num_blocks) is read as
+ *     an empty block, and a context length is clamped to
+ *     min(max_context_len, max_blocks_per_seq*block_size).  Results for such inputs are
+ *     otherwise unspecified.
+ *
+ * Data layout (row-major, no padding)
+ *   bf16 K/V rows written per token:  [num_tokens][num_kv_heads][head_dim]
+ *   query:                            [num_seqs][num_q_heads][head_dim] bf16
+ *   output:                           [num_seqs][num_q_heads][head_dim] bf16 or f32
+ *   key_cache:    [num_blocks][num_kv_heads][block_size][head_dim]   (token-major tiles)
+ *   value_cache:  [num_blocks][num_kv_heads][head_dim][block_size]   (channel-major tiles)
+ *     elements are u8 E4M3 codes (FP8KV_E4M3) or bf16 (FP8KV_BF16).  Each
+ *     (block, kv_head) tile is contiguous: block_size*head_dim elements.
+ *   slot_mapping: int64 [num_tokens]; token t goes to block slot/block_size, row
+ *     slot%block_size.
+ *   block_tables: int32 [num_seqs][max_blocks_per_seq]; logical block n of sequence b
+ *     is physical block block_tables[b][n].
+ *   context_lens: int32 [num_seqs]; the number of cached tokens of sequence b, counting
+ *     the token written for this decode step.  Query head hq reads kv head hq / g.
+ *
+ * Supported shapes: head_dim in {64, 128, 256}; block_size == 16; num_q_heads a
+ * multiple of num_kv_heads with g = num_q_heads/num_kv_heads <= 16.
+ */
+#ifndef FP8KV_H
+#define FP8KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (return values). */
+#define FP8KV_OK               0
+#define FP8KV_ERR_NULL        (-1)  /* a required pointer is NULL                         */
+#define FP8KV_ERR_SHAPE       (-2)  /* a size is negative or inconsistent                 */
+#define FP8KV_ERR_UNSUPPORTED (-3)  /* head_dim, block_size, group ratio or dtype code     */
+#define FP8KV_ERR_SCALE       (-4)  /* an fp8 scale is not finite and positive            */
+#define FP8KV_ERR_WORKSPACE   (-5)  /* workspace NULL, too small, or not 256-byte aligned */
+#define FP8KV_ERR_HIP         (-6)  /* a kernel launch failed                             */
+
+/* Element type codes. */
+#define FP8KV_E4M3 0   /* OCP FP8 E4M3 ("fn"): bias 7, max 448, no infinities, NaN = S.1111.111 */
+#define FP8KV_BF16 1
+#define FP8KV_F32  2   /* output only */
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* fp8kv_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fp8kv_version(void);
+
+/* Name of the HIP error behind the most recent FP8KV_ERR_HIP returned on the calling
+ * thread ("hipSuccess" if none).  Static storage; never NULL. */
+const char* fp8kv_last_hip_error(void);
+
+/*
+ * fp8kv_cache_write -- quantise new K/V rows and scatter them into the paged caches.
+ *
+ * For every token t with a valid slot, kv head h and channel i:
+ *   E4M3 caches: code = E4M3(f32(x) / scale), where "/" is the IEEE-754 binary32 division
+ *     (round to nearest even) and E4M3() rounds to nearest with ties to the even code,
+ *     saturates magnitudes >= 448 (and infinities) to +-448, keeps the sign of zero, and
+ *     maps NaN to 0x7F | sign.  k uses k_scale, v uses v_scale (page "FP8 KV Cache
+ *     Quantization: Capacity Gains and Accuracy Risk", "Scales and calibration": one
+ *     scale per tensor, elements divided by it before the cast).
+ *   BF16 caches: the bf16 bits are stored unchanged; the scales are ignored.
+ * Bytes of the caches that no valid slot addresses are left untouched.  Two tokens that
+ * name the same slot race; the result is one of the two rows.
+ *
+ *   key, value      device bf16 [num_tokens][num_kv_heads][head_dim]
+ *   key_cache,
+ *   value_cache     device caches in the layout above, of cache_dtype elements
+ *   slot_mapping    device int64 [num_tokens]
+ *   num_tokens      >= 0 (0 enqueues nothing)
+ *   k_scale,v_scale finite and > 0 for FP8KV_E4M3 (else FP8KV_ERR_SCALE)
+ */
+int fp8kv_cache_write(const void* key, const void* value,
+                      void* key_cache, void* value_cache, int cache_dtype,
+                      const int64_t* slot_mapping, int num_tokens,
+                      int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                      float k_scale, float v_scale, void* stream);
+
+/*
+ * fp8kv_paged_decode_num_splits -- number of context splits a decode will use.
+ *
+ * The context window of every (sequence, kv head) is cut into splits of a fixed number
+ * of blocks; each split yields fp32 partials (running max m, sum l, unnormalised
+ * accumulator acc[head_dim]) that a second pass merges.  num_splits > 0 requests at most
+ * that many splits for the longest sequence; 0 lets the library choose.  Returns the
+ * split count (>= 1) or a negative status.
+ */
+int fp8kv_paged_decode_num_splits(int num_seqs, int num_kv_heads, int head_dim,
+                                  int block_size, int max_context_len, int sliding_window,
+                                  int num_splits);
+
+/*
+ * fp8kv_paged_decode_workspace_size -- bytes of device workspace a decode with these
+ * arguments needs (0 on invalid arguments).  The workspace holds the fp32 split
+ * partials: num_seqs * num_q_heads * splits * (head_dim + 2) floats, rounded up.
+ */
+size_t fp8kv_paged_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int block_size, int max_context_len,
+                                         int sliding_window, int num_splits);
+
+/*
+ * fp8kv_paged_decode -- one decode step of GQA attention over the paged cache.
+ *
+ * For each sequence b and query head hq, with h = hq / g, L = min(context_lens[b],
+ * max_context_len, max_blocks_per_seq*block_size) and lo = (sliding_window > 0) ?
+ * max(0, L - sliding_window) : 0:
+ *   K_j = dequant(key_cache row of position j) * k_scale,  V_j likewise with v_scale,
+ *   s_j = q . K_j / sqrt(head_dim)  for j in [lo, L),
+ *   out = sum_j exp(s_j - max s) V_j / sum_j exp(s_j - max s);   out = 0 if L <= lo.
+ * (For FP8KV_BF16 caches K_j and V_j are the stored bf16 values and the scales are
+ * ignored.)  Arithmetic: fp8 -> bf16 conversion is exact; q.K and p.V products are
+ * formed on the matrix cores with fp32 accumulation; softmax statistics and all merges
+ * are fp32; p enters the p.V product as the sum of two bf16 values (about 16 significant
+ * bits).  The output is rounded to bf16 with round-to-nearest-even (or stored as f32).
+ *
+ *   out           device [num_seqs][num_q_heads][head_dim] of out_dtype (BF16 or F32)
+ *   query         device bf16 [num_seqs][num_q_heads][head_dim]
+ *   key_cache,
+ *   value_cache   device caches of cache_dtype (E4M3 or BF16), num_blocks blocks
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens  device int32 [num_seqs]
+ *   max_context_len  host upper bound on context_lens (sizes the grid and workspace)
+ *   sliding_window   0 = full attention, W > 0 = the last W positions
+ *   num_splits    0 = automatic, else requested split count (see above)
+ *   workspace     device buffer of at least fp8kv_paged_decode_workspace_size() bytes,
+ *                 256-byte aligned; may be NULL when that size is 0.  Its contents on
+ *                 entry do not matter; on return it holds the split partials.
+ */
+int fp8kv_paged_decode(void* out, int out_dtype, const void* query,
+                       const void* key_cache, const void* value_cache, int cache_dtype,
+                       const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* context_lens, int max_context_len,
+                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int block_size, int num_blocks,
+                       float k_scale, float v_scale, int sliding_window, int num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8kv_paged_decode_partial -- the first pass of fp8kv_paged_decode alone: writes the
+ * fp32 split partials (m, l, acc) of every (sequence, query head, split) into the
+ * workspace and nothing else.  Partials of different context ranges combine exactly
+ * like splits, so a sequence whose blocks are spread over several devices can run this
+ * pass per device, gather the partials, and finish with fp8kv_paged_decode_merge.
+ * Arguments as for fp8kv_paged_decode (v_scale is applied by the merge).  The partial
+ * m is kept in base-2 units: m = max_j s_j * log2(e).
+ */
+int fp8kv_paged_decode_partial(const void* query,
+                               const void* key_cache, const void* value_cache, int cache_dtype,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int max_context_len,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int num_blocks,
+                               float k_scale, int sliding_window, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8kv_paged_decode_merge -- the second pass: log-sum-exp merge of the split partials
+ * in the workspace, multiplication by v_scale, normalisation, and the store to `out`.
+ * Must be called with the same shape, window and num_splits arguments as the partial
+ * pass that filled the workspace, on the same stream (or after it completes).
+ */
+int fp8kv_paged_decode_merge(void* out, int out_dtype,
+                             const int32_t* context_lens, int max_context_len,
+                             int max_blocks_per_seq, int num_seqs, int num_q_heads,
+                             int num_kv_heads, int head_dim, int block_size,
+                             float v_scale, int sliding_window, int num_splits,
+                             const void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8KV_H */

@@ -248,9 +248,11 @@ def llama8b_long(context_len: int = 131072, scale_mode: str = "uncal", num_seqs:
                          scale_mode=scale_mode)
 
 
-def llama70b_needle(context_len: int, scale_mode: str = "amax") -> Workload:
-    """Llama-3.3-70B attention shape (64/8/128, g 8), batch 1, outliers and a planted needle."""
-    return make_workload(f"llama70b-needle-L{context_len}-{scale_mode}", 3,
+def llama70b_needle(context_len: int, scale_mode: str = "amax", variant: int = 0) -> Workload:
+    """Llama-3.3-70B attention shape (64/8/128, g 8), batch 1, outliers and a planted needle.
+
+    variant > 0 draws an independent replicate (seed family 3 + 10 * variant)."""
+    return make_workload(f"llama70b-needle-L{context_len}-{scale_mode}-v{variant}", 3 + 10 * variant,
                          num_q_heads=64, num_kv_heads=8, head_dim=128,
                          context_lens=[context_len], outlier_frac=0.01, scale_mode=scale_mode,
                          needle=True)

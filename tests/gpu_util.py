@@ -1,0 +1,140 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C-ABI binding and the CPU
+oracle on the same seeded inputs, and compare.  Imported only by tests marked `gpu`."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import fp8_kv_cache_reshape_amd as F
+import oracle
+import synthetic as syn
+
+DEV = "cuda"
+E4M3, BF16 = F.FP8KV_E4M3, F.FP8KV_BF16
+POISON = {E4M3: 0x7F, BF16: 0x7FC0}          # a NaN code / NaN bf16 in every untouched slot
+
+# Decode tolerance for bf16 outputs, elementwise: |gpu - oracle| <= ATOL + RTOL * |oracle|.
+ATOL, RTOL = 2e-3, 1e-2
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def code(layer: syn.Layer) -> int:
+    return E4M3 if layer.cache_dtype == syn.E4M3 else BF16
+
+
+def u16_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(DEV)
+
+
+def cache_numel(w: syn.Workload) -> int:
+    return w.num_blocks * w.num_kv_heads * w.block_size * w.head_dim
+
+
+def dev_caches(w: syn.Workload, cdt: int):
+    n = cache_numel(w)
+    if cdt == E4M3:
+        return (torch.full((n,), POISON[E4M3], dtype=torch.uint8, device=DEV),
+                torch.full((n,), POISON[E4M3], dtype=torch.uint8, device=DEV))
+    return (torch.full((n,), POISON[BF16], dtype=torch.int16, device=DEV),
+            torch.full((n,), POISON[BF16], dtype=torch.int16, device=DEV))
+
+
+def host_caches(w: syn.Workload, cdt: int):
+    n = cache_numel(w)
+    dt = np.uint8 if cdt == E4M3 else np.uint16
+    return np.full(n, POISON[cdt], dtype=dt), np.full(n, POISON[cdt], dtype=dt)
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def gpu_write(w: syn.Workload, layer: syn.Layer, kc, vc, rows=None, stream=None) -> None:
+    rows = np.arange(w.num_tokens) if rows is None else np.asarray(rows)
+    k, v = u16_dev(layer.k[rows]), u16_dev(layer.v[rows])
+    slots = torch.from_numpy(np.ascontiguousarray(w.slot_mapping[rows])).to(DEV)
+    F.fp8kv_cache_write(k, v, kc, vc, code(layer), slots, len(rows), w.num_kv_heads, w.head_dim,
+                        w.block_size, w.num_blocks, layer.k_scale, layer.v_scale, stream)
+
+
+def oracle_write(w: syn.Workload, layer: syn.Layer):
+    kc, vc = host_caches(w, code(layer))
+    oracle.cache_write(layer.k, layer.v, kc, vc, code(layer), w.slot_mapping, w.num_kv_heads,
+                       w.head_dim, w.block_size, w.num_blocks, layer.k_scale, layer.v_scale)
+    return kc, vc
+
+
+class DeviceInputs:
+    def __init__(self, w: syn.Workload, context_lens=None):
+        self.q = u16_dev(w.q)
+        self.bt = torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(DEV)
+        cl = w.context_lens if context_lens is None else context_lens
+        self.cl = torch.from_numpy(np.ascontiguousarray(cl, dtype=np.int32)).to(DEV)
+
+
+def gpu_decode(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_splits=0,
+               window=None, dev: DeviceInputs = None, max_context_len=None, split_api=False):
+    dev = dev or DeviceInputs(w)
+    win = layer.sliding_window if window is None else window
+    maxl = w.max_context_len if max_context_len is None else max_context_len
+    B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+    ws_bytes = F.fp8kv_paged_decode_workspace_size(B, Hq, Hkv, D, w.block_size, maxl, win, num_splits)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
+    out = torch.empty(B * Hq * D, dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
+    odt = F.FP8KV_F32 if out_f32 else F.FP8KV_BF16
+    cdt = code(layer)
+    if split_api:
+        F.fp8kv_paged_decode_partial(dev.q, kc, vc, cdt, dev.bt, w.max_blocks_per_seq, dev.cl, maxl,
+                                     B, Hq, Hkv, D, w.block_size, w.num_blocks, layer.k_scale, win,
+                                     num_splits, ws, ws_bytes)
+        F.fp8kv_paged_decode_merge(out, odt, dev.cl, maxl, w.max_blocks_per_seq, B, Hq, Hkv, D,
+                                   w.block_size, layer.v_scale if cdt == E4M3 else 1.0, win,
+                                   num_splits, ws, ws_bytes)
+    else:
+        F.fp8kv_paged_decode(out, odt, dev.q, kc, vc, cdt, dev.bt, w.max_blocks_per_seq, dev.cl, maxl,
+                             B, Hq, Hkv, D, w.block_size, w.num_blocks, layer.k_scale, layer.v_scale,
+                             win, num_splits, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D)
+
+
+def oracle_decode(w: syn.Workload, layer: syn.Layer, okc, ovc, pairs=None, window=None,
+                  context_lens=None):
+    win = layer.sliding_window if window is None else window
+    cl = w.context_lens if context_lens is None else context_lens
+    args = (w.q, okc, ovc, code(layer), w.block_tables, cl, w.num_q_heads, w.num_kv_heads,
+            w.head_dim, w.block_size, layer.k_scale, layer.v_scale, win)
+    if pairs is None:
+        return oracle.paged_decode(*args)
+    return oracle.paged_decode_pairs(pairs, *args)
+
+
+def assert_close(gpu: np.ndarray, ref: np.ndarray, atol=ATOL, rtol=RTOL, what=""):
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
+    err = np.abs(gpu - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = err > bound
+    if bad.any():
+        idx = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst at {idx}: "
+                             f"gpu {gpu[idx]!r} oracle {ref[idx]!r} (max abs err {err.max():.3g})")
+    return float(err.max())
+
+
+def sample_pairs(w: syn.Workload, n_per_seq: int = 3, seed: int = 0) -> np.ndarray:
+    """(b, hq) pairs: the first and last query head of every sequence plus random ones."""
+    rng = np.random.default_rng(seed)
+    pairs = []
+    for b in range(w.num_seqs):
+        heads = {0, w.num_q_heads - 1}
+        heads |= set(rng.integers(0, w.num_q_heads, n_per_seq).tolist())
+        pairs += [(b, h) for h in sorted(heads)]
+    return np.array(pairs, dtype=np.int32)

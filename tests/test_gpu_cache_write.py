@@ -1,0 +1,98 @@
+"""GPU parity of fp8kv_cache_write: cache bytes must equal the oracle's bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_cache_reshape_amd as F
+import oracle
+import synthetic as syn
+from gpu_util import (BF16, DEV, E4M3, dev_caches, gpu_write, host_caches, oracle_write, say,
+                      to_host_bits, u16_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _every_bf16_workload(Hkv=2, D=128, seed=0):
+    """Every bf16 bit pattern once as a key element and once (reversed) as a value element,
+    scattered to random slots of a pool with unused slots left poisoned."""
+    T = 65536 // (Hkv * D)
+    keys = np.arange(65536, dtype=np.uint16).reshape(T, Hkv, D)
+    vals = keys[::-1].reshape(T, Hkv, D).copy()
+    rng = np.random.default_rng(seed)
+    NB = T // 16 + 7
+    slots = rng.permutation(NB * 16)[:T].astype(np.int64)
+    w = syn.Workload(name="every-bf16", num_seqs=0, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D,
+                     block_size=16, num_blocks=NB, context_lens=np.zeros(0, np.int32),
+                     block_tables=np.zeros((0, 1), np.int32), seq_offsets=np.zeros(1, np.int64),
+                     slot_mapping=slots, q=np.zeros((0, Hkv, D), np.uint16), layers=[])
+    return w, keys, vals
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.125, 3.0), (0.1, 36.5 / 448.0),
+                                             (1e-3, 7.0), (4.40625 / 448.0, 0.0078125)])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_every_bf16_input_bit_exact(k_scale, v_scale, D):
+    say(f"cache_write every-bf16 D={D} scales={k_scale},{v_scale}")
+    w, keys, vals = _every_bf16_workload(D=D)
+    layer = syn.Layer(k=keys, v=vals, cache_dtype=syn.E4M3, k_scale=k_scale, v_scale=v_scale)
+    kc, vc = dev_caches(w, E4M3)
+    gpu_write(w, layer, kc, vc)
+    torch.cuda.synchronize()
+    okc, ovc = oracle_write(w, layer)
+    gk, gv = to_host_bits(kc), to_host_bits(vc)
+    bad_k, bad_v = np.nonzero(gk != okc)[0], np.nonzero(gv != ovc)[0]
+    assert bad_k.size == 0, f"key bytes differ at {bad_k[:8]}: gpu {gk[bad_k[:8]]} oracle {okc[bad_k[:8]]}"
+    assert bad_v.size == 0, f"value bytes differ at {bad_v[:8]}: gpu {gv[bad_v[:8]]} oracle {ovc[bad_v[:8]]}"
+
+
+def test_bf16_cache_keeps_bits():
+    say("cache_write bf16 cache")
+    w, keys, vals = _every_bf16_workload(Hkv=1, D=256, seed=3)
+    layer = syn.Layer(k=keys, v=vals, cache_dtype=syn.BF16, k_scale=1.0, v_scale=1.0)
+    kc, vc = dev_caches(w, BF16)
+    gpu_write(w, layer, kc, vc)
+    torch.cuda.synchronize()
+    okc, ovc = oracle_write(w, layer)
+    assert np.array_equal(to_host_bits(kc), okc) and np.array_equal(to_host_bits(vc), ovc)
+
+
+def test_out_of_range_slots_write_nothing():
+    say("cache_write out-of-range slots")
+    Hkv, D, NB = 2, 64, 3
+    k = torch.ones(4 * Hkv * D, dtype=torch.bfloat16, device=DEV)
+    kc = torch.full((NB * Hkv * 16 * D,), 0x5A, dtype=torch.uint8, device=DEV)
+    vc = torch.full_like(kc, 0x5A)
+    slots = torch.tensor([-1, -100, NB * 16, NB * 16 + 5], dtype=torch.int64, device=DEV)
+    F.fp8kv_cache_write(k, k, kc, vc, E4M3, slots, 4, Hkv, D, 16, NB, 1.0, 1.0)
+    torch.cuda.synchronize()
+    assert bool((kc == 0x5A).all()) and bool((vc == 0x5A).all())
+
+
+@pytest.mark.parametrize("make", [syn.tiny, lambda: syn.llama8b_batch("uncal", lens=[1, 17, 300, 4097]),
+                                  lambda: syn.llama8b_batch("amax", lens=[64, 1000]),
+                                  lambda: syn.gptoss_mixed(skip_sw=True, context_len=333, num_seqs=3),
+                                  lambda: syn.gemma_d256(context_len=1500, num_seqs=2)])
+def test_workload_caches_bit_exact(make):
+    w = make()
+    for layer in w.layers:
+        say(f"cache_write {w.name} layer {layer.name} ({layer.cache_dtype})")
+        kc, vc = dev_caches(w, E4M3 if layer.cache_dtype == syn.E4M3 else BF16)
+        gpu_write(w, layer, kc, vc)
+        torch.cuda.synchronize()
+        okc, ovc = oracle_write(w, layer)
+        assert np.array_equal(to_host_bits(kc), okc)
+        assert np.array_equal(to_host_bits(vc), ovc)
+
+
+def test_prefix_then_step_write_equals_one_write():
+    """Writing the context first and each sequence's last token afterwards (a decode step)
+    gives the same bytes as writing everything at once."""
+    say("cache_write prefix + step")
+    w = syn.llama8b_batch("amax", lens=[33, 200, 1])
+    layer = w.layers[0]
+    kc, vc = dev_caches(w, E4M3)
+    gpu_write(w, layer, kc, vc, rows=w.prefix_token_rows())
+    gpu_write(w, layer, kc, vc, rows=w.step_token_rows())
+    torch.cuda.synchronize()
+    okc, ovc = oracle_write(w, layer)
+    assert np.array_equal(to_host_bits(kc), okc) and np.array_equal(to_host_bits(vc), ovc)

@@ -1,0 +1,105 @@
+"""GPU parity at the measured workload sizes, in the launch configuration the benchmark uses
+(automatic split count unless stated), against the fp64 oracle on sampled (sequence, query
+head) outputs; cache bytes are compared in full.  Also the long-context checks: a planted
+needle key must be retrieved at 4K..256K, and the error must not grow with context length."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as syn
+from gpu_util import (BF16, E4M3, DeviceInputs, assert_close, dev_caches, gpu_decode, gpu_write,
+                      oracle_decode, oracle_write, sample_pairs, say, to_host_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer_parity(w, layer, pairs, num_splits_list=(0,), out_f32=False, check_cache=True):
+    cdt = E4M3 if layer.cache_dtype == syn.E4M3 else BF16
+    kc, vc = dev_caches(w, cdt)
+    gpu_write(w, layer, kc, vc)
+    okc, ovc = oracle_write(w, layer)
+    if check_cache:
+        assert np.array_equal(to_host_bits(kc), okc), f"{w.name}/{layer.name}: key cache bytes differ"
+        assert np.array_equal(to_host_bits(vc), ovc), f"{w.name}/{layer.name}: value cache bytes differ"
+    ref = oracle_decode(w, layer, okc, ovc, pairs=pairs)
+    dev = DeviceInputs(w)
+    results = {}
+    for ns in num_splits_list:
+        got = gpu_decode(w, layer, kc, vc, out_f32=out_f32, num_splits=ns, dev=dev)
+        sel = got[pairs[:, 0], pairs[:, 1]]
+        results[ns] = (sel, ref)
+        if not out_f32:
+            assert_close(sel, ref, what=f"{w.name}/{layer.name} splits={ns}")
+        assert np.all(np.isfinite(got)), "non-finite output somewhere in the batch"
+    del kc, vc
+    torch.cuda.empty_cache()
+    return results
+
+
+def test_tiny_all_heads():
+    w = syn.tiny()
+    say(f"workload {w.name}")
+    pairs = np.array([(0, h) for h in range(w.num_q_heads)], np.int32)
+    _layer_parity(w, w.layers[0], pairs)
+
+
+@pytest.mark.parametrize("scale_mode", ["uncal", "amax"])
+def test_llama8b_batch8_16k_24k(scale_mode):
+    w = syn.llama8b_batch(scale_mode)
+    say(f"workload {w.name} lens={w.context_lens.tolist()}")
+    _layer_parity(w, w.layers[0], sample_pairs(w, 2))
+
+
+def test_llama8b_headline_128k():
+    w = syn.llama8b_long(131072, "amax")
+    say(f"workload {w.name}")
+    _layer_parity(w, w.layers[0], sample_pairs(w, 6))
+
+
+@pytest.mark.parametrize("skip_sw", [False, True])
+def test_gptoss_mixed_layers(skip_sw):
+    w = syn.gptoss_mixed(skip_sw=skip_sw)
+    for layer in w.layers:
+        say(f"workload {w.name} layer {layer.name} ({layer.cache_dtype}, window {layer.sliding_window})")
+        _layer_parity(w, layer, sample_pairs(w, 2))
+
+
+def test_d256_global_and_window_layers():
+    w = syn.gemma_d256()
+    for layer in w.layers:
+        say(f"workload {w.name} layer {layer.name} (window {layer.sliding_window})")
+        _layer_parity(w, layer, sample_pairs(w, 1), num_splits_list=(0, 4, 8, 16))
+
+
+def _needle_case(L, variant=0):
+    w = syn.llama70b_needle(L, variant=variant)
+    layer = w.layers[0]
+    pairs = np.array([(0, 0), (0, 7), (0, 8), (0, 33), (0, 63)], np.int32)
+    res = _layer_parity(w, layer, pairs, out_f32=True, check_cache=(variant == 0))
+    got, ref = res[0]
+    return w, got, ref
+
+
+@pytest.mark.parametrize("L", [4096, 32768, 131072, 262144])
+def test_needle_retrieved(L):
+    w, got, ref = _needle_case(L)
+    say(f"needle L={L}: channel {w.needle['channel']} at position {w.needle['position']}")
+    c = w.needle["channel"]
+    assert int(np.argmax(ref[0])) == c, "the oracle itself does not retrieve the needle"
+    assert int(np.argmax(got[0])) == c, f"needle not retrieved at L={L}"
+    assert_close(got, ref, atol=2e-4, rtol=2e-3, what=f"needle f32 L={L}")
+
+
+def test_error_flat_from_4k_to_256k():
+    """e(L) = max|gpu - oracle| / max|oracle| over sampled heads, f32 output, median of 3
+    replicates; e(256K) must stay within 1.5x of e(4K)."""
+    def e(L):
+        vals = []
+        for v in range(3):
+            _, got, ref = _needle_case(L, variant=v)
+            vals.append(np.abs(got - ref).max() / np.abs(ref).max())
+        return float(np.median(vals)), vals
+    e4, v4 = e(4096)
+    e256, v256 = e(262144)
+    say(f"normalised error e(4K)={e4:.3g} {v4}  e(256K)={e256:.3g} {v256}")
+    assert e256 <= 1.5 * e4, f"error grew from {e4:.3g} at 4K to {e256:.3g} at 256K"
