@@ -14,7 +14,7 @@ using fp8kv::kBlockSize;
 using fp8kv::kMaxGroup;
 using fp8kv::kMaxSplits;
 
-constexpr int kTargetWorkgroups = 1024;   // about 4 decode workgroups per compute unit
+constexpr int kTargetWorkgroups = 256;    // one long-lived decode workgroup per compute unit
 constexpr int kMinBlocksPerSplit = 16;    // one wave step (4 blocks) for each of 4 waves
 
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
@@ -117,7 +117,7 @@ int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const voi
             return FP8KV_ERR_NULL;
         if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
             return FP8KV_ERR_SHAPE;
-        if (max_blocks_per_seq == 0 && max_context_len > 0) return FP8KV_ERR_SHAPE;
+        if ((max_blocks_per_seq == 0 || num_blocks == 0) && max_context_len > 0) return FP8KV_ERR_SHAPE;
     }
     const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, sliding_window, num_splits);
     const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits);

@@ -54,14 +54,14 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
     const int64_t th = gid / CHUNKS;              // token * Hkv + head
     const int h = (int)(th % p.num_kv_heads);
     const int64_t t = th / p.num_kv_heads;
+    // the row loads do not depend on the slot: issue them together with the slot load
+    const uint4 xk = *reinterpret_cast<const uint4*>(p.key + th * D + c * 8);
+    const uint4 xv = *reinterpret_cast<const uint4*>(p.value + th * D + c * 8);
     const int64_t slot = p.slot_mapping[t];
     if (slot < 0 || slot >= (int64_t)p.num_blocks * kBlockSize) return;
     const int64_t blk = slot / kBlockSize;
     const int off = (int)(slot % kBlockSize);
     const int64_t tile = (blk * p.num_kv_heads + h) * (int64_t)kBlockSize * D;   // elements
-
-    const uint4 xk = *reinterpret_cast<const uint4*>(p.key + th * D + c * 8);
-    const uint4 xv = *reinterpret_cast<const uint4*>(p.value + th * D + c * 8);
     if constexpr (FP8) {
         uint8_t* kc = static_cast<uint8_t*>(p.key_cache);
         uint8_t* vc = static_cast<uint8_t*>(p.value_cache);

@@ -9,7 +9,16 @@ namespace fp8kv {
 
 constexpr int kBlockSize = 16;     // tokens per cache block (the only supported size)
 constexpr int kMaxGroup = 16;      // query heads per kv head: one MFMA column tile
-constexpr int kDecodeWaves = 4;    // waves per decode workgroup
+#ifndef FP8KV_DECODE_WAVES
+#define FP8KV_DECODE_WAVES 4
+#endif
+#ifndef FP8KV_HEADS_FASTEST
+#define FP8KV_HEADS_FASTEST 0
+#endif
+constexpr int kDecodeWaves = FP8KV_DECODE_WAVES;   // waves per decode workgroup
+// Grid order of the partial pass: 1 puts the kv heads of one split next to each other in
+// dispatch order (the tiles of all heads of a cache block are adjacent in memory).
+constexpr bool kHeadsFastest = FP8KV_HEADS_FASTEST != 0;
 constexpr int kMaxSplits = 1024;   // upper bound on context splits per (seq, kv head)
 
 struct CacheWriteParams {

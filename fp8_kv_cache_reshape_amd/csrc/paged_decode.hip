@@ -6,10 +6,15 @@
 // Capacity Gains and Accuracy Risk", "Attention backend interactions"), grouped-query
 // heads sharing one kv head (page "ctx-fp8-kv-cache-long-context-accuracy",
 // "Arithmetic intensity").  The context is cut into fixed-size splits whose fp32
-// partials (m, l, acc) are merged by log-sum-exp in a second pass: partial sums stay in
-// real fp32 registers at both levels, the two-level accumulation the pages credit with
-// keeping 100K+ contractions accurate (page "The State of FP8 KV-Cache and Attention
-// Quantization in vLLM", "ACCURACY AT LONG CONTEXT").
+// partials (m, l, acc) are merged by log-sum-exp in a second pass.
+//
+// Two-level accumulation (page "The State of FP8 KV-Cache and Attention Quantization in
+// vLLM", "ACCURACY AT LONG CONTEXT": long contractions need partial sums moved out of
+// the matrix-core accumulator into real fp32 registers).  Here the matrix-core
+// accumulator only ever sums a bounded chunk of tokens (kFlushSteps wave steps); each
+// chunk is then added into a running fp32 pair (hi, lo) with an error-free TwoSum, and
+// the split partials are merged with the same compensated sum.  The rounding error of
+// the result therefore does not grow with the context length.
 //
 // Work mapping (pass 1).  A workgroup of 4 waves owns one (split, kv head, sequence).
 // Each wave step covers 4 consecutive cache blocks = 64 tokens, and both products run on
@@ -21,14 +26,20 @@
 //               4s..4s+3, head n; over s = 0..3 a lane owns all 16 tokens of one block.
 //               The 32-channel contraction slot of lane group grp is channels
 //               [grp*D/4 + 8kk, +8): every lane reads D/4 contiguous key bytes per row.
-//   O += P.V  : A = 16 heads x 32 tokens (the lane's own probabilities, rounded to
-//               bf16), B = 32 tokens x 16 channels.  The contraction slot of lane group
-//               grp is (block grp, tokens 8u..8u+7), exactly the 8 value bytes that one
-//               channel row of a channel-major value tile holds there, so each lane loads
-//               one 16-byte row per 16-channel output tile and no LDS transpose is needed.
+//   O += P.V  : A = 16 heads x 32 tokens (the lane's own probabilities), B = 32 tokens x
+//               16 channels.  The contraction slot of lane group grp is (block grp,
+//               tokens 8u..8u+7), exactly the 8 value bytes that one channel row of a
+//               channel-major value tile holds there, so each lane loads one 16-byte row
+//               per 16-channel output tile and no LDS transpose is needed.
 // fp8 codes become bf16 exactly (E4M3 is a subset of bf16) with the native gfx950
 // conversion; k_scale/sqrt(d)*log2(e) scales the fp32 scores and v_scale is applied at
 // the final normalisation, since the hardware's scaled conversions only take powers of 2.
+//
+// Memory pipeline: the KV stream is read once, so it uses nontemporal 16-byte loads.  The
+// next step's key rows are requested as soon as the current S product has consumed the
+// key registers, and the next value rows as soon as P.V has consumed the value
+// registers, so every wave keeps a step of loads in flight while it computes, without a
+// second register buffer.  Block ids come from wave-uniform loads one step ahead.
 #include "internal.h"
 
 namespace fp8kv {
@@ -37,11 +48,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline bf16x8 bits_as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    uint4 u = make_uint4(a, b, c, d);
-    return __builtin_bit_cast(bf16x8, u);
-}
+constexpr int kFlushSteps = 4;         // wave steps summed in the matrix-core accumulator
+#ifndef FP8KV_PREFETCH
+#define FP8KV_PREFETCH 1
+#endif
+constexpr int kPrefetch = FP8KV_PREFETCH;   // wave steps of KV loads kept in flight
+constexpr float kRescaleLog2 = 8.0f;   // reference max moves only when a score exceeds it by 2^8
 
 // 8 E4M3 codes (bytes of lo then hi, in memory order) -> 8 bf16, exactly.
 __device__ inline bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
@@ -59,8 +73,29 @@ __device__ inline f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ inline uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Byte mask keeping tokens [lo, hi) of a 16-token row (element size 1 or 2 bytes);
-// returns the mask for the dword holding tokens [4k/es .. ) i.e. dword index k.
+// Streaming 16-byte load (the KV cache is read once per step).
+__device__ inline uint4 load16_stream(const void* p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
+// Knuth's TwoSum: s + e == a + b exactly (round-to-nearest, no reassociation).
+__device__ inline void two_sum(float a, float b, float& s, float& e) {
+    s = a + b;
+    const float bp = s - a;
+    const float ap = s - bp;
+    e = (a - ap) + (b - bp);
+}
+
+// Add x into the compensated pair (hi, lo).
+__device__ inline void comp_add(float& hi, float& lo, float x) {
+    float s, e;
+    two_sum(hi, x, s, e);
+    hi = s;
+    lo += e;
+}
+
+// Mask keeping tokens [lo, hi) of dword k of a 16-token row (element size 1 or 2 bytes).
 template <int ES>
 __device__ inline uint32_t token_mask_dword(int lo, int hi, int k) {
     uint32_t m = 0;
@@ -80,8 +115,15 @@ __device__ inline void store_out(void* out, int out_f32, int64_t idx, float v) {
         static_cast<__bf16*>(out)[idx] = (__bf16)v;   // round to nearest even
 }
 
+// Two waves per SIMD (<= 256 registers per lane) wherever the tile fits; head_dim 256 and
+// 2-byte caches need more and run one wave per SIMD.
 template <int D, bool FP8>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(DecodeParams p) {
+constexpr int partial_waves_per_eu() { return kPrefetch == 1 && ((D <= 128 && FP8) || D == 64) ? 2 : 1; }
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(64 * kDecodeWaves)
+__attribute__((amdgpu_waves_per_eu(partial_waves_per_eu<D, FP8>(), 8)))
+void decode_partial_kernel(DecodeParams p) {
     constexpr int ES = FP8 ? 1 : 2;               // bytes per cache element
     constexpr int DG = D / 4;                     // channels per lane group in S = K.q^T
     constexpr int KK = D / 32;                    // MFMA k-steps for S
@@ -91,11 +133,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(Decod
     constexpr int TILE_BYTES = kBlockSize * D * ES;
 
     extern __shared__ float lds[];
-    const int split = blockIdx.x;
-    const int h = blockIdx.y;
+    const int split = kHeadsFastest ? blockIdx.y : blockIdx.x;
+    const int h = kHeadsFastest ? blockIdx.x : blockIdx.y;
     const int b = blockIdx.z;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;
     const int grp = lane >> 4;
     const int G = p.num_q_heads / p.num_kv_heads;
@@ -126,159 +168,236 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(Decod
 
     const char* kcache = static_cast<const char*>(p.key_cache);
     const char* vcache = static_cast<const char*>(p.value_cache);
-    const int32_t* bt = p.block_tables + (int64_t)b * p.max_blocks_per_seq + w.blk0 + sb;
+    const int32_t* __restrict__ bt = p.block_tables + (int64_t)b * p.max_blocks_per_seq + w.blk0 + sb;
     const float sscale = p.score_scale;
+    const int nblk = se - sb;                     // blocks of this split
+    const int nsteps = (nblk + 3) >> 2;
 
-    float m_run = -INFINITY;     // running max of base-2 scores for head n
-    float l_run = 0.0f;          // this lane's share of the running softmax sum
-    f32x4 acc[NT];
+    // Physical ids of the 4 blocks of wave step `stp` (-1 past the split or out of range);
+    // the addresses are wave-uniform.  Lanes pick their key block (n/4) and their
+    // score/value block (grp).
+    auto step_ids = [&](int stp, int& kid, int& vid) {
+        int id[4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nsteps = (se - sb + 3) >> 2;
-    for (int st = wave; st < nsteps; st += kDecodeWaves) {
-        const int j0 = st * 4;
-        const int kb = j0 + (n >> 2);            // block of the key rows this lane loads
-        const int vb = j0 + grp;                 // block of this lane's scores and values
-        int kphys = (sb + kb < se) ? bt[kb] : -1;
-        int vphys = (sb + vb < se) ? bt[vb] : -1;
-        const bool kval = (unsigned)kphys < (unsigned)p.num_blocks;
-        const bool vval = (unsigned)vphys < (unsigned)p.num_blocks;
-
-        // ---- loads: key rows (4 rows x DG channels) and value rows (NT channel rows)
-        uint4 kr[4][K16];
-        uint4 vr[NT][V16];
-        {
-            const char* kt = kcache + ((int64_t)(kval ? kphys : 0) * p.num_kv_heads + h) * TILE_BYTES
-                             + (int64_t)((n & 3) * D + grp * DG) * ES;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int x = 0; x < K16; ++x)
-                    kr[s][x] = kval ? load16(kt + (int64_t)(4 * s) * D * ES + 16 * x) : make_uint4(0, 0, 0, 0);
-            const char* vt = vcache + ((int64_t)(vval ? vphys : 0) * p.num_kv_heads + h) * TILE_BYTES
-                             + (int64_t)n * kBlockSize * ES;
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int x = 0; x < V16; ++x)
-                    vr[t][x] = vval ? load16(vt + (int64_t)(16 * t) * kBlockSize * ES + 16 * x) : make_uint4(0, 0, 0, 0);
-        }
-
-        // ---- S = K.q^T on the matrix cores
-        f32x4 sc[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                bf16x8 a;
-                if constexpr (FP8) {
-                    const uint4 u = kr[s][kk >> 1];
-                    a = (kk & 1) ? e4m3x8_to_bf16x8(u.z, u.w) : e4m3x8_to_bf16x8(u.x, u.y);
-                } else {
-                    a = __builtin_bit_cast(bf16x8, kr[s][kk]);
-                }
-                c = mfma16x16x32(a, qop[kk], c);
-            }
-            sc[s] = c;
-        }
-
-        // ---- mask and scale: lane holds block vb, tokens 4s+r, head n
-        const int pos0 = (w.blk0 + sb + vb) * kBlockSize;
-        const int tlo = max(0, w.lo - pos0);
-        const int thi = min(kBlockSize, w.L - pos0);
-        float sv[16];
-        float mloc = -INFINITY;
+        for (int x = 0; x < 4; ++x) id[x] = (4 * stp + x < nblk) ? bt[4 * stp + x] : -1;
+        const int kq = n >> 2;
+        kid = kq == 0 ? id[0] : kq == 1 ? id[1] : kq == 2 ? id[2] : id[3];
+        vid = grp == 0 ? id[0] : grp == 1 ? id[1] : grp == 2 ? id[2] : id[3];
+        if ((unsigned)kid >= (unsigned)p.num_blocks) kid = -1;
+        if ((unsigned)vid >= (unsigned)p.num_blocks) vid = -1;
+    };
+    // Loads are unconditional (branch-free, so the compiler can count them in flight): a
+    // missing block (-1) reads block 0, which exists whenever any block can be valid, and
+    // its scores are masked and its values zeroed below.  kPrefetch register buffers
+    // rotate over the wave's steps, so kPrefetch steps of loads are in flight.
+    struct Buf {
+        uint4 k[4][K16];
+        uint4 v[NT][V16];
+        int kid, vid;
+    };
+    auto issue_k = [&](Buf& bf, int kid) {
+        const char* kt = kcache + ((int64_t)max(kid, 0) * p.num_kv_heads + h) * TILE_BYTES
+                         + (int64_t)((n & 3) * D + grp * DG) * ES;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = 4 * s + r;
-                const bool ok = vval && tok >= tlo && tok < thi;
-                const float x = ok ? sc[s][r] * sscale : -INFINITY;
-                sv[4 * s + r] = x;
-                mloc = fmaxf(mloc, x);
-            }
-        float mt = fmaxf(mloc, __shfl_xor(mloc, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // exp2(-inf) = 0
-        float pv[16];
-        float psum = 0.0f;
+            for (int x = 0; x < K16; ++x) bf.k[s][x] = load16_stream(kt + (int64_t)(4 * s) * D * ES + 16 * x);
+    };
+    auto issue_v = [&](Buf& bf, int vid) {
+        const char* vt = vcache + ((int64_t)max(vid, 0) * p.num_kv_heads + h) * TILE_BYTES
+                         + (int64_t)n * kBlockSize * ES;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            pv[k] = __builtin_amdgcn_exp2f(sv[k] - m_use);
-            psum += pv[k];
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int x = 0; x < V16; ++x) bf.v[t][x] = load16_stream(vt + (int64_t)(16 * t) * kBlockSize * ES + 16 * x);
+    };
 
-        // rescale the accumulators of heads 4grp..4grp+3 when any running max moved
-        if (__any(alpha != 1.0f)) {
-            float ar[4];
+    float m_use = -INFINITY;     // reference max of base-2 scores for head n
+    float l_chunk = 0.0f;        // this lane's softmax sum over the current chunk
+    float l_hi = 0.0f, l_lo = 0.0f;
+    f32x4 acc[NT];               // matrix-core accumulator of the current chunk
+    f32x4 run_hi[NT], run_lo[NT];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * grp + r);
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[t][r] *= ar[r];
-        }
-
-        // values of tokens outside [lo, L) in a partial block are zeroed so that a
-        // poisoned (NaN) slot never reaches the accumulator through p = 0
-        if (vval && (tlo > 0 || thi < kBlockSize)) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int x = 0; x < V16; ++x) {
-                    vr[t][x].x &= token_mask_dword<ES>(tlo, thi, 4 * x + 0);
-                    vr[t][x].y &= token_mask_dword<ES>(tlo, thi, 4 * x + 1);
-                    vr[t][x].z &= token_mask_dword<ES>(tlo, thi, 4 * x + 2);
-                    vr[t][x].w &= token_mask_dword<ES>(tlo, thi, 4 * x + 3);
-                }
-        }
-
-        // ---- O += P.V on the matrix cores.  p is carried as a bf16 pair hi + lo (about 16
-        // significant bits): a single bf16 would cost up to 2^-9 * sum p|V| of error, which
-        // short windows do not average away.  V is exact in bf16.
-        bf16x8 phi[2], plo[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = pv[8 * u + e];
-                const __bf16 hi = (__bf16)x;
-                phi[u][e] = hi;
-                plo[u][e] = (__bf16)(x - (float)hi);
-            }
-        }
+    for (int t = 0; t < NT; ++t) {
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        run_hi[t] = acc[t];
+        run_lo[t] = acc[t];
+    }
+    auto flush = [&]() {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                bf16x8 vb8;
-                if constexpr (FP8) {
-                    const uint4 v = vr[t][0];
-                    vb8 = u ? e4m3x8_to_bf16x8(v.z, v.w) : e4m3x8_to_bf16x8(v.x, v.y);
-                } else {
-                    vb8 = __builtin_bit_cast(bf16x8, vr[t][u]);
-                }
-                acc[t] = mfma16x16x32(phi[u], vb8, acc[t]);
-                acc[t] = mfma16x16x32(plo[u], vb8, acc[t]);
+            for (int r = 0; r < 4; ++r) {
+                float hs = run_hi[t][r], ls = run_lo[t][r];
+                comp_add(hs, ls, acc[t][r]);
+                run_hi[t][r] = hs;
+                run_lo[t][r] = ls;
             }
+            acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        comp_add(l_hi, l_lo, l_chunk);
+        l_chunk = 0.0f;
+    };
+
+    int chunk_steps = 0;
+    // One wave step over the 4 blocks of step `stp` held in `bf`; refills `bf` with step
+    // `nstp` (if it exists) as soon as each half of the buffer has been consumed.
+    auto process = [&](Buf& bf, int stp, int nstp) {
+        const bool more = nstp < nsteps;
+        int nkid = -1, nvid = -1;
+        if (more) step_ids(nstp, nkid, nvid);
+
+            // ---- S = K.q^T on the matrix cores
+            f32x4 sc[4];
+    #pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    bf16x8 a;
+                    if constexpr (FP8) {
+                        const uint4 u = bf.k[s][kk >> 1];
+                        a = (kk & 1) ? e4m3x8_to_bf16x8(u.z, u.w) : e4m3x8_to_bf16x8(u.x, u.y);
+                    } else {
+                        a = __builtin_bit_cast(bf16x8, bf.k[s][kk]);
+                    }
+                    c = mfma16x16x32(a, qop[kk], c);
+                }
+                sc[s] = c;
+            }
+            if (more) issue_k(bf, nkid);   // key registers are free again
+
+            // ---- mask and scale: lane holds block grp of the step, tokens 4s+r, head n
+            const bool vval = bf.vid >= 0;
+            const int pos0 = (w.blk0 + sb + 4 * stp + grp) * kBlockSize;
+            const int tlo = vval ? max(0, w.lo - pos0) : kBlockSize;   // missing block: no tokens
+            const int thi = vval ? min(kBlockSize, w.L - pos0) : 0;
+            float sv[16];
+            float mloc = -INFINITY;
+    #pragma unroll
+            for (int s = 0; s < 4; ++s)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = 4 * s + r;
+                    const bool ok = tok >= tlo && tok < thi;
+                    const float x = ok ? sc[s][r] * sscale : -INFINITY;
+                    sv[4 * s + r] = x;
+                    mloc = fmaxf(mloc, x);
+                }
+            float mt = fmaxf(mloc, __shfl_xor(mloc, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            // move the reference max only when a score exceeds it by more than 2^kRescaleLog2
+            // (or on the first valid scores): p = 2^(s - m_use) then stays below 2^8
+            const float m_new = (mt > m_use + kRescaleLog2 || m_use == -INFINITY) ? mt : m_use;
+            if (__any(m_new != m_use)) {
+                const float alpha = (m_use == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_use - m_new);
+                float ar[4];
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * grp + r);
+    #pragma unroll
+                for (int t = 0; t < NT; ++t)
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        acc[t][r] *= ar[r];
+                        run_hi[t][r] *= ar[r];
+                        run_lo[t][r] *= ar[r];
+                    }
+                l_chunk *= alpha;
+                l_hi *= alpha;
+                l_lo *= alpha;
+                m_use = m_new;
+            }
+            const float m_ref = (m_use == -INFINITY) ? 0.0f : m_use;
+            float pv[16];
+            float psum = 0.0f;
+    #pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                pv[k] = __builtin_amdgcn_exp2f(sv[k] - m_ref);   // exp2(-inf) = 0
+                psum += pv[k];
+            }
+            l_chunk += psum;
+
+            // values of tokens outside [lo, L) (partial or missing blocks) are zeroed so that a
+            // poisoned (NaN) slot never reaches the accumulator through p = 0
+            if (tlo > 0 || thi < kBlockSize) {
+    #pragma unroll
+                for (int t = 0; t < NT; ++t)
+    #pragma unroll
+                    for (int x = 0; x < V16; ++x) {
+                        bf.v[t][x].x &= token_mask_dword<ES>(tlo, thi, 4 * x + 0);
+                        bf.v[t][x].y &= token_mask_dword<ES>(tlo, thi, 4 * x + 1);
+                        bf.v[t][x].z &= token_mask_dword<ES>(tlo, thi, 4 * x + 2);
+                        bf.v[t][x].w &= token_mask_dword<ES>(tlo, thi, 4 * x + 3);
+                    }
+            }
+
+            // ---- O += P.V on the matrix cores.  p is carried as a bf16 pair hi + lo (about 16
+            // significant bits): a single bf16 would cost up to 2^-9 * sum p|V| of error, which
+            // short windows do not average away.  V is exact in bf16.
+            bf16x8 phi[2], plo[2];
+    #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = pv[8 * u + e];
+                    const __bf16 hi = (__bf16)x;
+                    phi[u][e] = hi;
+                    plo[u][e] = (__bf16)(x - (float)hi);
+                }
+            }
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) {
+    #pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    bf16x8 vb8;
+                    if constexpr (FP8) {
+                        const uint4 v = bf.v[t][0];
+                        vb8 = u ? e4m3x8_to_bf16x8(v.z, v.w) : e4m3x8_to_bf16x8(v.x, v.y);
+                    } else {
+                        vb8 = __builtin_bit_cast(bf16x8, bf.v[t][u]);
+                    }
+                    acc[t] = mfma16x16x32(phi[u], vb8, acc[t]);
+                    acc[t] = mfma16x16x32(plo[u], vb8, acc[t]);
+                }
+            }
+        if (more) issue_v(bf, nvid);   // value registers are free again
+        bf.kid = nkid;
+        bf.vid = nvid;
+        if (++chunk_steps == kFlushSteps) {
+            flush();
+            chunk_steps = 0;
+        }
+    };
+
+    Buf buf[kPrefetch];
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) {
+        const int stp = wave + j * kDecodeWaves;
+        buf[j].kid = buf[j].vid = -1;
+        if (stp < nsteps) {
+            step_ids(stp, buf[j].kid, buf[j].vid);
+            issue_k(buf[j], buf[j].kid);
+            issue_v(buf[j], buf[j].vid);
         }
     }
+    for (int st = wave; st < nsteps; st += kPrefetch * kDecodeWaves) {
+#pragma unroll
+        for (int j = 0; j < kPrefetch; ++j) {
+            const int stp = st + j * kDecodeWaves;
+            if (stp < nsteps) process(buf[j], stp, stp + kPrefetch * kDecodeWaves);
+        }
+    }
+    flush();
 
     // ---- combine the waves of this workgroup in LDS
-    float l_tot = l_run + __shfl_xor(l_run, 16);
+    float l_tot = l_hi + l_lo;
+    l_tot += __shfl_xor(l_tot, 16);
     l_tot += __shfl_xor(l_tot, 32);
     float* sm_m = lds;                           // [waves][16]
     float* sm_l = lds + kDecodeWaves * 16;       // [waves][16]
     float* sm_a = lds + 2 * kDecodeWaves * 16;   // [waves][G][D]
     if (grp == 0) {
-        sm_m[wave * 16 + n] = m_run;
+        sm_m[wave * 16 + n] = m_use;
         sm_l[wave * 16 + n] = l_tot;
     }
 #pragma unroll
@@ -286,7 +405,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(Decod
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int head = 4 * grp + r;
-            if (head < G) sm_a[(wave * G + head) * D + 16 * t + n] = acc[t][r];
+            if (head < G) sm_a[(wave * G + head) * D + 16 * t + n] = run_hi[t][r] + run_lo[t][r];
         }
     __syncthreads();
 
@@ -297,13 +416,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(Decod
 #pragma unroll
         for (int v = 0; v < kDecodeWaves; ++v) M = fmaxf(M, sm_m[v * 16 + head]);
         const float Mu = (M == -INFINITY) ? 0.0f : M;
-        float lam = 0.0f, a = 0.0f;
+        float lam = 0.0f, lam_c = 0.0f, a = 0.0f, a_c = 0.0f;
 #pragma unroll
         for (int v = 0; v < kDecodeWaves; ++v) {
             const float wv = __builtin_amdgcn_exp2f(sm_m[v * 16 + head] - Mu);
-            lam += wv * sm_l[v * 16 + head];
-            a += wv * sm_a[(v * G + head) * D + i];
+            comp_add(lam, lam_c, wv * sm_l[v * 16 + head]);
+            comp_add(a, a_c, wv * sm_a[(v * G + head) * D + i]);
         }
+        lam += lam_c;
+        a += a_c;
         if (p.write_final) {
             store_out(p.out, p.out_f32, out_row0 + (int64_t)head * D + i,
                       lam > 0.0f ? p.v_scale * a / lam : 0.0f);
@@ -318,52 +439,98 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(Decod
     }
 }
 
-// Pass 2: log-sum-exp merge of one (sequence, query head) over its splits.
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
-    constexpr int NSUB = 256 / D;                // threads per channel
-    __shared__ float s_w[kMaxSplits];            // per-split weight exp2(m_s - M) / Lambda
-    __shared__ float s_part[256];
+// Pass 2: log-sum-exp merge of one (sequence, query head, 64-channel chunk) over its
+// splits, with compensated sums so the merge error does not grow with the split count.
+// 256 threads = 16 split lanes x 16 channel quads; each thread reads float4 partials.  The
+// first kMergeBatch partials of every thread and their (m, l) are requested together,
+// before the block-wide max, so a merge over up to 16 * kMergeBatch splits costs one
+// round trip to memory.
+constexpr int kMergeBatch = 4;
+
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D) {
+    __shared__ float s_red[2][4];
+    __shared__ float4 s_part[16][16][2];         // [split lane][channel quad][hi, lo]
     const int hq = blockIdx.x;
     const int b = blockIdx.y;
+    const int chunk = blockIdx.z;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int q = tid & 15;                      // channel quad: channels chunk*64 + 4q .. +3
+    const int sl = tid >> 4;                     // split lane: splits sl, sl + 16, ...
     const SeqWindow w = seq_window(p.context_lens[b], p.max_context_len, p.max_blocks_per_seq,
                                    p.sliding_window);
     const int ns = (w.nblk + p.blocks_per_split - 1) / p.blocks_per_split;
     const int64_t row0 = ((int64_t)b * p.num_q_heads + hq) * p.splits;
-    const int64_t out_idx = ((int64_t)b * p.num_q_heads + hq) * D;
+    const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row0;
+    const float* accp = p.ws_acc + row0 * D + chunk * 64 + 4 * q;
 
-    if (tid < 64) {
-        float M = -INFINITY;
-        for (int s = tid; s < ns; s += 64) M = fmaxf(M, p.ws_ml[(row0 + s) * 2]);
+    float4 x[kMergeBatch];
+    float2 mv[kMergeBatch];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        const float Mu = (M == -INFINITY) ? 0.0f : M;
-        float lam = 0.0f;
-        for (int s = tid; s < ns; s += 64) {
-            const float wv = __builtin_amdgcn_exp2f(p.ws_ml[(row0 + s) * 2] - Mu);
-            s_w[s] = wv;
-            lam += wv * p.ws_ml[(row0 + s) * 2 + 1];
+    for (int u = 0; u < kMergeBatch; ++u) {
+        const int s = sl + 16 * u;
+        x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        mv[u] = make_float2(-INFINITY, 0.0f);
+        if (s < ns) {
+            x[u] = *reinterpret_cast<const float4*>(accp + (int64_t)s * D);
+            mv[u] = ml[s];
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) lam += __shfl_xor(lam, o);
-        const float inv = lam > 0.0f ? p.v_scale / lam : 0.0f;
-        for (int s = tid; s < ns; s += 64) s_w[s] *= inv;
     }
+
+    // max of the split maxima
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) M = fmaxf(M, mv[u].x);
+    for (int s = sl + 16 * kMergeBatch; s < ns; s += 16) M = fmaxf(M, ml[s].x);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (lane == 0) s_red[0][wv] = M;
     __syncthreads();
+    M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+    const float Mu = (M == -INFINITY) ? 0.0f : M;
 
-    const int i = tid % D;
-    const int sub = tid / D;
-    float a = 0.0f;
-    for (int s = sub; s < ns; s += NSUB) a += s_w[s] * p.ws_acc[(row0 + s) * D + i];
-    if (NSUB > 1) {
-        s_part[tid] = a;
-        __syncthreads();
-        if (sub == 0) {
-            for (int k = 1; k < NSUB; ++k) a += s_part[k * D + i];
+    // weighted sums: acc over this thread's splits; Lambda = sum_s w_s l_s counted once per
+    // split (by the q == 0 thread of its split lane)
+    float4 hi = make_float4(0.f, 0.f, 0.f, 0.f), lo = hi;
+    float lh = 0.0f, ll = 0.0f;
+    auto add = [&](float4 v, float2 m) {
+        const float ws = __builtin_amdgcn_exp2f(m.x - Mu);   // 0 for an empty slot (m = -inf)
+        comp_add(hi.x, lo.x, ws * v.x);
+        comp_add(hi.y, lo.y, ws * v.y);
+        comp_add(hi.z, lo.z, ws * v.z);
+        comp_add(hi.w, lo.w, ws * v.w);
+        if (q == 0) comp_add(lh, ll, ws * m.y);
+    };
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) add(x[u], mv[u]);
+    for (int s = sl + 16 * kMergeBatch; s < ns; s += 16)
+        add(*reinterpret_cast<const float4*>(accp + (int64_t)s * D), ml[s]);
+
+    float lam = lh + ll;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lam += __shfl_xor(lam, o);
+    if (lane == 0) s_red[1][wv] = lam;
+    s_part[sl][q][0] = hi;
+    s_part[sl][q][1] = lo;
+    __syncthreads();
+    lam = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
+    const float scale = lam > 0.0f ? p.v_scale / lam : 0.0f;
+    if (tid < 64) {
+        const int qq = tid >> 2, comp = tid & 3;
+        float sh = 0.0f, sc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const float4 a = s_part[k][qq][0];
+            const float4 c = s_part[k][qq][1];
+            const float av = comp == 0 ? a.x : comp == 1 ? a.y : comp == 2 ? a.z : a.w;
+            const float cv = comp == 0 ? c.x : comp == 1 ? c.y : comp == 2 ? c.z : c.w;
+            comp_add(sh, sc, av);
+            sc += cv;
         }
+        const int ch = chunk * 64 + 4 * qq + comp;
+        store_out(p.out, p.out_f32, ((int64_t)b * p.num_q_heads + hq) * D + ch, scale * (sh + sc));
     }
-    if (sub == 0) store_out(p.out, p.out_f32, out_idx + i, a);
 }
 
 // Dynamic LDS of the partial kernel: per-wave (m, l) and the group's accumulators.
@@ -389,19 +556,14 @@ template <int D>
 hipError_t launch_partial_d(const DecodeParams& p, bool fp8, hipStream_t s) {
     const int G = p.num_q_heads / p.num_kv_heads;
     const size_t lds = partial_lds_bytes<D>(G);
-    const dim3 grid(p.splits, p.num_kv_heads, p.num_seqs);
+    const dim3 grid = kHeadsFastest ? dim3(p.num_kv_heads, p.splits, p.num_seqs)
+                                    : dim3(p.splits, p.num_kv_heads, p.num_seqs);
     const dim3 block(64 * kDecodeWaves);
     hipError_t e = fp8 ? allow_lds<D, true>() : allow_lds<D, false>();
     if (e != hipSuccess) return e;
     const void* fn = fp8 ? reinterpret_cast<const void*>(&decode_partial_kernel<D, true>)
                          : reinterpret_cast<const void*>(&decode_partial_kernel<D, false>);
     return launch_kernel(fn, grid, block, lds, s, p);
-}
-
-template <int D>
-hipError_t launch_merge_d(const DecodeParams& p, hipStream_t s) {
-    return launch_kernel(reinterpret_cast<const void*>(&decode_merge_kernel<D>),
-                         dim3(p.num_q_heads, p.num_seqs), dim3(256), 0, s, p);
 }
 
 }  // namespace
@@ -416,12 +578,12 @@ hipError_t launch_decode_partial(const DecodeParams& p, bool fp8, int head_dim, 
 }
 
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t s) {
-    switch (head_dim) {
-        case 64: return launch_merge_d<64>(p, s);
-        case 128: return launch_merge_d<128>(p, s);
-        case 256: return launch_merge_d<256>(p, s);
-        default: return hipErrorInvalidValue;
-    }
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256) return hipErrorInvalidValue;
+    const dim3 grid(p.num_q_heads, p.num_seqs, head_dim / 64);
+    int d = head_dim;
+    void* args[] = {const_cast<DecodeParams*>(&p), &d};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_merge_kernel), grid, dim3(256), args,
+                           0, s);
 }
 
 }  // namespace fp8kv

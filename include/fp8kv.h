@@ -152,6 +152,7 @@ size_t fp8kv_paged_decode_workspace_size(int num_seqs, int num_q_heads, int num_
  *   query         device bf16 [num_seqs][num_q_heads][head_dim]
  *   key_cache,
  *   value_cache   device caches of cache_dtype (E4M3 or BF16), num_blocks blocks
+ *                 (num_blocks >= 1 and max_blocks_per_seq >= 1 when max_context_len > 0)
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
  *   context_lens  device int32 [num_seqs]
  *   max_context_len  host upper bound on context_lens (sizes the grid and workspace)

@@ -90,14 +90,22 @@ def test_needle_retrieved(L):
     assert_close(got, ref, atol=2e-4, rtol=2e-3, what=f"needle f32 L={L}")
 
 
+def _normalised_error(got, ref):
+    """Largest per-output-vector relative error: for each sampled (sequence, query head),
+    max_i |gpu - oracle| / max_i |oracle|, then the maximum over the sampled heads.  The
+    normaliser is per head because output scales differ by head: the needle head's output
+    is dominated by the needle's value, whose weight shrinks with context length."""
+    return float((np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())
+
+
 def test_error_flat_from_4k_to_256k():
-    """e(L) = max|gpu - oracle| / max|oracle| over sampled heads, f32 output, median of 3
+    """e(L) = largest per-head normalised error over sampled heads, f32 output, median of 3
     replicates; e(256K) must stay within 1.5x of e(4K)."""
     def e(L):
         vals = []
         for v in range(3):
             _, got, ref = _needle_case(L, variant=v)
-            vals.append(np.abs(got - ref).max() / np.abs(ref).max())
+            vals.append(_normalised_error(got, ref))
         return float(np.median(vals)), vals
     e4, v4 = e(4096)
     e256, v256 = e(262144)
