@@ -3,10 +3,11 @@
 // Each element is divided by its tensor's scale in IEEE binary32 and cast once to OCP
 // E4M3 (page "FP8 KV Cache Quantization: Capacity Gains and Accuracy Risk", section
 // "Scales and calibration"); the bytes are scattered by slot into 16-token blocks
-// (same page, "Why the KV cache sets long-context capacity").  Keys land in token-major
-// tiles [block][kv_head][slot][dim]; values in channel-major tiles
-// [block][kv_head][dim][slot], the layout the decode kernel's P.V matrix-core operand
-// reads with one 16-byte load per lane.
+// (same page, "Why the KV cache sets long-context capacity").  Values land in
+// channel-major tiles [block][kv_head][dim][slot], the layout the decode kernel's P.V
+// matrix-core operand reads with one 16-byte load per lane.  Keys land in tiles of
+// 16-byte chunks ordered (slot quad, chunk, slot in quad, channel quarter), so that each
+// key load instruction of the decode kernel reads whole 256-byte runs of a tile.
 //
 // One thread handles 8 consecutive channels of one (token, kv head): a 16-byte bf16
 // load per tensor, eight f32 divisions, four packed conversions, an 8-byte key store
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
     if constexpr (FP8) {
         uint8_t* kc = static_cast<uint8_t*>(p.key_cache);
         uint8_t* vc = static_cast<uint8_t*>(p.value_cache);
-        *reinterpret_cast<uint2*>(kc + tile + (int64_t)off * D + c * 8) = quantize8(xk, p.k_scale);
+        *reinterpret_cast<uint2*>(kc + tile + key_chunk_offset<D, 1>(off, c * 8)) = quantize8(xk, p.k_scale);
         const uint2 qv = quantize8(xv, p.v_scale);
         uint8_t* vdst = vc + tile + (int64_t)(c * 8) * kBlockSize + off;
 #pragma unroll
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
     } else {
         uint16_t* kc = static_cast<uint16_t*>(p.key_cache);
         uint16_t* vc = static_cast<uint16_t*>(p.value_cache);
-        *reinterpret_cast<uint4*>(kc + tile + (int64_t)off * D + c * 8) = xk;
+        *reinterpret_cast<uint4*>(kc + tile + key_chunk_offset<D, 2>(off, c * 8) / 2) = xk;
         uint16_t* vdst = vc + tile + (int64_t)(c * 8) * kBlockSize + off;
         const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll

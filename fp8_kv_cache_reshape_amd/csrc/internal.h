@@ -79,6 +79,19 @@ __host__ __device__ inline SeqWindow seq_window(int ctx_len, int max_context_len
     return w;
 }
 
+// Byte offset, inside a key tile, of element (slot t, channel i) for D channels of ES bytes.
+// A key tile is 16 slots x D channels stored as 16-byte chunks ordered (slot quad t/4,
+// chunk c, slot t%4, channel quarter g): a decode wave's key load instruction then reads
+// 256 contiguous bytes per tile.  For D = 64, ES = 1 this is plain slot-major order.
+template <int D, int ES>
+__host__ __device__ constexpr int key_chunk_offset(int t, int i) {
+    constexpr int kQuarter = D / 4;           // channels per quarter
+    constexpr int kChunks = D * ES / 64;      // 16-byte chunks per quarter of one slot
+    const int g = i / kQuarter;
+    const int w = (i % kQuarter) * ES;        // byte within the quarter
+    return (((t / 4) * kChunks + w / 16) * 4 + t % 4) * 64 + g * 16 + w % 16;
+}
+
 // Launch a kernel whose only argument is a parameter struct and return the status of this
 // launch alone (hipGetLastError would also report errors other HIP users left behind).
 template <typename P>

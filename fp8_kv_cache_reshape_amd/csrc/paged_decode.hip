@@ -25,7 +25,8 @@
 //               the 16x16 result lands with lane l holding scores of block grp, tokens
 //               4s..4s+3, head n; over s = 0..3 a lane owns all 16 tokens of one block.
 //               The 32-channel contraction slot of lane group grp is channels
-//               [grp*D/4 + 8kk, +8): every lane reads D/4 contiguous key bytes per row.
+//               [grp*D/4 + 8kk, +8); key tiles are stored so that the 16-byte pieces
+//               one load instruction needs from a tile are 256 contiguous bytes.
 //   O += P.V  : A = 16 heads x 32 tokens (the lane's own probabilities), B = 32 tokens x
 //               16 channels.  The contraction slot of lane group grp is (block grp,
 //               tokens 8u..8u+7), exactly the 8 value bytes that one channel row of a
@@ -196,12 +197,14 @@ void decode_partial_kernel(DecodeParams p) {
         int kid, vid;
     };
     auto issue_k = [&](Buf& bf, int kid) {
+        // lane (n, grp) reads slot 4s + n%4, channels [grp*DG, +DG) of block n/4: chunk x of
+        // that row sits at key_chunk_offset(4s + n%4, grp*DG + 16x/ES)
         const char* kt = kcache + ((int64_t)max(kid, 0) * p.num_kv_heads + h) * TILE_BYTES
-                         + (int64_t)((n & 3) * D + grp * DG) * ES;
+                         + key_chunk_offset<D, ES>(n & 3, grp * DG);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int x = 0; x < K16; ++x) bf.k[s][x] = load16_stream(kt + (int64_t)(4 * s) * D * ES + 16 * x);
+            for (int x = 0; x < K16; ++x) bf.k[s][x] = load16_stream(kt + (s * K16 + x) * 256);
     };
     auto issue_v = [&](Buf& bf, int vid) {
         const char* vt = vcache + ((int64_t)max(vid, 0) * p.num_kv_heads + h) * TILE_BYTES

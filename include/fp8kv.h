@@ -36,10 +36,15 @@
  *   bf16 K/V rows written per token:  [num_tokens][num_kv_heads][head_dim]
  *   query:                            [num_seqs][num_q_heads][head_dim] bf16
  *   output:                           [num_seqs][num_q_heads][head_dim] bf16 or f32
- *   key_cache:    [num_blocks][num_kv_heads][block_size][head_dim]   (token-major tiles)
- *   value_cache:  [num_blocks][num_kv_heads][head_dim][block_size]   (channel-major tiles)
- *     elements are u8 E4M3 codes (FP8KV_E4M3) or bf16 (FP8KV_BF16).  Each
- *     (block, kv_head) tile is contiguous: block_size*head_dim elements.
+ *   key_cache, value_cache: [num_blocks][num_kv_heads] tiles of block_size*head_dim
+ *     elements (u8 E4M3 codes for FP8KV_E4M3, bf16 for FP8KV_BF16), each contiguous.
+ *     value tile: channel-major, element (slot t, channel i) at i*block_size + t.
+ *     key tile: 16-byte chunks ordered (slot quad, chunk, slot within quad, channel
+ *       quarter).  With e = element bytes, q = head_dim/4, g = i/q, w = (i%q)*e and
+ *       C = head_dim*e/64, element (t, i) starts at byte
+ *       ((t/4 * C + w/16) * 4 + t%4) * 64 + g*16 + w%16 of the tile.  (For head_dim 64
+ *       with E4M3 this is plain slot-major order.)  Both orders let one 16-byte load
+ *       per lane feed the decode kernel's matrix-core operands with whole cache lines.
  *   slot_mapping: int64 [num_tokens]; token t goes to block slot/block_size, row
  *     slot%block_size.
  *   block_tables: int32 [num_seqs][max_blocks_per_seq]; logical block n of sequence b

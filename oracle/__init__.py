@@ -134,6 +134,7 @@ def cache_write(key, value, key_cache: np.ndarray, value_cache: np.ndarray, cach
     sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
     T = sm.shape[0]
     assert k.size == T * num_kv_heads * head_dim and v.size == k.size
+    assert head_dim % 4 == 0 and block_size == 16, "the paged layout needs head_dim % 4 == 0, 16-slot blocks"
     want = np.uint8 if cache_dtype == CACHE_E4M3 else np.uint16
     for c in (key_cache, value_cache):
         assert c.dtype == want and c.flags["C_CONTIGUOUS"]
@@ -160,6 +161,7 @@ def attention_rows(q, K, V) -> np.ndarray:
 
 def _decode_common(q, key_cache, value_cache, cache_dtype, block_tables, context_lens):
     q = np.ascontiguousarray(q, dtype=np.uint16)
+    assert q.shape[-1] % 4 == 0, "the paged layout needs head_dim % 4 == 0"
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     cl = np.ascontiguousarray(context_lens, dtype=np.int32)
     want = np.uint8 if cache_dtype == CACHE_E4M3 else np.uint16

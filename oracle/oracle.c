@@ -26,10 +26,16 @@
  *     infinities) saturate to 448; NaN keeps its sign [CAP "Scales and
  *     calibration"]; rounding and saturation are not stated on the pages.
  *   - decoding multiplies the code's value by the same scale.
- *   - paged layout: key tiles are token-major  [block][kv_head][slot][dim],
- *     value tiles are channel-major            [block][kv_head][dim][slot].
- *     The pages fix only that the cache is held in fixed-size blocks
- *     [CAP "Why the KV cache sets long-context capacity"].
+ *   - paged layout: one tile per (block, kv_head), tiles ordered [block][kv_head].
+ *     Value tiles are channel-major: element (slot t, dim i) at i*bs + t.  Key tiles
+ *     are 16-byte chunks ordered (slot quad, chunk, slot within quad, dim quarter):
+ *     element (t, i) at byte ((t/4 * C + c) * 4 + t%4) * 4K + g*K + w%K, where
+ *     g = i / (D/4), w = (i % (D/4)) * elem_bytes, K = min(16, D*elem_bytes/4) is the
+ *     chunk size, c = w / K and C = D*elem_bytes/(4K).  (K = 16 for every head_dim the
+ *     library supports; when the quarter is at most 16 bytes, e.g. D = 64 with 1-byte
+ *     elements, this is plain token-major.)  The pages fix
+ *     only that the cache is held in fixed-size blocks [CAP "Why the KV cache sets
+ *     long-context capacity"].
  *   - query head hq reads kv head hq / g, g = Hq / Hkv (contiguous groups);
  *     the pages name only the group ratio g [FLOPS "Arithmetic intensity"].
  *   - positions attended: [lo, L) with lo = max(0, L - W) for a window W > 0,
@@ -135,9 +141,17 @@ void oracle_div_f32_n(const float* x, float scale, float* out, int64_t n) {
 
 /* ------------------------------------------------------- paged layout --- */
 
-/* Byte/element offset of (block, kv_head, slot, dim) in a key cache. */
-static int64_t key_index(int64_t blk, int h, int off, int i, int Hkv, int bs, int D) {
-    return ((blk * Hkv + h) * (int64_t)bs + off) * (int64_t)D + i;
+/* Element offset of (block, kv_head, slot, dim) in a key cache whose elements take
+ * `eb` bytes (1 for e4m3, 2 for bf16); see the layout note at the top. */
+static int64_t key_index(int64_t blk, int h, int off, int i, int Hkv, int bs, int D, int eb) {
+    int q = D / 4;                     /* dims per quarter (D is a multiple of 4) */
+    int g = i / q;                     /* quarter */
+    int w = (i % q) * eb;              /* byte within the quarter's part of the row */
+    int K = q * eb < 16 ? q * eb : 16; /* chunk bytes: 16, or the whole quarter if smaller */
+    int C = q * eb / K;                /* chunks per quarter */
+    int c = w / K;
+    int64_t byte_in_tile = ((int64_t)((off / 4) * C + c) * 4 + off % 4) * (4 * K) + g * K + w % K;
+    return (blk * Hkv + h) * (int64_t)bs * D + byte_in_tile / eb;
 }
 /* Offset of (block, kv_head, slot, dim) in a value cache (channel-major tile). */
 static int64_t value_index(int64_t blk, int h, int off, int i, int Hkv, int bs, int D) {
@@ -150,7 +164,8 @@ static int64_t value_index(int64_t blk, int h, int off, int i, int Hkv, int bs, 
  * Quantise-on-write [CAP "Scales and calibration"] and scatter by slot into
  * paged blocks [CAP "Why the KV cache sets long-context capacity"].
  *   key, value    bf16 [T][Hkv][D]
- *   key_cache     [NB][Hkv][bs][D], value_cache [NB][Hkv][D][bs], elements of
+ *   key_cache     [NB][Hkv] chunked key tiles, value_cache [NB][Hkv][D][bs] (layout
+ *                 note at the top; bs = 16), elements of
  *                 cache_dtype (u8 e4m3 codes, or bf16 kept as-is: the native-
  *                 dtype variant used for skipped sliding-window layers,
  *                 [FLOPS "Workarounds"]; scales are not applied to it)
@@ -170,7 +185,8 @@ void oracle_cache_write(const uint16_t* key, const uint16_t* value,
             for (int i = 0; i < D; ++i) {
                 uint16_t xk = key[((int64_t)t * Hkv + h) * D + i];
                 uint16_t xv = value[((int64_t)t * Hkv + h) * D + i];
-                int64_t ki = key_index(blk, h, off, i, Hkv, bs, D);
+                int64_t ki = key_index(blk, h, off, i, Hkv, bs, D,
+                                       cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2);
                 int64_t vi = value_index(blk, h, off, i, Hkv, bs, D);
                 if (cache_dtype == ORACLE_CACHE_E4M3) {
                     ((uint8_t*)key_cache)[ki] = oracle_quantize(xk, k_scale);
@@ -245,6 +261,7 @@ void oracle_paged_decode_head(double* out, const uint16_t* q,
     int64_t L = context_lens[b];
     int64_t lo = (window > 0 && L > window) ? L - window : 0;
     int64_t n = L > lo ? L - lo : 0;
+    int eb = cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2;
     double* qv = (double*)malloc(sizeof(double) * (size_t)D);
     double* K = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
     double* V = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
@@ -255,7 +272,7 @@ void oracle_paged_decode_head(double* out, const uint16_t* q,
         int off = (int)(j % bs);
         for (int i = 0; i < D; ++i) {
             K[(j - lo) * D + i] = cache_value(key_cache, cache_dtype,
-                                              key_index(pb, h, off, i, Hkv, bs, D), k_scale);
+                                              key_index(pb, h, off, i, Hkv, bs, D, eb), k_scale);
             V[(j - lo) * D + i] = cache_value(value_cache, cache_dtype,
                                               value_index(pb, h, off, i, Hkv, bs, D), v_scale);
         }

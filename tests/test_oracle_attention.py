@@ -23,6 +23,33 @@ def _dec(codes):
     return t.to(torch.float64).numpy()
 
 
+def key_tile_offset(t, i, D, eb):
+    """Element offset inside a key tile (16 slots x D channels): 16-byte chunks ordered
+    (slot quad, chunk, slot within quad, channel quarter), as the library header states."""
+    q = D // 4
+    g = i // q
+    w = (i % q) * eb
+    K = min(16, q * eb)
+    C = q * eb // K
+    byte = (((t // 4) * C + w // K) * 4 + t % 4) * (4 * K) + g * K + w % K
+    return byte // eb
+
+
+def test_key_tile_layout_is_a_bijection_and_token_major_at_d64():
+    for D in (8, 16, 64, 128, 256):
+        for eb in (1, 2):
+            t = np.arange(16)[:, None]
+            i = np.arange(D)[None, :]
+            off = key_tile_offset(t, i, D, eb)
+            assert sorted(off.reshape(-1).tolist()) == list(range(16 * D))
+    t = np.arange(16)[:, None]
+    i = np.arange(64)[None, :]
+    assert np.array_equal(key_tile_offset(t, i, 64, 1), t * 64 + i)
+    # a 16-byte chunk holds consecutive channels of one slot
+    off = key_tile_offset(np.full(16, 5), np.arange(32, 48), 128, 1)
+    assert np.array_equal(np.diff(off), np.ones(15))
+
+
 class Paged:
     """A tiny hand-built paged cache: sequences laid out with an explicit block table."""
 
@@ -73,7 +100,8 @@ class Paged:
         blk = self.bt[b, j // self.bs].astype(np.int64)
         off = j % self.bs
         i = np.arange(self.D)
-        kidx = ((blk[:, None] * self.Hkv + h) * self.bs + off[:, None]) * self.D + i[None, :]
+        kidx = blk[:, None] * self.Hkv * self.bs * self.D + h * self.bs * self.D + \
+            key_tile_offset(off[:, None], i[None, :], self.D, 1 if self.cache_dtype == E4M3 else 2)
         vidx = ((blk[:, None] * self.Hkv + h) * self.D + i[None, :]) * self.bs + off[:, None]
         if self.cache_dtype == E4M3:
             return _dec(self.kc[kidx]) * self.k_scale, _dec(self.vc[vidx]) * self.v_scale
@@ -167,9 +195,9 @@ def test_tiny_cases_against_60_digit_decimal(oracle_mod):
 
 # ------------------------------------------------------------- paged ----
 
-@pytest.mark.parametrize("cache_dtype", [E4M3, BF16])
-def test_paged_equals_rows_gathered_by_test(oracle_mod, cache_dtype):
-    P = Paged(oracle_mod, [1, 15, 16, 17, 50], Hq=6, Hkv=2, D=8, cache_dtype=cache_dtype)
+@pytest.mark.parametrize("cache_dtype,D", [(E4M3, 8), (BF16, 8), (E4M3, 128), (BF16, 64)])
+def test_paged_equals_rows_gathered_by_test(oracle_mod, cache_dtype, D):
+    P = Paged(oracle_mod, [1, 15, 16, 17, 50], Hq=6, Hkv=2, D=D, cache_dtype=cache_dtype)
     out = P.decode()
     g = P.Hq // P.Hkv
     for b in range(len(P.lens)):
@@ -276,8 +304,9 @@ def test_tail_poison_is_never_read(oracle_mod):
 
 # -------------------------------------------------------- cache write ----
 
-def test_cache_write_hand_layout(oracle_mod):
-    Hkv, D, bs, NB = 2, 4, 16, 4
+@pytest.mark.parametrize("D", [4, 128])
+def test_cache_write_hand_layout(oracle_mod, D):
+    Hkv, bs, NB = 2, 16, 4
     rng = np.random.default_rng(12)
     k = syn.f32_to_bf16_bits(rng.standard_normal((3, Hkv, D)).astype(np.float32))
     v = syn.f32_to_bf16_bits(rng.standard_normal((3, Hkv, D)).astype(np.float32))
@@ -291,12 +320,13 @@ def test_cache_write_hand_layout(oracle_mod):
         blk, off = slot // bs, slot % bs
         for h in range(Hkv):
             for i in range(D):
-                want_k[((blk * Hkv + h) * bs + off) * D + i] = oracle_mod.quantize(k[t, h, i:i + 1], 0.5)[0]
+                want_k[(blk * Hkv + h) * bs * D + key_tile_offset(off, i, D, 1)] = \
+                    oracle_mod.quantize(k[t, h, i:i + 1], 0.5)[0]
                 want_v[((blk * Hkv + h) * D + i) * bs + off] = oracle_mod.quantize(v[t, h, i:i + 1], 0.25)[0]
     assert np.array_equal(kc, want_k) and np.array_equal(vc, want_v)
     # a code's value times the scale is the bf16 input rounded to e4m3 precision
     x = syn.bf16_bits_to_f32(k[0, 1, 2:3]).astype(np.float64)[0]
-    code = kc[((0 * Hkv + 1) * bs + 5) * D + 2]
+    code = kc[(0 * Hkv + 1) * bs * D + key_tile_offset(5, 2, D, 1)]
     assert abs(_dec(np.array([code]))[0] * 0.5 - x) <= abs(x) * 2.0 ** -4 + 2.0 ** -10 * 0.5
 
 
@@ -322,7 +352,7 @@ def test_cache_write_bf16_keeps_bits(oracle_mod):
     for t, slot in enumerate(slots):
         blk, off = slot // bs, slot % bs
         for h in range(Hkv):
-            assert np.array_equal(kc[((blk * Hkv + h) * bs + off) * D + np.arange(D)], k[t, h])
+            assert np.array_equal(kc[(blk * Hkv + h) * bs * D + key_tile_offset(off, np.arange(D), D, 2)], k[t, h])
             assert np.array_equal(vc[((blk * Hkv + h) * D + np.arange(D)) * bs + off], v[t, h])
 
 

@@ -38,9 +38,12 @@ MUTANTS = {
     "value_tile_token_major": (
         "return ((blk * Hkv + h) * (int64_t)D + i) * (int64_t)bs + off;",
         "return ((blk * Hkv + h) * (int64_t)bs + off) * (int64_t)D + i;"),
-    "key_tile_channel_major": (
-        "return ((blk * Hkv + h) * (int64_t)bs + off) * (int64_t)D + i;\n}\n/* Offset",
-        "return ((blk * Hkv + h) * (int64_t)D + i) * (int64_t)bs + off;\n}\n/* Offset"),
+    "key_tile_token_major": (
+        "int64_t byte_in_tile = ((int64_t)((off / 4) * C + c) * 4 + off % 4) * (4 * K) + g * K + w % K;",
+        "int64_t byte_in_tile = ((int64_t)off * D + i) * eb;"),
+    "key_tile_quarters_swapped": (
+        "int g = i / q;                     /* quarter */",
+        "int g = (3 - i / q);               /* quarter */"),
     "gqa_interleaved_heads": ("int h = hq / g;", "int h = hq % Hkv;"),
     "window_off_by_one": ("? L - window : 0;", "? L - window + 1 : 0;"),
     "slot_offset_shift": ("int off = (int)(j % bs);", "int off = (int)((j + 1) % bs);"),
