@@ -172,25 +172,52 @@ class DecodeBench:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps, t_enq * 1e3 / steps
 
-    def time_kernels(self, steps: int):
-        """Region B: the same steps with events around each kernel of the step."""
+    def time_kernels(self, launches: int):
+        """Region B: each kernel of the step launched `launches` times back to back (rotating
+        over the cache instances) between one pair of events: the average launch duration,
+        including the short gap between dependent launches on one stream."""
         torch = self.torch
         R = len(self.kc)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-        torch.cuda.synchronize()
-        for s in range(steps):
-            ev[s][0].record()
-            self.write(s % R)
-            ev[s][1].record()
-            self.partial(s % R)
-            ev[s][2].record()
-            if self.nsplits > 1:
-                self.merge()
-            ev[s][3].record()
-        torch.cuda.synchronize()
-        t = np.array([[ev[s][k].elapsed_time(ev[s][k + 1]) for k in range(3)] for s in range(steps)])
-        return {"write_ms": float(np.median(t[:, 0])), "pass1_ms": float(np.mean(t[:, 1])),
-                "pass1_median_ms": float(np.median(t[:, 1])), "merge_ms": float(np.median(t[:, 2]))}
+
+        def avg(fn):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            fn(0)
+            torch.cuda.synchronize()
+            e0.record()
+            for s in range(launches):
+                fn(s % R)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / launches
+
+        out = {"write_ms": avg(self.write), "pass1_ms": avg(self.partial)}
+        out["merge_ms"] = avg(lambda i: self.merge()) if self.nsplits > 1 else 0.0
+        return out
+
+
+PROFILE_SUMMARY = "profiles/decode_llama8b_b1_128k.txt"
+KERNEL_SOURCES = ["fp8_kv_cache_reshape_amd/csrc/paged_decode.hip",
+                  "fp8_kv_cache_reshape_amd/csrc/internal.h"]
+
+
+def measured_traffic(root: str):
+    """HBM bytes per pass-1 launch from the committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy), or None when the kernel sources have changed since the
+    counters were taken (the summary records a hash of them)."""
+    import hashlib
+    path = os.path.join(root, PROFILE_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(root, f), "rb").read())
+    text = open(path).read()
+    if f"(paged_decode.hip + internal.h): {h.hexdigest()[:16]}" not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("decode_partial_traffic_bytes_per_launch"):
+            return int(line.split()[1])
+    return None
 
 
 def cpu_baseline(w, layer, pairs_kv_heads: int = 2) -> dict:
@@ -294,7 +321,9 @@ def main(argv=None):
                    "head_dim": w.head_dim, "block_size": BLOCK, "splits": bench.nsplits,
                    "rotated_instances": R, "instance_bytes": one, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (measured_traffic(root) if args.workload == "llama8b-b1-128k"
+                                 and layer.cache_dtype == "e4m3" and args.num_splits == 0 else None),
                      "kernel": "decode_partial_kernel", "bytes_per_launch": by["pass1"],
                      "avg_launch_us": round(kern["pass1_ms"] * 1e3, 3)},
         "kernels_us": {"cache_write": round(kern["write_ms"] * 1e3, 3),
