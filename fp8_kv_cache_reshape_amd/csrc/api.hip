@@ -90,6 +90,12 @@ WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, in
     return l;
 }
 
+// The fused decode step keeps one arrival counter per (sequence, kv head) at the start of
+// its workspace (a fixed place, whatever split plan a call uses), then the partials.
+size_t step_counter_bytes(int num_seqs, int num_kv_heads) {
+    return ((size_t)num_seqs * num_kv_heads * sizeof(unsigned int) + 255) / 256 * 256;
+}
+
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
 int hip_status(hipError_t e) {
@@ -149,6 +155,11 @@ int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const voi
     p.write_final = single ? 1 : 0;
     p.out = nullptr;
     p.out_f32 = 0;
+    p.k_new = nullptr;
+    p.v_new = nullptr;
+    p.k_scale_q = 1.0f;
+    p.v_scale_q = 1.0f;
+    p.counters = nullptr;
     return FP8KV_OK;
 }
 
@@ -243,6 +254,51 @@ int fp8kv_paged_decode(void* out, int out_dtype, const void* query, const void* 
     st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
     if (st != FP8KV_OK || p.write_final) return st;
     return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
+}
+
+size_t fp8kv_decode_step_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int max_context_len,
+                                        int sliding_window, int num_splits) {
+    if (check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, sliding_window, num_splits) != FP8KV_OK)
+        return 0;
+    const Plan pl = make_plan(num_seqs, num_kv_heads, max_context_len, sliding_window, num_splits);
+    return step_counter_bytes(num_seqs, num_kv_heads) +
+           workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits).total;
+}
+
+int fp8kv_decode_step(void* out, int out_dtype, const void* query, const void* key_new,
+                      const void* value_new, void* key_cache, void* value_cache, int cache_dtype,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int max_context_len, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, float k_scale, float v_scale, int sliding_window,
+                      int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_kv_heads <= 0) return FP8KV_ERR_SHAPE;
+    // counters first, then the partials (checked by setup_decode)
+    const size_t cbytes = step_counter_bytes(num_seqs, num_kv_heads);
+    const bool have_ws = workspace != nullptr && workspace_bytes >= cbytes;
+    fp8kv::DecodeParams p;
+    bool fp8 = true;
+    int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
+                          max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, k_scale,
+                          v_scale, sliding_window, num_splits,
+                          have_ws ? static_cast<char*>(workspace) + cbytes : nullptr,
+                          have_ws ? workspace_bytes - cbytes : 0, false);
+    if (st != FP8KV_OK) return st;
+    if (num_seqs == 0) return FP8KV_OK;
+    if (!out || !key_new || !value_new) return FP8KV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(key_new) || !aligned16(value_new)) return FP8KV_ERR_SHAPE;
+    if (!p.write_final) p.counters = static_cast<unsigned int*>(workspace);
+    p.out = out;
+    p.out_f32 = out_dtype == FP8KV_F32;
+    p.k_new = static_cast<const uint16_t*>(key_new);
+    p.v_new = static_cast<const uint16_t*>(value_new);
+    p.k_scale_q = fp8 ? k_scale : 1.0f;
+    p.v_scale_q = fp8 ? v_scale : 1.0f;
+    return hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
 }
 
 int fp8kv_paged_decode_partial(const void* query, const void* key_cache, const void* value_cache,

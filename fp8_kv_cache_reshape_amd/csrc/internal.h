@@ -56,6 +56,12 @@ struct DecodeParams {
     float* ws_ml;                  // [B][Hq][splits][2]  (m, l)
     float* ws_acc;                 // [B][Hq][splits][D]
     int write_final;               // single split: pass 1 normalises and stores `out`
+    // fused decode step (all null/unused for the plain decode)
+    const uint16_t* k_new;         // bf16 [B][Hkv][D]: the token at position L-1, or null
+    const uint16_t* v_new;
+    float k_scale_q;               // quantisation scales of the step token (fp8 caches)
+    float v_scale_q;
+    unsigned int* counters;        // [B][Hkv] split arrival counters (zero between calls), or null
 };
 
 // Context window of one sequence in blocks: positions [lo, L), blocks [blk0, blk0+nblk).

@@ -41,6 +41,9 @@
 // key registers, and the next value rows as soon as P.V has consumed the value
 // registers, so every wave keeps a step of loads in flight while it computes, without a
 // second register buffer.  Block ids come from wave-uniform loads one step ahead.
+#include <type_traits>
+
+#include "codec.h"
 #include "internal.h"
 
 namespace fp8kv {
@@ -116,6 +119,106 @@ __device__ inline void store_out(void* out, int out_f32, int64_t idx, float v) {
         static_cast<__bf16*>(out)[idx] = (__bf16)v;   // round to nearest even
 }
 
+// Log-sum-exp merge of the `ns` split partials of the G query heads of (sequence b, kv
+// head h), by one workgroup, into `out` (compensated sums; x v_scale / Lambda).  LDS use:
+// G*ns weights, 16 scales, and 2 float4 per thread (see merge_lds_floats).
+template <int D>
+__device__ void merge_group(const DecodeParams& p, float* lds, int b, int h, int G, int ns) {
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int lane = tid & 63;
+    float* s_w = lds;                                          // [G][ns]
+    float* s_scale = lds + G * ns;                             // [16]
+    float4* s_part = reinterpret_cast<float4*>(lds + ((G * ns + 16 + 3) & ~3));   // [nthr][2]
+    const int64_t hq0 = (int64_t)b * p.num_q_heads + (int64_t)h * G;
+    const float2* ml = reinterpret_cast<const float2*>(p.ws_ml);
+
+    for (int hi = tid >> 6; hi < G; hi += nthr >> 6) {        // one wave per head
+        const int64_t row0 = (hq0 + hi) * p.splits;
+        float M = -INFINITY;
+        for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[row0 + s].x);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float Mu = (M == -INFINITY) ? 0.0f : M;
+        float lh = 0.0f, ll = 0.0f;
+        for (int s = lane; s < ns; s += 64) {
+            const float2 v = ml[row0 + s];
+            const float ws = __builtin_amdgcn_exp2f(v.x - Mu);
+            s_w[hi * ns + s] = ws;
+            comp_add(lh, ll, ws * v.y);
+        }
+        float lam = lh + ll;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) lam += __shfl_xor(lam, o);
+        if (lane == 0) s_scale[hi] = lam > 0.0f ? p.v_scale / lam : 0.0f;
+    }
+    __syncthreads();
+
+    const int NQ = G * D / 4;                                  // channel quads of the group
+    const int SL = NQ >= nthr ? 1 : nthr / NQ;                 // split lanes per quad
+    const int QP = nthr / SL;                                  // quads per pass
+    for (int q0 = 0; q0 < NQ; q0 += QP) {
+        const int qi = q0 + tid % QP;
+        const int sl = tid / QP;
+        float4 hi = make_float4(0.f, 0.f, 0.f, 0.f), lo = hi;
+        if (qi < NQ && sl < SL) {
+            const int hh = qi / (D / 4), c4 = qi % (D / 4);
+            const float* accp = p.ws_acc + (hq0 + hh) * p.splits * D + 4 * c4;
+            const float* wrow = s_w + hh * ns;
+            int s = sl;
+            for (; s + 3 * SL < ns; s += 4 * SL) {             // four loads in flight
+                float4 x[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const float4*>(accp + (int64_t)(s + u * SL) * D);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float ws = wrow[s + u * SL];
+                    comp_add(hi.x, lo.x, ws * x[u].x);
+                    comp_add(hi.y, lo.y, ws * x[u].y);
+                    comp_add(hi.z, lo.z, ws * x[u].z);
+                    comp_add(hi.w, lo.w, ws * x[u].w);
+                }
+            }
+            for (; s < ns; s += SL) {
+                const float4 x = *reinterpret_cast<const float4*>(accp + (int64_t)s * D);
+                const float ws = wrow[s];
+                comp_add(hi.x, lo.x, ws * x.x);
+                comp_add(hi.y, lo.y, ws * x.y);
+                comp_add(hi.z, lo.z, ws * x.z);
+                comp_add(hi.w, lo.w, ws * x.w);
+            }
+        }
+        s_part[2 * tid] = hi;
+        s_part[2 * tid + 1] = lo;
+        __syncthreads();
+        if (tid < QP && q0 + tid < NQ) {
+            const int qq = q0 + tid;
+            const int hh = qq / (D / 4), c4 = qq % (D / 4);
+            float r[4];
+#pragma unroll
+            for (int comp = 0; comp < 4; ++comp) {
+                float sh = 0.0f, sc = 0.0f;
+                for (int k = 0; k < SL; ++k) {
+                    const float4 a = s_part[2 * (k * QP + tid)];
+                    const float4 c = s_part[2 * (k * QP + tid) + 1];
+                    comp_add(sh, sc, comp == 0 ? a.x : comp == 1 ? a.y : comp == 2 ? a.z : a.w);
+                    sc += comp == 0 ? c.x : comp == 1 ? c.y : comp == 2 ? c.z : c.w;
+                }
+                r[comp] = s_scale[hh] * (sh + sc);
+            }
+            const int64_t o = (hq0 + hh) * D + 4 * c4;
+#pragma unroll
+            for (int comp = 0; comp < 4; ++comp) store_out(p.out, p.out_f32, o + comp, r[comp]);
+        }
+        __syncthreads();
+    }
+}
+
+// LDS floats merge_group needs for a group of G heads over `splits` splits.
+inline size_t merge_lds_floats(int G, int splits, int threads) {
+    return (size_t)((G * splits + 16 + 3) & ~3) + 8 * (size_t)threads;
+}
+
 // Two waves per SIMD (<= 256 registers per lane) wherever the tile fits; head_dim 256 and
 // 2-byte caches need more and run one wave per SIMD.
 template <int D, bool FP8>
@@ -149,7 +252,8 @@ void decode_partial_kernel(DecodeParams p) {
     const int se = min(w.nblk, sb + p.blocks_per_split);
     const int64_t out_row0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * D;
     if (sb >= se) {
-        if (p.write_final && split == 0)
+        // an empty context: the first split writes the zero output when no merge will
+        if ((p.write_final || p.counters != nullptr) && split == 0)
             for (int i = threadIdx.x; i < G * D; i += blockDim.x) store_out(p.out, p.out_f32, out_row0 + i, 0.0f);
         return;
     }
@@ -169,7 +273,11 @@ void decode_partial_kernel(DecodeParams p) {
 
     const char* kcache = static_cast<const char*>(p.key_cache);
     const char* vcache = static_cast<const char*>(p.value_cache);
-    const int32_t* __restrict__ bt = p.block_tables + (int64_t)b * p.max_blocks_per_seq + w.blk0 + sb;
+    // The block table is read-only while the kernel runs: reading it through the constant
+    // address space lets the wave-uniform id reads below be scalar loads, which do not queue
+    // behind the vector KV loads in flight.
+    typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+    const ConstI32Ptr bt = (ConstI32Ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq + w.blk0 + sb);
     const float sscale = p.score_scale;
     const int nblk = se - sb;                     // blocks of this split
     const int nsteps = (nblk + 3) >> 2;
@@ -245,8 +353,12 @@ void decode_partial_kernel(DecodeParams p) {
     int chunk_steps = 0;
     // One wave step over the 4 blocks of step `stp` held in `bf`; refills `bf` with step
     // `nstp` (if it exists) as soon as each half of the buffer has been consumed.
-    auto process = [&](Buf& bf, int stp, int nstp) {
-        const bool more = nstp < nsteps;
+    // `steady` (a compile-time tag) marks steps whose successor is known to exist: their
+    // prefetch is unconditional, which keeps the loads in straight-line code so the
+    // compiler can wait for exactly the loads each use needs.
+    auto process = [&](Buf& bf, int stp, int nstp, auto steady) {
+        constexpr bool kSteady = decltype(steady)::value;
+        const bool more = kSteady || nstp < nsteps;
         int nkid = -1, nvid = -1;
         if (more) step_ids(nstp, nkid, nvid);
 
@@ -269,6 +381,10 @@ void decode_partial_kernel(DecodeParams p) {
                 sc[s] = c;
             }
             if (more) issue_k(bf, nkid);   // key registers are free again
+            // Keep the value-side work below the softmax: without this the scheduler hoists
+            // the value conversions above the q.K products, and every step then waits for
+            // its value loads before it can start.
+            __builtin_amdgcn_sched_barrier(0);
 
             // ---- mask and scale: lane holds block grp of the step, tokens 4s+r, head n
             const bool vval = bf.vid >= 0;
@@ -320,6 +436,7 @@ void decode_partial_kernel(DecodeParams p) {
             }
             l_chunk += psum;
 
+            __builtin_amdgcn_sched_barrier(0);
             // values of tokens outside [lo, L) (partial or missing blocks) are zeroed so that a
             // poisoned (NaN) slot never reaches the accumulator through p = 0
             if (tlo > 0 || thi < kBlockSize) {
@@ -372,6 +489,50 @@ void decode_partial_kernel(DecodeParams p) {
         }
     };
 
+    // Fused decode step: the wave that owns the sequence's last block (its last step)
+    // quantises the step token and stores it at position L-1 before that block is read.
+    // Lanes [0, D/8) write 8 key channels each, lanes [32, 32 + D/8) 8 value channels.
+    auto write_step_token = [&]() {
+        const int L1 = w.L - 1;
+        const int blk = p.block_tables[(int64_t)b * p.max_blocks_per_seq + L1 / kBlockSize];
+        const int c = lane & 31;
+        if ((unsigned)blk < (unsigned)p.num_blocks && c < D / 8) {
+            const bool val = lane >= 32;
+            const int off = L1 % kBlockSize;
+            const uint4 x = load16((val ? p.v_new : p.k_new) + ((int64_t)b * p.num_kv_heads + h) * D + c * 8);
+            char* tile = static_cast<char*>(const_cast<void*>(val ? p.value_cache : p.key_cache))
+                         + ((int64_t)blk * p.num_kv_heads + h) * TILE_BYTES;
+            if constexpr (FP8) {
+                const uint2 q8 = quantize8(x, val ? p.v_scale_q : p.k_scale_q);
+                if (!val) {
+                    *reinterpret_cast<uint2*>(tile + key_chunk_offset<D, 1>(off, c * 8)) = q8;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        tile[(c * 8 + i) * kBlockSize + off] = (char)(((i < 4 ? q8.x : q8.y) >> (8 * (i & 3))) & 0xFF);
+                }
+            } else {
+                if (!val) {
+                    *reinterpret_cast<uint4*>(tile + key_chunk_offset<D, 2>(off, c * 8)) = x;
+                } else {
+                    const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+                    uint16_t* vt16 = reinterpret_cast<uint16_t*>(tile);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        vt16[(c * 8 + i) * kBlockSize + off] = (uint16_t)(wd[i >> 1] >> (16 * (i & 1)));
+                }
+            }
+        }
+        // Only this wave reads the block, later, from this CU: the stores must have reached
+        // the L2 this CU reads through (L1 is write-through).  A workgroup-scope fence waits
+        // for them; no device-wide cache maintenance is needed.
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    };
+    const bool writer = p.k_new != nullptr && se == w.nblk && wave == (nsteps - 1) % kDecodeWaves;
+    const int wave_steps = wave < nsteps ? (nsteps - 1 - wave) / kDecodeWaves + 1 : 0;
+    // the writer's prefetch reaches the last block at once only when it has few steps
+    if (writer && wave_steps <= kPrefetch) write_step_token();
+
     Buf buf[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
@@ -383,11 +544,27 @@ void decode_partial_kernel(DecodeParams p) {
             issue_v(buf[j], buf[j].vid);
         }
     }
-    for (int st = wave; st < nsteps; st += kPrefetch * kDecodeWaves) {
+    if (writer && wave_steps > kPrefetch) write_step_token();
+    // Consume the query operands here, once: afterwards the compiler knows they have
+    // arrived, and the loop waits only for the key or value loads each use needs (without
+    // this it waits for every load in flight at the top of each step).
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[kk]));
+    int st = wave;
+    // steady state: every step of the round has a successor kPrefetch rounds later
+    for (; st + (2 * kPrefetch - 1) * kDecodeWaves < nsteps; st += kPrefetch * kDecodeWaves) {
 #pragma unroll
         for (int j = 0; j < kPrefetch; ++j) {
             const int stp = st + j * kDecodeWaves;
-            if (stp < nsteps) process(buf[j], stp, stp + kPrefetch * kDecodeWaves);
+            process(buf[j], stp, stp + kPrefetch * kDecodeWaves, std::true_type{});
+        }
+    }
+    // the last rounds, whose successors may not exist
+    for (; st < nsteps; st += kPrefetch * kDecodeWaves) {
+#pragma unroll
+        for (int j = 0; j < kPrefetch; ++j) {
+            const int stp = st + j * kDecodeWaves;
+            if (stp < nsteps) process(buf[j], stp, stp + kPrefetch * kDecodeWaves, std::false_type{});
         }
     }
     flush();
@@ -438,6 +615,29 @@ void decode_partial_kernel(DecodeParams p) {
                 p.ws_ml[row * 2 + 0] = M;
                 p.ws_ml[row * 2 + 1] = lam;
             }
+        }
+    }
+
+    // Fused merge: the last workgroup of this (sequence, kv head) to finish combines the
+    // partials of all its splits.  Each workgroup publishes its partials, then counts
+    // itself in; the one that completes the count acquires everyone's partials, merges,
+    // and zeroes the counter for the next call.  No workgroup ever waits for another.
+    if (!p.write_final && p.counters != nullptr) {
+        __shared__ int s_last;
+        const int ns = (w.nblk + p.blocks_per_split - 1) / p.blocks_per_split;
+        __syncthreads();                                  // all partial stores of this group issued
+        if (threadIdx.x == 0) {
+            // release: this workgroup's partials become visible device-wide before it counts in
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            unsigned int* cnt = p.counters + (int64_t)b * p.num_kv_heads + h;
+            const unsigned int old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (int)(old + 1 == (unsigned int)ns);
+            if (s_last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (s_last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // see every group's partials
+            merge_group<D>(p, lds, b, h, G, ns);
         }
     }
 }
@@ -536,6 +736,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
     }
 }
 
+// Largest dynamic LDS a partial-kernel launch may request (the g = 16, head_dim 256 tile
+// needs about 66 KB; the fused merge of a large split count needs more).  Launches that
+// need more than 64 KB also need the device to allow it.
+constexpr size_t kMaxFusedLds = 128 * 1024;
+
 // Dynamic LDS of the partial kernel: per-wave (m, l) and the group's accumulators.
 template <int D>
 size_t partial_lds_bytes(int G) {
@@ -545,24 +750,36 @@ size_t partial_lds_bytes(int G) {
 // Kernels whose dynamic LDS can exceed 64 KiB (g = 16 at head_dim 256) get their limit
 // raised once, to the largest size any group ratio needs.
 template <int D, bool FP8>
-hipError_t allow_lds() {
-    static const hipError_t e = [] {
-        const size_t need = partial_lds_bytes<D>(kMaxGroup);
-        if (need <= 65536) return hipSuccess;
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, FP8>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)need);
+hipError_t allow_lds(size_t need) {
+    if (need <= 65536) return hipSuccess;
+    // raise this kernel's limit once, to what the device allows (up to kMaxFusedLds)
+    static const int allowed = [] {
+        int dev = 0, lim = 65536;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return 65536;
+        if ((size_t)lim > kMaxFusedLds) lim = (int)kMaxFusedLds;
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, FP8>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lim) != hipSuccess)
+            return 65536;
+        return lim;
     }();
-    return e;
+    return need <= (size_t)allowed ? hipSuccess : hipErrorInvalidValue;
 }
 
 template <int D>
 hipError_t launch_partial_d(const DecodeParams& p, bool fp8, hipStream_t s) {
     const int G = p.num_q_heads / p.num_kv_heads;
-    const size_t lds = partial_lds_bytes<D>(G);
+    size_t lds = partial_lds_bytes<D>(G);
+    if (p.counters != nullptr && !p.write_final) {
+        const size_t m = sizeof(float) * merge_lds_floats(G, p.splits, 64 * kDecodeWaves);
+        if (m > lds) lds = m;
+    }
+
     const dim3 grid = kHeadsFastest ? dim3(p.num_kv_heads, p.splits, p.num_seqs)
                                     : dim3(p.splits, p.num_kv_heads, p.num_seqs);
     const dim3 block(64 * kDecodeWaves);
-    hipError_t e = fp8 ? allow_lds<D, true>() : allow_lds<D, false>();
+    hipError_t e = fp8 ? allow_lds<D, true>(lds) : allow_lds<D, false>(lds);
     if (e != hipSuccess) return e;
     const void* fn = fp8 ? reinterpret_cast<const void*>(&decode_partial_kernel<D, true>)
                          : reinterpret_cast<const void*>(&decode_partial_kernel<D, false>);

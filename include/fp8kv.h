@@ -207,6 +207,51 @@ int fp8kv_paged_decode_merge(void* out, int out_dtype,
                              float v_scale, int sliding_window, int num_splits,
                              const void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fp8kv_decode_step_workspace_size -- bytes of device workspace fp8kv_decode_step needs
+ * (0 on invalid arguments): first one 32-bit arrival counter per (sequence, kv head),
+ * padded to a multiple of 256 bytes, then the split partials of fp8kv_paged_decode.  The
+ * counters sit at the same place whatever split plan a call uses.
+ */
+size_t fp8kv_decode_step_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int max_context_len,
+                                        int sliding_window, int num_splits);
+
+/*
+ * fp8kv_decode_step -- one whole decode step in a single kernel launch: write each
+ * sequence's new token into the cache, then decode attention over the cache.
+ *
+ * Equivalent to fp8kv_cache_write(key_new, value_new, ...) with num_tokens = num_seqs and
+ * slot_mapping[b] = block_tables[b][(L_b-1)/16]*16 + (L_b-1)%16 for every sequence with
+ * L_b >= 1 (L_b as clamped in fp8kv_paged_decode; sequences with L_b = 0 write nothing,
+ * and a block id outside [0, num_blocks) writes nothing), followed by
+ * fp8kv_paged_decode(...) with the same arguments.  The bytes written are identical; the
+ * output agrees with the two-call path to within fp32 rounding (the split partials are
+ * combined inside the launch by the last workgroup of each (sequence, kv head) instead of
+ * in a second kernel).
+ *
+ *   key_new, value_new  device bf16 [num_seqs][num_kv_heads][head_dim]: the token at
+ *                       position L_b - 1 of every sequence
+ *   key_cache,
+ *   value_cache         written and read
+ *   workspace           at least fp8kv_decode_step_workspace_size() bytes, 256-byte
+ *                       aligned.  Its counter region (the first
+ *                       round_up(num_seqs*num_kv_heads*4, 256) bytes) must be zero before
+ *                       the first call (allocate the workspace zero-filled); every call
+ *                       leaves it zero again, so consecutive steps can reuse it even as the
+ *                       split plan changes.  One workspace serves one call at a time.
+ * Other arguments, layout and error behaviour as for fp8kv_paged_decode.
+ */
+int fp8kv_decode_step(void* out, int out_dtype, const void* query,
+                      const void* key_new, const void* value_new,
+                      void* key_cache, void* value_cache, int cache_dtype,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks,
+                      float k_scale, float v_scale, int sliding_window, int num_splits,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -138,3 +138,37 @@ def sample_pairs(w: syn.Workload, n_per_seq: int = 3, seed: int = 0) -> np.ndarr
         heads |= set(rng.integers(0, w.num_q_heads, n_per_seq).tolist())
         pairs += [(b, h) for h in sorted(heads)]
     return np.array(pairs, dtype=np.int32)
+
+
+def step_rows_by_seq(w: syn.Workload, layer: syn.Layer):
+    """bf16 [B][Hkv][D] K and V of each sequence's token at position L_b - 1 (zeros for an
+    empty sequence, whose row the step ignores)."""
+    k = np.zeros((w.num_seqs, w.num_kv_heads, w.head_dim), np.uint16)
+    v = np.zeros_like(k)
+    for b in range(w.num_seqs):
+        L = int(w.context_lens[b])
+        if L > 0:
+            r = int(w.seq_offsets[b]) + L - 1
+            k[b], v[b] = layer.k[r], layer.v[r]
+    return k, v
+
+
+def gpu_decode_step(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_splits=0,
+                    dev: DeviceInputs = None, workspace=None):
+    """One fused step: writes each sequence's last token and decodes.  Returns (out, workspace)."""
+    dev = dev or DeviceInputs(w)
+    B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+    win = layer.sliding_window
+    maxl = w.max_context_len
+    ws_bytes = F.fp8kv_decode_step_workspace_size(B, Hq, Hkv, D, w.block_size, maxl, win, num_splits)
+    if workspace is None:
+        workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
+    ws_bytes = workspace.numel()           # the library checks what it needs against this
+    kn, vn = step_rows_by_seq(w, layer)
+    out = torch.empty(B * Hq * D, dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
+    F.fp8kv_decode_step(out, F.FP8KV_F32 if out_f32 else F.FP8KV_BF16, dev.q, u16_dev(kn), u16_dev(vn),
+                        kc, vc, code(layer), dev.bt, w.max_blocks_per_seq, dev.cl, maxl, B, Hq, Hkv, D,
+                        w.block_size, w.num_blocks, layer.k_scale, layer.v_scale, win, num_splits,
+                        workspace, ws_bytes)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D), workspace
