@@ -291,14 +291,21 @@ int fp8kv_decode_step(void* out, int out_dtype, const void* query, const void* k
     if (num_seqs == 0) return FP8KV_OK;
     if (!out || !key_new || !value_new) return FP8KV_ERR_NULL;
     if (!aligned16(out) || !aligned16(key_new) || !aligned16(value_new)) return FP8KV_ERR_SHAPE;
-    if (!p.write_final) p.counters = static_cast<unsigned int*>(workspace);
+    // merge inside the decode kernel when one workgroup merges a group cheaply, else in the
+    // merge kernel queued behind it
+    const bool fused = !p.write_final &&
+                       fp8kv::fused_merge_fits(num_q_heads / num_kv_heads, head_dim, p.splits);
+    if (fused) p.counters = static_cast<unsigned int*>(workspace);
     p.out = out;
     p.out_f32 = out_dtype == FP8KV_F32;
     p.k_new = static_cast<const uint16_t*>(key_new);
     p.v_new = static_cast<const uint16_t*>(value_new);
     p.k_scale_q = fp8 ? k_scale : 1.0f;
     p.v_scale_q = fp8 ? v_scale : 1.0f;
-    return hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
+    if (st != FP8KV_OK || p.write_final || fused) return st;
+    return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
 }
 
 int fp8kv_paged_decode_partial(const void* query, const void* key_cache, const void* value_cache,

@@ -110,5 +110,9 @@ inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, size_t ld
 hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, int head_dim, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeParams& p, bool fp8, int head_dim, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t s);
+// Whether the decode kernel can merge the `splits` partials of a (sequence, kv head) group
+// of `group` query heads itself, in at most two batched round trips to memory; larger
+// merges run in the separate merge kernel.
+bool fused_merge_fits(int group, int head_dim, int splits);
 
 }  // namespace fp8kv

@@ -119,104 +119,97 @@ __device__ inline void store_out(void* out, int out_f32, int64_t idx, float v) {
         static_cast<__bf16*>(out)[idx] = (__bf16)v;   // round to nearest even
 }
 
-// Log-sum-exp merge of the `ns` split partials of the G query heads of (sequence b, kv
-// head h), by one workgroup, into `out` (compensated sums; x v_scale / Lambda).  LDS use:
-// G*ns weights, 16 scales, and 2 float4 per thread (see merge_lds_floats).
-template <int D>
-__device__ void merge_group(const DecodeParams& p, float* lds, int b, int h, int G, int ns) {
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const int lane = tid & 63;
-    float* s_w = lds;                                          // [G][ns]
-    float* s_scale = lds + G * ns;                             // [16]
-    float4* s_part = reinterpret_cast<float4*>(lds + ((G * ns + 16 + 3) & ~3));   // [nthr][2]
-    const int64_t hq0 = (int64_t)b * p.num_q_heads + (int64_t)h * G;
-    const float2* ml = reinterpret_cast<const float2*>(p.ws_ml);
-
-    for (int hi = tid >> 6; hi < G; hi += nthr >> 6) {        // one wave per head
-        const int64_t row0 = (hq0 + hi) * p.splits;
-        float M = -INFINITY;
-        for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[row0 + s].x);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        const float Mu = (M == -INFINITY) ? 0.0f : M;
-        float lh = 0.0f, ll = 0.0f;
-        for (int s = lane; s < ns; s += 64) {
-            const float2 v = ml[row0 + s];
-            const float ws = __builtin_amdgcn_exp2f(v.x - Mu);
-            s_w[hi * ns + s] = ws;
-            comp_add(lh, ll, ws * v.y);
-        }
-        float lam = lh + ll;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) lam += __shfl_xor(lam, o);
-        if (lane == 0) s_scale[hi] = lam > 0.0f ? p.v_scale / lam : 0.0f;
-    }
-    __syncthreads();
-
-    const int NQ = G * D / 4;                                  // channel quads of the group
-    const int SL = NQ >= nthr ? 1 : nthr / NQ;                 // split lanes per quad
-    const int QP = nthr / SL;                                  // quads per pass
-    for (int q0 = 0; q0 < NQ; q0 += QP) {
-        const int qi = q0 + tid % QP;
-        const int sl = tid / QP;
-        float4 hi = make_float4(0.f, 0.f, 0.f, 0.f), lo = hi;
-        if (qi < NQ && sl < SL) {
-            const int hh = qi / (D / 4), c4 = qi % (D / 4);
-            const float* accp = p.ws_acc + (hq0 + hh) * p.splits * D + 4 * c4;
-            const float* wrow = s_w + hh * ns;
-            int s = sl;
-            for (; s + 3 * SL < ns; s += 4 * SL) {             // four loads in flight
-                float4 x[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const float4*>(accp + (int64_t)(s + u * SL) * D);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float ws = wrow[s + u * SL];
-                    comp_add(hi.x, lo.x, ws * x[u].x);
-                    comp_add(hi.y, lo.y, ws * x[u].y);
-                    comp_add(hi.z, lo.z, ws * x[u].z);
-                    comp_add(hi.w, lo.w, ws * x[u].w);
-                }
-            }
-            for (; s < ns; s += SL) {
-                const float4 x = *reinterpret_cast<const float4*>(accp + (int64_t)s * D);
-                const float ws = wrow[s];
-                comp_add(hi.x, lo.x, ws * x.x);
-                comp_add(hi.y, lo.y, ws * x.y);
-                comp_add(hi.z, lo.z, ws * x.z);
-                comp_add(hi.w, lo.w, ws * x.w);
-            }
-        }
-        s_part[2 * tid] = hi;
-        s_part[2 * tid + 1] = lo;
-        __syncthreads();
-        if (tid < QP && q0 + tid < NQ) {
-            const int qq = q0 + tid;
-            const int hh = qq / (D / 4), c4 = qq % (D / 4);
-            float r[4];
-#pragma unroll
-            for (int comp = 0; comp < 4; ++comp) {
-                float sh = 0.0f, sc = 0.0f;
-                for (int k = 0; k < SL; ++k) {
-                    const float4 a = s_part[2 * (k * QP + tid)];
-                    const float4 c = s_part[2 * (k * QP + tid) + 1];
-                    comp_add(sh, sc, comp == 0 ? a.x : comp == 1 ? a.y : comp == 2 ? a.z : a.w);
-                    sc += comp == 0 ? c.x : comp == 1 ? c.y : comp == 2 ? c.z : c.w;
-                }
-                r[comp] = s_scale[hh] * (sh + sc);
-            }
-            const int64_t o = (hq0 + hh) * D + 4 * c4;
-#pragma unroll
-            for (int comp = 0; comp < 4; ++comp) store_out(p.out, p.out_f32, o + comp, r[comp]);
-        }
-        __syncthreads();
-    }
+// Device-scope (relaxed atomic) store of one float.  On this chip it writes through the
+// L2 of the issuing XCD to the device coherence point, so the partials need no L2
+// write-back before another XCD reads them (an agent-scope release fence would write back
+// the whole L2, which costs microseconds per workgroup).
+__device__ inline void store_device(float* ptr, float v) {
+    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// LDS floats merge_group needs for a group of G heads over `splits` splits.
-inline size_t merge_lds_floats(int G, int splits, int threads) {
-    return (size_t)((G * splits + 16 + 3) & ~3) + 8 * (size_t)threads;
+// Value of lane l ^ 1 (a DPP quad permutation: no LDS round trip).
+__device__ inline float pair_swap(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
+// Splits one lane of the fused merge reads (the lane pair of a channel quad covers twice
+// as many), and partials it holds at once.
+constexpr int kMergeLaneSplits = 32;
+constexpr int kMergeLaneBatch = 16;
+
+// Log-sum-exp merge of the `ns` split partials of the G query heads of (sequence b, kv
+// head h), by one workgroup, into `out` (compensated sums; x v_scale / Lambda).
+// Lanes 2q and 2q + 1 own channel quad q and read the even and the odd splits.  Every
+// (m, l) pair of a lane and its first kMergeLaneBatch partials are requested at once (one
+// round trip for up to 2 * kMergeLaneBatch splits); the pair agrees on the maximum, each
+// lane forms the weights, normaliser and weighted sums of its splits, and the pair
+// combines through lane swaps -- no LDS and no barrier.
+template <int D>
+__device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) {
+    const int par = threadIdx.x & 1;
+    const int NQ = G * D / 4;                                  // channel quads of the group
+    const int64_t hq0 = (int64_t)b * p.num_q_heads + (int64_t)h * G;
+    for (int q = threadIdx.x >> 1; q < NQ; q += blockDim.x >> 1) {
+        const int hh = q / (D / 4), c4 = q % (D / 4);
+        const int64_t row = (hq0 + hh) * p.splits;
+        // one base pointer per array: the loads below differ by constant offsets
+        const float4* xp = reinterpret_cast<const float4*>(p.ws_acc + (row + par) * D + 4 * c4);
+        const float2* mp = reinterpret_cast<const float2*>(p.ws_ml) + row + par;
+        float2 mv[kMergeLaneSplits];
+        float4 xv[kMergeLaneBatch];
+        auto load_x = [&](int u0) {
+#pragma unroll
+            for (int u = 0; u < kMergeLaneBatch; ++u) {
+                xv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (2 * (u0 + u) + par < ns) xv[u] = xp[(u0 + u) * (D / 2)];
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < kMergeLaneSplits; ++u) {
+            mv[u] = make_float2(-INFINITY, 0.0f);
+            if (2 * u + par < ns) mv[u] = mp[2 * u];
+        }
+        load_x(0);
+        float M = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kMergeLaneSplits; ++u) M = fmaxf(M, mv[u].x);
+        M = fmaxf(M, pair_swap(M));
+        const float Mu = (M == -INFINITY) ? 0.0f : M;
+        float lh = 0.0f, ll = 0.0f;
+        float4 hi = make_float4(0.f, 0.f, 0.f, 0.f), lo = hi;
+#pragma unroll
+        for (int u = 0; u < kMergeLaneSplits; ++u)
+            comp_add(lh, ll, __builtin_amdgcn_exp2f(mv[u].x - Mu) * mv[u].y);   // 0 if absent
+#pragma unroll
+        for (int u0 = 0; u0 < kMergeLaneSplits; u0 += kMergeLaneBatch) {
+            if (u0 > 0) {
+                if (2 * u0 >= ns) break;
+                load_x(u0);
+            }
+#pragma unroll
+            for (int u = 0; u < kMergeLaneBatch; ++u) {
+                const float ws = __builtin_amdgcn_exp2f(mv[u0 + u].x - Mu);
+                comp_add(hi.x, lo.x, ws * xv[u].x);
+                comp_add(hi.y, lo.y, ws * xv[u].y);
+                comp_add(hi.z, lo.z, ws * xv[u].z);
+                comp_add(hi.w, lo.w, ws * xv[u].w);
+            }
+        }
+        // (hi, lo) + the partner's (hi', lo'): hi + hi' with its rounding error, plus lo + lo'
+        auto pair_sum = [](float h0, float l0) {
+            const float h1 = pair_swap(h0), l1 = pair_swap(l0);
+            float sh = h0, sc = l0 + l1;
+            comp_add(sh, sc, h1);
+            return sh + sc;
+        };
+        const float lam = pair_sum(lh, ll);
+        const float scale = lam > 0.0f ? p.v_scale / lam : 0.0f;
+        const float r0 = pair_sum(hi.x, lo.x), r1 = pair_sum(hi.y, lo.y);
+        const float r2 = pair_sum(hi.z, lo.z), r3 = pair_sum(hi.w, lo.w);
+        const int64_t o = (hq0 + hh) * D + 4 * c4 + 2 * par;
+        store_out(p.out, p.out_f32, o, scale * (par ? r2 : r0));
+        store_out(p.out, p.out_f32, o + 1, scale * (par ? r3 : r1));
+    }
 }
 
 // Two waves per SIMD (<= 256 registers per lane) wherever the tile fits; head_dim 256 and
@@ -491,19 +484,27 @@ void decode_partial_kernel(DecodeParams p) {
 
     // Fused decode step: the wave that owns the sequence's last block (its last step)
     // quantises the step token and stores it at position L-1 before that block is read.
-    // Lanes [0, D/8) write 8 key channels each, lanes [32, 32 + D/8) 8 value channels.
-    auto write_step_token = [&]() {
-        const int L1 = w.L - 1;
-        const int blk = p.block_tables[(int64_t)b * p.max_blocks_per_seq + L1 / kBlockSize];
+    // Lanes [0, D/8) write 8 key channels each, lanes [32, 32 + D/8) 8 value channels.  The
+    // token and its block id are requested before the first KV loads; the stores go out
+    // after them unless the last block is among the first loads.
+    const bool writer = p.k_new != nullptr && se == w.nblk && wave == (nsteps - 1) % kDecodeWaves;
+    const int wave_steps = wave < nsteps ? (nsteps - 1 - wave) / kDecodeWaves + 1 : 0;
+    uint4 tok = make_uint4(0, 0, 0, 0);
+    int tok_blk = -1;
+    if (writer) {
+        tok_blk = ((ConstI32Ptr)p.block_tables)[(int64_t)b * p.max_blocks_per_seq + (w.L - 1) / kBlockSize];
+        const int c = min(lane & 31, D / 8 - 1);
+        tok = load16((lane >= 32 ? p.v_new : p.k_new) + ((int64_t)b * p.num_kv_heads + h) * D + c * 8);
+    }
+    auto store_step_token = [&]() {
         const int c = lane & 31;
-        if ((unsigned)blk < (unsigned)p.num_blocks && c < D / 8) {
+        if ((unsigned)tok_blk < (unsigned)p.num_blocks && c < D / 8) {
             const bool val = lane >= 32;
-            const int off = L1 % kBlockSize;
-            const uint4 x = load16((val ? p.v_new : p.k_new) + ((int64_t)b * p.num_kv_heads + h) * D + c * 8);
+            const int off = (w.L - 1) % kBlockSize;
             char* tile = static_cast<char*>(const_cast<void*>(val ? p.value_cache : p.key_cache))
-                         + ((int64_t)blk * p.num_kv_heads + h) * TILE_BYTES;
+                         + ((int64_t)tok_blk * p.num_kv_heads + h) * TILE_BYTES;
             if constexpr (FP8) {
-                const uint2 q8 = quantize8(x, val ? p.v_scale_q : p.k_scale_q);
+                const uint2 q8 = quantize8(tok, val ? p.v_scale_q : p.k_scale_q);
                 if (!val) {
                     *reinterpret_cast<uint2*>(tile + key_chunk_offset<D, 1>(off, c * 8)) = q8;
                 } else {
@@ -513,9 +514,9 @@ void decode_partial_kernel(DecodeParams p) {
                 }
             } else {
                 if (!val) {
-                    *reinterpret_cast<uint4*>(tile + key_chunk_offset<D, 2>(off, c * 8)) = x;
+                    *reinterpret_cast<uint4*>(tile + key_chunk_offset<D, 2>(off, c * 8)) = tok;
                 } else {
-                    const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+                    const uint32_t wd[4] = {tok.x, tok.y, tok.z, tok.w};
                     uint16_t* vt16 = reinterpret_cast<uint16_t*>(tile);
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
@@ -523,15 +524,14 @@ void decode_partial_kernel(DecodeParams p) {
                 }
             }
         }
-        // Only this wave reads the block, later, from this CU: the stores must have reached
-        // the L2 this CU reads through (L1 is write-through).  A workgroup-scope fence waits
-        // for them; no device-wide cache maintenance is needed.
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        // Only this wave reads the block, with loads it issues after these stores, and a
+        // wave's memory operations are performed in issue order: wavefront-scope ordering
+        // suffices (no wait for the stores, nor for the loads already in flight).
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     };
-    const bool writer = p.k_new != nullptr && se == w.nblk && wave == (nsteps - 1) % kDecodeWaves;
-    const int wave_steps = wave < nsteps ? (nsteps - 1 - wave) / kDecodeWaves + 1 : 0;
     // the writer's prefetch reaches the last block at once only when it has few steps
-    if (writer && wave_steps <= kPrefetch) write_step_token();
+    if (writer && wave_steps <= kPrefetch) store_step_token();
 
     Buf buf[kPrefetch];
 #pragma unroll
@@ -544,7 +544,7 @@ void decode_partial_kernel(DecodeParams p) {
             issue_v(buf[j], buf[j].vid);
         }
     }
-    if (writer && wave_steps > kPrefetch) write_step_token();
+    if (writer && wave_steps > kPrefetch) store_step_token();
     // Consume the query operands here, once: afterwards the compiler knows they have
     // arrived, and the loop waits only for the key or value loads each use needs (without
     // this it waits for every load in flight at the top of each step).
@@ -610,35 +610,44 @@ void decode_partial_kernel(DecodeParams p) {
                       lam > 0.0f ? p.v_scale * a / lam : 0.0f);
         } else {
             const int64_t row = ((int64_t)b * p.num_q_heads + (int64_t)h * G + head) * p.splits + split;
-            p.ws_acc[row * D + i] = a;
+            store_device(p.ws_acc + row * D + i, a);
             if (i == 0) {
-                p.ws_ml[row * 2 + 0] = M;
-                p.ws_ml[row * 2 + 1] = lam;
+                store_device(p.ws_ml + row * 2 + 0, M);
+                store_device(p.ws_ml + row * 2 + 1, lam);
             }
         }
     }
 
     // Fused merge: the last workgroup of this (sequence, kv head) to finish combines the
     // partials of all its splits.  Each workgroup publishes its partials, then counts
-    // itself in; the one that completes the count acquires everyone's partials, merges,
-    // and zeroes the counter for the next call.  No workgroup ever waits for another.
+    // itself in; the one that completes the count merges and zeroes the counter for the
+    // next call.  No workgroup ever waits for another.
+    // Ordering: the partials are device-scope stores, and every thread waits until its own
+    // have completed (reached the device coherence point) before the barrier after which
+    // thread 0 counts in with a device-scope atomic.  The workgroup that completes the
+    // count invalidates its caches (agent-scope acquire) before any of its threads reads a
+    // partial.  This is the ordering an agent-scope release/acquire pair gives, without the
+    // release's L2 write-back, which only data stored through the L2 without device scope
+    // would need.
     if (!p.write_final && p.counters != nullptr) {
         __shared__ int s_last;
         const int ns = (w.nblk + p.blocks_per_split - 1) / p.blocks_per_split;
-        __syncthreads();                                  // all partial stores of this group issued
+        __builtin_amdgcn_s_waitcnt(0);                   // this thread's partial stores done
+        __syncthreads();                                  // ... and every thread's
         if (threadIdx.x == 0) {
-            // release: this workgroup's partials become visible device-wide before it counts in
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             unsigned int* cnt = p.counters + (int64_t)b * p.num_kv_heads + h;
             const unsigned int old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (int)(old + 1 == (unsigned int)ns);
-            if (s_last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = old + 1 == (unsigned int)ns;
+            if (last) {
+                __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // drop stale copies of the partials from this CU's L1 and this XCD's L2;
+                // the barrier below orders the other threads' loads after it
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            s_last = (int)last;
         }
         __syncthreads();
-        if (s_last) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // see every group's partials
-            merge_group<D>(p, lds, b, h, G, ns);
-        }
+        if (s_last) merge_group<D>(p, b, h, G, ns);
     }
 }
 
@@ -737,9 +746,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
 }
 
 // Largest dynamic LDS a partial-kernel launch may request (the g = 16, head_dim 256 tile
-// needs about 66 KB; the fused merge of a large split count needs more).  Launches that
-// need more than 64 KB also need the device to allow it.
-constexpr size_t kMaxFusedLds = 128 * 1024;
+// needs about 66 KB).  Launches that need more than 64 KB also need the device to allow it.
+constexpr size_t kMaxPartialLds = 80 * 1024;
 
 // Dynamic LDS of the partial kernel: per-wave (m, l) and the group's accumulators.
 template <int D>
@@ -752,13 +760,13 @@ size_t partial_lds_bytes(int G) {
 template <int D, bool FP8>
 hipError_t allow_lds(size_t need) {
     if (need <= 65536) return hipSuccess;
-    // raise this kernel's limit once, to what the device allows (up to kMaxFusedLds)
+    // raise this kernel's limit once, to what the device allows (up to kMaxPartialLds)
     static const int allowed = [] {
         int dev = 0, lim = 65536;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
             return 65536;
-        if ((size_t)lim > kMaxFusedLds) lim = (int)kMaxFusedLds;
+        if ((size_t)lim > kMaxPartialLds) lim = (int)kMaxPartialLds;
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, FP8>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, lim) != hipSuccess)
             return 65536;
@@ -770,11 +778,7 @@ hipError_t allow_lds(size_t need) {
 template <int D>
 hipError_t launch_partial_d(const DecodeParams& p, bool fp8, hipStream_t s) {
     const int G = p.num_q_heads / p.num_kv_heads;
-    size_t lds = partial_lds_bytes<D>(G);
-    if (p.counters != nullptr && !p.write_final) {
-        const size_t m = sizeof(float) * merge_lds_floats(G, p.splits, 64 * kDecodeWaves);
-        if (m > lds) lds = m;
-    }
+    const size_t lds = partial_lds_bytes<D>(G);
 
     const dim3 grid = kHeadsFastest ? dim3(p.num_kv_heads, p.splits, p.num_seqs)
                                     : dim3(p.splits, p.num_kv_heads, p.num_seqs);
@@ -795,6 +799,12 @@ hipError_t launch_decode_partial(const DecodeParams& p, bool fp8, int head_dim, 
         case 256: return launch_partial_d<256>(p, fp8, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+bool fused_merge_fits(int group, int head_dim, int splits) {
+    // every lane reads at most kMergeLaneSplits splits, in at most two passes over the quads
+    const int pairs = 64 * kDecodeWaves / 2;
+    return splits <= 2 * kMergeLaneSplits && group * head_dim / 4 <= 2 * pairs;
 }
 
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t s) {

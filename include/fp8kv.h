@@ -218,8 +218,10 @@ size_t fp8kv_decode_step_workspace_size(int num_seqs, int num_q_heads, int num_k
                                         int sliding_window, int num_splits);
 
 /*
- * fp8kv_decode_step -- one whole decode step in a single kernel launch: write each
- * sequence's new token into the cache, then decode attention over the cache.
+ * fp8kv_decode_step -- one whole decode step: write each sequence's new token into the
+ * cache, then decode attention over the cache, normally in a single kernel launch (when the
+ * split partials of one (sequence, kv head) are too many for one workgroup to merge
+ * quickly -- more than 32 float4 per thread -- a second, merge launch follows on `stream`).
  *
  * Equivalent to fp8kv_cache_write(key_new, value_new, ...) with num_tokens = num_seqs and
  * slot_mapping[b] = block_tables[b][(L_b-1)/16]*16 + (L_b-1)%16 for every sequence with
@@ -227,11 +229,13 @@ size_t fp8kv_decode_step_workspace_size(int num_seqs, int num_q_heads, int num_k
  * and a block id outside [0, num_blocks) writes nothing), followed by
  * fp8kv_paged_decode(...) with the same arguments.  The bytes written are identical; the
  * output agrees with the two-call path to within fp32 rounding (the split partials are
- * combined inside the launch by the last workgroup of each (sequence, kv head) instead of
- * in a second kernel).
+ * combined by the last workgroup of each (sequence, kv head) to finish, in a different
+ * order from the merge kernel).
  *
  *   key_new, value_new  device bf16 [num_seqs][num_kv_heads][head_dim]: the token at
- *                       position L_b - 1 of every sequence
+ *                       position L_b - 1 of every sequence.  The block holding position
+ *                       L_b - 1 must belong to sequence b alone (as with any write, two
+ *                       sequences may not write one slot).
  *   key_cache,
  *   value_cache         written and read
  *   workspace           at least fp8kv_decode_step_workspace_size() bytes, 256-byte

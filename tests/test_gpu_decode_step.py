@@ -49,7 +49,9 @@ def test_step_matches_oracle(Hq, Hkv, D, cache):
     _check_step(w)
 
 
-@pytest.mark.parametrize("num_splits", [1, 2, 5, 64])
+# 64 asks for 43 splits of 3 blocks (two merge batches per thread); 129 gives one block per
+# split, more partials than the in-kernel merge takes, so the step queues the merge kernel
+@pytest.mark.parametrize("num_splits", [1, 2, 5, 64, 129])
 def test_step_split_counts(num_splits):
     w = _mk(32, 8, 128, [5, 700, 2049, 16], cid=61)
     say(f"decode_step splits={num_splits}")
