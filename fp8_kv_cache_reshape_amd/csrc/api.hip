@@ -90,10 +90,18 @@ WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, in
     return l;
 }
 
-// The fused decode step keeps one arrival counter per (sequence, kv head) at the start of
-// its workspace (a fixed place, whatever split plan a call uses), then the partials.
-size_t step_counter_bytes(int num_seqs, int num_kv_heads) {
+// The fused decode step keeps its counters at the start of its workspace (a fixed place,
+// whatever split plan a call uses): one arrival counter per (sequence, kv head), padded to
+// 256 bytes, then one step claim counter per (sequence, kv head, wave) every 256 bytes.
+// The split partials follow.
+size_t arrival_bytes(int num_seqs, int num_kv_heads) {
     return ((size_t)num_seqs * num_kv_heads * sizeof(unsigned int) + 255) / 256 * 256;
+}
+static_assert(fp8kv::kDecodeWaves * fp8kv::kClaimStride * sizeof(unsigned int) == 1024,
+              "the public header documents 1024 claim-counter bytes per (sequence, kv head)");
+size_t step_counter_bytes(int num_seqs, int num_kv_heads) {
+    return arrival_bytes(num_seqs, num_kv_heads) +
+           (size_t)num_seqs * num_kv_heads * fp8kv::kDecodeWaves * fp8kv::kClaimStride * sizeof(unsigned int);
 }
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
@@ -160,6 +168,8 @@ int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const voi
     p.k_scale_q = 1.0f;
     p.v_scale_q = 1.0f;
     p.counters = nullptr;
+    p.claims = nullptr;
+    p.merge_in_kernel = 0;
     return FP8KV_OK;
 }
 
@@ -291,11 +301,17 @@ int fp8kv_decode_step(void* out, int out_dtype, const void* query, const void* k
     if (num_seqs == 0) return FP8KV_OK;
     if (!out || !key_new || !value_new) return FP8KV_ERR_NULL;
     if (!aligned16(out) || !aligned16(key_new) || !aligned16(value_new)) return FP8KV_ERR_SHAPE;
-    // merge inside the decode kernel when one workgroup merges a group cheaply, else in the
-    // merge kernel queued behind it
+    // several splits: workgroups claim steps from counters (load balance) and the last one
+    // of each group merges inside the decode kernel when one workgroup merges a group
+    // cheaply, else the merge kernel queued behind it does
     const bool fused = !p.write_final &&
                        fp8kv::fused_merge_fits(num_q_heads / num_kv_heads, head_dim, p.splits);
-    if (fused) p.counters = static_cast<unsigned int*>(workspace);
+    if (!p.write_final) {
+        p.counters = static_cast<unsigned int*>(workspace);
+        p.claims = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) +
+                                                   arrival_bytes(num_seqs, num_kv_heads));
+        p.merge_in_kernel = fused ? 1 : 0;
+    }
     p.out = out;
     p.out_f32 = out_dtype == FP8KV_F32;
     p.k_new = static_cast<const uint16_t*>(key_new);

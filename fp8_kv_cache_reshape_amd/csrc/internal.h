@@ -62,7 +62,14 @@ struct DecodeParams {
     float k_scale_q;               // quantisation scales of the step token (fp8 caches)
     float v_scale_q;
     unsigned int* counters;        // [B][Hkv] split arrival counters (zero between calls), or null
+    unsigned int* claims;          // [B][Hkv][waves] step claim counters, kClaimStride apart
+                                   // (zero between calls), or null; needs `counters`
+    int merge_in_kernel;           // with `counters`: the last workgroup of a group merges
 };
+
+// Claim counters sit this many 32-bit words (256 bytes) apart, so that the counters of
+// different waves and groups never share a line.
+constexpr int kClaimStride = 64;
 
 // Context window of one sequence in blocks: positions [lo, L), blocks [blk0, blk0+nblk).
 struct SeqWindow {

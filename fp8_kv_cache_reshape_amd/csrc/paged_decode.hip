@@ -41,6 +41,7 @@
 // key registers, and the next value rows as soon as P.V has consumed the value
 // registers, so every wave keeps a step of loads in flight while it computes, without a
 // second register buffer.  Block ids come from wave-uniform loads one step ahead.
+#include <climits>
 #include <type_traits>
 
 #include "codec.h"
@@ -55,10 +56,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFlushSteps = 4;         // wave steps summed in the matrix-core accumulator
-#ifndef FP8KV_PREFETCH
-#define FP8KV_PREFETCH 1
-#endif
-constexpr int kPrefetch = FP8KV_PREFETCH;   // wave steps of KV loads kept in flight
 constexpr float kRescaleLog2 = 8.0f;   // reference max moves only when a score exceeds it by 2^8
 
 // 8 E4M3 codes (bytes of lo then hi, in memory order) -> 8 bf16, exactly.
@@ -138,12 +135,15 @@ constexpr int kMergeLaneSplits = 32;
 constexpr int kMergeLaneBatch = 16;
 
 // Log-sum-exp merge of the `ns` split partials of the G query heads of (sequence b, kv
-// head h), by one workgroup, into `out` (compensated sums; x v_scale / Lambda).
+// head h), by one workgroup, into `out` (x v_scale / Lambda).
 // Lanes 2q and 2q + 1 own channel quad q and read the even and the odd splits.  Every
 // (m, l) pair of a lane and its first kMergeLaneBatch partials are requested at once (one
 // round trip for up to 2 * kMergeLaneBatch splits); the pair agrees on the maximum, each
 // lane forms the weights, normaliser and weighted sums of its splits, and the pair
-// combines through lane swaps -- no LDS and no barrier.
+// combines through lane swaps -- no LDS and no barrier.  The sums are plain fp32: over at
+// most 2 * kMergeLaneSplits terms their relative rounding error stays below 2^-18, far
+// under the bf16 rounding of the output (the merge kernel, which takes up to kMaxSplits
+// partials, compensates its sums).
 template <int D>
 __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) {
     const int par = threadIdx.x & 1;
@@ -175,37 +175,28 @@ __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) 
         for (int u = 0; u < kMergeLaneSplits; ++u) M = fmaxf(M, mv[u].x);
         M = fmaxf(M, pair_swap(M));
         const float Mu = (M == -INFINITY) ? 0.0f : M;
-        float lh = 0.0f, ll = 0.0f;
-        float4 hi = make_float4(0.f, 0.f, 0.f, 0.f), lo = hi;
-#pragma unroll
-        for (int u = 0; u < kMergeLaneSplits; ++u)
-            comp_add(lh, ll, __builtin_amdgcn_exp2f(mv[u].x - Mu) * mv[u].y);   // 0 if absent
-#pragma unroll
-        for (int u0 = 0; u0 < kMergeLaneSplits; u0 += kMergeLaneBatch) {
-            if (u0 > 0) {
-                if (2 * u0 >= ns) break;
-                load_x(u0);
-            }
+        float lam = 0.0f;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        auto accumulate = [&](int u0) {
 #pragma unroll
             for (int u = 0; u < kMergeLaneBatch; ++u) {
-                const float ws = __builtin_amdgcn_exp2f(mv[u0 + u].x - Mu);
-                comp_add(hi.x, lo.x, ws * xv[u].x);
-                comp_add(hi.y, lo.y, ws * xv[u].y);
-                comp_add(hi.z, lo.z, ws * xv[u].z);
-                comp_add(hi.w, lo.w, ws * xv[u].w);
+                const float ws = __builtin_amdgcn_exp2f(mv[u0 + u].x - Mu);   // 0 if absent
+                lam = fmaf(ws, mv[u0 + u].y, lam);
+                a.x = fmaf(ws, xv[u].x, a.x);
+                a.y = fmaf(ws, xv[u].y, a.y);
+                a.z = fmaf(ws, xv[u].z, a.z);
+                a.w = fmaf(ws, xv[u].w, a.w);
             }
-        }
-        // (hi, lo) + the partner's (hi', lo'): hi + hi' with its rounding error, plus lo + lo'
-        auto pair_sum = [](float h0, float l0) {
-            const float h1 = pair_swap(h0), l1 = pair_swap(l0);
-            float sh = h0, sc = l0 + l1;
-            comp_add(sh, sc, h1);
-            return sh + sc;
         };
-        const float lam = pair_sum(lh, ll);
+        accumulate(0);
+        if (ns > 2 * kMergeLaneBatch) {
+            load_x(kMergeLaneBatch);
+            accumulate(kMergeLaneBatch);
+        }
+        lam += pair_swap(lam);
         const float scale = lam > 0.0f ? p.v_scale / lam : 0.0f;
-        const float r0 = pair_sum(hi.x, lo.x), r1 = pair_sum(hi.y, lo.y);
-        const float r2 = pair_sum(hi.z, lo.z), r3 = pair_sum(hi.w, lo.w);
+        const float r0 = a.x + pair_swap(a.x), r1 = a.y + pair_swap(a.y);
+        const float r2 = a.z + pair_swap(a.z), r3 = a.w + pair_swap(a.w);
         const int64_t o = (hq0 + hh) * D + 4 * c4 + 2 * par;
         store_out(p.out, p.out_f32, o, scale * (par ? r2 : r0));
         store_out(p.out, p.out_f32, o + 1, scale * (par ? r3 : r1));
@@ -215,7 +206,7 @@ __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) 
 // Two waves per SIMD (<= 256 registers per lane) wherever the tile fits; head_dim 256 and
 // 2-byte caches need more and run one wave per SIMD.
 template <int D, bool FP8>
-constexpr int partial_waves_per_eu() { return kPrefetch == 1 && ((D <= 128 && FP8) || D == 64) ? 2 : 1; }
+constexpr int partial_waves_per_eu() { return (D <= 128 && FP8) || D == 64 ? 2 : 1; }
 
 template <int D, bool FP8>
 __global__ __launch_bounds__(64 * kDecodeWaves)
@@ -241,12 +232,11 @@ void decode_partial_kernel(DecodeParams p) {
 
     const SeqWindow w = seq_window(p.context_lens[b], p.max_context_len, p.max_blocks_per_seq,
                                    p.sliding_window);
-    const int sb = split * p.blocks_per_split;
-    const int se = min(w.nblk, sb + p.blocks_per_split);
+    const int ns = (w.nblk + p.blocks_per_split - 1) / p.blocks_per_split;   // workgroups taking part
     const int64_t out_row0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * D;
-    if (sb >= se) {
-        // an empty context: the first split writes the zero output when no merge will
-        if ((p.write_final || p.counters != nullptr) && split == 0)
+    if (split >= ns) {
+        // an empty context: the first split writes the zero output when no merge kernel will
+        if ((p.write_final || (p.counters != nullptr && p.merge_in_kernel)) && split == 0)
             for (int i = threadIdx.x; i < G * D; i += blockDim.x) store_out(p.out, p.out_f32, out_row0 + i, 0.0f);
         return;
     }
@@ -270,12 +260,12 @@ void decode_partial_kernel(DecodeParams p) {
     // address space lets the wave-uniform id reads below be scalar loads, which do not queue
     // behind the vector KV loads in flight.
     typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
-    const ConstI32Ptr bt = (ConstI32Ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq + w.blk0 + sb);
+    const ConstI32Ptr bt = (ConstI32Ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq + w.blk0);
     const float sscale = p.score_scale;
-    const int nblk = se - sb;                     // blocks of this split
-    const int nsteps = (nblk + 3) >> 2;
+    const int nblk = w.nblk;                      // blocks of the window
+    const int nsteps = (nblk + 3) >> 2;           // wave steps (4 blocks) of the window
 
-    // Physical ids of the 4 blocks of wave step `stp` (-1 past the split or out of range);
+    // Physical ids of the 4 blocks of wave step `stp` (-1 past the window or out of range);
     // the addresses are wave-uniform.  Lanes pick their key block (n/4) and their
     // score/value block (grp).
     auto step_ids = [&](int stp, int& kid, int& vid) {
@@ -290,8 +280,8 @@ void decode_partial_kernel(DecodeParams p) {
     };
     // Loads are unconditional (branch-free, so the compiler can count them in flight): a
     // missing block (-1) reads block 0, which exists whenever any block can be valid, and
-    // its scores are masked and its values zeroed below.  kPrefetch register buffers
-    // rotate over the wave's steps, so kPrefetch steps of loads are in flight.
+    // its scores are masked and its values zeroed below.  One step of loads is in flight
+    // while the previous step is processed.
     struct Buf {
         uint4 k[4][K16];
         uint4 v[NT][V16];
@@ -345,13 +335,13 @@ void decode_partial_kernel(DecodeParams p) {
 
     int chunk_steps = 0;
     // One wave step over the 4 blocks of step `stp` held in `bf`; refills `bf` with step
-    // `nstp` (if it exists) as soon as each half of the buffer has been consumed.
-    // `steady` (a compile-time tag) marks steps whose successor is known to exist: their
-    // prefetch is unconditional, which keeps the loads in straight-line code so the
-    // compiler can wait for exactly the loads each use needs.
+    // `nstp` as soon as each half of the buffer has been consumed.  `steady` (a compile-time
+    // tag) marks steps with a successor: their prefetch is unconditional, which keeps the
+    // loads in straight-line code so the compiler can wait for exactly the loads each use
+    // needs; the wave's last step (no successor) prefetches nothing.
     auto process = [&](Buf& bf, int stp, int nstp, auto steady) {
         constexpr bool kSteady = decltype(steady)::value;
-        const bool more = kSteady || nstp < nsteps;
+        constexpr bool more = kSteady;
         int nkid = -1, nvid = -1;
         if (more) step_ids(nstp, nkid, nvid);
 
@@ -381,7 +371,7 @@ void decode_partial_kernel(DecodeParams p) {
 
             // ---- mask and scale: lane holds block grp of the step, tokens 4s+r, head n
             const bool vval = bf.vid >= 0;
-            const int pos0 = (w.blk0 + sb + 4 * stp + grp) * kBlockSize;
+            const int pos0 = (w.blk0 + 4 * stp + grp) * kBlockSize;
             const int tlo = vval ? max(0, w.lo - pos0) : kBlockSize;   // missing block: no tokens
             const int thi = vval ? min(kBlockSize, w.L - pos0) : 0;
             float sv[16];
@@ -482,13 +472,27 @@ void decode_partial_kernel(DecodeParams p) {
         }
     };
 
-    // Fused decode step: the wave that owns the sequence's last block (its last step)
-    // quantises the step token and stores it at position L-1 before that block is read.
-    // Lanes [0, D/8) write 8 key channels each, lanes [32, 32 + D/8) 8 value channels.  The
-    // token and its block id are requested before the first KV loads; the stores go out
-    // after them unless the last block is among the first loads.
-    const bool writer = p.k_new != nullptr && se == w.nblk && wave == (nsteps - 1) % kDecodeWaves;
-    const int wave_steps = wave < nsteps ? (nsteps - 1 - wave) / kDecodeWaves + 1 : 0;
+    // ---- which wave steps this wave processes
+    // Slot `wave` of this (sequence, kv head) owns the window steps 4k + wave, k = 0, 1, ...
+    // (its pool).  Workgroup `split` (of the ns taking part) takes pool entries split and
+    // split + ns; after those it claims entries from the slot's counter when the caller
+    // provides one -- whichever wave is free takes the next step, which evens out speed
+    // differences between compute units and XCDs -- and otherwise continues statically with
+    // split + 2ns, split + 3ns, ...  With a step token to write, the window's last step
+    // (which holds position L-1) leaves the pools: the writer wave writes the token and
+    // then processes that step first, so its own loads of the block come after its stores.
+    const bool writing = p.k_new != nullptr;
+    const int np = writing ? nsteps - 1 : nsteps;            // steps in the pools
+    const bool writer = writing && split == 0 && wave == (nsteps - 1) % kDecodeWaves;
+    auto pool_step = [&](int k) {
+        const int st = kDecodeWaves * k + wave;
+        return st < np ? st : -1;
+    };
+    unsigned int* claim = p.claims == nullptr ? nullptr
+        : p.claims + (((int64_t)b * p.num_kv_heads + h) * kDecodeWaves + wave) * kClaimStride;
+
+    // Fused decode step: lanes [0, D/8) write 8 key channels of the token each, lanes
+    // [32, 32 + D/8) 8 value channels.
     uint4 tok = make_uint4(0, 0, 0, 0);
     int tok_blk = -1;
     if (writer) {
@@ -530,42 +534,48 @@ void decode_partial_kernel(DecodeParams p) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
     };
-    // the writer's prefetch reaches the last block at once only when it has few steps
-    if (writer && wave_steps <= kPrefetch) store_step_token();
-
-    Buf buf[kPrefetch];
+    // Pool entries e < e_static of this wave are static (split + e*ns).  With claim
+    // counters, the last entries of the slot -- about two per workgroup, enough to absorb
+    // the differences in speed that show up by the end -- are claimed instead: entry
+    // e >= e_static is e_static*ns + (a claim on the slot's counter).  Claims are only used
+    // at the end because each one is a device-scope atomic whose completion the step loads
+    // issued before it also wait for.  A claim is requested at the end of an iteration,
+    // after that step's loads, and read at the end of the next one.
+    const bool dyn = claim != nullptr;
+    const int slot_entries = np > wave ? (np - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
+    const int e_static = dyn ? max(3, slot_entries / ns - 2) : INT_MAX;
+    int cur = writer ? nsteps - 1 : pool_step(split);
+    int e_nxt = writer ? 0 : 1;                   // pool entry that `nxt` is
+    int nxt = cur >= 0 ? pool_step(split + e_nxt * ns) : -1;
+    if (cur >= 0) {
+        if (writer) store_step_token();
+        Buf buf;
+        step_ids(cur, buf.kid, buf.vid);
+        issue_k(buf, buf.kid);
+        issue_v(buf, buf.vid);
+        // Consume the query operands here, once: afterwards the compiler knows they have
+        // arrived, and the loop waits only for the key or value loads each use needs
+        // (without this it waits for every load in flight at the top of each step).
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
-        const int stp = wave + j * kDecodeWaves;
-        buf[j].kid = buf[j].vid = -1;
-        if (stp < nsteps) {
-            step_ids(stp, buf[j].kid, buf[j].vid);
-            issue_k(buf[j], buf[j].kid);
-            issue_v(buf[j], buf[j].vid);
+        for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[kk]));
+        unsigned int c_pend = 0;                  // claim for entry e_nxt + 1, when claimed
+        while (nxt >= 0) {
+            process(buf, cur, nxt, std::true_type{});
+            // (keeps the read of the claim, and the wait for it, here)
+            asm volatile("" : "+v"(c_pend));
+            const int e = e_nxt + 1;
+            const int k = e >= e_static ? e_static * ns + (int)__builtin_amdgcn_readfirstlane(c_pend)
+                                        : split + e * ns;
+            cur = nxt;
+            nxt = pool_step(k);
+            e_nxt = e;
+            // request entry e + 1 (a wrapping increment with no reachable wrap: unlike an add,
+            // the compiler does not turn it into a wave-wide form that waits for the result)
+            c_pend = 0;
+            if (e + 1 >= e_static && nxt >= 0 && lane == 0)
+                c_pend = __builtin_amdgcn_atomic_inc32(claim, 0xFFFFFFFFu, __ATOMIC_RELAXED, "agent");
         }
-    }
-    if (writer && wave_steps > kPrefetch) store_step_token();
-    // Consume the query operands here, once: afterwards the compiler knows they have
-    // arrived, and the loop waits only for the key or value loads each use needs (without
-    // this it waits for every load in flight at the top of each step).
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[kk]));
-    int st = wave;
-    // steady state: every step of the round has a successor kPrefetch rounds later
-    for (; st + (2 * kPrefetch - 1) * kDecodeWaves < nsteps; st += kPrefetch * kDecodeWaves) {
-#pragma unroll
-        for (int j = 0; j < kPrefetch; ++j) {
-            const int stp = st + j * kDecodeWaves;
-            process(buf[j], stp, stp + kPrefetch * kDecodeWaves, std::true_type{});
-        }
-    }
-    // the last rounds, whose successors may not exist
-    for (; st < nsteps; st += kPrefetch * kDecodeWaves) {
-#pragma unroll
-        for (int j = 0; j < kPrefetch; ++j) {
-            const int stp = st + j * kDecodeWaves;
-            if (stp < nsteps) process(buf[j], stp, stp + kPrefetch * kDecodeWaves, std::false_type{});
-        }
+        process(buf, cur, -1, std::false_type{});
     }
     flush();
 
@@ -618,36 +628,39 @@ void decode_partial_kernel(DecodeParams p) {
         }
     }
 
-    // Fused merge: the last workgroup of this (sequence, kv head) to finish combines the
-    // partials of all its splits.  Each workgroup publishes its partials, then counts
-    // itself in; the one that completes the count merges and zeroes the counter for the
-    // next call.  No workgroup ever waits for another.
-    // Ordering: the partials are device-scope stores, and every thread waits until its own
-    // have completed (reached the device coherence point) before the barrier after which
-    // thread 0 counts in with a device-scope atomic.  The workgroup that completes the
-    // count invalidates its caches (agent-scope acquire) before any of its threads reads a
-    // partial.  This is the ordering an agent-scope release/acquire pair gives, without the
-    // release's L2 write-back, which only data stored through the L2 without device scope
-    // would need.
+    // Arrival: the last workgroup of this (sequence, kv head) to finish resets the group's
+    // counters for the next call and, when asked, merges the partials of all its splits.
+    // No workgroup ever waits for another.
+    // Ordering of the merge: the partials are device-scope stores, and every thread waits
+    // until its own have completed (reached the device coherence point) before the barrier
+    // after which thread 0 counts in with a device-scope atomic.  The workgroup that
+    // completes the count invalidates its caches (agent-scope acquire) before any of its
+    // threads reads a partial.  This is the ordering an agent-scope release/acquire pair
+    // gives, without the release's L2 write-back, which only data stored through the L2
+    // without device scope would need.
     if (!p.write_final && p.counters != nullptr) {
         __shared__ int s_last;
-        const int ns = (w.nblk + p.blocks_per_split - 1) / p.blocks_per_split;
-        __builtin_amdgcn_s_waitcnt(0);                   // this thread's partial stores done
-        __syncthreads();                                  // ... and every thread's
+        if (p.merge_in_kernel) __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores done
+        __syncthreads();                                         // ... and every thread's
         if (threadIdx.x == 0) {
             unsigned int* cnt = p.counters + (int64_t)b * p.num_kv_heads + h;
             const unsigned int old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const bool last = old + 1 == (unsigned int)ns;
             if (last) {
+                // every wave of the group has made its last claim
                 __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (p.claims != nullptr)
+                    for (int v = 0; v < kDecodeWaves; ++v)
+                        __hip_atomic_store(p.claims + (((int64_t)b * p.num_kv_heads + h) * kDecodeWaves + v) * kClaimStride,
+                                           0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 // drop stale copies of the partials from this CU's L1 and this XCD's L2;
                 // the barrier below orders the other threads' loads after it
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                if (p.merge_in_kernel) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             s_last = (int)last;
         }
         __syncthreads();
-        if (s_last) merge_group<D>(p, b, h, G, ns);
+        if (s_last && p.merge_in_kernel) merge_group<D>(p, b, h, G, ns);
     }
 }
 

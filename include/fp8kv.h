@@ -209,9 +209,11 @@ int fp8kv_paged_decode_merge(void* out, int out_dtype,
 
 /*
  * fp8kv_decode_step_workspace_size -- bytes of device workspace fp8kv_decode_step needs
- * (0 on invalid arguments): first one 32-bit arrival counter per (sequence, kv head),
- * padded to a multiple of 256 bytes, then the split partials of fp8kv_paged_decode.  The
- * counters sit at the same place whatever split plan a call uses.
+ * (0 on invalid arguments): first the counter region -- one 32-bit arrival counter per
+ * (sequence, kv head), padded to a multiple of 256 bytes, then one 32-bit step claim
+ * counter per (sequence, kv head, wave of a decode workgroup) every 256 bytes, that is
+ * num_seqs*num_kv_heads*1024 bytes -- then the split partials of fp8kv_paged_decode.  The
+ * counter region sits at the same place whatever split plan a call uses.
  */
 size_t fp8kv_decode_step_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                         int head_dim, int block_size, int max_context_len,
@@ -240,10 +242,11 @@ size_t fp8kv_decode_step_workspace_size(int num_seqs, int num_q_heads, int num_k
  *   value_cache         written and read
  *   workspace           at least fp8kv_decode_step_workspace_size() bytes, 256-byte
  *                       aligned.  Its counter region (the first
- *                       round_up(num_seqs*num_kv_heads*4, 256) bytes) must be zero before
- *                       the first call (allocate the workspace zero-filled); every call
- *                       leaves it zero again, so consecutive steps can reuse it even as the
- *                       split plan changes.  One workspace serves one call at a time.
+ *                       round_up(num_seqs*num_kv_heads*4, 256) + num_seqs*num_kv_heads*1024
+ *                       bytes) must be zero before the first call (allocate the workspace
+ *                       zero-filled); every call leaves it zero again, so consecutive steps
+ *                       can reuse it even as the split plan changes.  One workspace serves
+ *                       one call at a time.
  * Other arguments, layout and error behaviour as for fp8kv_paged_decode.
  */
 int fp8kv_decode_step(void* out, int out_dtype, const void* query,

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import fp8_kv_cache_reshape_amd as F
+import oracle
 import synthetic as syn
 from gpu_util import (BF16, E4M3, DeviceInputs, assert_close, dev_caches, gpu_decode,
                       gpu_decode_step, gpu_write, oracle_decode, oracle_write, say, to_host_bits)
@@ -108,7 +109,11 @@ def test_step_agrees_with_two_calls():
     gpu_write(w, layer, kc2, vc2, rows=w.prefix_token_rows())
     one, _ = gpu_decode_step(w, layer, kc2, vc2, out_f32=True)
     assert torch.equal(kc, kc2) and torch.equal(vc, vc2)
-    assert np.abs(one - two).max() <= 1e-6 * np.abs(two).max() + 1e-9
+    # Both merge the same fp32 partials: sum_s w_s x_s / Lambda with sum_s w_s |x_s| <=
+    # max|V| * Lambda.  The in-kernel merge sums at most 64 terms in plain fp32, the merge
+    # kernel compensates, so they differ by at most about 2 * 64 * 2^-24 * max|V|.
+    vmax = float(np.nanmax(np.abs(oracle.e4m3_decode(to_host_bits(vc))))) * layer.v_scale   # NaN: unwritten
+    assert np.abs(one - two).max() <= 2 * 64 * 2.0 ** -24 * vmax
 
 
 def test_step_headline_128k():
