@@ -149,7 +149,7 @@ __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) 
     const int par = threadIdx.x & 1;
     const int NQ = G * D / 4;                                  // channel quads of the group
     const int64_t hq0 = (int64_t)b * p.num_q_heads + (int64_t)h * G;
-    for (int q = threadIdx.x >> 1; q < NQ; q += blockDim.x >> 1) {
+    for (int q = threadIdx.x >> 1; q < NQ; q += 32 * kDecodeWaves) {   // lane pairs of the workgroup
         const int hh = q / (D / 4), c4 = q % (D / 4);
         const int64_t row = (hq0 + hh) * p.splits;
         // one base pointer per array: the loads below differ by constant offsets
@@ -221,6 +221,17 @@ void decode_partial_kernel(DecodeParams p) {
     constexpr int TILE_BYTES = kBlockSize * D * ES;
 
     extern __shared__ float lds[];
+    // Read every argument now, in one batch of scalar loads: left to itself the compiler
+    // loads each field just before its first use, which puts several round trips to memory
+    // in series before the first KV load.
+    asm volatile("" :: "s"(p.out), "s"(p.query), "s"(p.key_cache), "s"(p.value_cache),
+                 "s"(p.block_tables), "s"(p.context_lens), "s"(p.ws_ml), "s"(p.ws_acc));
+    asm volatile("" :: "s"(p.k_new), "s"(p.v_new), "s"(p.counters), "s"(p.claims),
+                 "s"(p.max_blocks_per_seq), "s"(p.max_context_len), "s"(p.num_q_heads),
+                 "s"(p.num_kv_heads), "s"(p.num_blocks), "s"(p.sliding_window));
+    asm volatile("" :: "s"(p.score_scale), "s"(p.v_scale), "s"(p.splits), "s"(p.blocks_per_split),
+                 "s"(p.write_final), "s"(p.k_scale_q), "s"(p.v_scale_q), "s"(p.merge_in_kernel),
+                 "s"(p.out_f32));
     const int split = kHeadsFastest ? blockIdx.y : blockIdx.x;
     const int h = kHeadsFastest ? blockIdx.x : blockIdx.y;
     const int b = blockIdx.z;
@@ -230,14 +241,30 @@ void decode_partial_kernel(DecodeParams p) {
     const int grp = lane >> 4;
     const int G = p.num_q_heads / p.num_kv_heads;
 
-    const SeqWindow w = seq_window(p.context_lens[b], p.max_context_len, p.max_blocks_per_seq,
-                                   p.sliding_window);
+    // The block ids of this wave's first pool step (4*split + wave) do not depend on the
+    // context length when there is no sliding window (the window then starts at block 0):
+    // request them together with the length, so that the first KV loads wait for one round
+    // trip to memory instead of two.  They are used only if that step is the wave's first.
+    typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
+    const int st_early = kDecodeWaves * split + wave;
+    int id_early[4];
+    {
+        const ConstI32Ptr row = (ConstI32Ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int i = 4 * st_early + x;
+            id_early[x] = (p.sliding_window <= 0 && i < p.max_blocks_per_seq) ? row[i] : -1;
+        }
+    }
+    // (a scalar load, like the block ids)
+    const SeqWindow w = seq_window(((ConstI32Ptr)p.context_lens)[b], p.max_context_len,
+                                   p.max_blocks_per_seq, p.sliding_window);
     const int ns = (w.nblk + p.blocks_per_split - 1) / p.blocks_per_split;   // workgroups taking part
     const int64_t out_row0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * D;
     if (split >= ns) {
         // an empty context: the first split writes the zero output when no merge kernel will
         if ((p.write_final || (p.counters != nullptr && p.merge_in_kernel)) && split == 0)
-            for (int i = threadIdx.x; i < G * D; i += blockDim.x) store_out(p.out, p.out_f32, out_row0 + i, 0.0f);
+            for (int i = threadIdx.x; i < G * D; i += 64 * kDecodeWaves) store_out(p.out, p.out_f32, out_row0 + i, 0.0f);
         return;
     }
 
@@ -245,11 +272,12 @@ void decode_partial_kernel(DecodeParams p) {
     // [grp*DG + 8kk, +8) for kk = 0..KK-1; heads >= G are zero columns.
     bf16x8 qop[KK];
     {
-        const uint16_t* qrow = p.query + out_row0 + (int64_t)n * D + grp * DG;
+        // heads n >= G read head 0's row (in bounds) and are zeroed: no branch around the loads
+        const uint16_t* qrow = p.query + out_row0 + (int64_t)(n < G ? n : 0) * D + grp * DG;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (n < G) u = load16(qrow + 8 * kk);
+            uint4 u = load16(qrow + 8 * kk);
+            if (n >= G) u = make_uint4(0, 0, 0, 0);
             qop[kk] = __builtin_bit_cast(bf16x8, u);
         }
     }
@@ -259,7 +287,6 @@ void decode_partial_kernel(DecodeParams p) {
     // The block table is read-only while the kernel runs: reading it through the constant
     // address space lets the wave-uniform id reads below be scalar loads, which do not queue
     // behind the vector KV loads in flight.
-    typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
     const ConstI32Ptr bt = (ConstI32Ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq + w.blk0);
     const float sscale = p.score_scale;
     const int nblk = w.nblk;                      // blocks of the window
@@ -268,15 +295,18 @@ void decode_partial_kernel(DecodeParams p) {
     // Physical ids of the 4 blocks of wave step `stp` (-1 past the window or out of range);
     // the addresses are wave-uniform.  Lanes pick their key block (n/4) and their
     // score/value block (grp).
-    auto step_ids = [&](int stp, int& kid, int& vid) {
-        int id[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) id[x] = (4 * stp + x < nblk) ? bt[4 * stp + x] : -1;
+    auto pick_ids = [&](const int* id, int& kid, int& vid) {
         const int kq = n >> 2;
         kid = kq == 0 ? id[0] : kq == 1 ? id[1] : kq == 2 ? id[2] : id[3];
         vid = grp == 0 ? id[0] : grp == 1 ? id[1] : grp == 2 ? id[2] : id[3];
         if ((unsigned)kid >= (unsigned)p.num_blocks) kid = -1;
         if ((unsigned)vid >= (unsigned)p.num_blocks) vid = -1;
+    };
+    auto step_ids = [&](int stp, int& kid, int& vid) {
+        int id[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) id[x] = (4 * stp + x < nblk) ? bt[4 * stp + x] : -1;
+        pick_ids(id, kid, vid);
     };
     // Loads are unconditional (branch-free, so the compiler can count them in flight): a
     // missing block (-1) reads block 0, which exists whenever any block can be valid, and
@@ -492,15 +522,13 @@ void decode_partial_kernel(DecodeParams p) {
         : p.claims + (((int64_t)b * p.num_kv_heads + h) * kDecodeWaves + wave) * kClaimStride;
 
     // Fused decode step: lanes [0, D/8) write 8 key channels of the token each, lanes
-    // [32, 32 + D/8) 8 value channels.
-    uint4 tok = make_uint4(0, 0, 0, 0);
-    int tok_blk = -1;
-    if (writer) {
-        tok_blk = ((ConstI32Ptr)p.block_tables)[(int64_t)b * p.max_blocks_per_seq + (w.L - 1) / kBlockSize];
-        const int c = min(lane & 31, D / 8 - 1);
-        tok = load16((lane >= 32 ? p.v_new : p.k_new) + ((int64_t)b * p.num_kv_heads + h) * D + c * 8);
-    }
+    // [32, 32 + D/8) 8 value channels.  Load and store sit in one branch: a token load left
+    // pending across branches makes the compiler wait for every load in flight (the query
+    // rows included) before the first KV loads of every wave.
     auto store_step_token = [&]() {
+        const int tok_blk = ((ConstI32Ptr)p.block_tables)[(int64_t)b * p.max_blocks_per_seq + (w.L - 1) / kBlockSize];
+        const uint4 tok = load16((lane >= 32 ? p.v_new : p.k_new) + ((int64_t)b * p.num_kv_heads + h) * D +
+                                 min(lane & 31, D / 8 - 1) * 8);
         const int c = lane & 31;
         if ((unsigned)tok_blk < (unsigned)p.num_blocks && c < D / 8) {
             const bool val = lane >= 32;
@@ -550,7 +578,14 @@ void decode_partial_kernel(DecodeParams p) {
     if (cur >= 0) {
         if (writer) store_step_token();
         Buf buf;
-        step_ids(cur, buf.kid, buf.vid);
+        if (cur == st_early && p.sliding_window <= 0) {
+            int id[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) id[x] = (4 * cur + x < nblk) ? id_early[x] : -1;
+            pick_ids(id, buf.kid, buf.vid);
+        } else {
+            step_ids(cur, buf.kid, buf.vid);
+        }
         issue_k(buf, buf.kid);
         issue_v(buf, buf.vid);
         // Consume the query operands here, once: afterwards the compiler knows they have
@@ -599,7 +634,7 @@ void decode_partial_kernel(DecodeParams p) {
         }
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kDecodeWaves) {
         const int head = idx / D;
         const int i = idx - head * D;
         float M = -INFINITY;
