@@ -103,7 +103,8 @@ class DecodeBench:
                                 w.num_blocks, layer.k_scale, layer.v_scale, self.stream)
             self.kc.append(kc)
             self.vc.append(vc)
-        del kp, vp, sp
+        # kept for the bulk cache-write measurement
+        self.kp, self.vp, self.sp, self.T_prefix = kp, vp, sp, len(prefix)
         # the step's new token of every sequence (all sequences are non-empty here)
         rows = w.step_token_rows()
         assert len(rows) == B, "every sequence needs a step token"
@@ -216,6 +217,43 @@ class DecodeBench:
             out["merge_ms"] = avg(lambda i: self.merge()) if self.nsplits > 1 else 0.0
         return out
 
+    def step_percentiles(self, steps: int):
+        """Region C: every step between its own pair of events (the events add a little
+        work between steps): p10, median and p90 of the step time in ms."""
+        torch = self.torch
+        R = len(self.kc)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        self.step(0)
+        torch.cuda.synchronize()
+        for s, (a, b) in enumerate(ev):
+            a.record()
+            self.step(s % R)
+            b.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev])
+        return {q: float(np.percentile(t, q)) for q in (10, 50, 90)}
+
+    def bulk_write_ms(self, launches: int):
+        """The whole context written by one fp8kv_cache_write call, back to back over the
+        rotated instances: average ms per call."""
+        torch, F, w, L = self.torch, self.F, self.w, self.layer
+        R = len(self.kc)
+
+        def write(i):
+            F.fp8kv_cache_write(self.kp, self.vp, self.kc[i], self.vc[i], self.cdt, self.sp, self.T_prefix,
+                                w.num_kv_heads, w.head_dim, BLOCK, w.num_blocks, L.k_scale, L.v_scale,
+                                self.stream)
+        write(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(launches):
+            write(s % R)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / launches
+
 
 PROFILE_SUMMARY = "profiles/decode_llama8b_b1_128k.txt"
 KERNEL_SOURCES = ["fp8_kv_cache_reshape_amd/csrc/paged_decode.hip",
@@ -242,6 +280,52 @@ def measured_traffic(root: str):
     return None
 
 
+def read_ceiling(torch, root: str, gib: int = 2, launches: int = 10) -> dict:
+    """Streaming-read ceiling of this GPU: a plain kernel reading `gib` GiB once with 16-byte
+    nontemporal loads (libfp8kv_probe.so), averaged over back-to-back launches, for a few
+    grid sizes; the best is the ceiling."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(root, "fp8_kv_cache_reshape_amd", "libfp8kv_probe.so"))
+    lib.fp8kv_probe_read_granule.restype = ctypes.c_size_t
+    lib.fp8kv_probe_read_granule.argtypes = [ctypes.c_int]
+    lib.fp8kv_probe_read.restype = ctypes.c_int
+    lib.fp8kv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    grids = (1024, 2048, 4096, 8192)
+    n = (gib << 30) // lib.fp8kv_probe_read_granule(max(grids)) * lib.fp8kv_probe_read_granule(max(grids))
+    buf = torch.ones(n, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    rates = {}
+    for grid in grids:
+        call = lambda: lib.fp8kv_probe_read(buf.data_ptr(), n, grid, sink.data_ptr(), stream)
+        for _ in range(2):
+            assert call() == 0, "read-ceiling probe launch failed"
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        rates[grid] = n / (e0.elapsed_time(e1) / launches * 1e-3) / 1e9
+    del buf
+    best = max(rates, key=rates.get)
+    return {"GBps": round(rates[best], 1), "bytes": n, "grid": best,
+            "GBps_by_grid": {str(g): round(r, 1) for g, r in rates.items()},
+            "kernel": "grid-stride 16-byte nontemporal reads, 256 threads per workgroup, 8 loads in flight"}
+
+
+def _oracle_threads() -> int:
+    """Host threads for the multi-threaded oracle run: the CPUs this process may use, at most
+    16 (one GPU's share of the box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def cpu_baseline(w, layer, pairs_kv_heads: int = 2) -> dict:
     """The oracle (plain C, fp64, single thread) on a bounded sample of the same workload:
     every query head of the first `pairs_kv_heads` KV heads over the full context."""
@@ -260,11 +344,39 @@ def cpu_baseline(w, layer, pairs_kv_heads: int = 2) -> dict:
     frac = pairs_kv_heads / w.num_kv_heads
     sample_bytes = algorithmic_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, 1,
                                      layer.sliding_window)["pass1"] * frac
+    # the same oracle over every query head, one (sequence, head) pair per task on a thread
+    # pool: the C calls release the interpreter lock, so the threads run in parallel
+    from concurrent.futures import ThreadPoolExecutor
+    threads = _oracle_threads()
+    all_pairs = [np.array([(b, hq)], np.int32) for b in range(w.num_seqs) for hq in range(w.num_q_heads)]
+    args = (w.q, okc, ovc, oracle.CACHE_E4M3, w.block_tables, w.context_lens, w.num_q_heads,
+            w.num_kv_heads, w.head_dim, BLOCK, layer.k_scale, layer.v_scale, layer.sliding_window)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda pr: oracle.paged_decode_pairs(pr, *args), all_pairs))
+    dt_mt = time.perf_counter() - t0
+    full_bytes = algorithmic_bytes(w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, 1,
+                                   layer.sliding_window)["pass1"]
     return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"fp64 C oracle decode of query heads 0..{len(pairs) - 1} (KV heads 0..{pairs_kv_heads - 1} "
                       f"of {w.num_kv_heads}) over the full {int(w.context_lens[0])}-token context, single thread; "
-                      f"GB/s = the sample's algorithmic KV+q+table bytes / time"}
+                      f"GB/s = the sample's algorithmic KV+q+table bytes / time",
+            "multi_thread": {"value": round(full_bytes / dt_mt / 1e9, 4), "unit": "GB/s", "cores": threads,
+                             "seconds": round(dt_mt, 3), "ms_per_step": round(dt_mt * 1e3, 1),
+                             "sample": f"every query head ({len(all_pairs)} (sequence, head) tasks) of the "
+                                       f"whole step on {threads} threads"},
+            "host": _host_cpu()}
+
+
+def _host_cpu() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 WORKLOADS = {
@@ -294,6 +406,9 @@ def main(argv=None):
                     help="short run for a profiler: fused step only, no bf16 variant, no CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (for counter scaling)")
+    ap.add_argument("--slope", action="store_true",
+                    help="only sweep the context length at the 8B shape (B = 1, fp8 and bf16 KV) and fit "
+                         "us/step = slope * L + intercept")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -317,6 +432,10 @@ def main(argv=None):
     import fp8_kv_cache_reshape_amd as F
     import synthetic as syn
 
+    if args.slope:
+        print(json.dumps(slope_sweep(F, torch, syn, args)), flush=True)
+        return 0
+
     t0 = time.perf_counter()
     w = WORKLOADS[args.workload](syn)
     layer = w.layers[args.layer]
@@ -329,6 +448,9 @@ def main(argv=None):
     # kernel in the trace is a fused step
     ms_two = bench.time_steps(args.steps, args.warmup, bench.two_call_step)[0] if not args.profile else float("nan")
     kern = bench.time_kernels(min(args.steps, 100), two_call=not args.profile)
+    pct = bench.step_percentiles(args.steps) if not args.profile else None
+    bulk_ms = bench.bulk_write_ms(10) if not args.profile else float("nan")
+    bulk_tokens = bench.T_prefix
     by = bench.bytes
     value = by["step"] / (ms_step * 1e-3) / 1e9
     # the dominant (and only) kernel of a step is the fused decode-step kernel: it moves the
@@ -361,11 +483,22 @@ def main(argv=None):
                                          "decode_partial": round(kern["pass1_ms"] * 1e3, 3),
                                          "decode_merge": round(kern["merge_ms"] * 1e3, 3)}},
         "two_call_us_per_step": round(ms_two * 1e3, 2),
+        "step_us_p10_p50_p90": ([round(pct[q] * 1e3, 2) for q in (10, 50, 90)] if pct else None),
+        "cache_write_bulk": {"tokens": bulk_tokens, "us": round(bulk_ms * 1e3, 2),
+                             "GBps": round(bulk_tokens * (w.num_kv_heads * w.head_dim * (2 * 2 + 2 * bench.ebytes) + 8)
+                                           / (bulk_ms * 1e-3) / 1e9, 1),
+                             "bytes_per_token": w.num_kv_heads * w.head_dim * (2 * 2 + 2 * bench.ebytes) + 8},
         "bytes_per_step": by["step"], "flops_per_step": by["flops"],
         "enqueue_us_per_step": round(ms_enqueue * 1e3, 2), "input_gen_s": round(gen_s, 1),
     }
     del bench
     torch.cuda.empty_cache()
+
+    if not args.profile:
+        rc = read_ceiling(torch, root)
+        result["read_ceiling"] = rc
+        result["pct_of_read_ceiling"] = round(100 * value / rc["GBps"], 2)
+        torch.cuda.empty_cache()
 
     if not (args.no_bf16 or args.profile) and layer.cache_dtype == "e4m3":
         import dataclasses
@@ -386,6 +519,43 @@ def main(argv=None):
 
     print(json.dumps(_finite(result)), flush=True)
     return 0
+
+
+SLOPE_CONTEXTS = (4096, 8192, 16384, 32768, 65536, 131072, 262144)
+
+
+def slope_sweep(F, torch, syn, args) -> dict:
+    """us/step of the fused step at the 8B shape, B = 1, over the context lengths above, for
+    the fp8 cache and the bf16 cache; least-squares fit us = slope * L + intercept.  The
+    slope x 32 layers / 1000 is the attention share of a 32-layer model's time per token
+    per context token (ms/token), comparable to the inter-token-latency slopes the pages
+    quote (Llama-3.1-8B: 2.37e-05 on H100 with fp8 KV, 9.72e-06 on B200)."""
+    import dataclasses
+    points = {"e4m3": [], "bf16": []}
+    for L in SLOPE_CONTEXTS:
+        w = syn.llama8b_long(L, "amax")
+        for dt in ("e4m3", "bf16"):
+            layer = w.layers[0] if dt == "e4m3" else dataclasses.replace(w.layers[0], cache_dtype="bf16",
+                                                                         k_scale=1.0, v_scale=1.0)
+            one = 2 * w.num_blocks * w.num_kv_heads * BLOCK * w.head_dim * (1 if dt == "e4m3" else 2)
+            R = max(1, math.ceil((1 << 30) / one))
+            b = DecodeBench(F, torch, w, layer, R, 0)
+            ms, _ = b.time_steps(args.steps, args.warmup)
+            points[dt].append((L, ms * 1e3, b.bytes["step"] / (ms * 1e-3) / 1e9))
+            del b
+            torch.cuda.empty_cache()
+    out = {"metric": "decode step us vs context length, 8B shape, B = 1", "steps": args.steps,
+           "warmup": args.warmup}
+    for dt, pts in points.items():
+        x = np.array([p[0] for p in pts], float)
+        y = np.array([p[1] for p in pts], float)
+        slope, icpt = np.polyfit(x, y, 1)
+        out[dt] = {"points": [{"L": int(L), "us": round(us, 2), "GBps": round(g, 1)} for L, us, g in pts],
+                   "slope_us_per_token": float(slope), "intercept_us": round(float(icpt), 2),
+                   "ms_per_token_x32_layers": float(slope * 32 / 1000)}
+    out["fp8_over_bf16_slope"] = round(out["e4m3"]["slope_us_per_token"] / out["bf16"]["slope_us_per_token"], 4)
+    out["pages_ms_per_token"] = {"H100 FA3 fp8": 2.37e-05, "B200 FlashInfer fp8": 9.72e-06}
+    return out
 
 
 def _finite(x):

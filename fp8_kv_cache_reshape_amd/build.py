@@ -21,18 +21,26 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libfp8kv.so.  Always recompiles."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *sources(), "-o", tmp]
+PROBE_LIB = os.path.join(HERE, "libfp8kv_probe.so")
+
+
+def _compile(srcs, out, includes, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *HIP_FLAGS, *[a for inc in includes for a in ("-I", inc)], *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libfp8kv.so")
-    os.replace(tmp, LIB)
+        raise RuntimeError("hipcc failed building " + os.path.basename(out))
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libfp8kv.so, and the benchmark's read-ceiling probe into
+    libfp8kv_probe.so.  Always recompiles."""
+    _compile(sources(), LIB, [os.path.join(ROOT, "include"), os.path.join(HERE, "csrc")], verbose)
+    _compile([os.path.join(HERE, "probe", "read_ceiling.hip")], PROBE_LIB, [], verbose)
     return LIB
 
 
