@@ -620,7 +620,9 @@ void decode_partial_kernel(DecodeParams p) {
     l_tot += __shfl_xor(l_tot, 32);
     float* sm_m = lds;                           // [waves][16]
     float* sm_l = lds + kDecodeWaves * 16;       // [waves][16]
-    float* sm_a = lds + 2 * kDecodeWaves * 16;   // [waves][G][D]
+    // [waves][16][D]: every MFMA row (heads >= G are padding) is written, with no condition
+    // per element -- a guard per write becomes a branch per write
+    float* sm_a = lds + 2 * kDecodeWaves * 16;
     if (grp == 0) {
         sm_m[wave * 16 + n] = m_use;
         sm_l[wave * 16 + n] = l_tot;
@@ -628,37 +630,51 @@ void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int head = 4 * grp + r;
-            if (head < G) sm_a[(wave * G + head) * D + 16 * t + n] = run_hi[t][r] + run_lo[t][r];
+        for (int r = 0; r < 4; ++r)
+            sm_a[(wave * 16 + 4 * grp + r) * D + 16 * t + n] = run_hi[t][r] + run_lo[t][r];
+    __syncthreads();
+
+    // per head, once: the waves' weights w_v = 2^(m_v - M), the normaliser and the output
+    // scale (threads 0..G-1)
+    float* sm_w = lds + 2 * kDecodeWaves * 16 + kDecodeWaves * 16 * D;  // [waves][16]
+    float* sm_s = sm_w + kDecodeWaves * 16;                              // [16] v_scale / Lambda
+    float* sm_M = sm_s + 16;                                             // [16] M
+    float* sm_L = sm_M + 16;                                             // [16] Lambda
+    if (threadIdx.x < G) {
+        const int hd = threadIdx.x;
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < kDecodeWaves; ++v) M = fmaxf(M, sm_m[v * 16 + hd]);
+        const float Mu = (M == -INFINITY) ? 0.0f : M;
+        float lam = 0.0f, lam_c = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kDecodeWaves; ++v) {
+            const float wv = __builtin_amdgcn_exp2f(sm_m[v * 16 + hd] - Mu);
+            sm_w[v * 16 + hd] = wv;
+            comp_add(lam, lam_c, wv * sm_l[v * 16 + hd]);
         }
+        lam += lam_c;
+        sm_s[hd] = lam > 0.0f ? p.v_scale / lam : 0.0f;
+        sm_M[hd] = M;
+        sm_L[hd] = lam;
+    }
     __syncthreads();
 
     for (int idx = threadIdx.x; idx < G * D; idx += 64 * kDecodeWaves) {
         const int head = idx / D;
         const int i = idx - head * D;
-        float M = -INFINITY;
+        float a = 0.0f, a_c = 0.0f;
 #pragma unroll
-        for (int v = 0; v < kDecodeWaves; ++v) M = fmaxf(M, sm_m[v * 16 + head]);
-        const float Mu = (M == -INFINITY) ? 0.0f : M;
-        float lam = 0.0f, lam_c = 0.0f, a = 0.0f, a_c = 0.0f;
-#pragma unroll
-        for (int v = 0; v < kDecodeWaves; ++v) {
-            const float wv = __builtin_amdgcn_exp2f(sm_m[v * 16 + head] - Mu);
-            comp_add(lam, lam_c, wv * sm_l[v * 16 + head]);
-            comp_add(a, a_c, wv * sm_a[(v * G + head) * D + i]);
-        }
-        lam += lam_c;
+        for (int v = 0; v < kDecodeWaves; ++v) comp_add(a, a_c, sm_w[v * 16 + head] * sm_a[(v * 16 + head) * D + i]);
         a += a_c;
         if (p.write_final) {
-            store_out(p.out, p.out_f32, out_row0 + (int64_t)head * D + i,
-                      lam > 0.0f ? p.v_scale * a / lam : 0.0f);
+            store_out(p.out, p.out_f32, out_row0 + (int64_t)head * D + i, sm_s[head] * a);
         } else {
             const int64_t row = ((int64_t)b * p.num_q_heads + (int64_t)h * G + head) * p.splits + split;
             store_device(p.ws_acc + row * D + i, a);
             if (i == 0) {
-                store_device(p.ws_ml + row * 2 + 0, M);
-                store_device(p.ws_ml + row * 2 + 1, lam);
+                store_device(p.ws_ml + row * 2 + 0, sm_M[head]);
+                store_device(p.ws_ml + row * 2 + 1, sm_L[head]);
             }
         }
     }
@@ -793,14 +809,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
     }
 }
 
-// Largest dynamic LDS a partial-kernel launch may request (the g = 16, head_dim 256 tile
-// needs about 66 KB).  Launches that need more than 64 KB also need the device to allow it.
+// Largest dynamic LDS a partial-kernel launch may request (head_dim 256 keeps all 16 MFMA
+// rows of 4 waves: about 65 KB).  Launches above 64 KB also need the device to allow it.
 constexpr size_t kMaxPartialLds = 80 * 1024;
 
-// Dynamic LDS of the partial kernel: per-wave (m, l) and the group's accumulators.
+// Dynamic LDS of the partial kernel: per-wave (m, l), every wave's accumulators over all 16
+// MFMA rows, and the per-head wave weights, scale, max and normaliser.
 template <int D>
 size_t partial_lds_bytes(int G) {
-    return sizeof(float) * (2 * kDecodeWaves * 16 + (size_t)kDecodeWaves * G * D);
+    (void)G;
+    return sizeof(float) * (2 * kDecodeWaves * 16 + (size_t)kDecodeWaves * 16 * D + kDecodeWaves * 16 + 48);
 }
 
 // Kernels whose dynamic LDS can exceed 64 KiB (g = 16 at head_dim 256) get their limit
