@@ -144,11 +144,76 @@ constexpr int kMergeLaneBatch = 16;
 // most 2 * kMergeLaneSplits terms their relative rounding error stays below 2^-18, far
 // under the bf16 rounding of the output (the merge kernel, which takes up to kMaxSplits
 // partials, compensates its sums).
+//
+// Two passes over the quads with at most 2 * kMergeLaneBatch splits (group ratio 8 at
+// head_dim 128): each lane takes both of its quads at once -- every load of both is issued
+// before the first wait, unconditionally (absent splits read the last split and weigh 0) so
+// the compiler can count them -- one round trip instead of two.
+template <int D>
+__device__ void merge_two_quads(const DecodeParams& p, int64_t hq0, int NQ, int ns) {
+    constexpr int Q = 2;
+    constexpr int S = kMergeLaneBatch;
+    const int par = threadIdx.x & 1;
+    float2 mv[Q][S];
+    float4 xv[Q][S];
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+        const int q = min((int)(threadIdx.x >> 1) + j * 32 * kDecodeWaves, NQ - 1);
+        const int hh = q / (D / 4), c4 = q % (D / 4);
+        const int64_t row = (hq0 + hh) * p.splits;
+        const float4* xp = reinterpret_cast<const float4*>(p.ws_acc + row * D + 4 * c4);
+        const float2* mp = reinterpret_cast<const float2*>(p.ws_ml) + row;
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int sp = min(2 * u + par, ns - 1);
+            mv[j][u] = mp[sp];
+            xv[j][u] = xp[sp * (D / 4)];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            if (2 * u + par >= ns) mv[j][u] = make_float2(-INFINITY, 0.0f);   // absent: weight 0
+            M = fmaxf(M, mv[j][u].x);
+        }
+        M = fmaxf(M, pair_swap(M));
+        const float Mu = (M == -INFINITY) ? 0.0f : M;
+        float lam = 0.0f;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const float ws = __builtin_amdgcn_exp2f(mv[j][u].x - Mu);
+            lam = fmaf(ws, mv[j][u].y, lam);
+            a.x = fmaf(ws, xv[j][u].x, a.x);
+            a.y = fmaf(ws, xv[j][u].y, a.y);
+            a.z = fmaf(ws, xv[j][u].z, a.z);
+            a.w = fmaf(ws, xv[j][u].w, a.w);
+        }
+        lam += pair_swap(lam);
+        const float scale = lam > 0.0f ? p.v_scale / lam : 0.0f;
+        const float r0 = a.x + pair_swap(a.x), r1 = a.y + pair_swap(a.y);
+        const float r2 = a.z + pair_swap(a.z), r3 = a.w + pair_swap(a.w);
+        const int q = (int)(threadIdx.x >> 1) + j * 32 * kDecodeWaves;
+        if (q < NQ) {
+            const int hh = q / (D / 4), c4 = q % (D / 4);
+            const int64_t o = (hq0 + hh) * D + 4 * c4 + 2 * par;
+            store_out(p.out, p.out_f32, o, scale * (par ? r2 : r0));
+            store_out(p.out, p.out_f32, o + 1, scale * (par ? r3 : r1));
+        }
+    }
+}
+
 template <int D>
 __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) {
     const int par = threadIdx.x & 1;
     const int NQ = G * D / 4;                                  // channel quads of the group
     const int64_t hq0 = (int64_t)b * p.num_q_heads + (int64_t)h * G;
+    if (NQ > 32 * kDecodeWaves && NQ <= 64 * kDecodeWaves && ns <= 2 * kMergeLaneBatch) {
+        merge_two_quads<D>(p, hq0, NQ, ns);
+        return;
+    }
     for (int q = threadIdx.x >> 1; q < NQ; q += 32 * kDecodeWaves) {   // lane pairs of the workgroup
         const int hh = q / (D / 4), c4 = q % (D / 4);
         const int64_t row = (hq0 + hh) * p.splits;
