@@ -200,6 +200,39 @@ void oracle_cache_write(const uint16_t* key, const uint16_t* value,
     }
 }
 
+/*
+ * Per-attention-head scales [CAP "Scales and calibration"]: the same write with one
+ * scale pair per kv head -- head h's key elements are divided by k_scales[h] and its
+ * value elements by v_scales[h] before the cast (k_scales, v_scales float [Hkv]).
+ */
+void oracle_cache_write_per_head(const uint16_t* key, const uint16_t* value,
+                                 void* key_cache, void* value_cache, int cache_dtype,
+                                 const int64_t* slot_mapping, int T, int Hkv, int D,
+                                 int bs, int NB, const float* k_scales, const float* v_scales) {
+    for (int t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= (int64_t)NB * bs) continue;
+        int64_t blk = slot / bs;
+        int off = (int)(slot % bs);
+        for (int h = 0; h < Hkv; ++h) {
+            for (int i = 0; i < D; ++i) {
+                uint16_t xk = key[((int64_t)t * Hkv + h) * D + i];
+                uint16_t xv = value[((int64_t)t * Hkv + h) * D + i];
+                int64_t ki = key_index(blk, h, off, i, Hkv, bs, D,
+                                       cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2);
+                int64_t vi = value_index(blk, h, off, i, Hkv, bs, D);
+                if (cache_dtype == ORACLE_CACHE_E4M3) {
+                    ((uint8_t*)key_cache)[ki] = oracle_quantize(xk, k_scales[h]);
+                    ((uint8_t*)value_cache)[vi] = oracle_quantize(xv, v_scales[h]);
+                } else {
+                    ((uint16_t*)key_cache)[ki] = xk;
+                    ((uint16_t*)value_cache)[vi] = xv;
+                }
+            }
+        }
+    }
+}
+
 /* Dequantised cache element: e4m3 value times scale, or the bf16 value. */
 static double cache_value(const void* cache, int cache_dtype, int64_t idx, double scale) {
     if (cache_dtype == ORACLE_CACHE_E4M3)
@@ -309,4 +342,26 @@ void oracle_paged_decode_pairs(double* out, const int32_t* pairs, int npairs,
                                  cache_dtype, block_tables, max_blocks, context_lens,
                                  Hq, Hkv, D, bs, k_scale, v_scale, window,
                                  pairs[2 * p], pairs[2 * p + 1]);
+}
+
+/*
+ * Per-attention-head scales [CAP "Scales and calibration"]: selected (b, hq) pairs, each
+ * query head dequantising with the scales of its kv head h = hq / g (k_scales, v_scales
+ * double [Hkv]).  out double [n][D].
+ */
+void oracle_paged_decode_pairs_per_head(double* out, const int32_t* pairs, int npairs,
+                                        const uint16_t* q, const void* key_cache,
+                                        const void* value_cache, int cache_dtype,
+                                        const int32_t* block_tables, int max_blocks,
+                                        const int32_t* context_lens, int Hq, int Hkv, int D,
+                                        int bs, const double* k_scales, const double* v_scales,
+                                        int window) {
+    int g = Hq / Hkv;
+    for (int p = 0; p < npairs; ++p) {
+        int kv = pairs[2 * p + 1] / g;
+        oracle_paged_decode_head(out + (int64_t)p * D, q, key_cache, value_cache,
+                                 cache_dtype, block_tables, max_blocks, context_lens,
+                                 Hq, Hkv, D, bs, k_scales[kv], v_scales[kv], window,
+                                 pairs[2 * p], pairs[2 * p + 1]);
+    }
 }

@@ -151,6 +151,27 @@ def _amax_scale(bits: np.ndarray) -> float:
     return float(np.float32(amax) / np.float32(448.0))
 
 
+def per_head_amax_scales(bits: np.ndarray) -> np.ndarray:
+    """Calibrated per-kv-head scales of bf16 rows [T][Hkv][D]: amax over each head's
+    elements divided by 448, in f32 (1.0 for an all-zero head).  float32 [Hkv]."""
+    T, Hkv, D = bits.shape
+    amax = np.zeros(Hkv, dtype=np.float32)
+    step = max(1, (1 << 22) // (Hkv * D))
+    for s in range(0, T, step):
+        blk = np.abs(bf16_bits_to_f32(bits[s:s + step]))
+        amax = np.maximum(amax, blk.reshape(-1, Hkv, D).max(axis=(0, 2)).astype(np.float32))
+    sc = amax / np.float32(448.0)
+    sc[sc == 0] = np.float32(1.0)
+    return sc.astype(np.float32)
+
+
+def spread_head_scales(Hkv: int, cid: int, lo: float = 0.05, hi: float = 8.0) -> np.ndarray:
+    """Seeded per-head scales spread log-uniformly over [lo, hi] (float32 [Hkv]): inputs
+    that make a wrong head's scale visible."""
+    rng = np.random.Generator(np.random.PCG64(4000 + cid))
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), size=Hkv)).astype(np.float32)
+
+
 def make_workload(name: str, cid: int, *, num_q_heads: int, num_kv_heads: int, head_dim: int,
                   context_lens=None, num_seqs: int = 1, len_range=None, std: float = 1.0,
                   outlier_frac: float = 0.0, outlier_mult: float = 8.0, scale_mode: str = "amax",

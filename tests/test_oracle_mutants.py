@@ -16,7 +16,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_codec.py"),
-        os.path.join(ROOT, "tests", "test_oracle_attention.py")]
+        os.path.join(ROOT, "tests", "test_oracle_attention.py"),
+        os.path.join(ROOT, "tests", "test_oracle_per_head.py")]
 
 MUTANTS = {
     "subnormal_ties_away": ("double m = rint(a * 512.0);", "double m = round(a * 512.0);"),
@@ -51,8 +52,15 @@ MUTANTS = {
                            "((uint8_t*)value_cache)[vi] = oracle_quantize(xv, k_scale);"),
     "scale_dropped_in_decode": ("return oracle_e4m3_decode(((const uint8_t*)cache)[idx]) * scale;",
                                 "return oracle_e4m3_decode(((const uint8_t*)cache)[idx]);"),
-    "bf16_cache_bits_altered": ("((uint16_t*)key_cache)[ki] = xk;",
-                          "((uint16_t*)key_cache)[ki] = (uint16_t)(xk ^ 0x0001);"),
+    "bf16_cache_bits_altered": (
+        "oracle_quantize(xv, v_scale);\n                } else {\n                    ((uint16_t*)key_cache)[ki] = xk;",
+        "oracle_quantize(xv, v_scale);\n                } else {\n                    ((uint16_t*)key_cache)[ki] = (uint16_t)(xk ^ 0x0001);"),
+    "per_head_write_head0_scale": ("((uint8_t*)key_cache)[ki] = oracle_quantize(xk, k_scales[h]);",
+                                   "((uint8_t*)key_cache)[ki] = oracle_quantize(xk, k_scales[0]);"),
+    "per_head_values_with_key_scales": ("((uint8_t*)value_cache)[vi] = oracle_quantize(xv, v_scales[h]);",
+                                        "((uint8_t*)value_cache)[vi] = oracle_quantize(xv, k_scales[h]);"),
+    "per_head_decode_interleaved_heads": ("int kv = pairs[2 * p + 1] / g;",
+                                          "int kv = pairs[2 * p + 1] % Hkv;"),
 }
 
 
