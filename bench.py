@@ -78,7 +78,9 @@ def algorithmic_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_di
 class DecodeBench:
     """Device buffers for one workload layer and the calls of one decode step."""
 
-    def __init__(self, F, torch, w, layer, instances: int, num_splits: int):
+    def __init__(self, F, torch, w, layer, instances: int, num_splits: int, heads=None):
+        """heads: None (the layer's per-tensor scales) or float32 [Hkv] (k_scales, v_scales)
+        for the per-head entry points."""
         self.F, self.torch, self.w, self.layer = F, torch, w, layer
         dev = "cuda"
         self.cdt = F.FP8KV_E4M3 if layer.cache_dtype == "e4m3" else F.FP8KV_BF16
@@ -91,20 +93,19 @@ class DecodeBench:
         self.bt = torch.from_numpy(w.block_tables).to(dev)
         self.cl = torch.from_numpy(w.context_lens).to(dev)
         self.stream = int(torch.cuda.current_stream().cuda_stream)
+        self.heads = None if heads is None else tuple(
+            torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) for a in heads)
         # the context before this step, written once into every rotated cache instance
         prefix = w.prefix_token_rows()
         kp, vp = u16(layer.k[prefix]), u16(layer.v[prefix])
         sp = torch.from_numpy(w.slot_mapping[prefix]).to(dev)
         self.kc, self.vc = [], []
-        for _ in range(instances):
-            kc = torch.zeros(n, dtype=cache_dtype, device=dev)
-            vc = torch.zeros(n, dtype=cache_dtype, device=dev)
-            F.fp8kv_cache_write(kp, vp, kc, vc, self.cdt, sp, len(prefix), Hkv, D, BLOCK,
-                                w.num_blocks, layer.k_scale, layer.v_scale, self.stream)
-            self.kc.append(kc)
-            self.vc.append(vc)
         # kept for the bulk cache-write measurement
         self.kp, self.vp, self.sp, self.T_prefix = kp, vp, sp, len(prefix)
+        for i in range(instances):
+            self.kc.append(torch.zeros(n, dtype=cache_dtype, device=dev))
+            self.vc.append(torch.zeros(n, dtype=cache_dtype, device=dev))
+            self._write_rows(kp, vp, sp, len(prefix), i)
         # the step's new token of every sequence (all sequences are non-empty here)
         rows = w.step_token_rows()
         assert len(rows) == B, "every sequence needs a step token"
@@ -127,19 +128,35 @@ class DecodeBench:
         self.footprint = 2 * n * self.ebytes
 
     # -- the three kernels of a step, called through the C-ABI binding
-    def write(self, i):
+    def _write_rows(self, k, v, slots, T, i):
         w, L = self.w, self.layer
-        self.F.fp8kv_cache_write(self.k_new, self.v_new, self.kc[i], self.vc[i], self.cdt,
-                                 self.slots_new, self.T_new, w.num_kv_heads, w.head_dim, BLOCK,
-                                 w.num_blocks, L.k_scale, L.v_scale, self.stream)
+        if self.heads is None:
+            self.F.fp8kv_cache_write(k, v, self.kc[i], self.vc[i], self.cdt, slots, T,
+                                     w.num_kv_heads, w.head_dim, BLOCK, w.num_blocks, L.k_scale,
+                                     L.v_scale, self.stream)
+        else:
+            self.F.fp8kv_cache_write_per_head(k, v, self.kc[i], self.vc[i], self.cdt, slots, T,
+                                              w.num_kv_heads, w.head_dim, BLOCK, w.num_blocks,
+                                              self.heads[0], self.heads[1], self.stream)
+
+    def write(self, i):
+        self._write_rows(self.k_new, self.v_new, self.slots_new, self.T_new, i)
 
     def decode(self, i):
         w, L = self.w, self.layer
-        self.F.fp8kv_paged_decode(self.out, self.F.FP8KV_BF16, self.q, self.kc[i], self.vc[i],
-                                  self.cdt, self.bt, w.max_blocks_per_seq, self.cl, self.maxl,
-                                  w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, BLOCK,
-                                  w.num_blocks, L.k_scale, L.v_scale, self.win, self.splits,
-                                  self.ws, self.ws_bytes, self.stream)
+        if self.heads is None:
+            self.F.fp8kv_paged_decode(self.out, self.F.FP8KV_BF16, self.q, self.kc[i], self.vc[i],
+                                      self.cdt, self.bt, w.max_blocks_per_seq, self.cl, self.maxl,
+                                      w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, BLOCK,
+                                      w.num_blocks, L.k_scale, L.v_scale, self.win, self.splits,
+                                      self.ws, self.ws_bytes, self.stream)
+        else:
+            self.F.fp8kv_paged_decode_per_head(self.out, self.F.FP8KV_BF16, self.q, self.kc[i],
+                                               self.vc[i], self.cdt, self.bt, w.max_blocks_per_seq,
+                                               self.cl, self.maxl, w.num_seqs, w.num_q_heads,
+                                               w.num_kv_heads, w.head_dim, BLOCK, w.num_blocks,
+                                               self.heads[0], self.heads[1], self.win,
+                                               self.splits, self.ws, self.ws_bytes, self.stream)
 
     def partial(self, i):
         w, L = self.w, self.layer
@@ -160,11 +177,20 @@ class DecodeBench:
     def fused_step(self, i):
         """The whole step in one launch: write each sequence's token at L-1, then decode."""
         w, L = self.w, self.layer
-        self.F.fp8kv_decode_step(self.out, self.F.FP8KV_BF16, self.q, self.k_new, self.v_new,
-                                 self.kc[i], self.vc[i], self.cdt, self.bt, w.max_blocks_per_seq,
-                                 self.cl, self.maxl, w.num_seqs, w.num_q_heads, w.num_kv_heads,
-                                 w.head_dim, BLOCK, w.num_blocks, L.k_scale, L.v_scale, self.win,
-                                 self.splits, self.step_ws, self.step_ws_bytes, self.stream)
+        if self.heads is None:
+            self.F.fp8kv_decode_step(self.out, self.F.FP8KV_BF16, self.q, self.k_new, self.v_new,
+                                     self.kc[i], self.vc[i], self.cdt, self.bt, w.max_blocks_per_seq,
+                                     self.cl, self.maxl, w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                     w.head_dim, BLOCK, w.num_blocks, L.k_scale, L.v_scale, self.win,
+                                     self.splits, self.step_ws, self.step_ws_bytes, self.stream)
+        else:
+            self.F.fp8kv_decode_step_per_head(self.out, self.F.FP8KV_BF16, self.q, self.k_new,
+                                              self.v_new, self.kc[i], self.vc[i], self.cdt, self.bt,
+                                              w.max_blocks_per_seq, self.cl, self.maxl, w.num_seqs,
+                                              w.num_q_heads, w.num_kv_heads, w.head_dim, BLOCK,
+                                              w.num_blocks, self.heads[0], self.heads[1], self.win,
+                                              self.splits, self.step_ws, self.step_ws_bytes,
+                                              self.stream)
 
     def two_call_step(self, i):
         self.write(i)
@@ -213,8 +239,9 @@ class DecodeBench:
                "merge_ms": float("nan")}
         if two_call:
             out["write_ms"] = avg(self.write)
-            out["pass1_ms"] = avg(self.partial)
-            out["merge_ms"] = avg(lambda i: self.merge()) if self.nsplits > 1 else 0.0
+            if self.heads is None:     # the split passes take per-tensor scales only
+                out["pass1_ms"] = avg(self.partial)
+                out["merge_ms"] = avg(lambda i: self.merge()) if self.nsplits > 1 else 0.0
         return out
 
     def step_percentiles(self, steps: int):
@@ -241,9 +268,7 @@ class DecodeBench:
         R = len(self.kc)
 
         def write(i):
-            F.fp8kv_cache_write(self.kp, self.vp, self.kc[i], self.vc[i], self.cdt, self.sp, self.T_prefix,
-                                w.num_kv_heads, w.head_dim, BLOCK, w.num_blocks, L.k_scale, L.v_scale,
-                                self.stream)
+            self._write_rows(self.kp, self.vp, self.sp, self.T_prefix, i)
         write(0)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -406,6 +431,9 @@ def main(argv=None):
                     help="short run for a profiler: fused step only, no bf16 variant, no CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (for counter scaling)")
+    ap.add_argument("--per-head-scales", action="store_true",
+                    help="kv heads of different magnitudes with calibrated per-head scales, through "
+                         "the per-head entry points (fp8 cache)")
     ap.add_argument("--slope", action="store_true",
                     help="only sweep the context length at the 8B shape (B = 1, fp8 and bf16 KV) and fit "
                          "us/step = slope * L + intercept")
@@ -438,11 +466,15 @@ def main(argv=None):
 
     t0 = time.perf_counter()
     w = WORKLOADS[args.workload](syn)
+    heads = None
+    if args.per_head_scales:
+        w, scales = syn.with_head_magnitudes(w, 140)
+        heads = scales[args.layer]
     layer = w.layers[args.layer]
     gen_s = time.perf_counter() - t0
     one = 2 * w.num_blocks * w.num_kv_heads * BLOCK * w.head_dim * (1 if layer.cache_dtype == "e4m3" else 2)
     R = max(1, math.ceil(args.rotate_bytes * (1 << 30) / one))
-    bench = DecodeBench(F, torch, w, layer, R, args.num_splits)
+    bench = DecodeBench(F, torch, w, layer, R, args.num_splits, heads)
     ms_step, ms_enqueue = bench.time_steps(args.steps, args.warmup)
     # under a profiler (--profile) only the fused step runs, so every dispatch of the decode
     # kernel in the trace is a fused step
@@ -466,7 +498,8 @@ def main(argv=None):
         "dtype": "e4m3 KV -> bf16 MFMA, f32 accumulate" if bench.ebytes == 1 else "bf16 KV, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {w.name}, layer {layer.name} "
-                               f"({layer.cache_dtype} cache, window {layer.sliding_window})",
+                               f"({layer.cache_dtype} cache, window {layer.sliding_window}"
+                               f"{', per-head scales' if heads is not None else ''})",
                    "num_seqs": w.num_seqs, "context_lens": sorted(set(int(x) for x in w.context_lens))[:4],
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": BLOCK, "splits": bench.nsplits,
@@ -474,7 +507,8 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (measured_traffic(root) if args.workload == "llama8b-b1-128k"
-                                 and layer.cache_dtype == "e4m3" and args.num_splits == 0 else None),
+                                 and layer.cache_dtype == "e4m3" and args.num_splits == 0
+                                 and heads is None else None),
                      "kernel": "decode_partial_kernel (fp8kv_decode_step: write + decode + merge)",
                      "bytes_per_launch": by["step"],
                      "avg_launch_us": round(kern["step_ms"] * 1e3, 3)},
@@ -500,7 +534,7 @@ def main(argv=None):
         result["pct_of_read_ceiling"] = round(100 * value / rc["GBps"], 2)
         torch.cuda.empty_cache()
 
-    if not (args.no_bf16 or args.profile) and layer.cache_dtype == "e4m3":
+    if not (args.no_bf16 or args.profile or heads is not None) and layer.cache_dtype == "e4m3":
         import dataclasses
         bl = dataclasses.replace(layer, cache_dtype="bf16", k_scale=1.0, v_scale=1.0)
         R2 = max(1, math.ceil(args.rotate_bytes * (1 << 30) / (2 * one)))
@@ -514,7 +548,7 @@ def main(argv=None):
         del b2
         torch.cuda.empty_cache()
 
-    if not (args.no_cpu_baseline or args.profile) and layer.cache_dtype == "e4m3":
+    if not (args.no_cpu_baseline or args.profile or heads is not None) and layer.cache_dtype == "e4m3":
         result["cpu_baseline"] = cpu_baseline(w, layer)
 
     print(json.dumps(_finite(result)), flush=True)

@@ -35,10 +35,13 @@ SIGNATURES = {
     "fp8kv_version": (_I, []),
     "fp8kv_last_hip_error": (ctypes.c_char_p, []),
     "fp8kv_cache_write": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _F, _P]),
+    "fp8kv_cache_write_per_head": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "fp8kv_paged_decode_num_splits": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "fp8kv_paged_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "fp8kv_paged_decode": (_I, [_P, _I, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
                                 _F, _F, _I, _I, _P, _SZ, _P]),
+    "fp8kv_paged_decode_per_head": (_I, [_P, _I, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I,
+                                         _I, _I, _P, _P, _I, _I, _P, _SZ, _P]),
     "fp8kv_paged_decode_partial": (_I, [_P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
                                         _F, _I, _I, _P, _SZ, _P]),
     "fp8kv_paged_decode_merge": (_I, [_P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P,
@@ -46,10 +49,12 @@ SIGNATURES = {
     "fp8kv_decode_step_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "fp8kv_decode_step": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I,
                                _I, _F, _F, _I, _I, _P, _SZ, _P]),
+    "fp8kv_decode_step_per_head": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I,
+                                        _I, _I, _I, _I, _P, _P, _I, _I, _P, _SZ, _P]),
 }
 
 if not os.path.exists(LIBRARY_PATH):
-    raise ImportError(f"{LIBRARY_PATH} is not built: run `python -m fp8_kv_cache_reshape_amd.build` "
+    raise ImportError(f"{LIBRARY_PATH} is not built: run `python fp8_kv_cache_reshape_amd/build.py` "
                       "(hipcc, gfx950) first; this package has no non-HIP fallback")
 
 # torch ships its own HIP runtime under the same soname as the system one.  Loading torch
@@ -59,6 +64,9 @@ import torch  # noqa: E402,F401  (imported for its HIP runtime, before the libra
 
 lib = ctypes.CDLL(LIBRARY_PATH)
 for _name, (_res, _args) in SIGNATURES.items():
+    if not hasattr(lib, _name):
+        raise ImportError(f"{LIBRARY_PATH} lacks {_name}: it is older than the sources; rebuild it "
+                          "with `python fp8_kv_cache_reshape_amd/build.py`")
     _fn = getattr(lib, _name)
     _fn.restype = _res
     _fn.argtypes = _args
@@ -116,6 +124,17 @@ def fp8kv_cache_write(key, value, key_cache, value_cache, cache_dtype, slot_mapp
                                         k_scale, v_scale, _stream(stream)), "fp8kv_cache_write")
 
 
+def fp8kv_cache_write_per_head(key, value, key_cache, value_cache, cache_dtype, slot_mapping,
+                               num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                               k_scales, v_scales, stream=None) -> int:
+    return _check(lib.fp8kv_cache_write_per_head(_addr(key), _addr(value), _addr(key_cache),
+                                                 _addr(value_cache), cache_dtype,
+                                                 _addr(slot_mapping), num_tokens, num_kv_heads,
+                                                 head_dim, block_size, num_blocks, _addr(k_scales),
+                                                 _addr(v_scales), _stream(stream)),
+                  "fp8kv_cache_write_per_head")
+
+
 def fp8kv_paged_decode_num_splits(num_seqs, num_kv_heads, head_dim, block_size, max_context_len,
                                   sliding_window, num_splits) -> int:
     return _check(lib.fp8kv_paged_decode_num_splits(num_seqs, num_kv_heads, head_dim, block_size,
@@ -141,6 +160,22 @@ def fp8kv_paged_decode(out, out_dtype, query, key_cache, value_cache, cache_dtyp
                                          num_blocks, k_scale, v_scale, sliding_window, num_splits,
                                          _addr(workspace), workspace_bytes, _stream(stream)),
                   "fp8kv_paged_decode")
+
+
+def fp8kv_paged_decode_per_head(out, out_dtype, query, key_cache, value_cache, cache_dtype,
+                                block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                                num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                num_blocks, k_scales, v_scales, sliding_window, num_splits,
+                                workspace, workspace_bytes, stream=None) -> int:
+    return _check(lib.fp8kv_paged_decode_per_head(_addr(out), out_dtype, _addr(query),
+                                                  _addr(key_cache), _addr(value_cache), cache_dtype,
+                                                  _addr(block_tables), max_blocks_per_seq,
+                                                  _addr(context_lens), max_context_len, num_seqs,
+                                                  num_q_heads, num_kv_heads, head_dim, block_size,
+                                                  num_blocks, _addr(k_scales), _addr(v_scales),
+                                                  sliding_window, num_splits, _addr(workspace),
+                                                  workspace_bytes, _stream(stream)),
+                  "fp8kv_paged_decode_per_head")
 
 
 def fp8kv_paged_decode_partial(query, key_cache, value_cache, cache_dtype, block_tables,
@@ -189,3 +224,20 @@ def fp8kv_decode_step(out, out_dtype, query, key_new, value_new, key_cache, valu
                                         k_scale, v_scale, sliding_window, num_splits,
                                         _addr(workspace), workspace_bytes, _stream(stream)),
                   "fp8kv_decode_step")
+
+
+def fp8kv_decode_step_per_head(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
+                               cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                               max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                               block_size, num_blocks, k_scales, v_scales, sliding_window,
+                               num_splits, workspace, workspace_bytes, stream=None) -> int:
+    return _check(lib.fp8kv_decode_step_per_head(_addr(out), out_dtype, _addr(query),
+                                                 _addr(key_new), _addr(value_new),
+                                                 _addr(key_cache), _addr(value_cache), cache_dtype,
+                                                 _addr(block_tables), max_blocks_per_seq,
+                                                 _addr(context_lens), max_context_len, num_seqs,
+                                                 num_q_heads, num_kv_heads, head_dim, block_size,
+                                                 num_blocks, _addr(k_scales), _addr(v_scales),
+                                                 sliding_window, num_splits, _addr(workspace),
+                                                 workspace_bytes, _stream(stream)),
+                  "fp8kv_decode_step_per_head")

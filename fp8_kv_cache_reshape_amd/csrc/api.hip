@@ -25,6 +25,31 @@ bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
 
+// Scales of one call: per tensor (arrays null) or per kv head (device arrays of num_kv_heads
+// floats, whose values the kernels read; they are not inspected here).
+struct Scales {
+    float k, v;
+    const float* ks;
+    const float* vs;
+    bool per_head() const { return ks != nullptr || vs != nullptr; }
+};
+
+Scales tensor_scales(float k, float v) { return Scales{k, v, nullptr, nullptr}; }
+Scales head_scales(const float* ks, const float* vs) { return Scales{1.0f, 1.0f, ks, vs}; }
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Validation shared by every entry point that takes scales, for an fp8 cache (a bf16 cache
+// ignores them).  A per-head call must give both arrays.
+int check_scales(const Scales& sc, bool per_head_call) {
+    if (per_head_call) {
+        if (!sc.ks || !sc.vs) return FP8KV_ERR_NULL;
+        if (!aligned4(sc.ks) || !aligned4(sc.vs)) return FP8KV_ERR_SHAPE;
+        return FP8KV_OK;
+    }
+    return scale_ok(sc.k) && scale_ok(sc.v) ? FP8KV_OK : FP8KV_ERR_SCALE;
+}
+
 int check_decode_shape(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                        int block_size, int max_context_len, int sliding_window, int num_splits) {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
@@ -121,15 +146,19 @@ int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const voi
                  const void* value_cache, int cache_dtype, const int32_t* block_tables,
                  int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                 int num_blocks, float k_scale, float v_scale, int sliding_window, int num_splits,
-                 void* workspace, size_t workspace_bytes, bool need_workspace_for_single) {
+                 int num_blocks, const Scales& sc, bool per_head_call, int sliding_window,
+                 int num_splits, void* workspace, size_t workspace_bytes,
+                 bool need_workspace_for_single) {
     int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_context_len, sliding_window, num_splits);
     if (st != FP8KV_OK) return st;
     if (max_blocks_per_seq < 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
     if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
     fp8 = cache_dtype == FP8KV_E4M3;
-    if (fp8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return FP8KV_ERR_SCALE;
+    if (fp8) {
+        st = check_scales(sc, per_head_call);
+        if (st != FP8KV_OK) return st;
+    }
     if (num_seqs > 0) {
         if (!query || !context_lens || !block_tables || !key_cache || !value_cache)
             return FP8KV_ERR_NULL;
@@ -156,9 +185,13 @@ int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const voi
     p.num_kv_heads = num_kv_heads;
     p.num_blocks = num_blocks;
     p.sliding_window = sliding_window;
+    // per-head key scales are applied in the kernel, to log2(e)/sqrt(D) rounded to float
     const double log2e = 1.4426950408889634;
-    p.score_scale = (float)((fp8 ? (double)k_scale : 1.0) * log2e / sqrt((double)head_dim));
-    p.v_scale = fp8 ? v_scale : 1.0f;
+    const bool heads = fp8 && per_head_call;
+    p.score_scale = (float)((fp8 && !heads ? (double)sc.k : 1.0) * log2e / sqrt((double)head_dim));
+    p.v_scale = fp8 && !heads ? sc.v : 1.0f;
+    p.k_scales = heads ? sc.ks : nullptr;
+    p.v_scales = heads ? sc.vs : nullptr;
     p.splits = pl.splits;
     p.blocks_per_split = pl.blocks_per_split;
     p.ws_ml = single ? nullptr : reinterpret_cast<float*>(workspace);
@@ -175,6 +208,112 @@ int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const voi
     p.claims = nullptr;
     p.merge_in_kernel = 0;
     return FP8KV_OK;
+}
+
+int cache_write_impl(const void* key, const void* value, void* key_cache, void* value_cache,
+                     int cache_dtype, const int64_t* slot_mapping, int num_tokens,
+                     int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                     const Scales& sc, bool per_head_call, void* stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
+    if (!head_dim_ok(head_dim) || block_size != kBlockSize) return FP8KV_ERR_UNSUPPORTED;
+    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype == FP8KV_E4M3;
+    if (fp8) {
+        const int st = check_scales(sc, per_head_call);
+        if (st != FP8KV_OK) return st;
+    }
+    if (num_tokens == 0) return FP8KV_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping) return FP8KV_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+        return FP8KV_ERR_SHAPE;
+    fp8kv::CacheWriteParams p;
+    p.key = static_cast<const uint16_t*>(key);
+    p.value = static_cast<const uint16_t*>(value);
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.slot_mapping = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_kv_heads = num_kv_heads;
+    p.num_blocks = num_blocks;
+    p.k_scale = sc.k;
+    p.v_scale = sc.v;
+    p.k_scales = fp8 && per_head_call ? sc.ks : nullptr;
+    p.v_scales = fp8 && per_head_call ? sc.vs : nullptr;
+    return hip_status(fp8kv::launch_cache_write(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int paged_decode_impl(void* out, int out_dtype, const void* query, const void* key_cache,
+                      const void* value_cache, int cache_dtype, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, const Scales& sc, bool per_head_call,
+                      int sliding_window, int num_splits, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    fp8kv::DecodeParams p;
+    bool fp8 = true;
+    int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
+                          max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, sc,
+                          per_head_call, sliding_window, num_splits, workspace, workspace_bytes,
+                          false);
+    if (st != FP8KV_OK) return st;
+    if (num_seqs == 0) return FP8KV_OK;
+    if (!out) return FP8KV_ERR_NULL;
+    if (!aligned16(out)) return FP8KV_ERR_SHAPE;
+    p.out = out;
+    p.out_f32 = out_dtype == FP8KV_F32;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
+    if (st != FP8KV_OK || p.write_final) return st;
+    return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
+}
+
+int decode_step_impl(void* out, int out_dtype, const void* query, const void* key_new,
+                     const void* value_new, void* key_cache, void* value_cache, int cache_dtype,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* context_lens, int max_context_len, int num_seqs,
+                     int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                     int num_blocks, const Scales& sc, bool per_head_call, int sliding_window,
+                     int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_kv_heads <= 0) return FP8KV_ERR_SHAPE;
+    // counters first, then the partials (checked by setup_decode)
+    const size_t cbytes = step_counter_bytes(num_seqs, num_kv_heads);
+    const bool have_ws = workspace != nullptr && workspace_bytes >= cbytes;
+    fp8kv::DecodeParams p;
+    bool fp8 = true;
+    int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
+                          max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, sc,
+                          per_head_call, sliding_window, num_splits,
+                          have_ws ? static_cast<char*>(workspace) + cbytes : nullptr,
+                          have_ws ? workspace_bytes - cbytes : 0, false);
+    if (st != FP8KV_OK) return st;
+    if (num_seqs == 0) return FP8KV_OK;
+    if (!out || !key_new || !value_new) return FP8KV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(key_new) || !aligned16(value_new)) return FP8KV_ERR_SHAPE;
+    // several splits: workgroups claim steps from counters (load balance) and the last one
+    // of each group merges inside the decode kernel when one workgroup merges a group
+    // cheaply, else the merge kernel queued behind it does
+    const bool fused = !p.write_final &&
+                       fp8kv::fused_merge_fits(num_q_heads / num_kv_heads, head_dim, p.splits);
+    if (!p.write_final) {
+        p.counters = static_cast<unsigned int*>(workspace);
+        p.claims = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) +
+                                                   arrival_bytes(num_seqs, num_kv_heads));
+        p.merge_in_kernel = fused ? 1 : 0;
+    }
+    p.out = out;
+    p.out_f32 = out_dtype == FP8KV_F32;
+    p.k_new = static_cast<const uint16_t*>(key_new);
+    p.v_new = static_cast<const uint16_t*>(value_new);
+    p.k_scale_q = fp8 && !per_head_call ? sc.k : 1.0f;
+    p.v_scale_q = fp8 && !per_head_call ? sc.v : 1.0f;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
+    if (st != FP8KV_OK || p.write_final || fused) return st;
+    return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
 }
 
 }  // namespace
@@ -194,7 +333,7 @@ const char* fp8kv_status_string(int status) {
     }
 }
 
-int fp8kv_version(void) { return 100; }
+int fp8kv_version(void) { return 200; }
 
 const char* fp8kv_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
 
@@ -202,29 +341,21 @@ int fp8kv_cache_write(const void* key, const void* value, void* key_cache, void*
                       int cache_dtype, const int64_t* slot_mapping, int num_tokens,
                       int num_kv_heads, int head_dim, int block_size, int num_blocks,
                       float k_scale, float v_scale, void* stream) {
-    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
-    if (!head_dim_ok(head_dim) || block_size != kBlockSize) return FP8KV_ERR_UNSUPPORTED;
-    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
-    if (cache_dtype == FP8KV_E4M3 && (!scale_ok(k_scale) || !scale_ok(v_scale)))
-        return FP8KV_ERR_SCALE;
-    if (num_tokens == 0) return FP8KV_OK;
-    if (!key || !value || !key_cache || !value_cache || !slot_mapping) return FP8KV_ERR_NULL;
-    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
-        return FP8KV_ERR_SHAPE;
-    fp8kv::CacheWriteParams p;
-    p.key = static_cast<const uint16_t*>(key);
-    p.value = static_cast<const uint16_t*>(value);
-    p.key_cache = key_cache;
-    p.value_cache = value_cache;
-    p.slot_mapping = slot_mapping;
-    p.num_tokens = num_tokens;
-    p.num_kv_heads = num_kv_heads;
-    p.num_blocks = num_blocks;
-    p.k_scale = k_scale;
-    p.v_scale = v_scale;
-    return hip_status(fp8kv::launch_cache_write(p, cache_dtype == FP8KV_E4M3, head_dim,
-                                                static_cast<hipStream_t>(stream)));
+    return cache_write_impl(key, value, key_cache, value_cache, cache_dtype, slot_mapping,
+                            num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                            tensor_scales(k_scale, v_scale), false, stream);
 }
+
+int fp8kv_cache_write_per_head(const void* key, const void* value, void* key_cache,
+                               void* value_cache, int cache_dtype, const int64_t* slot_mapping,
+                               int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, const float* k_scales, const float* v_scales,
+                               void* stream) {
+    return cache_write_impl(key, value, key_cache, value_cache, cache_dtype, slot_mapping,
+                            num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                            head_scales(k_scales, v_scales), true, stream);
+}
+
 
 int fp8kv_paged_decode_num_splits(int num_seqs, int num_kv_heads, int head_dim, int block_size,
                                   int max_context_len, int sliding_window, int num_splits) {
@@ -251,24 +382,28 @@ int fp8kv_paged_decode(void* out, int out_dtype, const void* query, const void* 
                        int block_size, int num_blocks, float k_scale, float v_scale,
                        int sliding_window, int num_splits, void* workspace,
                        size_t workspace_bytes, void* stream) {
-    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
-    fp8kv::DecodeParams p;
-    bool fp8 = true;
-    int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
-                          max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, k_scale,
-                          v_scale, sliding_window, num_splits, workspace, workspace_bytes, false);
-    if (st != FP8KV_OK) return st;
-    if (num_seqs == 0) return FP8KV_OK;
-    if (!out) return FP8KV_ERR_NULL;
-    if (!aligned16(out)) return FP8KV_ERR_SHAPE;
-    p.out = out;
-    p.out_f32 = out_dtype == FP8KV_F32;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
-    if (st != FP8KV_OK || p.write_final) return st;
-    return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
+    return paged_decode_impl(out, out_dtype, query, key_cache, value_cache, cache_dtype,
+                             block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                             num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             num_blocks, tensor_scales(k_scale, v_scale), false, sliding_window,
+                             num_splits, workspace, workspace_bytes, stream);
 }
+
+int fp8kv_paged_decode_per_head(void* out, int out_dtype, const void* query,
+                                const void* key_cache, const void* value_cache, int cache_dtype,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int max_context_len, int num_seqs,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int num_blocks, const float* k_scales, const float* v_scales,
+                                int sliding_window, int num_splits, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return paged_decode_impl(out, out_dtype, query, key_cache, value_cache, cache_dtype,
+                             block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                             num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             num_blocks, head_scales(k_scales, v_scales), true, sliding_window,
+                             num_splits, workspace, workspace_bytes, stream);
+}
+
 
 size_t fp8kv_decode_step_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                         int head_dim, int block_size, int max_context_len,
@@ -288,45 +423,29 @@ int fp8kv_decode_step(void* out, int out_dtype, const void* query, const void* k
                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                       int num_blocks, float k_scale, float v_scale, int sliding_window,
                       int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
-    if (num_seqs < 0 || num_kv_heads <= 0) return FP8KV_ERR_SHAPE;
-    // counters first, then the partials (checked by setup_decode)
-    const size_t cbytes = step_counter_bytes(num_seqs, num_kv_heads);
-    const bool have_ws = workspace != nullptr && workspace_bytes >= cbytes;
-    fp8kv::DecodeParams p;
-    bool fp8 = true;
-    int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
-                          max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, k_scale,
-                          v_scale, sliding_window, num_splits,
-                          have_ws ? static_cast<char*>(workspace) + cbytes : nullptr,
-                          have_ws ? workspace_bytes - cbytes : 0, false);
-    if (st != FP8KV_OK) return st;
-    if (num_seqs == 0) return FP8KV_OK;
-    if (!out || !key_new || !value_new) return FP8KV_ERR_NULL;
-    if (!aligned16(out) || !aligned16(key_new) || !aligned16(value_new)) return FP8KV_ERR_SHAPE;
-    // several splits: workgroups claim steps from counters (load balance) and the last one
-    // of each group merges inside the decode kernel when one workgroup merges a group
-    // cheaply, else the merge kernel queued behind it does
-    const bool fused = !p.write_final &&
-                       fp8kv::fused_merge_fits(num_q_heads / num_kv_heads, head_dim, p.splits);
-    if (!p.write_final) {
-        p.counters = static_cast<unsigned int*>(workspace);
-        p.claims = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) +
-                                                   arrival_bytes(num_seqs, num_kv_heads));
-        p.merge_in_kernel = fused ? 1 : 0;
-    }
-    p.out = out;
-    p.out_f32 = out_dtype == FP8KV_F32;
-    p.k_new = static_cast<const uint16_t*>(key_new);
-    p.v_new = static_cast<const uint16_t*>(value_new);
-    p.k_scale_q = fp8 ? k_scale : 1.0f;
-    p.v_scale_q = fp8 ? v_scale : 1.0f;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
-    if (st != FP8KV_OK || p.write_final || fused) return st;
-    return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
+    return decode_step_impl(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
+                            cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                            max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            block_size, num_blocks, tensor_scales(k_scale, v_scale), false,
+                            sliding_window, num_splits, workspace, workspace_bytes, stream);
 }
+
+int fp8kv_decode_step_per_head(void* out, int out_dtype, const void* query, const void* key_new,
+                               const void* value_new, void* key_cache, void* value_cache,
+                               int cache_dtype, const int32_t* block_tables,
+                               int max_blocks_per_seq, const int32_t* context_lens,
+                               int max_context_len, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               const float* k_scales, const float* v_scales, int sliding_window,
+                               int num_splits, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return decode_step_impl(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
+                            cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                            max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            block_size, num_blocks, head_scales(k_scales, v_scales), true,
+                            sliding_window, num_splits, workspace, workspace_bytes, stream);
+}
+
 
 int fp8kv_paged_decode_partial(const void* query, const void* key_cache, const void* value_cache,
                                int cache_dtype, const int32_t* block_tables,
@@ -339,8 +458,9 @@ int fp8kv_paged_decode_partial(const void* query, const void* key_cache, const v
     bool fp8 = true;
     int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
                           max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, k_scale,
-                          1.0f, sliding_window, num_splits, workspace, workspace_bytes, true);
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          tensor_scales(k_scale, 1.0f), false, sliding_window, num_splits,
+                          workspace, workspace_bytes, true);
     if (st != FP8KV_OK || num_seqs == 0) return st;
     return hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
 }
@@ -363,7 +483,7 @@ int fp8kv_paged_decode_merge(void* out, int out_dtype, const int32_t* context_le
     const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits);
     if (!workspace || workspace_bytes < wl.total) return FP8KV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP8KV_ERR_WORKSPACE;
-    fp8kv::DecodeParams p = {};
+    fp8kv::DecodeParams p = {};   // per-tensor: no scale arrays
     p.out = out;
     p.out_f32 = out_dtype == FP8KV_F32;
     p.context_lens = context_lens;

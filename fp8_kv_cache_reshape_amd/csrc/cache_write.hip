@@ -1,6 +1,7 @@
 // cache_write.hip -- quantise-on-write of new K/V rows into the paged caches.
 //
-// Each element is divided by its tensor's scale in IEEE binary32 and cast once to OCP
+// Each element is divided by its tensor's scale -- or its kv head's, with per-attention-head
+// scales (same page and section) -- in IEEE binary32 and cast once to OCP
 // E4M3 (page "FP8 KV Cache Quantization: Capacity Gains and Accuracy Risk", section
 // "Scales and calibration"); the bytes are scattered by slot into 16-token blocks
 // (same page, "Why the KV cache sets long-context capacity").  Values land in
@@ -40,8 +41,9 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
     if constexpr (FP8) {
         uint8_t* kc = static_cast<uint8_t*>(p.key_cache);
         uint8_t* vc = static_cast<uint8_t*>(p.value_cache);
-        *reinterpret_cast<uint2*>(kc + tile + key_chunk_offset<D, 1>(off, c * 8)) = quantize8(xk, p.k_scale);
-        const uint2 qv = quantize8(xv, p.v_scale);
+        *reinterpret_cast<uint2*>(kc + tile + key_chunk_offset<D, 1>(off, c * 8)) =
+            quantize8(xk, p.k_scales != nullptr ? p.k_scales[h] : p.k_scale);
+        const uint2 qv = quantize8(xv, p.v_scales != nullptr ? p.v_scales[h] : p.v_scale);
         uint8_t* vdst = vc + tile + (int64_t)(c * 8) * kBlockSize + off;
 #pragma unroll
         for (int i = 0; i < 4; ++i) vdst[i * kBlockSize] = (uint8_t)(qv.x >> (8 * i));

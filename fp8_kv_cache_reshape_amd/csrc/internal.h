@@ -32,6 +32,8 @@ struct CacheWriteParams {
     int num_blocks;
     float k_scale;
     float v_scale;
+    const float* k_scales;         // per-kv-head scales [Hkv] (device), or null: k_scale
+    const float* v_scales;         // ... or null: v_scale
 };
 
 struct DecodeParams {
@@ -65,7 +67,19 @@ struct DecodeParams {
     unsigned int* claims;          // [B][Hkv][waves] step claim counters, kClaimStride apart
                                    // (zero between calls), or null; needs `counters`
     int merge_in_kernel;           // with `counters`: the last workgroup of a group merges
+    // per-attention-head scales [Hkv] (device), or null for the per-tensor values above;
+    // with them score_scale excludes the key scale and v_scale / k_scale_q / v_scale_q are
+    // unused
+    const float* k_scales;
+    const float* v_scales;
 };
+
+// The scale of kv head h: from a per-head array (a wave-uniform scalar load), or the
+// per-tensor value when there is no array.
+__device__ inline float head_scale(const float* per_head, int h, float per_tensor) {
+    typedef const __attribute__((address_space(4))) float* ConstF32Ptr;
+    return per_head != nullptr ? ((ConstF32Ptr)per_head)[h] : per_tensor;
+}
 
 // Claim counters sit this many 32-bit words (256 bytes) apart, so that the counters of
 // different waves and groups never share a line.

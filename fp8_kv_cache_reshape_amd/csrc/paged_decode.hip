@@ -150,7 +150,7 @@ constexpr int kMergeLaneBatch = 16;
 // before the first wait, unconditionally (absent splits read the last split and weigh 0) so
 // the compiler can count them -- one round trip instead of two.
 template <int D>
-__device__ void merge_two_quads(const DecodeParams& p, int64_t hq0, int NQ, int ns) {
+__device__ void merge_two_quads(const DecodeParams& p, int64_t hq0, int NQ, int ns, float vsc) {
     constexpr int Q = 2;
     constexpr int S = kMergeLaneBatch;
     const int par = threadIdx.x & 1;
@@ -192,7 +192,7 @@ __device__ void merge_two_quads(const DecodeParams& p, int64_t hq0, int NQ, int 
             a.w = fmaf(ws, xv[j][u].w, a.w);
         }
         lam += pair_swap(lam);
-        const float scale = lam > 0.0f ? p.v_scale / lam : 0.0f;
+        const float scale = lam > 0.0f ? vsc / lam : 0.0f;
         const float r0 = a.x + pair_swap(a.x), r1 = a.y + pair_swap(a.y);
         const float r2 = a.z + pair_swap(a.z), r3 = a.w + pair_swap(a.w);
         const int q = (int)(threadIdx.x >> 1) + j * 32 * kDecodeWaves;
@@ -207,11 +207,12 @@ __device__ void merge_two_quads(const DecodeParams& p, int64_t hq0, int NQ, int 
 
 template <int D>
 __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) {
+    const float vsc = head_scale(p.v_scales, h, p.v_scale);
     const int par = threadIdx.x & 1;
     const int NQ = G * D / 4;                                  // channel quads of the group
     const int64_t hq0 = (int64_t)b * p.num_q_heads + (int64_t)h * G;
     if (NQ > 32 * kDecodeWaves && NQ <= 64 * kDecodeWaves && ns <= 2 * kMergeLaneBatch) {
-        merge_two_quads<D>(p, hq0, NQ, ns);
+        merge_two_quads<D>(p, hq0, NQ, ns, vsc);
         return;
     }
     for (int q = threadIdx.x >> 1; q < NQ; q += 32 * kDecodeWaves) {   // lane pairs of the workgroup
@@ -259,7 +260,7 @@ __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) 
             accumulate(kMergeLaneBatch);
         }
         lam += pair_swap(lam);
-        const float scale = lam > 0.0f ? p.v_scale / lam : 0.0f;
+        const float scale = lam > 0.0f ? vsc / lam : 0.0f;
         const float r0 = a.x + pair_swap(a.x), r1 = a.y + pair_swap(a.y);
         const float r2 = a.z + pair_swap(a.z), r3 = a.w + pair_swap(a.w);
         const int64_t o = (hq0 + hh) * D + 4 * c4 + 2 * par;
@@ -296,6 +297,7 @@ void decode_partial_kernel(DecodeParams p) {
                  "s"(p.num_kv_heads), "s"(p.num_blocks), "s"(p.sliding_window));
     asm volatile("" :: "s"(p.score_scale), "s"(p.v_scale), "s"(p.splits), "s"(p.blocks_per_split),
                  "s"(p.write_final), "s"(p.k_scale_q), "s"(p.v_scale_q), "s"(p.merge_in_kernel),
+                 "s"(p.k_scales), "s"(p.v_scales),
                  "s"(p.out_f32));
     const int split = kHeadsFastest ? blockIdx.y : blockIdx.x;
     const int h = kHeadsFastest ? blockIdx.x : blockIdx.y;
@@ -353,7 +355,7 @@ void decode_partial_kernel(DecodeParams p) {
     // address space lets the wave-uniform id reads below be scalar loads, which do not queue
     // behind the vector KV loads in flight.
     const ConstI32Ptr bt = (ConstI32Ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq + w.blk0);
-    const float sscale = p.score_scale;
+    const float sscale = p.score_scale * head_scale(p.k_scales, h, 1.0f);
     const int nblk = w.nblk;                      // blocks of the window
     const int nsteps = (nblk + 3) >> 2;           // wave steps (4 blocks) of the window
 
@@ -601,7 +603,8 @@ void decode_partial_kernel(DecodeParams p) {
             char* tile = static_cast<char*>(const_cast<void*>(val ? p.value_cache : p.key_cache))
                          + ((int64_t)tok_blk * p.num_kv_heads + h) * TILE_BYTES;
             if constexpr (FP8) {
-                const uint2 q8 = quantize8(tok, val ? p.v_scale_q : p.k_scale_q);
+                const uint2 q8 = quantize8(tok, val ? head_scale(p.v_scales, h, p.v_scale_q)
+                                                    : head_scale(p.k_scales, h, p.k_scale_q));
                 if (!val) {
                     *reinterpret_cast<uint2*>(tile + key_chunk_offset<D, 1>(off, c * 8)) = q8;
                 } else {
@@ -719,7 +722,7 @@ void decode_partial_kernel(DecodeParams p) {
             comp_add(lam, lam_c, wv * sm_l[v * 16 + hd]);
         }
         lam += lam_c;
-        sm_s[hd] = lam > 0.0f ? p.v_scale / lam : 0.0f;
+        sm_s[hd] = lam > 0.0f ? head_scale(p.v_scales, h, p.v_scale) / lam : 0.0f;
         sm_M[hd] = M;
         sm_L[hd] = lam;
     }
@@ -856,7 +859,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
     s_part[sl][q][1] = lo;
     __syncthreads();
     lam = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
-    const float scale = lam > 0.0f ? p.v_scale / lam : 0.0f;
+    const int h = hq / (p.num_q_heads / p.num_kv_heads);
+    const float scale = lam > 0.0f ? head_scale(p.v_scales, h, p.v_scale) / lam : 0.0f;
     if (tid < 64) {
         const int qq = tid >> 2, comp = tid & 3;
         float sh = 0.0f, sc = 0.0f;

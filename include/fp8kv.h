@@ -117,6 +117,26 @@ int fp8kv_cache_write(const void* key, const void* value,
                       float k_scale, float v_scale, void* stream);
 
 /*
+ * fp8kv_cache_write_per_head -- fp8kv_cache_write with one key and one value scale per kv
+ * head: elements of kv head h are divided by k_scales[h] / v_scales[h] (page "FP8 KV Cache
+ * Quantization: Capacity Gains and Accuracy Risk", "Scales and calibration": the
+ * per-attention-head granularity, scale arrays of length num_kv_heads).  Rounding,
+ * saturation, layout, slot handling and the BF16 case (scales ignored) as above.
+ *
+ *   k_scales, v_scales  device float32 [num_kv_heads], 4-byte aligned, read by the kernel
+ *                       on `stream`; the caller owns them.  For FP8KV_E4M3 both must be
+ *                       non-NULL (else FP8KV_ERR_NULL; misaligned: FP8KV_ERR_SHAPE) and
+ *                       every entry finite and > 0 -- a precondition the library does not
+ *                       check (it does not read device memory on the host).  Ignored for
+ *                       FP8KV_BF16 (may be NULL).
+ */
+int fp8kv_cache_write_per_head(const void* key, const void* value,
+                               void* key_cache, void* value_cache, int cache_dtype,
+                               const int64_t* slot_mapping, int num_tokens,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               const float* k_scales, const float* v_scales, void* stream);
+
+/*
  * fp8kv_paged_decode_num_splits -- number of context splits a decode will use.
  *
  * The context window of every (sequence, kv head) is cut into splits of a fixed number
@@ -177,13 +197,33 @@ int fp8kv_paged_decode(void* out, int out_dtype, const void* query,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fp8kv_paged_decode_per_head -- fp8kv_paged_decode with per-kv-head scales: for query
+ * head hq, K_j and V_j are dequantised with k_scales[h] and v_scales[h], h = hq / g (page
+ * "FP8 KV Cache Quantization: Capacity Gains and Accuracy Risk", "Scales and
+ * calibration", per-attention-head granularity).  The key scale multiplies
+ * log2(e)/sqrt(head_dim) (rounded to float) inside the kernel; the value scale multiplies
+ * the merged output.  k_scales / v_scales as for fp8kv_cache_write_per_head; every other
+ * argument, the workspace and the error behaviour as for fp8kv_paged_decode.
+ */
+int fp8kv_paged_decode_per_head(void* out, int out_dtype, const void* query,
+                                const void* key_cache, const void* value_cache, int cache_dtype,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int max_context_len,
+                                int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                int block_size, int num_blocks,
+                                const float* k_scales, const float* v_scales,
+                                int sliding_window, int num_splits,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fp8kv_paged_decode_partial -- the first pass of fp8kv_paged_decode alone: writes the
  * fp32 split partials (m, l, acc) of every (sequence, query head, split) into the
  * workspace and nothing else.  Partials of different context ranges combine exactly
  * like splits, so a sequence whose blocks are spread over several devices can run this
  * pass per device, gather the partials, and finish with fp8kv_paged_decode_merge.
  * Arguments as for fp8kv_paged_decode (v_scale is applied by the merge).  The partial
- * m is kept in base-2 units: m = max_j s_j * log2(e).
+ * m is kept in base-2 units: m = max_j s_j * log2(e).  This pass and the merge below take
+ * per-tensor scales only.
  */
 int fp8kv_paged_decode_partial(const void* query,
                                const void* key_cache, const void* value_cache, int cache_dtype,
@@ -258,6 +298,26 @@ int fp8kv_decode_step(void* out, int out_dtype, const void* query,
                       int block_size, int num_blocks,
                       float k_scale, float v_scale, int sliding_window, int num_splits,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8kv_decode_step_per_head -- fp8kv_decode_step with per-kv-head scales: the new token
+ * of kv head h is quantised with k_scales[h] / v_scales[h] exactly as
+ * fp8kv_cache_write_per_head does, and the attention dequantises as
+ * fp8kv_paged_decode_per_head does (page "FP8 KV Cache Quantization: Capacity Gains and
+ * Accuracy Risk", "Scales and calibration").  k_scales / v_scales as for
+ * fp8kv_cache_write_per_head; everything else, the workspace and its counter region
+ * included, as for fp8kv_decode_step.
+ */
+int fp8kv_decode_step_per_head(void* out, int out_dtype, const void* query,
+                               const void* key_new, const void* value_new,
+                               void* key_cache, void* value_cache, int cache_dtype,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int max_context_len,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int num_blocks,
+                               const float* k_scales, const float* v_scales,
+                               int sliding_window, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -172,6 +172,26 @@ def spread_head_scales(Hkv: int, cid: int, lo: float = 0.05, hi: float = 8.0) ->
     return np.exp(rng.uniform(np.log(lo), np.log(hi), size=Hkv)).astype(np.float32)
 
 
+def with_head_magnitudes(w: "Workload", cid: int, max_exp: int = 3):
+    """A copy of workload `w` whose every layer has kv heads of different magnitudes: the K
+    and V rows of head h are multiplied by 2**e (seeded e in [-max_exp, max_exp], drawn
+    separately for K and V; exact in bf16), with calibrated per-head scales.  Returns
+    (workload, [(k_scales, v_scales) per layer]) -- the input a per-head calibration is for."""
+    rng = np.random.Generator(np.random.PCG64(5000 + cid))
+    layers, scales = [], []
+    for L in w.layers:
+        ek = rng.integers(-max_exp, max_exp + 1, size=w.num_kv_heads)
+        ev = rng.integers(-max_exp, max_exp + 1, size=w.num_kv_heads)
+        fk = np.exp2(ek).astype(np.float32)[None, :, None]
+        fv = np.exp2(ev).astype(np.float32)[None, :, None]
+        k = f32_to_bf16_bits(bf16_bits_to_f32(L.k) * fk)
+        v = f32_to_bf16_bits(bf16_bits_to_f32(L.v) * fv)
+        layers.append(Layer(k=k, v=v, cache_dtype=L.cache_dtype, k_scale=L.k_scale,
+                            v_scale=L.v_scale, sliding_window=L.sliding_window, name=L.name))
+        scales.append((per_head_amax_scales(k), per_head_amax_scales(v)))
+    return Workload(**{**w.__dict__, "layers": layers}), scales
+
+
 def make_workload(name: str, cid: int, *, num_q_heads: int, num_kv_heads: int, head_dim: int,
                   context_lens=None, num_seqs: int = 1, len_range=None, std: float = 1.0,
                   outlier_frac: float = 0.0, outlier_mult: float = 8.0, scale_mode: str = "amax",

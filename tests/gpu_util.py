@@ -56,18 +56,35 @@ def to_host_bits(t: torch.Tensor) -> np.ndarray:
     return a.view(np.uint16) if a.dtype == np.int16 else a
 
 
-def gpu_write(w: syn.Workload, layer: syn.Layer, kc, vc, rows=None, stream=None) -> None:
+def f32_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+# `heads`, where a helper takes it, is None (the layer's per-tensor scales) or a pair of
+# float32 [Hkv] arrays (k_scales, v_scales): the per-head entry points and oracle functions.
+
+def gpu_write(w: syn.Workload, layer: syn.Layer, kc, vc, rows=None, stream=None, heads=None) -> None:
     rows = np.arange(w.num_tokens) if rows is None else np.asarray(rows)
     k, v = u16_dev(layer.k[rows]), u16_dev(layer.v[rows])
     slots = torch.from_numpy(np.ascontiguousarray(w.slot_mapping[rows])).to(DEV)
-    F.fp8kv_cache_write(k, v, kc, vc, code(layer), slots, len(rows), w.num_kv_heads, w.head_dim,
-                        w.block_size, w.num_blocks, layer.k_scale, layer.v_scale, stream)
+    if heads is None:
+        F.fp8kv_cache_write(k, v, kc, vc, code(layer), slots, len(rows), w.num_kv_heads, w.head_dim,
+                            w.block_size, w.num_blocks, layer.k_scale, layer.v_scale, stream)
+    else:
+        F.fp8kv_cache_write_per_head(k, v, kc, vc, code(layer), slots, len(rows), w.num_kv_heads,
+                                     w.head_dim, w.block_size, w.num_blocks, f32_dev(heads[0]),
+                                     f32_dev(heads[1]), stream)
 
 
-def oracle_write(w: syn.Workload, layer: syn.Layer):
+def oracle_write(w: syn.Workload, layer: syn.Layer, heads=None):
     kc, vc = host_caches(w, code(layer))
-    oracle.cache_write(layer.k, layer.v, kc, vc, code(layer), w.slot_mapping, w.num_kv_heads,
-                       w.head_dim, w.block_size, w.num_blocks, layer.k_scale, layer.v_scale)
+    if heads is None:
+        oracle.cache_write(layer.k, layer.v, kc, vc, code(layer), w.slot_mapping, w.num_kv_heads,
+                           w.head_dim, w.block_size, w.num_blocks, layer.k_scale, layer.v_scale)
+    else:
+        oracle.cache_write_per_head(layer.k, layer.v, kc, vc, code(layer), w.slot_mapping,
+                                    w.num_kv_heads, w.head_dim, w.block_size, w.num_blocks,
+                                    heads[0], heads[1])
     return kc, vc
 
 
@@ -80,7 +97,8 @@ class DeviceInputs:
 
 
 def gpu_decode(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_splits=0,
-               window=None, dev: DeviceInputs = None, max_context_len=None, split_api=False):
+               window=None, dev: DeviceInputs = None, max_context_len=None, split_api=False,
+               heads=None):
     dev = dev or DeviceInputs(w)
     win = layer.sliding_window if window is None else window
     maxl = w.max_context_len if max_context_len is None else max_context_len
@@ -90,7 +108,13 @@ def gpu_decode(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_spl
     out = torch.empty(B * Hq * D, dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
     odt = F.FP8KV_F32 if out_f32 else F.FP8KV_BF16
     cdt = code(layer)
-    if split_api:
+    if heads is not None:
+        assert not split_api, "the split passes take per-tensor scales only"
+        F.fp8kv_paged_decode_per_head(out, odt, dev.q, kc, vc, cdt, dev.bt, w.max_blocks_per_seq,
+                                      dev.cl, maxl, B, Hq, Hkv, D, w.block_size, w.num_blocks,
+                                      f32_dev(heads[0]), f32_dev(heads[1]), win, num_splits, ws,
+                                      ws_bytes)
+    elif split_api:
         F.fp8kv_paged_decode_partial(dev.q, kc, vc, cdt, dev.bt, w.max_blocks_per_seq, dev.cl, maxl,
                                      B, Hq, Hkv, D, w.block_size, w.num_blocks, layer.k_scale, win,
                                      num_splits, ws, ws_bytes)
@@ -106,9 +130,15 @@ def gpu_decode(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_spl
 
 
 def oracle_decode(w: syn.Workload, layer: syn.Layer, okc, ovc, pairs=None, window=None,
-                  context_lens=None):
+                  context_lens=None, heads=None):
     win = layer.sliding_window if window is None else window
     cl = w.context_lens if context_lens is None else context_lens
+    if heads is not None:
+        args = (w.q, okc, ovc, code(layer), w.block_tables, cl, w.num_q_heads, w.num_kv_heads,
+                w.head_dim, w.block_size, heads[0], heads[1], win)
+        if pairs is None:
+            return oracle.paged_decode_per_head(*args)
+        return oracle.paged_decode_pairs_per_head(pairs, *args)
     args = (w.q, okc, ovc, code(layer), w.block_tables, cl, w.num_q_heads, w.num_kv_heads,
             w.head_dim, w.block_size, layer.k_scale, layer.v_scale, win)
     if pairs is None:
@@ -154,7 +184,7 @@ def step_rows_by_seq(w: syn.Workload, layer: syn.Layer):
 
 
 def gpu_decode_step(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_splits=0,
-                    dev: DeviceInputs = None, workspace=None):
+                    dev: DeviceInputs = None, workspace=None, heads=None):
     """One fused step: writes each sequence's last token and decodes.  Returns (out, workspace)."""
     dev = dev or DeviceInputs(w)
     B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
@@ -166,9 +196,16 @@ def gpu_decode_step(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, nu
     ws_bytes = workspace.numel()           # the library checks what it needs against this
     kn, vn = step_rows_by_seq(w, layer)
     out = torch.empty(B * Hq * D, dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
-    F.fp8kv_decode_step(out, F.FP8KV_F32 if out_f32 else F.FP8KV_BF16, dev.q, u16_dev(kn), u16_dev(vn),
-                        kc, vc, code(layer), dev.bt, w.max_blocks_per_seq, dev.cl, maxl, B, Hq, Hkv, D,
-                        w.block_size, w.num_blocks, layer.k_scale, layer.v_scale, win, num_splits,
-                        workspace, ws_bytes)
+    odt = F.FP8KV_F32 if out_f32 else F.FP8KV_BF16
+    if heads is None:
+        F.fp8kv_decode_step(out, odt, dev.q, u16_dev(kn), u16_dev(vn), kc, vc, code(layer), dev.bt,
+                            w.max_blocks_per_seq, dev.cl, maxl, B, Hq, Hkv, D, w.block_size,
+                            w.num_blocks, layer.k_scale, layer.v_scale, win, num_splits, workspace,
+                            ws_bytes)
+    else:
+        F.fp8kv_decode_step_per_head(out, odt, dev.q, u16_dev(kn), u16_dev(vn), kc, vc, code(layer),
+                                     dev.bt, w.max_blocks_per_seq, dev.cl, maxl, B, Hq, Hkv, D,
+                                     w.block_size, w.num_blocks, f32_dev(heads[0]),
+                                     f32_dev(heads[1]), win, num_splits, workspace, ws_bytes)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D), workspace

@@ -68,6 +68,31 @@ def test_cache_write_accepts_edge_cases_without_launch():
     assert _write(num_tokens=0, cache_dtype=F.FP8KV_BF16, k_scale=0.0) == F.FP8KV_OK
 
 
+def _write_ph(**kw):
+    a = dict(key=FAKE, value=FAKE, key_cache=FAKE, value_cache=FAKE, cache_dtype=F.FP8KV_E4M3,
+             slot_mapping=FAKE, num_tokens=4, num_kv_heads=8, head_dim=128, block_size=16,
+             num_blocks=10, k_scales=FAKE, v_scales=FAKE, stream=0)
+    a.update(kw)
+    return F.lib.fp8kv_cache_write_per_head(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_scales=0), F.FP8KV_ERR_NULL), (dict(v_scales=0), F.FP8KV_ERR_NULL),
+    (dict(k_scales=FAKE + 2), F.FP8KV_ERR_SHAPE), (dict(v_scales=FAKE + 1), F.FP8KV_ERR_SHAPE),
+    (dict(key=0), F.FP8KV_ERR_NULL), (dict(head_dim=96), F.FP8KV_ERR_UNSUPPORTED),
+    # the arrays are checked with the other scale arguments, before the zero-token exit
+    (dict(k_scales=0, num_tokens=0), F.FP8KV_ERR_NULL),
+])
+def test_cache_write_per_head_rejects(kw, status):
+    assert _write_ph(**kw) == status
+
+
+def test_cache_write_per_head_edge_cases_without_launch():
+    assert _write_ph(num_tokens=0) == F.FP8KV_OK
+    # bf16 caches ignore the scale arrays, which may then be NULL
+    assert _write_ph(num_tokens=0, cache_dtype=F.FP8KV_BF16, k_scales=0, v_scales=0) == F.FP8KV_OK
+
+
 def _decode(**kw):
     a = dict(out=FAKE, out_dtype=F.FP8KV_BF16, query=FAKE, key_cache=FAKE, value_cache=FAKE,
              cache_dtype=F.FP8KV_E4M3, block_tables=FAKE, max_blocks_per_seq=64, context_lens=FAKE,
@@ -96,6 +121,37 @@ def _decode(**kw):
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
+
+
+def _decode_ph(step=False, **kw):
+    a = dict(out=FAKE, out_dtype=F.FP8KV_BF16, query=FAKE, key_cache=FAKE, value_cache=FAKE,
+             cache_dtype=F.FP8KV_E4M3, block_tables=FAKE, max_blocks_per_seq=64, context_lens=FAKE,
+             max_context_len=1024, num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=128,
+             block_size=16, num_blocks=200, k_scales=FAKE, v_scales=FAKE, sliding_window=0,
+             num_splits=4, workspace=FAKE, workspace_bytes=0, stream=0)
+    a.update(kw)
+    if step:
+        v = list(a.values())
+        return F.lib.fp8kv_decode_step_per_head(*v[:3], FAKE, FAKE, *v[3:])
+    return F.lib.fp8kv_paged_decode_per_head(*a.values())
+
+
+@pytest.mark.parametrize("step", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_scales=0), F.FP8KV_ERR_NULL), (dict(v_scales=0), F.FP8KV_ERR_NULL),
+    (dict(k_scales=FAKE + 2), F.FP8KV_ERR_SHAPE), (dict(v_scales=FAKE + 3), F.FP8KV_ERR_SHAPE),
+    (dict(query=0), F.FP8KV_ERR_NULL), (dict(num_q_heads=30), F.FP8KV_ERR_SHAPE),
+    (dict(workspace=0), F.FP8KV_ERR_WORKSPACE), (dict(out_dtype=0), F.FP8KV_ERR_UNSUPPORTED),
+])
+def test_decode_per_head_rejects(kw, status, step):
+    assert _decode_ph(step=step, **kw) == status
+
+
+def test_decode_per_head_bf16_ignores_scale_arrays():
+    # a bf16 cache needs no scales: NULL arrays pass validation (the workspace check follows)
+    assert _decode_ph(cache_dtype=F.FP8KV_BF16, k_scales=0, v_scales=0, workspace=0) == \
+        F.FP8KV_ERR_WORKSPACE
+    assert _decode_ph(num_seqs=0, query=0, out=0, workspace=0) == F.FP8KV_OK
 
 
 def test_decode_with_no_sequences_is_a_no_op():
