@@ -10,62 +10,172 @@
 // 16-byte chunks ordered (slot quad, chunk, slot in quad, channel quarter), so that each
 // key load instruction of the decode kernel reads whole 256-byte runs of a tile.
 //
-// One thread handles 8 consecutive channels of one (token, kv head): a 16-byte bf16
-// load per tensor, eight f32 divisions, four packed conversions, an 8-byte key store
-// and eight strided value bytes.  At decode time the write moves a few KiB per step,
-// so this kernel is sized for simplicity and exactness, not bandwidth.
+// One thread handles 8 consecutive channels of 4 consecutive input tokens of one kv head:
+// four 16-byte bf16 loads per tensor, 64 f32 divisions, then the stores.  When the four
+// tokens go to four consecutive slots starting at a multiple of 4 (what a prefill or any
+// in-order write of a sequence produces, except at its two ends) the four value bytes of
+// one channel are adjacent in the channel-major tile: a 4 x 8 byte transpose in registers
+// (byte permutes) turns the thread's codes into 8 four-byte channel stores, and the keys
+// go out as 4 eight-byte stores.  Any other quad (scattered slots, the decode step's one
+// token per sequence, a tail) takes the per-token path: 8-byte key stores and single-byte
+// value stores.  Lanes are ordered (token quad, channel chunk, kv head, group of 4 quads),
+// quad fastest, so the 4 lanes that complete one 16-byte channel row of a tile are
+// adjacent.  Rows of tokens past the end are loaded clamped (in bounds) and never stored.
 #include "codec.h"
 #include "internal.h"
+
+#include <type_traits>
 
 namespace fp8kv {
 namespace {
 
+// In: a[k] = 4 one-byte codes (channels 0..3) of token k.  Out: r[c] = the 4 tokens'
+// codes of channel c (token k in byte k).  Plain shifts and masks; the compiler turns them
+// into byte permutes.
+__device__ inline void transpose4x4(const uint32_t a[4], uint32_t r[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        r[c] = ((a[0] >> (8 * c)) & 0xFFu) | (((a[1] >> (8 * c)) & 0xFFu) << 8) |
+               (((a[2] >> (8 * c)) & 0xFFu) << 16) | (((a[3] >> (8 * c)) & 0xFFu) << 24);
+}
+
+// f(k) for k = 0..3 as compile-time constants: register arrays indexed by k stay in
+// registers.
+template <typename F>
+__device__ inline void for4(F f) {
+    f(std::integral_constant<int, 0>{});
+    f(std::integral_constant<int, 1>{});
+    f(std::integral_constant<int, 2>{});
+    f(std::integral_constant<int, 3>{});
+}
+
+// 16 bytes as a native vector: copies of it stay in registers (copies of the uint4 struct
+// wrapper are lowered as memory copies, which can move the arrays below out of registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline uint32_t dword(const u32x4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
 template <int D, bool FP8>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
-    constexpr int CHUNKS = D / 8;
+    constexpr int CH = D / 8;                     // 8-channel chunks per row
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * CHUNKS;
-    if (gid >= total) return;
-    const int c = (int)(gid % CHUNKS);
-    const int64_t th = gid / CHUNKS;              // token * Hkv + head
-    const int h = (int)(th % p.num_kv_heads);
-    const int64_t t = th / p.num_kv_heads;
-    // the row loads do not depend on the slot: issue them together with the slot load
-    const uint4 xk = *reinterpret_cast<const uint4*>(p.key + th * D + c * 8);
-    const uint4 xv = *reinterpret_cast<const uint4*>(p.value + th * D + c * 8);
-    const int64_t slot = p.slot_mapping[t];
-    if (slot < 0 || slot >= (int64_t)p.num_blocks * kBlockSize) return;
-    const int64_t blk = slot / kBlockSize;
-    const int off = (int)(slot % kBlockSize);
-    const int64_t tile = (blk * p.num_kv_heads + h) * (int64_t)kBlockSize * D;   // elements
+    const int64_t T = p.num_tokens;
+    const int Hkv = p.num_kv_heads;
+    const int64_t groups = (T + 15) / 16;
+    if (gid >= groups * Hkv * CH * 4) return;
+    const int tq = (int)(gid & 3);
+    int64_t r = gid >> 2;
+    const int c = (int)(r % CH);
+    r /= CH;
+    const int h = (int)(r % Hkv);
+    const int64_t t0 = ((r / Hkv) * 4 + tq) * 4;  // first token of this thread's quad
+    if (t0 >= T) return;
+
+    // loads of clamped rows (always in bounds); only the stores below are guarded
+    u32x4 xk[4], xv[4];
+    int64_t sl[4];
+    for4([&](auto kk) {
+        constexpr int k = decltype(kk)::value;
+        const int64_t tk = t0 + k < T ? t0 + k : T - 1;
+        const int64_t row = (tk * Hkv + h) * D + c * 8;
+        xk[k] = *reinterpret_cast<const u32x4*>(p.key + row);
+        xv[k] = *reinterpret_cast<const u32x4*>(p.value + row);
+        sl[k] = p.slot_mapping[tk];
+    });
+    const int64_t nslots = (int64_t)p.num_blocks * kBlockSize;
+    const bool fast = t0 + 3 < T && sl[0] >= 0 && sl[0] < nslots && (sl[0] & 3) == 0 &&
+                      sl[1] == sl[0] + 1 && sl[2] == sl[0] + 2 && sl[3] == sl[0] + 3;
+
     if constexpr (FP8) {
         uint8_t* kc = static_cast<uint8_t*>(p.key_cache);
         uint8_t* vc = static_cast<uint8_t*>(p.value_cache);
-        *reinterpret_cast<uint2*>(kc + tile + key_chunk_offset<D, 1>(off, c * 8)) =
-            quantize8(xk, p.k_scales != nullptr ? p.k_scales[h] : p.k_scale);
-        const uint2 qv = quantize8(xv, p.v_scales != nullptr ? p.v_scales[h] : p.v_scale);
-        uint8_t* vdst = vc + tile + (int64_t)(c * 8) * kBlockSize + off;
+        const float ks = p.k_scales != nullptr ? p.k_scales[h] : p.k_scale;
+        const float vs = p.v_scales != nullptr ? p.v_scales[h] : p.v_scale;
+        uint2 qk[4], qv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vdst[i * kBlockSize] = (uint8_t)(qv.x >> (8 * i));
+        for (int k = 0; k < 4; ++k) {
+            qk[k] = quantize8(make_uint4(xk[k].x, xk[k].y, xk[k].z, xk[k].w), ks);
+            qv[k] = quantize8(make_uint4(xv[k].x, xv[k].y, xv[k].z, xv[k].w), vs);
+        }
+        if (fast) {
+            const int64_t blk = sl[0] / kBlockSize;
+            const int off0 = (int)(sl[0] % kBlockSize);
+            const int64_t tile = (blk * Hkv + h) * (int64_t)kBlockSize * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vdst[(i + 4) * kBlockSize] = (uint8_t)(qv.y >> (8 * i));
+            for (int k = 0; k < 4; ++k)
+                *reinterpret_cast<uint2*>(kc + tile + key_chunk_offset<D, 1>(off0 + k, c * 8)) = qk[k];
+            const uint32_t lo[4] = {qv[0].x, qv[1].x, qv[2].x, qv[3].x};
+            const uint32_t hi[4] = {qv[0].y, qv[1].y, qv[2].y, qv[3].y};
+            uint32_t col[8];
+            transpose4x4(lo, col);
+            transpose4x4(hi, col + 4);
+            uint8_t* vdst = vc + tile + (int64_t)(c * 8) * kBlockSize + off0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) *reinterpret_cast<uint32_t*>(vdst + j * kBlockSize) = col[j];
+        } else {
+            for4([&](auto kk) {
+                constexpr int k = decltype(kk)::value;
+                const int64_t slot = sl[k];
+                if (t0 + k < T && slot >= 0 && slot < nslots) {
+                    const int64_t blk = slot / kBlockSize;
+                    const int off = (int)(slot % kBlockSize);
+                    const int64_t tile = (blk * Hkv + h) * (int64_t)kBlockSize * D;
+                    *reinterpret_cast<uint2*>(kc + tile + key_chunk_offset<D, 1>(off, c * 8)) = qk[k];
+                    uint8_t* vdst = vc + tile + (int64_t)(c * 8) * kBlockSize + off;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) vdst[i * kBlockSize] = (uint8_t)(qv[k].x >> (8 * i));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) vdst[(i + 4) * kBlockSize] = (uint8_t)(qv[k].y >> (8 * i));
+                }
+            });
+        }
     } else {
         uint16_t* kc = static_cast<uint16_t*>(p.key_cache);
         uint16_t* vc = static_cast<uint16_t*>(p.value_cache);
-        *reinterpret_cast<uint4*>(kc + tile + key_chunk_offset<D, 2>(off, c * 8) / 2) = xk;
-        uint16_t* vdst = vc + tile + (int64_t)(c * 8) * kBlockSize + off;
-        const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+        if (fast) {
+            const int64_t blk = sl[0] / kBlockSize;
+            const int off0 = (int)(sl[0] % kBlockSize);
+            const int64_t tile = (blk * Hkv + h) * (int64_t)kBlockSize * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            vdst[(2 * i) * kBlockSize] = (uint16_t)(w[i] & 0xFFFFu);
-            vdst[(2 * i + 1) * kBlockSize] = (uint16_t)(w[i] >> 16);
+            for (int k = 0; k < 4; ++k)
+                *reinterpret_cast<u32x4*>(kc + tile + key_chunk_offset<D, 2>(off0 + k, c * 8) / 2) = xk[k];
+            // channel 2i of token k is the low half of dword i of xv[k], channel 2i+1 the high
+            uint16_t* vdst = vc + tile + (int64_t)(c * 8) * kBlockSize + off0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t a0 = dword(xv[0], i), a1 = dword(xv[1], i);
+                const uint32_t a2 = dword(xv[2], i), a3 = dword(xv[3], i);
+                *reinterpret_cast<uint2*>(vdst + (2 * i) * kBlockSize) =
+                    make_uint2((a0 & 0xFFFFu) | (a1 << 16), (a2 & 0xFFFFu) | (a3 << 16));
+                *reinterpret_cast<uint2*>(vdst + (2 * i + 1) * kBlockSize) =
+                    make_uint2((a0 >> 16) | (a1 & 0xFFFF0000u), (a2 >> 16) | (a3 & 0xFFFF0000u));
+            }
+        } else {
+            for4([&](auto kk) {
+                constexpr int k = decltype(kk)::value;
+                const int64_t slot = sl[k];
+                if (t0 + k < T && slot >= 0 && slot < nslots) {
+                    const int64_t blk = slot / kBlockSize;
+                    const int off = (int)(slot % kBlockSize);
+                    const int64_t tile = (blk * Hkv + h) * (int64_t)kBlockSize * D;
+                    *reinterpret_cast<u32x4*>(kc + tile + key_chunk_offset<D, 2>(off, c * 8) / 2) = xk[k];
+                    uint16_t* vdst = vc + tile + (int64_t)(c * 8) * kBlockSize + off;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        vdst[(2 * i) * kBlockSize] = (uint16_t)(dword(xv[k], i) & 0xFFFFu);
+                        vdst[(2 * i + 1) * kBlockSize] = (uint16_t)(dword(xv[k], i) >> 16);
+                    }
+                }
+            });
         }
     }
 }
 
 template <int D>
 hipError_t launch_d(const CacheWriteParams& p, bool fp8, hipStream_t s) {
-    const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * (D / 8);
+    const int64_t total = (((int64_t)p.num_tokens + 15) / 16) * p.num_kv_heads * (D / 8) * 4;
     const int threads = 256;
     const int64_t blocks = (total + threads - 1) / threads;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;

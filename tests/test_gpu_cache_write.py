@@ -96,3 +96,50 @@ def test_prefix_then_step_write_equals_one_write():
     torch.cuda.synchronize()
     okc, ovc = oracle_write(w, layer)
     assert np.array_equal(to_host_bits(kc), okc) and np.array_equal(to_host_bits(vc), ovc)
+
+
+def _slot_pattern(name: str, T: int, NB: int, rng) -> np.ndarray:
+    """Slot mappings that send token quads down the kernel's two store paths: runs of
+    consecutive slots starting at a multiple of 4 (the transposed path) and everything else
+    (the per-token path), with tails that do not fill a quad."""
+    base = rng.permutation(NB)[: (T + 15) // 16 + 2].astype(np.int64) * 16
+    if name == "in_order_blocks":         # whole blocks in order, T not a multiple of 4
+        return np.concatenate([b + np.arange(16) for b in base])[:T]
+    if name == "shifted_by_one":          # consecutive but never 4-aligned at a quad start
+        return np.concatenate([b + np.arange(16) for b in base])[1:T + 1]
+    if name == "shifted_by_four":         # aligned, but each quad starts 4 slots into a block
+        s = np.concatenate([b + np.arange(16) for b in base])
+        return s[4:T + 4]
+    if name == "broken_runs":             # aligned starts with a gap or a skipped slot inside
+        s = np.concatenate([b + np.arange(16) for b in base])[:T].copy()
+        s[2::8] = -1                       # quads 0, 2, 4, ... lose their third token
+        return s
+    if name == "scattered":
+        return rng.permutation(NB * 16)[:T].astype(np.int64)
+    raise ValueError(name)
+
+
+@pytest.mark.parametrize("pattern", ["in_order_blocks", "shifted_by_one", "shifted_by_four",
+                                     "broken_runs", "scattered"])
+@pytest.mark.parametrize("cache", [syn.E4M3, syn.BF16])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_slot_patterns_bit_exact(pattern, cache, D):
+    Hkv, T = 3, 203
+    rng = np.random.default_rng(D + len(pattern))
+    NB = (T + 15) // 16 + 8
+    slots = _slot_pattern(pattern, T, NB, rng)
+    keys = syn.f32_to_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32) * 3)
+    vals = syn.f32_to_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32) * 3)
+    w = syn.Workload(name=f"slots-{pattern}", num_seqs=0, num_q_heads=Hkv, num_kv_heads=Hkv,
+                     head_dim=D, block_size=16, num_blocks=NB, context_lens=np.zeros(0, np.int32),
+                     block_tables=np.zeros((0, 1), np.int32), seq_offsets=np.zeros(1, np.int64),
+                     slot_mapping=slots, q=np.zeros((0, Hkv, D), np.uint16), layers=[])
+    layer = syn.Layer(k=keys, v=vals, cache_dtype=cache, k_scale=0.0213, v_scale=0.0172)
+    cdt = E4M3 if cache == syn.E4M3 else BF16
+    say(f"cache_write slot pattern {pattern} {cache} D={D}")
+    kc, vc = dev_caches(w, cdt)
+    gpu_write(w, layer, kc, vc)
+    torch.cuda.synchronize()
+    okc, ovc = oracle_write(w, layer)
+    assert np.array_equal(to_host_bits(kc), okc), "key cache bytes differ"
+    assert np.array_equal(to_host_bits(vc), ovc), "value cache bytes differ"
