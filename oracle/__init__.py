@@ -73,6 +73,8 @@ def _bind(path: str) -> ctypes.CDLL:
         "oracle_cache_write_per_head": [P, P, P, P, i32, P, i32, i32, i32, i32, i32, P, P],
         "oracle_paged_decode_pairs_per_head": [P, P, i32, P, P, P, i32, P, i32, P, i32, i32, i32,
                                                i32, P, P, i32],
+        "oracle_paged_prefill_pairs": [P, P, i32, P, P, i32, P, P, i32, P, i32, P, i32, i32, i32,
+                                       i32, f64, f64, i32],
     }.items():
         fn = getattr(L, name)
         fn.restype = None
@@ -253,3 +255,41 @@ def paged_decode_per_head(q, key_cache, value_cache, cache_dtype: int, block_tab
                                       context_lens, num_q_heads, num_kv_heads, head_dim, block_size,
                                       k_scales, v_scales, sliding_window)
     return out.reshape(B, num_q_heads, head_dim)
+
+
+# ------------------------------------------------------------- prefill ----
+
+def paged_prefill_pairs(pairs, q, query_start_loc, key_cache, value_cache, cache_dtype: int,
+                        block_tables, context_lens, num_q_heads: int, num_kv_heads: int,
+                        head_dim: int, block_size: int, k_scale: float, v_scale: float,
+                        sliding_window: int = 0) -> np.ndarray:
+    """fp64 prefill attention for the selected (query row, query head) pairs: [n][D].
+    q is bf16 [Tq][Hq][D]; the rows of sequence b are [qsl[b], qsl[b+1]) and sit at the
+    last positions of its context (see oracle.c)."""
+    q, bt, cl = _decode_common(q, key_cache, value_cache, cache_dtype, block_tables, context_lens)
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    B = cl.shape[0]
+    assert qsl.shape == (B + 1,) and qsl[0] == 0 and np.all(np.diff(qsl) >= 0)
+    assert q.shape[0] == qsl[-1]
+    pr = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    assert np.all((pr[:, 0] >= 0) & (pr[:, 0] < qsl[-1]))
+    out = np.empty((pr.shape[0], head_dim), dtype=np.float64)
+    lib().oracle_paged_prefill_pairs(_ptr(out), _ptr(pr), pr.shape[0], _ptr(q), _ptr(qsl), B,
+                                     _ptr(key_cache), _ptr(value_cache), cache_dtype, _ptr(bt),
+                                     bt.shape[1], _ptr(cl), num_q_heads, num_kv_heads, head_dim,
+                                     block_size, float(k_scale), float(v_scale),
+                                     int(sliding_window))
+    return out
+
+
+def paged_prefill(q, query_start_loc, key_cache, value_cache, cache_dtype: int, block_tables,
+                  context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                  block_size: int, k_scale: float, v_scale: float,
+                  sliding_window: int = 0) -> np.ndarray:
+    """Every (query row, query head): [Tq][Hq][D]."""
+    Tq = int(np.asarray(query_start_loc)[-1])
+    pairs = np.array([(r, hq) for r in range(Tq) for hq in range(num_q_heads)], np.int32)
+    out = paged_prefill_pairs(pairs, q, query_start_loc, key_cache, value_cache, cache_dtype,
+                              block_tables, context_lens, num_q_heads, num_kv_heads, head_dim,
+                              block_size, k_scale, v_scale, sliding_window)
+    return out.reshape(Tq, num_q_heads, head_dim)

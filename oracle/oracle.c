@@ -365,3 +365,62 @@ void oracle_paged_decode_pairs_per_head(double* out, const int32_t* pairs, int n
                                  pairs[2 * p], pairs[2 * p + 1]);
     }
 }
+
+/* ---------------------------------------------------- prefill attention --- */
+
+/*
+ * Prefill / chunked prefill over the paged cache: the query tokens of a prompt chunk
+ * attend to the cached context, the chunk itself included, with K and V dequantised
+ * inside the attention [CAP "Attention backend interactions"]; this is the pass whose
+ * contraction runs over the whole context [VLLM "ACCURACY AT LONG CONTEXT"].
+ * Sequence b's chunk is the query rows [qsl[b], qsl[b+1]); its n_b = qsl[b+1] - qsl[b]
+ * tokens occupy the last n_b positions of the context, so row qsl[b] + j sits at position
+ * p = L_b - n_b + j (L_b = context_lens[b], which counts the chunk).  Position p attends
+ * causally to positions [lo, p] with lo = max(0, p + 1 - W) for a window W > 0, else 0:
+ * exactly a decode over a context of length p + 1.  A row with p < 0 attends to nothing
+ * and gets a zero output.
+ *   q      bf16 [Tq][Hq][D]
+ *   pairs  int32 [n][2]: (query row, query head) to compute;  out double [n][D]
+ */
+void oracle_paged_prefill_pairs(double* out, const int32_t* pairs, int npairs,
+                                const uint16_t* q, const int32_t* qsl, int B,
+                                const void* key_cache, const void* value_cache,
+                                int cache_dtype, const int32_t* block_tables, int max_blocks,
+                                const int32_t* context_lens, int Hq, int Hkv, int D, int bs,
+                                double k_scale, double v_scale, int window) {
+    int group = Hq / Hkv;
+    int eb = cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2;
+    for (int p = 0; p < npairs; ++p) {
+        int64_t row = pairs[2 * p];
+        int hq = pairs[2 * p + 1];
+        int kvh = hq / group;
+        int b = 0;                               /* the sequence that owns this row */
+        while (b + 1 < B && qsl[b + 1] <= row) ++b;
+        int64_t chunk = qsl[b + 1] - qsl[b];
+        int64_t pos = (int64_t)context_lens[b] - chunk + (row - qsl[b]);
+        int64_t end = pos + 1;                   /* attended positions: [start, end) */
+        int64_t start = (window > 0 && end > window) ? end - window : 0;
+        int64_t n = end > start ? end - start : 0;
+        double* qv = (double*)malloc(sizeof(double) * (size_t)D);
+        double* K = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
+        double* V = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
+        for (int i = 0; i < D; ++i)
+            qv[i] = (double)oracle_bf16_to_f32(q[(row * Hq + hq) * D + i]);
+        for (int64_t j = start; j < end; ++j) {
+            int64_t phys = block_tables[(int64_t)b * max_blocks + j / bs];
+            int slot = (int)(j % bs);
+            for (int i = 0; i < D; ++i) {
+                K[(j - start) * D + i] = cache_value(key_cache, cache_dtype,
+                                                     key_index(phys, kvh, slot, i, Hkv, bs, D, eb),
+                                                     k_scale);
+                V[(j - start) * D + i] = cache_value(value_cache, cache_dtype,
+                                                     value_index(phys, kvh, slot, i, Hkv, bs, D),
+                                                     v_scale);
+            }
+        }
+        oracle_attention_rows(out + (int64_t)p * D, qv, K, V, n, D);
+        free(qv);
+        free(K);
+        free(V);
+    }
+}

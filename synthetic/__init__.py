@@ -192,6 +192,35 @@ def with_head_magnitudes(w: "Workload", cid: int, max_exp: int = 3):
     return Workload(**{**w.__dict__, "layers": layers}), scales
 
 
+@dataclasses.dataclass
+class PrefillQueries:
+    """The query rows of one prefill / chunked-prefill call: sequence b's chunk is the
+    last chunk_lens[b] positions of its context, rows [qsl[b], qsl[b+1]) of q."""
+    q: np.ndarray                # bf16 bits [Tq][Hq][D]
+    query_start_loc: np.ndarray  # int32 [B + 1]
+    chunk_lens: np.ndarray       # int32 [B]
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start_loc[-1])
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.chunk_lens.max()) if self.chunk_lens.size else 0
+
+
+def prefill_queries(w: "Workload", chunk_lens, cid: int, std: float = 1.0) -> PrefillQueries:
+    """Seeded N(0, std) bf16 query rows for a chunk of chunk_lens[b] tokens per sequence
+    (seed 6000 + cid)."""
+    rng = np.random.Generator(np.random.PCG64(6000 + cid))
+    n = np.asarray(chunk_lens, dtype=np.int32)
+    assert n.shape == (w.num_seqs,)
+    qsl = np.zeros(w.num_seqs + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(n)
+    q = f32_to_bf16_bits(_normal_bf16(rng, (int(qsl[-1]), w.num_q_heads, w.head_dim), std))
+    return PrefillQueries(q=q, query_start_loc=qsl, chunk_lens=n)
+
+
 def make_workload(name: str, cid: int, *, num_q_heads: int, num_kv_heads: int, head_dim: int,
                   context_lens=None, num_seqs: int = 1, len_range=None, std: float = 1.0,
                   outlier_frac: float = 0.0, outlier_mult: float = 8.0, scale_mode: str = "amax",

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_codec.py"),
         os.path.join(ROOT, "tests", "test_oracle_attention.py"),
-        os.path.join(ROOT, "tests", "test_oracle_per_head.py")]
+        os.path.join(ROOT, "tests", "test_oracle_per_head.py"),
+        os.path.join(ROOT, "tests", "test_oracle_prefill.py")]
 
 MUTANTS = {
     "subnormal_ties_away": ("double m = rint(a * 512.0);", "double m = round(a * 512.0);"),
@@ -61,6 +62,15 @@ MUTANTS = {
                                         "((uint8_t*)value_cache)[vi] = oracle_quantize(xv, k_scales[h]);"),
     "per_head_decode_interleaved_heads": ("int kv = pairs[2 * p + 1] / g;",
                                           "int kv = pairs[2 * p + 1] % Hkv;"),
+    "prefill_excludes_own_position": ("int64_t end = pos + 1;", "int64_t end = pos;"),
+    "prefill_chunk_at_context_start": (
+        "int64_t pos = (int64_t)context_lens[b] - chunk + (row - qsl[b]);",
+        "int64_t pos = (row - qsl[b]);"),
+    "prefill_first_query_row_for_all": (
+        "qv[i] = (double)oracle_bf16_to_f32(q[(row * Hq + hq) * D + i]);",
+        "qv[i] = (double)oracle_bf16_to_f32(q[((int64_t)qsl[b] * Hq + hq) * D + i]);"),
+    "prefill_interleaved_kv_heads": ("int kvh = hq / group;", "int kvh = hq % Hkv;"),
+    "prefill_window_off_by_one": ("? end - window : 0;", "? end - window + 1 : 0;"),
 }
 
 
