@@ -30,6 +30,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, published
 BLOCK = 16
 
 
@@ -434,6 +435,11 @@ def main(argv=None):
     ap.add_argument("--per-head-scales", action="store_true",
                     help="kv heads of different magnitudes with calibrated per-head scales, through "
                          "the per-head entry points (fp8 cache)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="only time fp8kv_paged_prefill (whole-prompt prefill, fp8 and bf16 caches) "
+                         "on the --prefill-workload shapes")
+    ap.add_argument("--prefill-workload", default="llama8b-8k,d256-8k",
+                    help="comma-separated: " + ", ".join(sorted(PREFILL_WORKLOADS)))
     ap.add_argument("--slope", action="store_true",
                     help="only sweep the context length at the 8B shape (B = 1, fp8 and bf16 KV) and fit "
                          "us/step = slope * L + intercept")
@@ -462,6 +468,10 @@ def main(argv=None):
 
     if args.slope:
         print(json.dumps(slope_sweep(F, torch, syn, args)), flush=True)
+        return 0
+    if args.prefill:
+        for name in args.prefill_workload.split(","):
+            print(json.dumps(_finite(prefill_bench(F, torch, syn, name, args))), flush=True)
         return 0
 
     t0 = time.perf_counter()
@@ -590,6 +600,85 @@ def slope_sweep(F, torch, syn, args) -> dict:
     out["fp8_over_bf16_slope"] = round(out["e4m3"]["slope_us_per_token"] / out["bf16"]["slope_us_per_token"], 4)
     out["pages_ms_per_token"] = {"H100 FA3 fp8": 2.37e-05, "B200 FlashInfer fp8": 9.72e-06}
     return out
+
+
+# Whole-prompt prefill shapes: (builder, chunk length per sequence).
+PREFILL_WORKLOADS = {
+    "llama8b-8k": (lambda syn: syn.llama8b_long(8192, "amax"), 8192),
+    "llama8b-chunk2k-at-32k": (lambda syn: syn.llama8b_long(32768, "amax"), 2048),
+    "d256-8k": (lambda syn: syn.make_workload("d256-b1-L8192", 5, num_q_heads=8, num_kv_heads=1,
+                                              head_dim=256, context_lens=[8192], std=0.5),
+                8192),
+}
+
+
+def prefill_flops(context_lens, chunk_lens, num_q_heads: int, head_dim: int, window: int = 0) -> int:
+    """Algorithmic flops of one prefill call: 4 * Hq * d per (query token, attended key)
+    (2 d for q.K, 2 d for p.V)."""
+    total = 0
+    for L, n in zip(context_lens, chunk_lens):
+        pos = np.arange(int(L) - int(n), int(L), dtype=np.int64)
+        pos = pos[pos >= 0]
+        keys = pos + 1 if window <= 0 else np.minimum(pos + 1, window)
+        total += int(keys.sum())
+    return 4 * num_q_heads * head_dim * total
+
+
+def prefill_bench(F, torch, syn, name: str, args) -> dict:
+    """Time fp8kv_paged_prefill over one whole-prompt chunk per sequence, for the fp8 cache
+    and the same data in a bf16 cache (HIP events around `launches` back-to-back calls)."""
+    build, chunk = PREFILL_WORKLOADS[name]
+    w = build(syn)
+    layer = w.layers[0]
+    pq = syn.prefill_queries(w, [chunk] * w.num_seqs, 170)
+    flops = prefill_flops(w.context_lens, pq.chunk_lens, w.num_q_heads, w.head_dim)
+    dev = "cuda"
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    q, qsl = u16(pq.q), torch.from_numpy(pq.query_start_loc).to(dev)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    cl = torch.from_numpy(w.context_lens).to(dev)
+    k_all, v_all = u16(layer.k), u16(layer.v)
+    slots = torch.from_numpy(w.slot_mapping).to(dev)
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    n = w.num_blocks * Hkv * BLOCK * D
+    out = torch.empty(pq.num_tokens * Hq * D, dtype=torch.bfloat16, device=dev)
+    res = {"metric": "prefill attention over the paged cache: TFLOP/s (% of bf16 MFMA peak)",
+           "workload": f"{name}: {w.name}, chunk {chunk}, Hq {Hq}, Hkv {Hkv}, d {D}",
+           "flops_per_call": flops}
+    launches = 20
+    for cache in ("e4m3", "bf16"):
+        cdt = F.FP8KV_E4M3 if cache == "e4m3" else F.FP8KV_BF16
+        dt = torch.uint8 if cache == "e4m3" else torch.int16
+        kc, vc = torch.zeros(n, dtype=dt, device=dev), torch.zeros(n, dtype=dt, device=dev)
+        ks = layer.k_scale if cache == "e4m3" else 1.0
+        vs = layer.v_scale if cache == "e4m3" else 1.0
+        F.fp8kv_cache_write(k_all, v_all, kc, vc, cdt, slots, w.num_tokens, Hkv, D, BLOCK,
+                            w.num_blocks, ks, vs)
+
+        def call():
+            F.fp8kv_paged_prefill(out, F.FP8KV_BF16, q, qsl, kc, vc, cdt, bt, w.max_blocks_per_seq,
+                                  cl, w.max_context_len, w.num_seqs, pq.max_query_len, Hq, Hkv, D,
+                                  BLOCK, w.num_blocks, ks, vs, 0)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        tf = flops / (ms * 1e-3) / 1e12
+        res[cache] = {"us_per_call": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+                      "pct_of_bf16_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2)}
+        del kc, vc
+        torch.cuda.empty_cache()
+    res["fp8_over_bf16_time"] = round(res["e4m3"]["us_per_call"] / res["bf16"]["us_per_call"], 4)
+    res["roofline"] = {"bound": "mfma", "achieved": res["e4m3"]["TFLOPs"],
+                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(res["e4m3"]["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return res
 
 
 def _finite(x):

@@ -51,6 +51,10 @@ SIGNATURES = {
                                _I, _F, _F, _I, _I, _P, _SZ, _P]),
     "fp8kv_decode_step_per_head": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I,
                                         _I, _I, _I, _I, _P, _P, _I, _I, _P, _SZ, _P]),
+    "fp8kv_paged_prefill": (_I, [_P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I,
+                                 _I, _I, _F, _F, _I, _P]),
+    "fp8kv_paged_prefill_per_head": (_I, [_P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
+                                          _I, _I, _I, _I, _P, _P, _I, _P]),
 }
 
 if not os.path.exists(LIBRARY_PATH):
@@ -241,3 +245,35 @@ def fp8kv_decode_step_per_head(out, out_dtype, query, key_new, value_new, key_ca
                                                  sliding_window, num_splits, _addr(workspace),
                                                  workspace_bytes, _stream(stream)),
                   "fp8kv_decode_step_per_head")
+
+
+def fp8kv_paged_prefill(out, out_dtype, query, query_start_loc, key_cache, value_cache,
+                        cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                        max_context_len, num_seqs, max_query_len, num_q_heads, num_kv_heads,
+                        head_dim, block_size, num_blocks, k_scale, v_scale, sliding_window,
+                        stream=None) -> int:
+    return _check(lib.fp8kv_paged_prefill(_addr(out), out_dtype, _addr(query),
+                                          _addr(query_start_loc), _addr(key_cache),
+                                          _addr(value_cache), cache_dtype, _addr(block_tables),
+                                          max_blocks_per_seq, _addr(context_lens), max_context_len,
+                                          num_seqs, max_query_len, num_q_heads, num_kv_heads,
+                                          head_dim, block_size, num_blocks, k_scale, v_scale,
+                                          sliding_window, _stream(stream)),
+                  "fp8kv_paged_prefill")
+
+
+def fp8kv_paged_prefill_per_head(out, out_dtype, query, query_start_loc, key_cache, value_cache,
+                                 cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                                 max_context_len, num_seqs, max_query_len, num_q_heads,
+                                 num_kv_heads, head_dim, block_size, num_blocks, k_scales,
+                                 v_scales, sliding_window, stream=None) -> int:
+    return _check(lib.fp8kv_paged_prefill_per_head(_addr(out), out_dtype, _addr(query),
+                                                   _addr(query_start_loc), _addr(key_cache),
+                                                   _addr(value_cache), cache_dtype,
+                                                   _addr(block_tables), max_blocks_per_seq,
+                                                   _addr(context_lens), max_context_len, num_seqs,
+                                                   max_query_len, num_q_heads, num_kv_heads,
+                                                   head_dim, block_size, num_blocks,
+                                                   _addr(k_scales), _addr(v_scales),
+                                                   sliding_window, _stream(stream)),
+                  "fp8kv_paged_prefill_per_head")

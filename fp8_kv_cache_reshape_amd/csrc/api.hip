@@ -316,6 +316,58 @@ int decode_step_impl(void* out, int out_dtype, const void* query, const void* ke
     return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
 }
 
+int paged_prefill_impl(void* out, int out_dtype, const void* query,
+                       const int32_t* query_start_loc, const void* key_cache,
+                       const void* value_cache, int cache_dtype, const int32_t* block_tables,
+                       int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                       int num_seqs, int max_query_len, int num_q_heads, int num_kv_heads,
+                       int head_dim, int block_size, int num_blocks, const Scales& sc,
+                       bool per_head_call, int sliding_window, void* stream) {
+    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_context_len, sliding_window, 0);
+    if (st != FP8KV_OK) return st;
+    if (max_query_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
+    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype == FP8KV_E4M3;
+    if (fp8) {
+        st = check_scales(sc, per_head_call);
+        if (st != FP8KV_OK) return st;
+    }
+    if (num_seqs > 65535 || num_kv_heads > 65535) return FP8KV_ERR_UNSUPPORTED;   // grid extents
+    if (num_seqs == 0 || max_query_len == 0) return FP8KV_OK;
+    if (!out || !query || !query_start_loc || !context_lens || !block_tables || !key_cache ||
+        !value_cache)
+        return FP8KV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+        return FP8KV_ERR_SHAPE;
+    if ((max_blocks_per_seq == 0 || num_blocks == 0) && max_context_len > 0) return FP8KV_ERR_SHAPE;
+    fp8kv::PrefillParams p;
+    p.out = out;
+    p.out_f32 = out_dtype == FP8KV_F32;
+    p.query = static_cast<const uint16_t*>(query);
+    p.query_start_loc = query_start_loc;
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_context_len = max_context_len;
+    p.max_query_len = max_query_len;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.num_blocks = num_blocks;
+    p.sliding_window = sliding_window;
+    const double log2e = 1.4426950408889634;
+    const bool heads = fp8 && per_head_call;
+    p.score_scale = (float)((fp8 && !heads ? (double)sc.k : 1.0) * log2e / sqrt((double)head_dim));
+    p.v_scale = fp8 && !heads ? sc.v : 1.0f;
+    p.k_scales = heads ? sc.ks : nullptr;
+    p.v_scales = heads ? sc.vs : nullptr;
+    return hip_status(fp8kv::launch_prefill(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -499,6 +551,36 @@ int fp8kv_paged_decode_merge(void* out, int out_dtype, const int32_t* context_le
     p.ws_ml = reinterpret_cast<float*>(const_cast<void*>(workspace));
     p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) + wl.acc_offset);
     return hip_status(fp8kv::launch_decode_merge(p, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int fp8kv_paged_prefill(void* out, int out_dtype, const void* query,
+                        const int32_t* query_start_loc, const void* key_cache,
+                        const void* value_cache, int cache_dtype, const int32_t* block_tables,
+                        int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                        int num_seqs, int max_query_len, int num_q_heads, int num_kv_heads,
+                        int head_dim, int block_size, int num_blocks, float k_scale,
+                        float v_scale, int sliding_window, void* stream) {
+    return paged_prefill_impl(out, out_dtype, query, query_start_loc, key_cache, value_cache,
+                              cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                              max_context_len, num_seqs, max_query_len, num_q_heads, num_kv_heads,
+                              head_dim, block_size, num_blocks, tensor_scales(k_scale, v_scale),
+                              false, sliding_window, stream);
+}
+
+int fp8kv_paged_prefill_per_head(void* out, int out_dtype, const void* query,
+                                 const int32_t* query_start_loc, const void* key_cache,
+                                 const void* value_cache, int cache_dtype,
+                                 const int32_t* block_tables, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int max_context_len, int num_seqs,
+                                 int max_query_len, int num_q_heads, int num_kv_heads,
+                                 int head_dim, int block_size, int num_blocks,
+                                 const float* k_scales, const float* v_scales,
+                                 int sliding_window, void* stream) {
+    return paged_prefill_impl(out, out_dtype, query, query_start_loc, key_cache, value_cache,
+                              cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                              max_context_len, num_seqs, max_query_len, num_q_heads, num_kv_heads,
+                              head_dim, block_size, num_blocks, head_scales(k_scales, v_scales),
+                              true, sliding_window, stream);
 }
 
 }  // extern "C"

@@ -74,6 +74,29 @@ struct DecodeParams {
     const float* v_scales;
 };
 
+struct PrefillParams {
+    void* out;                     // [Tq][Hq][D] bf16 or f32
+    int out_f32;
+    const uint16_t* query;         // bf16 [Tq][Hq][D]
+    const int32_t* query_start_loc;   // [B + 1]: chunk rows of sequence b
+    const void* key_cache;
+    const void* value_cache;
+    const int32_t* block_tables;   // [B][max_blocks]
+    const int32_t* context_lens;   // [B], the chunk included
+    int max_blocks_per_seq;
+    int max_context_len;
+    int max_query_len;             // host bound on chunk lengths (sizes the grid)
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int num_blocks;
+    int sliding_window;
+    float score_scale;             // (k_scale or 1) * log2(e) / sqrt(D)
+    float v_scale;
+    const float* k_scales;         // per-kv-head scales [Hkv] (device), or null
+    const float* v_scales;
+};
+
 // The scale of kv head h: from a per-head array (a wave-uniform scalar load), or the
 // per-tensor value when there is no array.
 __device__ inline float head_scale(const float* per_head, int h, float per_tensor) {
@@ -135,5 +158,6 @@ hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t 
 // of `group` query heads itself, in at most two batched round trips to memory; larger
 // merges run in the separate merge kernel.
 bool fused_merge_fits(int group, int head_dim, int splits);
+hipError_t launch_prefill(const PrefillParams& p, bool fp8, int head_dim, hipStream_t s);
 
 }  // namespace fp8kv

@@ -319,6 +319,60 @@ int fp8kv_decode_step_per_head(void* out, int out_dtype, const void* query,
                                int sliding_window, int num_splits,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fp8kv_paged_prefill -- prefill / chunked-prefill attention over the paged cache: the
+ * query tokens of each sequence's prompt chunk attend causally to its cached context, the
+ * chunk included, with K and V dequantised inside the kernel (page "FP8 KV Cache
+ * Quantization: Capacity Gains and Accuracy Risk", "Attention backend interactions"); the
+ * contraction over the context keeps two-level accumulation (page "The State of FP8
+ * KV-Cache and Attention Quantization in vLLM", "ACCURACY AT LONG CONTEXT").
+ *
+ * Sequence b's chunk is the query rows [query_start_loc[b], query_start_loc[b+1]); its
+ * n_b tokens are the last n_b positions of the context, L_b = context_lens[b] (clamped as
+ * in fp8kv_paged_decode), so row query_start_loc[b] + j sits at position
+ * p = L_b - n_b + j.  For every such row and query head hq (h = hq / g):
+ *   lo = (sliding_window > 0) ? max(0, p + 1 - sliding_window) : 0,
+ *   s_j = q . K_j / sqrt(head_dim) for j in [lo, p],
+ *   out = sum_j exp(s_j - max s) V_j / sum_j exp(s_j - max s);   out = 0 if p < 0.
+ * K_j and V_j as in fp8kv_paged_decode.  The chunk's own K/V must already be in the cache
+ * (fp8kv_cache_write first, on the same stream).  Arithmetic: S = K.Q^T and O = P.V on
+ * the matrix cores (bf16 operands, fp32 accumulation); probabilities enter P.V as the sum
+ * of two bf16 values (about 16 significant bits); the matrix-core accumulator holds at most
+ * 256 keys before its sums move into fp32 registers.
+ *
+ *   out              device [num_query_tokens][num_q_heads][head_dim] of out_dtype
+ *   query            device bf16 [num_query_tokens][num_q_heads][head_dim]
+ *   query_start_loc  device int32 [num_seqs + 1], non-decreasing, query_start_loc[0] = 0
+ *   max_query_len    host bound on every n_b (sizes the grid; rows beyond it are not
+ *                    computed)
+ *   other arguments as for fp8kv_paged_decode; no workspace.  num_seqs and num_kv_heads
+ *   are at most 65535 (else FP8KV_ERR_UNSUPPORTED).
+ */
+int fp8kv_paged_prefill(void* out, int out_dtype, const void* query,
+                        const int32_t* query_start_loc,
+                        const void* key_cache, const void* value_cache, int cache_dtype,
+                        const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* context_lens, int max_context_len,
+                        int num_seqs, int max_query_len, int num_q_heads, int num_kv_heads,
+                        int head_dim, int block_size, int num_blocks,
+                        float k_scale, float v_scale, int sliding_window, void* stream);
+
+/*
+ * fp8kv_paged_prefill_per_head -- fp8kv_paged_prefill with per-kv-head scales (page "FP8
+ * KV Cache Quantization: Capacity Gains and Accuracy Risk", "Scales and calibration"):
+ * k_scales / v_scales as for fp8kv_cache_write_per_head, applied as in
+ * fp8kv_paged_decode_per_head.
+ */
+int fp8kv_paged_prefill_per_head(void* out, int out_dtype, const void* query,
+                                 const int32_t* query_start_loc,
+                                 const void* key_cache, const void* value_cache, int cache_dtype,
+                                 const int32_t* block_tables, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int max_context_len,
+                                 int num_seqs, int max_query_len, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                 const float* k_scales, const float* v_scales,
+                                 int sliding_window, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

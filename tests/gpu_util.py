@@ -209,3 +209,55 @@ def gpu_decode_step(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, nu
                                      f32_dev(heads[1]), win, num_splits, workspace, ws_bytes)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D), workspace
+
+
+def gpu_prefill(w: syn.Workload, layer: syn.Layer, kc, vc, pq: syn.PrefillQueries, out_f32=False,
+                window=None, heads=None, context_lens=None, max_query_len=None):
+    """fp8kv_paged_prefill (or the per-head variant) over caches kc / vc: [Tq][Hq][D]."""
+    win = layer.sliding_window if window is None else window
+    dev = DeviceInputs(w, context_lens=context_lens)
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    Tq = pq.num_tokens
+    out = torch.full((max(Tq, 1) * Hq * D,), float("nan"),
+                     dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
+    q = u16_dev(pq.q) if Tq else torch.zeros(8, dtype=torch.int16, device=DEV)
+    qsl = torch.from_numpy(np.ascontiguousarray(pq.query_start_loc)).to(DEV)
+    mql = pq.max_query_len if max_query_len is None else max_query_len
+    odt = F.FP8KV_F32 if out_f32 else F.FP8KV_BF16
+    maxl = w.max_context_len if context_lens is None else int(np.max(context_lens))
+    if heads is None:
+        F.fp8kv_paged_prefill(out, odt, q, qsl, kc, vc, code(layer), dev.bt, w.max_blocks_per_seq,
+                              dev.cl, maxl, w.num_seqs, mql, Hq, Hkv, D, w.block_size,
+                              w.num_blocks, layer.k_scale, layer.v_scale, win)
+    else:
+        F.fp8kv_paged_prefill_per_head(out, odt, q, qsl, kc, vc, code(layer), dev.bt,
+                                       w.max_blocks_per_seq, dev.cl, maxl, w.num_seqs, mql, Hq,
+                                       Hkv, D, w.block_size, w.num_blocks, f32_dev(heads[0]),
+                                       f32_dev(heads[1]), win)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)[: Tq * Hq * D].reshape(Tq, Hq, D)
+
+
+def oracle_prefill(w: syn.Workload, layer: syn.Layer, okc, ovc, pq: syn.PrefillQueries,
+                   pairs=None, window=None, heads=None, context_lens=None):
+    """The oracle's prefill for (row, head) pairs ([n][D]) or every row ([Tq][Hq][D]); with
+    per-head scales each kv head's pairs use that head's scales."""
+    win = layer.sliding_window if window is None else window
+    cl = w.context_lens if context_lens is None else context_lens
+    full = pairs is None
+    if full:
+        pairs = np.array([(r, hq) for r in range(pq.num_tokens) for hq in range(w.num_q_heads)],
+                         np.int32).reshape(-1, 2)
+    pairs = np.asarray(pairs, np.int32).reshape(-1, 2)
+    out = np.zeros((pairs.shape[0], w.head_dim))
+    g = w.num_q_heads // w.num_kv_heads
+    groups = [(None, np.arange(pairs.shape[0]))] if heads is None else \
+        [(h, np.nonzero(pairs[:, 1] // g == h)[0]) for h in range(w.num_kv_heads)]
+    for h, idx in groups:
+        if idx.size == 0:
+            continue
+        ks, vs = (layer.k_scale, layer.v_scale) if h is None else (float(heads[0][h]), float(heads[1][h]))
+        out[idx] = oracle.paged_prefill_pairs(pairs[idx], pq.q, pq.query_start_loc, okc, ovc,
+                                              code(layer), w.block_tables, cl, w.num_q_heads,
+                                              w.num_kv_heads, w.head_dim, w.block_size, ks, vs, win)
+    return out.reshape(pq.num_tokens, w.num_q_heads, w.head_dim) if full else out
