@@ -108,10 +108,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     constexpr int NK = D / 16;             // contraction slices of S (16 channels each)
     constexpr int NT = D / 32;             // 32-channel output tiles of O
     constexpr int TILE = kBlockSize * D * ES;   // bytes of one (block, kv head) tile
+    constexpr int NV = TILE / 64 / 16;     // 16-byte pieces per lane of one staged tile
+    // a staged step: key tiles of its two blocks, then their value tiles
+    __shared__ __attribute__((aligned(16))) uint8_t sm_kv[2][4 * TILE];
     __shared__ float sm_f[kWaves][kCols];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform (kept in a scalar register: block ids then come from scalar loads, whose
+    // waits do not drain the vector loads in flight)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31;             // this lane's query column (S layout)
     const int half = lane >> 5;            // contraction half
     const int h = blockIdx.y;              // kv head
@@ -122,8 +127,10 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     const int nq = ((ConstI32Ptr)p.query_start_loc)[b + 1] - q0;       // chunk tokens
     const int tile = (int)gridDim.x - 1 - (int)blockIdx.x;             // heaviest tiles first
     const int64_t ncols = (int64_t)(nq > 0 ? nq : 0) * G;
-    const int64_t c0 = (int64_t)tile * (kWaves * kCols) + wave * kCols;   // first column of the wave
-    if (c0 >= ncols) return;
+    const int64_t cw0 = (int64_t)tile * (kWaves * kCols);             // first column of the workgroup
+    if (cw0 >= ncols) return;                                         // (whole workgroup)
+    const int64_t c0 = cw0 + wave * kCols;                            // first column of the wave
+    const bool wactive = c0 < ncols;
 
     int L = ((ConstI32Ptr)p.context_lens)[b];
     if (L > p.max_context_len) L = p.max_context_len;
@@ -140,12 +147,18 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     const int pos = L - nq + tok;          // < 0: the column attends to nothing
     const int clo = lo_of(pos);
 
-    // the wave's key range: [lo of its first position, its last position]
-    const int64_t clast = (c0 + kCols <= ncols ? c0 + kCols : ncols) - 1;
+    // key ranges: the workgroup stages [lo of its first position, its last position]; a
+    // wave computes only the steps its own columns can see
+    const int64_t cwlast = (cw0 + kWaves * kCols <= ncols ? cw0 + kWaves * kCols : ncols) - 1;
+    const int pwmin = L - nq + (int)(cw0 / G);
+    const int kend = L - nq + (int)(cwlast / G) + 1;                  // exclusive, <= L
+    const int kfirst = pwmin >= 0 ? (lo_of(pwmin) / kStep) * kStep : 0;
+    const int nsteps = kend > kfirst ? (kend - kfirst + kStep - 1) / kStep : 0;
+    const int64_t clast = wactive ? (c0 + kCols <= ncols ? c0 + kCols : ncols) - 1 : c0;
     const int pmin = L - nq + (int)(c0 / G);
     const int pmax = L - nq + (int)(clast / G);
-    const int kfirst = pmin >= 0 ? (lo_of(pmin) / kStep) * kStep : 0;
-    const int kend = pmax + 1;             // exclusive; <= L
+    const int lomax = lo_of(pmax);
+    const int lomin = lo_of(pmin);
 
     // query operand of S: slice kk = q[hq][key_slice_channel(half, kk) .. +8)
     bf16x8 qb[NK];
@@ -164,9 +177,55 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
                              ? ((const __attribute__((address_space(4))) float*)p.k_scales)[h]
                              : 1.0f;
     const float sscale = p.score_scale * kscale;
-    const uint8_t* kc = static_cast<const uint8_t*>(p.key_cache);
-    const uint8_t* vc = static_cast<const uint8_t*>(p.value_cache);
     const ConstI32Ptr bt = (ConstI32Ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
+
+    // block c of the step at kb: valid id, or -1 (past the table, outside [0, num_blocks),
+    // or starting at or after kend)
+    auto block_of = [&](int kb, int c) {
+        const int n = kb / kBlockSize + c;
+        const int id = n < p.max_blocks_per_seq ? bt[n] : -1;
+        return (id >= 0 && id < p.num_blocks && kb + c * kBlockSize < kend) ? id : -1;
+    };
+
+    // ---- staging: wave w moves piece w of a step (key block 0, key block 1, value block 0,
+    // value block 1).  The loads are always issued (a missing block or a step past the end
+    // reads block 0 of the cache, in bounds) so that no branch sits between a load and
+    // its use; missing blocks become zeros and value slots at or past kend are zeroed when
+    // the piece is written to LDS, where the wait for the data happens anyway.
+    const int part_c = wave & 1;
+    const bool part_v = wave >= 2;
+    const uint8_t* part_src = static_cast<const uint8_t*>(part_v ? p.value_cache : p.key_cache);
+    auto stage_load = [&](int st, u32x4 (&r)[NV]) {
+        const int kb = kfirst + (st < nsteps ? st : 0) * kStep;
+        const int id = block_of(kb, part_c);
+        const uint8_t* src = part_src + ((int64_t)(id >= 0 ? id : 0) * p.num_kv_heads + h) * TILE +
+                             lane * (NV * 16);
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            r[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16 * i));
+    };
+    auto stage_store = [&](int buf, int st, const u32x4 (&r)[NV]) {
+        const int kb = kfirst + st * kStep;
+        const bool ok = block_of(kb, part_c) >= 0;
+        // value slots kept: a 16-byte piece holds 16 slots (fp8) or 8 slots (bf16) of one row
+        const int nvalid = part_v ? kend - (kb + part_c * kBlockSize) : kBlockSize;
+        uint8_t* dst = &sm_kv[buf][wave * TILE + lane * (NV * 16)];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            u32x4 v = r[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+                for (int k = 0; k < 4 / ES; ++k) {
+                    const int slot = ((lane * NV + i) * (16 / ES) + e * (4 / ES) + k) % kBlockSize;
+                    if (slot >= nvalid) m &= ~((ES == 1 ? 0xFFu : 0xFFFFu) << (8 * ES * k));
+                }
+                v[e] &= m;
+            }
+            *reinterpret_cast<u32x4*>(dst + 16 * i) = v;
+        }
+    };
 
     f32x16 oacc[NT], osum[NT];
 #pragma unroll
@@ -176,6 +235,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     }
     float mref = -INFINITY;                // running reference maximum of this column
     float l_hi = 0.0f, l_lo = 0.0f;        // sum of this lane's half of the probabilities
+    int flush = 0;
 
     // rescale the O rows (columns 8j + 4*half + i) by the per-column factors in sm_f
     auto rescale_rows = [&](float f) {
@@ -198,61 +258,77 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     };
 
     const int kt = key_token(col);         // token (within the step) of this lane's key row
-    int flush = 0;
-    for (int kb = kfirst; kb < kend; kb += kStep) {
-        // the step's two blocks (wave-uniform); an index past the table or an id outside
-        // [0, num_blocks) reads as an empty block
-        int blk[2];
-        bool bok[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int n = kb / kBlockSize + c;
-            const int id = n < p.max_blocks_per_seq ? bt[n] : -1;
-            bok[c] = id >= 0 && id < p.num_blocks && kb + c * kBlockSize < kend;
-            blk[c] = bok[c] ? id : 0;
-        }
-        const int64_t tile_base[2] = {((int64_t)blk[0] * p.num_kv_heads + h) * TILE,
-                                      ((int64_t)blk[1] * p.num_kv_heads + h) * TILE};
-
-        // ---- S = K.Q^T
-        f32x16 s = f32x16{};
+    // one step of the wave from staged buffer `buf`
+    // whether step st holds any key this wave's columns attend to
+    auto visible = [&](int st) {
+        const int kb = kfirst + st * kStep;
+        return st < nsteps && wactive && kb <= pmax && kb + kStep > lomin;
+    };
+    // S = K.Q^T of the step staged in buffer `buf`
+    auto s_product = [&](int buf) {
+        const uint8_t* sk = sm_kv[buf];
+        // ---- S = K.Q^T, as two independent accumulator chains (even and odd slices) up to
+        // head_dim 128
+        f32x16 s;
         {
-            const int c = kt / kBlockSize, slot = kt % kBlockSize;
-            const uint8_t* ktile = kc + tile_base[c];
+            f32x16 s0 = f32x16{}, s1 = f32x16{};
+            const uint8_t* ktile = sk + (kt / kBlockSize) * TILE;
+            const int slot = kt % kBlockSize;
             if constexpr (ES == 1) {
 #pragma unroll
                 for (int kk = 0; kk < NK; kk += 2) {
-                    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                        ktile + key_chunk_offset<D, 1>(slot, key_slice_channel<D, 1>(half, kk))));
-                    s = mfma32(e4m3x8_to_bf16x8(v[0], v[1]), qb[kk], s);
-                    s = mfma32(e4m3x8_to_bf16x8(v[2], v[3]), qb[kk + 1], s);
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(
+                        ktile + key_chunk_offset<D, 1>(slot, key_slice_channel<D, 1>(half, kk)));
+                    s0 = mfma32(e4m3x8_to_bf16x8(v[0], v[1]), qb[kk], s0);
+                    if constexpr (D <= 128)
+                        s1 = mfma32(e4m3x8_to_bf16x8(v[2], v[3]), qb[kk + 1], s1);
+                    else    // (head_dim 256: one chain, to stay within the registers)
+                        s0 = mfma32(e4m3x8_to_bf16x8(v[2], v[3]), qb[kk + 1], s0);
                 }
             } else {
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                        ktile + key_chunk_offset<D, 2>(slot, key_slice_channel<D, 2>(half, kk))));
-                    s = mfma32(as_bf16x8(v), qb[kk], s);
+                for (int kk = 0; kk < NK; kk += 2) {
+                    const u32x4 v0 = *reinterpret_cast<const u32x4*>(
+                        ktile + key_chunk_offset<D, 2>(slot, key_slice_channel<D, 2>(half, kk)));
+                    const u32x4 v1 = *reinterpret_cast<const u32x4*>(
+                        ktile + key_chunk_offset<D, 2>(slot, key_slice_channel<D, 2>(half, kk + 1)));
+                    s0 = mfma32(as_bf16x8(v0), qb[kk], s0);
+                    if constexpr (D <= 128)
+                        s1 = mfma32(as_bf16x8(v1), qb[kk + 1], s1);
+                    else
+                        s0 = mfma32(as_bf16x8(v1), qb[kk + 1], s0);
                 }
             }
+            if constexpr (D <= 128)
+                s = s0 + s1;
+            else
+                s = s0;
         }
+        return s;
+    };
+    // softmax update and O += P.V of step st, whose scores are s, staged in buffer `buf`
+    auto finish = [&](int st, f32x16 s, int buf) {
+        const int kb = kfirst + st * kStep;
+        const bool bok0 = block_of(kb, 0) >= 0, bok1 = block_of(kb, 1) >= 0;
+        const uint8_t* sk = sm_kv[buf];
 
-        // ---- scores in base-2 units, masked outside [clo, pos] and outside valid blocks
-        const bool edge = kb + kStep > pmin + 1 || kb < lo_of(pmax) || !bok[0] || !bok[1];
+        // ---- raw scores masked outside [clo, pos] and outside valid blocks; the base-2
+        // scale (> 0) is applied to the maximum and inside the exponent's FMA
+        const bool edge = kb + kStep > pmin + 1 || kb < lomax || !bok0 || !bok1;
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float v = s[r] * sscale;
+            float v = s[r];
             if (edge) {
                 const int tr = key_token((r / 4) * 8 + 4 * half + (r % 4));
                 const int kp = kb + tr;
-                const bool ok = kp >= clo && kp <= pos && bok[tr / kBlockSize];
+                const bool ok = kp >= clo && kp <= pos && (tr < kBlockSize ? bok0 : bok1);
                 v = ok ? v : -INFINITY;
             }
             s[r] = v;
             mx = fmaxf(mx, v);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sscale;
         // lazy reference move: only when a score exceeds it by 2^8 (or on the first keys)
         const bool move = mx > mref + kRescaleLog2;
         if (__ballot(move) != 0) {
@@ -268,49 +344,34 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
 
         // ---- probabilities as the sum of two bf16 terms (about 16 significant bits: one
         // bf16 term alone moves a weighted average by up to 2^-9 of the value spread)
+        // (the high term is pf truncated to bf16, so pf - hi is exact; the low term is
+        // that remainder rounded to bf16)
         bf16x8 pa[2], pb[2];
         float psum = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float pf = __builtin_amdgcn_exp2f(s[r] - mu);
-            const __bf16 hi = (__bf16)pf;
-            pa[r / 8][r % 8] = hi;
-            pb[r / 8][r % 8] = (__bf16)(pf - (float)hi);
+            const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sscale, -mu));
+            const float hf = __uint_as_float(__float_as_uint(pf) & 0xFFFF0000u);
+            pa[r / 8][r % 8] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(pf) >> 16));
+            pb[r / 8][r % 8] = (__bf16)(pf - hf);
             psum += pf;
         }
         comp_add(l_hi, l_lo, psum);
 
         // ---- O += P.V: chunk c = block c of the step, lane reads tokens 8*half .. +7
+        // (value slots past the context were zeroed when staged)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const uint8_t* vtile = vc + tile_base[c];
-            // tokens of this lane's 8 that lie past the context, or a missing block: zero
-            const int t0 = kb + c * kBlockSize + 8 * half;
-            const int nvalid = bok[c] ? (kend - t0 < 8 ? (kend - t0 > 0 ? kend - t0 : 0) : 8) : 0;
+            const uint8_t* vtile = sk + (2 + c) * TILE;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int ch = 32 * t + col;
                 bf16x8 vb;
                 if constexpr (ES == 1) {
-                    u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
-                        vtile + ch * kBlockSize + 8 * half));
-                    if (nvalid < 8) {
-                        const uint64_t keep = nvalid <= 0 ? 0ull : (~0ull >> (64 - 8 * nvalid));
-                        v[0] &= (uint32_t)keep;
-                        v[1] &= (uint32_t)(keep >> 32);
-                    }
+                    const u32x2 v = *reinterpret_cast<const u32x2*>(vtile + ch * kBlockSize + 8 * half);
                     vb = e4m3x8_to_bf16x8(v[0], v[1]);
                 } else {
-                    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                        vtile + (ch * kBlockSize + 8 * half) * 2));
-                    if (nvalid < 8) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int n2 = nvalid - 2 * e;
-                            v[e] &= n2 >= 2 ? 0xFFFFFFFFu : (n2 == 1 ? 0x0000FFFFu : 0u);
-                        }
-                    }
-                    vb = as_bf16x8(v);
+                    vb = as_bf16x8(*reinterpret_cast<const u32x4*>(vtile + (ch * kBlockSize + 8 * half) * 2));
                 }
                 oacc[t] = mfma32(pa[c], vb, oacc[t]);
                 oacc[t] = mfma32(pb[c], vb, oacc[t]);
@@ -326,7 +387,43 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
                 oacc[t] = f32x16{};
             }
         }
+    };
+    auto compute = [&](int st, int buf) {
+        if (visible(st)) finish(st, s_product(buf), buf);
+    };
+
+    if constexpr (D <= 128) {
+        // ---- the pipeline: step s+2 is loaded into registers while step s is computed
+        // from one LDS buffer and step s+1 is written into the other; one barrier per step
+        u32x4 ra[NV], rb[NV];
+        stage_load(0, ra);
+        stage_load(1, rb);
+        stage_store(0, 0, ra);
+        __syncthreads();
+        for (int st = 0; st < nsteps; st += 2) {
+            stage_load(st + 2, ra);
+            compute(st, 0);
+            stage_store(1, st + 1, rb);
+            __syncthreads();
+            if (st + 1 >= nsteps) break;
+            stage_load(st + 3, rb);
+            compute(st + 1, 1);
+            stage_store(0, st + 2, ra);
+            __syncthreads();
+        }
+    } else {
+        // ---- head_dim 256 (twice the accumulators): one register set, step s+1 loaded
+        // while step s is computed
+        u32x4 ra[NV];
+        stage_load(0, ra);
+        for (int st = 0; st < nsteps; ++st) {
+            stage_store(st & 1, st, ra);
+            __syncthreads();
+            stage_load(st + 1, ra);
+            compute(st, st & 1);
+        }
     }
+    if (!wactive) return;
 #pragma unroll
     for (int t = 0; t < NT; ++t) osum[t] += oacc[t];
 
