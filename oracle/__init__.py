@@ -75,6 +75,11 @@ def _bind(path: str) -> ctypes.CDLL:
                                                i32, P, P, i32],
         "oracle_paged_prefill_pairs": [P, P, i32, P, P, i32, P, P, i32, P, i32, P, i32, i32, i32,
                                        i32, f64, f64, i32],
+        "oracle_hadamard_f32": [P, i32],
+        "oracle_hadamard_f64": [P, i32],
+        "oracle_cache_write_rotated": [P, P, P, P, i32, P, i32, i32, i32, i32, i32, f32, f32],
+        "oracle_paged_decode_rotated_pairs": [P, P, i32, P, P, P, i32, P, i32, P, i32, i32, i32,
+                                              i32, f64, f64, i32],
     }.items():
         fn = getattr(L, name)
         fn.restype = None
@@ -293,3 +298,78 @@ def paged_prefill(q, query_start_loc, key_cache, value_cache, cache_dtype: int, 
                               block_tables, context_lens, num_q_heads, num_kv_heads, head_dim,
                               block_size, k_scale, v_scale, sliding_window)
     return out.reshape(Tq, num_q_heads, head_dim)
+
+
+# ------------------------------------------------------------ rotation ----
+
+def hadamard_f32(x) -> np.ndarray:
+    """Normalized Hadamard rotation of the last axis in f32 (oracle.c's butterfly order)."""
+    a = np.array(x, dtype=np.float32, order="C", copy=True)
+    d = a.shape[-1]
+    assert d & (d - 1) == 0
+    rows = a.reshape(-1, d)
+    for r in range(rows.shape[0]):
+        row = np.ascontiguousarray(rows[r])
+        lib().oracle_hadamard_f32(_ptr(row), d)
+        rows[r] = row
+    return rows.reshape(a.shape)
+
+
+def hadamard_f64(x) -> np.ndarray:
+    """The same rotation in double."""
+    a = np.array(x, dtype=np.float64, order="C", copy=True)
+    d = a.shape[-1]
+    assert d & (d - 1) == 0
+    rows = a.reshape(-1, d)
+    for r in range(rows.shape[0]):
+        row = np.ascontiguousarray(rows[r])
+        lib().oracle_hadamard_f64(_ptr(row), d)
+        rows[r] = row
+    return rows.reshape(a.shape)
+
+
+def cache_write_rotated(key, value, key_cache: np.ndarray, value_cache: np.ndarray,
+                        cache_dtype: int, slot_mapping, num_kv_heads: int, head_dim: int,
+                        block_size: int, num_blocks: int, k_scale: float, v_scale: float) -> None:
+    """cache_write of Hadamard-rotated K and V rows (rotation in f32, then the quantiser)."""
+    k = np.ascontiguousarray(key, dtype=np.uint16)
+    v = np.ascontiguousarray(value, dtype=np.uint16)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    T = sm.shape[0]
+    assert k.size == T * num_kv_heads * head_dim and v.size == k.size
+    assert head_dim & (head_dim - 1) == 0 and block_size == 16
+    want = np.uint8 if cache_dtype == CACHE_E4M3 else np.uint16
+    assert key_cache.dtype == want and value_cache.dtype == want
+    assert key_cache.flags["C_CONTIGUOUS"] and value_cache.flags["C_CONTIGUOUS"]
+    lib().oracle_cache_write_rotated(_ptr(k), _ptr(v), _ptr(key_cache), _ptr(value_cache),
+                                     cache_dtype, _ptr(sm), T, num_kv_heads, head_dim,
+                                     block_size, num_blocks, float(k_scale), float(v_scale))
+
+
+def paged_decode_rotated_pairs(pairs, q, key_cache, value_cache, cache_dtype: int, block_tables,
+                               context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                               block_size: int, k_scale: float, v_scale: float,
+                               sliding_window: int = 0) -> np.ndarray:
+    """Decode over a rotated cache for selected (b, hq) pairs: q rotated, attention in the
+    rotated space, output rotated back (fp64): [n][D]."""
+    q, bt, cl = _decode_common(q, key_cache, value_cache, cache_dtype, block_tables, context_lens)
+    pr = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    out = np.empty((pr.shape[0], head_dim), dtype=np.float64)
+    lib().oracle_paged_decode_rotated_pairs(_ptr(out), _ptr(pr), pr.shape[0], _ptr(q),
+                                            _ptr(key_cache), _ptr(value_cache), cache_dtype,
+                                            _ptr(bt), bt.shape[1], _ptr(cl), num_q_heads,
+                                            num_kv_heads, head_dim, block_size, float(k_scale),
+                                            float(v_scale), int(sliding_window))
+    return out
+
+
+def paged_decode_rotated(q, key_cache, value_cache, cache_dtype: int, block_tables, context_lens,
+                         num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                         k_scale: float, v_scale: float, sliding_window: int = 0) -> np.ndarray:
+    """Every (sequence, query head) over a rotated cache: [B][Hq][D]."""
+    B = np.asarray(context_lens).shape[0]
+    pairs = np.array([(b, hq) for b in range(B) for hq in range(num_q_heads)], np.int32)
+    out = paged_decode_rotated_pairs(pairs, q, key_cache, value_cache, cache_dtype, block_tables,
+                                     context_lens, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     k_scale, v_scale, sliding_window)
+    return out.reshape(B, num_q_heads, head_dim)

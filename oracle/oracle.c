@@ -424,3 +424,147 @@ void oracle_paged_prefill_pairs(double* out, const int32_t* pairs, int npairs,
         free(V);
     }
 }
+
+/* --------------------------------------------------- Hadamard rotation --- */
+
+/*
+ * Normalized Hadamard rotation of one d-vector (d a power of two), applied to Q, K and V
+ * before caching so that outliers spread across coordinates while dot products stay the
+ * same; attention runs in the rotated space and its output is rotated back [ACC,
+ * paragraph on the llama.cpp rotation merged 2026-04-01].  The Sylvester Hadamard matrix
+ * is symmetric and, divided by sqrt(d), orthonormal, so the same transform rotates back.
+ *
+ * f32 form (the one the quantised codes are defined by, so that a code decision is taken
+ * in f32 on both sides): the fast Walsh-Hadamard butterflies in the order
+ * h = 1, 2, 4, ..., d/2 -- each pair (x[i], x[i+h]) of a 2h-block becomes
+ * (x[i] + x[i+h], x[i] - x[i+h]), one f32 rounding each -- then every element times the
+ * f32 constant (float)(1/sqrt(d)).
+ */
+void oracle_hadamard_f32(float* x, int d) {
+    for (int h = 1; h < d; h *= 2)
+        for (int i = 0; i < d; i += 2 * h)
+            for (int j = i; j < i + h; ++j) {
+                float a = x[j], b = x[j + h];
+                x[j] = a + b;
+                x[j + h] = a - b;
+            }
+    float c = (float)(1.0 / sqrt((double)d));
+    for (int i = 0; i < d; ++i) x[i] = x[i] * c;
+}
+
+/* fp64 form, for the attention oracle: the same butterflies and 1/sqrt(d) in double. */
+void oracle_hadamard_f64(double* x, int d) {
+    for (int h = 1; h < d; h *= 2)
+        for (int i = 0; i < d; i += 2 * h)
+            for (int j = i; j < i + h; ++j) {
+                double a = x[j], b = x[j + h];
+                x[j] = a + b;
+                x[j + h] = -b + a;             /* (the same value as a - b) */
+            }
+    double c = 1.0 / sqrt((double)d);
+    for (int i = 0; i < d; ++i) x[i] *= c;
+}
+
+/* An f32 value divided by the scale in f32 and cast once to e4m3 (the quantiser of
+ * oracle_quantize, for an input that is already f32). */
+static uint8_t quantize_f32(float y, float scale) {
+    float q = y / scale;
+    return oracle_e4m3_encode((double)q);
+}
+
+/* bf16 nearest to an f32 (round to nearest, ties to even; NaN kept quiet). */
+static uint16_t f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(r >> 16);
+}
+
+/*
+ * Rotated cache write: each K and V row (d elements of one token and kv head) is widened
+ * to f32, rotated by oracle_hadamard_f32, then quantised exactly as oracle_cache_write
+ * quantises (e4m3 cache) or rounded to bf16 (bf16 cache).
+ */
+void oracle_cache_write_rotated(const uint16_t* key, const uint16_t* value,
+                                void* key_cache, void* value_cache, int cache_dtype,
+                                const int64_t* slot_mapping, int T, int Hkv, int D, int bs,
+                                int NB, float k_scale, float v_scale) {
+    float* rk = (float*)malloc(sizeof(float) * (size_t)D);
+    float* rv = (float*)malloc(sizeof(float) * (size_t)D);
+    for (int t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= (int64_t)NB * bs) continue;
+        int64_t blk = slot / bs;
+        int in_block = (int)(slot % bs);
+        for (int h = 0; h < Hkv; ++h) {
+            for (int i = 0; i < D; ++i) {
+                rk[i] = oracle_bf16_to_f32(key[((int64_t)t * Hkv + h) * D + i]);
+                rv[i] = oracle_bf16_to_f32(value[((int64_t)t * Hkv + h) * D + i]);
+            }
+            oracle_hadamard_f32(rk, D);
+            oracle_hadamard_f32(rv, D);
+            for (int i = 0; i < D; ++i) {
+                int64_t ki = key_index(blk, h, in_block, i, Hkv, bs, D,
+                                       cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2);
+                int64_t vi = value_index(blk, h, in_block, i, Hkv, bs, D);
+                if (cache_dtype == ORACLE_CACHE_E4M3) {
+                    ((uint8_t*)key_cache)[ki] = quantize_f32(rk[i], k_scale);
+                    ((uint8_t*)value_cache)[vi] = quantize_f32(rv[i], v_scale);
+                } else {
+                    ((uint16_t*)key_cache)[ki] = f32_to_bf16(rk[i]);
+                    ((uint16_t*)value_cache)[vi] = f32_to_bf16(rv[i]);
+                }
+            }
+        }
+    }
+    free(rk);
+    free(rv);
+}
+
+/*
+ * Decode over a rotated cache: the query row is rotated (fp64), attention runs over the
+ * dequantised rotated rows exactly as oracle_paged_decode_head, and the output is rotated
+ * back (fp64).  Selected (b, hq) pairs, out double [n][D].
+ */
+void oracle_paged_decode_rotated_pairs(double* out, const int32_t* pairs, int npairs,
+                                       const uint16_t* q, const void* key_cache,
+                                       const void* value_cache, int cache_dtype,
+                                       const int32_t* block_tables, int max_blocks,
+                                       const int32_t* context_lens, int Hq, int Hkv, int D,
+                                       int bs, double k_scale, double v_scale, int window) {
+    int g = Hq / Hkv;
+    int eb = cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2;
+    double* qr = (double*)malloc(sizeof(double) * (size_t)D);
+    for (int p = 0; p < npairs; ++p) {
+        int b = pairs[2 * p], hq = pairs[2 * p + 1];
+        int kvh = hq / g;
+        int64_t L = context_lens[b];
+        int64_t lo = 0;                          /* window: the last W positions */
+        if (window > 0 && L > window) lo = L - window;
+        int64_t n = L > lo ? L - lo : 0;
+        double* K = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
+        double* V = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
+        for (int i = 0; i < D; ++i)
+            qr[i] = (double)oracle_bf16_to_f32(q[((int64_t)b * Hq + hq) * D + i]);
+        oracle_hadamard_f64(qr, D);
+        for (int64_t j = lo; j < L; ++j) {
+            int64_t pb = block_tables[(int64_t)b * max_blocks + j / bs];
+            int in_block = (int)(j % bs);
+            for (int i = 0; i < D; ++i) {
+                K[(j - lo) * D + i] = cache_value(key_cache, cache_dtype,
+                                                  key_index(pb, kvh, in_block, i, Hkv, bs, D, eb),
+                                                  k_scale);
+                V[(j - lo) * D + i] = cache_value(value_cache, cache_dtype,
+                                                  value_index(pb, kvh, in_block, i, Hkv, bs, D),
+                                                  v_scale);
+            }
+        }
+        double* o = out + (int64_t)p * D;
+        oracle_attention_rows(o, qr, K, V, n, D);
+        oracle_hadamard_f64(o, D);              /* back to the original coordinates */
+        free(K);
+        free(V);
+    }
+    free(qr);
+}

@@ -18,7 +18,8 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_codec.py"),
         os.path.join(ROOT, "tests", "test_oracle_attention.py"),
         os.path.join(ROOT, "tests", "test_oracle_per_head.py"),
-        os.path.join(ROOT, "tests", "test_oracle_prefill.py")]
+        os.path.join(ROOT, "tests", "test_oracle_prefill.py"),
+        os.path.join(ROOT, "tests", "test_oracle_rotation.py")]
 
 MUTANTS = {
     "subnormal_ties_away": ("double m = rint(a * 512.0);", "double m = round(a * 512.0);"),
@@ -71,6 +72,14 @@ MUTANTS = {
         "qv[i] = (double)oracle_bf16_to_f32(q[((int64_t)qsl[b] * Hq + hq) * D + i]);"),
     "prefill_interleaved_kv_heads": ("int kvh = hq / group;", "int kvh = hq % Hkv;"),
     "prefill_window_off_by_one": ("? end - window : 0;", "? end - window + 1 : 0;"),
+    "rotation_unnormalised": ("float c = (float)(1.0 / sqrt((double)d));", "float c = 1.0f;"),
+    "rotation_f32_butterfly_sign": ("x[j + h] = a - b;", "x[j + h] = b - a;"),
+    "rotation_f64_butterfly_sign": ("x[j + h] = -b + a;", "x[j + h] = b - a;"),
+    "rotated_decode_output_not_rotated_back": (
+        "oracle_hadamard_f64(o, D);              /* back to the original coordinates */",
+        "(void)o;"),
+    "rotated_decode_query_not_rotated": ("oracle_hadamard_f64(qr, D);", "(void)qr;"),
+    "rotated_write_values_unrotated": ("oracle_hadamard_f32(rv, D);", "(void)rv;"),
 }
 
 
