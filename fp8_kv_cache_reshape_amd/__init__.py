@@ -55,6 +55,10 @@ SIGNATURES = {
                                  _I, _I, _F, _F, _I, _P]),
     "fp8kv_paged_prefill_per_head": (_I, [_P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
                                           _I, _I, _I, _I, _P, _P, _I, _P]),
+    "fp8kv_cache_write_rotated": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _F, _P]),
+    "fp8kv_paged_decode_rotated_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "fp8kv_paged_decode_rotated": (_I, [_P, _I, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I,
+                                        _I, _F, _F, _I, _I, _P, _SZ, _P]),
 }
 
 if not os.path.exists(LIBRARY_PATH):
@@ -277,3 +281,37 @@ def fp8kv_paged_prefill_per_head(out, out_dtype, query, query_start_loc, key_cac
                                                    _addr(k_scales), _addr(v_scales),
                                                    sliding_window, _stream(stream)),
                   "fp8kv_paged_prefill_per_head")
+
+
+def fp8kv_cache_write_rotated(key, value, key_cache, value_cache, cache_dtype, slot_mapping,
+                              num_tokens, num_kv_heads, head_dim, block_size, num_blocks, k_scale,
+                              v_scale, stream=None) -> int:
+    return _check(lib.fp8kv_cache_write_rotated(_addr(key), _addr(value), _addr(key_cache),
+                                                _addr(value_cache), cache_dtype, _addr(slot_mapping),
+                                                num_tokens, num_kv_heads, head_dim, block_size,
+                                                num_blocks, k_scale, v_scale, _stream(stream)),
+                  "fp8kv_cache_write_rotated")
+
+
+def fp8kv_paged_decode_rotated_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              block_size, max_context_len, sliding_window,
+                                              num_splits) -> int:
+    return int(lib.fp8kv_paged_decode_rotated_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                             head_dim, block_size, max_context_len,
+                                                             sliding_window, num_splits))
+
+
+def fp8kv_paged_decode_rotated(out, out_dtype, query, key_cache, value_cache, cache_dtype,
+                               block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, k_scale, v_scale, sliding_window, num_splits, workspace,
+                               workspace_bytes, stream=None) -> int:
+    return _check(lib.fp8kv_paged_decode_rotated(_addr(out), out_dtype, _addr(query),
+                                                 _addr(key_cache), _addr(value_cache), cache_dtype,
+                                                 _addr(block_tables), max_blocks_per_seq,
+                                                 _addr(context_lens), max_context_len, num_seqs,
+                                                 num_q_heads, num_kv_heads, head_dim, block_size,
+                                                 num_blocks, k_scale, v_scale, sliding_window,
+                                                 num_splits, _addr(workspace), workspace_bytes,
+                                                 _stream(stream)),
+                  "fp8kv_paged_decode_rotated")

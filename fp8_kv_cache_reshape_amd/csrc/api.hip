@@ -174,6 +174,7 @@ int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const voi
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP8KV_ERR_WORKSPACE;
     }
     p.query = static_cast<const uint16_t*>(query);
+    p.query_lo = nullptr;
     p.key_cache = key_cache;
     p.value_cache = value_cache;
     p.block_tables = block_tables;
@@ -366,6 +367,23 @@ int paged_prefill_impl(void* out, int out_dtype, const void* query,
     p.k_scales = heads ? sc.ks : nullptr;
     p.v_scales = heads ? sc.vs : nullptr;
     return hip_status(fp8kv::launch_prefill(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+// The rotated decode's workspace: the decode's own (split partials), then the rotated
+// query as two bf16 terms, then the f32 output before it is rotated back; each 256-aligned.
+struct RotatedLayout {
+    size_t q_hi, q_lo, out, total;
+};
+
+RotatedLayout rotated_layout(size_t decode_bytes, int num_seqs, int num_q_heads, int head_dim) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t rows = (size_t)num_seqs * num_q_heads * head_dim;
+    RotatedLayout l;
+    l.q_hi = up(decode_bytes);
+    l.q_lo = l.q_hi + up(rows * 2);
+    l.out = l.q_lo + up(rows * 2);
+    l.total = l.out + up(rows * 4);
+    return l;
 }
 
 }  // namespace
@@ -581,6 +599,95 @@ int fp8kv_paged_prefill_per_head(void* out, int out_dtype, const void* query,
                               max_context_len, num_seqs, max_query_len, num_q_heads, num_kv_heads,
                               head_dim, block_size, num_blocks, head_scales(k_scales, v_scales),
                               true, sliding_window, stream);
+}
+
+int fp8kv_cache_write_rotated(const void* key, const void* value, void* key_cache,
+                              void* value_cache, int cache_dtype, const int64_t* slot_mapping,
+                              int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, float k_scale, float v_scale, void* stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
+    if (!head_dim_ok(head_dim) || block_size != kBlockSize) return FP8KV_ERR_UNSUPPORTED;
+    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype == FP8KV_E4M3;
+    if (fp8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return FP8KV_ERR_SCALE;
+    if (num_tokens == 0) return FP8KV_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping) return FP8KV_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+        return FP8KV_ERR_SHAPE;
+    fp8kv::CacheWriteParams p = {};
+    p.key = static_cast<const uint16_t*>(key);
+    p.value = static_cast<const uint16_t*>(value);
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.slot_mapping = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_kv_heads = num_kv_heads;
+    p.num_blocks = num_blocks;
+    p.k_scale = fp8 ? k_scale : 1.0f;
+    p.v_scale = fp8 ? v_scale : 1.0f;
+    return hip_status(fp8kv::launch_rotate_write(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
+}
+
+size_t fp8kv_paged_decode_rotated_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                                 int head_dim, int block_size, int max_context_len,
+                                                 int sliding_window, int num_splits) {
+    if (check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, sliding_window, num_splits) != FP8KV_OK)
+        return 0;
+    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, max_context_len, sliding_window, num_splits);
+    const size_t dec = workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits).total;
+    return rotated_layout(dec, num_seqs, num_q_heads, head_dim).total;
+}
+
+int fp8kv_paged_decode_rotated(void* out, int out_dtype, const void* query, const void* key_cache,
+                               const void* value_cache, int cache_dtype,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int max_context_len, int num_seqs,
+                               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, float k_scale, float v_scale, int sliding_window,
+                               int num_splits, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_context_len, sliding_window, num_splits);
+    if (st != FP8KV_OK) return st;
+    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, max_context_len, sliding_window, num_splits);
+    const size_t dec = workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits).total;
+    const RotatedLayout rl = rotated_layout(dec, num_seqs, num_q_heads, head_dim);
+    fp8kv::DecodeParams p;
+    bool fp8 = true;
+    // the decode's part of the workspace is checked by setup_decode; the rotation buffers here
+    st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
+                      max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, tensor_scales(k_scale, v_scale),
+                      false, sliding_window, num_splits, workspace,
+                      workspace_bytes < dec ? workspace_bytes : dec, false);
+    if (st != FP8KV_OK) return st;
+    if (num_seqs == 0) return FP8KV_OK;
+    if (!workspace || workspace_bytes < rl.total) return FP8KV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP8KV_ERR_WORKSPACE;
+    if (!out) return FP8KV_ERR_NULL;
+    if (!aligned16(out)) return FP8KV_ERR_SHAPE;
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* q_hi = reinterpret_cast<uint16_t*>(ws + rl.q_hi);
+    uint16_t* q_lo = reinterpret_cast<uint16_t*>(ws + rl.q_lo);
+    float* out_rot = reinterpret_cast<float*>(ws + rl.out);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t rows = (int64_t)num_seqs * num_q_heads;
+    st = hip_status(fp8kv::launch_rotate_query(static_cast<const uint16_t*>(query), q_hi, q_lo, rows,
+                                               head_dim, s));
+    if (st != FP8KV_OK) return st;
+    p.query = q_hi;
+    p.query_lo = q_lo;
+    p.out = out_rot;
+    p.out_f32 = 1;
+    st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
+    if (st != FP8KV_OK) return st;
+    if (!p.write_final) {
+        st = hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
+        if (st != FP8KV_OK) return st;
+    }
+    return hip_status(fp8kv::launch_rotate_out(out_rot, out, out_dtype == FP8KV_F32, rows, head_dim, s));
 }
 
 }  // extern "C"

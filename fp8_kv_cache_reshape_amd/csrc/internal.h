@@ -40,6 +40,7 @@ struct DecodeParams {
     void* out;                     // [B][Hq][D] bf16 or f32 (final output)
     int out_f32;
     const uint16_t* query;         // bf16 [B][Hq][D]
+    const uint16_t* query_lo;      // bf16 [B][Hq][D]: a second (low) query term, or null
     const void* key_cache;
     const void* value_cache;
     const int32_t* block_tables;   // [B][max_blocks]
@@ -159,5 +160,12 @@ hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t 
 // merges run in the separate merge kernel.
 bool fused_merge_fits(int group, int head_dim, int splits);
 hipError_t launch_prefill(const PrefillParams& p, bool fp8, int head_dim, hipStream_t s);
+// Hadamard rotation (rotation.hip): the rotated cache write (CacheWriteParams' per-tensor
+// scales), the query rotation into hi + lo bf16 terms, and the output rotation back.
+hipError_t launch_rotate_write(const CacheWriteParams& p, bool fp8, int head_dim, hipStream_t s);
+hipError_t launch_rotate_query(const uint16_t* q, uint16_t* q_hi, uint16_t* q_lo, int64_t rows,
+                               int head_dim, hipStream_t s);
+hipError_t launch_rotate_out(const float* in, void* out, int out_f32, int64_t rows, int head_dim,
+                             hipStream_t s);
 
 }  // namespace fp8kv

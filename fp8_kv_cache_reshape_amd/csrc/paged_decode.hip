@@ -271,12 +271,14 @@ __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) 
 
 // Two waves per SIMD (<= 256 registers per lane) wherever the tile fits; head_dim 256 and
 // 2-byte caches need more and run one wave per SIMD.
-template <int D, bool FP8>
-constexpr int partial_waves_per_eu() { return (D <= 128 && FP8) || D == 64 ? 2 : 1; }
+// The variant with a second (low) query term -- the rotated query, carried as two bf16
+// terms -- runs one wave per SIMD.
+template <int D, bool FP8, bool QLO>
+constexpr int partial_waves_per_eu() { return QLO ? 1 : ((D <= 128 && FP8) || D == 64 ? 2 : 1); }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool QLO>
 __global__ __launch_bounds__(64 * kDecodeWaves)
-__attribute__((amdgpu_waves_per_eu(partial_waves_per_eu<D, FP8>(), 8)))
+__attribute__((amdgpu_waves_per_eu(partial_waves_per_eu<D, FP8, QLO>(), 8)))
 void decode_partial_kernel(DecodeParams p) {
     constexpr int ES = FP8 ? 1 : 2;               // bytes per cache element
     constexpr int DG = D / 4;                     // channels per lane group in S = K.q^T
@@ -338,14 +340,24 @@ void decode_partial_kernel(DecodeParams p) {
     // Query group as the B operand of S = K.q^T: lane (n, grp) holds head n, channels
     // [grp*DG + 8kk, +8) for kk = 0..KK-1; heads >= G are zero columns.
     bf16x8 qop[KK];
+    bf16x8 qlo[QLO ? KK : 1];                     // the query's low bf16 term (QLO only)
     {
         // heads n >= G read head 0's row (in bounds) and are zeroed: no branch around the loads
-        const uint16_t* qrow = p.query + out_row0 + (int64_t)(n < G ? n : 0) * D + grp * DG;
+        const int64_t qoff = out_row0 + (int64_t)(n < G ? n : 0) * D + grp * DG;
+        const uint16_t* qrow = p.query + qoff;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             uint4 u = load16(qrow + 8 * kk);
             if (n >= G) u = make_uint4(0, 0, 0, 0);
             qop[kk] = __builtin_bit_cast(bf16x8, u);
+        }
+        if constexpr (QLO) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                uint4 u = load16(p.query_lo + qoff + 8 * kk);
+                if (n >= G) u = make_uint4(0, 0, 0, 0);
+                qlo[kk] = __builtin_bit_cast(bf16x8, u);
+            }
         }
     }
 
@@ -457,6 +469,7 @@ void decode_partial_kernel(DecodeParams p) {
                         a = __builtin_bit_cast(bf16x8, bf.k[s][kk]);
                     }
                     c = mfma16x16x32(a, qop[kk], c);
+                    if constexpr (QLO) c = mfma16x16x32(a, qlo[kk], c);
                 }
                 sc[s] = c;
             }
@@ -661,6 +674,10 @@ void decode_partial_kernel(DecodeParams p) {
         // (without this it waits for every load in flight at the top of each step).
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[kk]));
+        if constexpr (QLO) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qlo[kk]));
+        }
         unsigned int c_pend = 0;                  // claim for entry e_nxt + 1, when claimed
         while (nxt >= 0) {
             process(buf, cur, nxt, std::true_type{});
@@ -892,7 +909,7 @@ size_t partial_lds_bytes(int G) {
 
 // Kernels whose dynamic LDS can exceed 64 KiB (g = 16 at head_dim 256) get their limit
 // raised once, to the largest size any group ratio needs.
-template <int D, bool FP8>
+template <int D, bool FP8, bool QLO>
 hipError_t allow_lds(size_t need) {
     if (need <= 65536) return hipSuccess;
     // raise this kernel's limit once, to what the device allows (up to kMaxPartialLds)
@@ -902,7 +919,7 @@ hipError_t allow_lds(size_t need) {
             hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
             return 65536;
         if ((size_t)lim > kMaxPartialLds) lim = (int)kMaxPartialLds;
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, FP8>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, FP8, QLO>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, lim) != hipSuccess)
             return 65536;
         return lim;
@@ -918,10 +935,15 @@ hipError_t launch_partial_d(const DecodeParams& p, bool fp8, hipStream_t s) {
     const dim3 grid = kHeadsFastest ? dim3(p.num_kv_heads, p.splits, p.num_seqs)
                                     : dim3(p.splits, p.num_kv_heads, p.num_seqs);
     const dim3 block(64 * kDecodeWaves);
-    hipError_t e = fp8 ? allow_lds<D, true>(lds) : allow_lds<D, false>(lds);
+    const bool qlo = p.query_lo != nullptr;
+    hipError_t e = fp8 ? (qlo ? allow_lds<D, true, true>(lds) : allow_lds<D, true, false>(lds))
+                       : (qlo ? allow_lds<D, false, true>(lds) : allow_lds<D, false, false>(lds));
     if (e != hipSuccess) return e;
-    const void* fn = fp8 ? reinterpret_cast<const void*>(&decode_partial_kernel<D, true>)
-                         : reinterpret_cast<const void*>(&decode_partial_kernel<D, false>);
+    const void* fn =
+        fp8 ? (qlo ? reinterpret_cast<const void*>(&decode_partial_kernel<D, true, true>)
+                   : reinterpret_cast<const void*>(&decode_partial_kernel<D, true, false>))
+            : (qlo ? reinterpret_cast<const void*>(&decode_partial_kernel<D, false, true>)
+                   : reinterpret_cast<const void*>(&decode_partial_kernel<D, false, false>));
     return launch_kernel(fn, grid, block, lds, s, p);
 }
 

@@ -373,6 +373,60 @@ int fp8kv_paged_prefill_per_head(void* out, int out_dtype, const void* query,
                                  const float* k_scales, const float* v_scales,
                                  int sliding_window, void* stream);
 
+/*
+ * Hadamard rotation around the cache (page "KV Cache Quantization: What FP8 and q8_0 Cost
+ * in Accuracy", paragraph on the llama.cpp rotation merged on 2026-04-01): K and V rows
+ * are rotated by the normalized Sylvester Hadamard matrix H/sqrt(d) before they are cached,
+ * attention runs in the rotated space with the query rotated the same way, and the output
+ * is rotated back.  Dot products are unchanged; outliers spread across coordinates, which
+ * lowers the quantisation error of per-tensor scales.  A cache written by
+ * fp8kv_cache_write_rotated must be read by fp8kv_paged_decode_rotated (and vice versa);
+ * scales should be calibrated on the rotated rows.
+ *
+ * fp8kv_cache_write_rotated -- fp8kv_cache_write of rotated rows.  Each row x (d elements
+ * of one token and kv head, widened to f32) becomes y = R(x): the fast Walsh-Hadamard
+ * butterflies in f32 in the order h = 1, 2, ..., d/2 (each pair of a 2h-block becomes
+ * (a + b, a - b), one rounding each), then each element times the f32 constant
+ * (float)(1/sqrt(d)).  E4M3 caches store E4M3(y / scale) exactly as fp8kv_cache_write does
+ * for an f32 input; BF16 caches store bf16(y) (round to nearest even).  Arguments, layout
+ * and errors as for fp8kv_cache_write.
+ */
+int fp8kv_cache_write_rotated(const void* key, const void* value,
+                              void* key_cache, void* value_cache, int cache_dtype,
+                              const int64_t* slot_mapping, int num_tokens,
+                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                              float k_scale, float v_scale, void* stream);
+
+/*
+ * fp8kv_paged_decode_rotated_workspace_size -- bytes of device workspace
+ * fp8kv_paged_decode_rotated needs (0 on invalid arguments): the decode's split partials,
+ * the rotated query (two bf16 terms) and the f32 output before it is rotated back.
+ */
+size_t fp8kv_paged_decode_rotated_workspace_size(int num_seqs, int num_q_heads,
+                                                 int num_kv_heads, int head_dim,
+                                                 int block_size, int max_context_len,
+                                                 int sliding_window, int num_splits);
+
+/*
+ * fp8kv_paged_decode_rotated -- fp8kv_paged_decode over a rotated cache:
+ *   out = H/sqrt(d) . Attention(H/sqrt(d) . q, K_rot, V_rot)
+ * with K_rot, V_rot the dequantised rotated rows.  The query is rotated in f32 and enters
+ * S = K.q^T as the sum of two bf16 terms (one bf16 term alone would move the scores by up
+ * to 2^-9 relative); the output is rotated back from f32.  Three launches on `stream`
+ * (query rotation, decode, output rotation; four with a separate merge).  workspace: at
+ * least fp8kv_paged_decode_rotated_workspace_size() bytes, 256-byte aligned, contents on
+ * entry irrelevant.  Other arguments, layout and errors as for fp8kv_paged_decode
+ * (per-tensor scales).
+ */
+int fp8kv_paged_decode_rotated(void* out, int out_dtype, const void* query,
+                               const void* key_cache, const void* value_cache, int cache_dtype,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int max_context_len,
+                               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int num_blocks,
+                               float k_scale, float v_scale, int sliding_window, int num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

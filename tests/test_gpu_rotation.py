@@ -1,0 +1,101 @@
+"""GPU parity of the Hadamard-rotation entry points: the rotated cache write is bit-exact
+against the oracle's rotated write (rotation in f32 in the same butterfly order, then the
+same quantiser), and the rotated decode (query rotation, decode, output rotated back)
+matches the oracle's rotated decode within the decode tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_cache_reshape_amd as F
+import oracle
+import synthetic as syn
+from gpu_util import (BF16, DEV, E4M3, DeviceInputs, assert_close, dev_caches, host_caches, say,
+                      to_host_bits, u16_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _mk(Hq, Hkv, D, lens, cid, cache=syn.E4M3, window=0):
+    w = syn.make_workload(f"rot-{Hq}-{Hkv}-{D}-{cache}-w{window}", cid, num_q_heads=Hq,
+                          num_kv_heads=Hkv, head_dim=D, context_lens=lens, outlier_frac=0.01,
+                          layers=(("l0", window, cache),))
+    L = w.layers[0]
+    # scales calibrated on the rotated rows (amax / 448), as a caller would
+    rk = oracle.hadamard_f32(syn.bf16_bits_to_f32(L.k))
+    rv = oracle.hadamard_f32(syn.bf16_bits_to_f32(L.v))
+    ks = float(np.float32(np.abs(rk).max()) / np.float32(448.0)) if cache == syn.E4M3 else 1.0
+    vs = float(np.float32(np.abs(rv).max()) / np.float32(448.0)) if cache == syn.E4M3 else 1.0
+    return w, L, ks, vs
+
+
+def _write_both(w, L, ks, vs):
+    cdt = E4M3 if L.cache_dtype == syn.E4M3 else BF16
+    kc, vc = dev_caches(w, cdt)
+    slots = torch.from_numpy(w.slot_mapping).to(DEV)
+    F.fp8kv_cache_write_rotated(u16_dev(L.k), u16_dev(L.v), kc, vc, cdt, slots, w.num_tokens,
+                                w.num_kv_heads, w.head_dim, 16, w.num_blocks, ks, vs)
+    torch.cuda.synchronize()
+    okc, ovc = host_caches(w, cdt)
+    oracle.cache_write_rotated(L.k, L.v, okc, ovc, cdt, w.slot_mapping, w.num_kv_heads, w.head_dim,
+                               16, w.num_blocks, ks, vs)
+    return cdt, kc, vc, okc, ovc
+
+
+@pytest.mark.parametrize("cache", [syn.E4M3, syn.BF16])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rotated_write_bit_exact(D, cache):
+    w, L, ks, vs = _mk(2 * 4, 4, D, [37, 300, 1027, 16], cid=180 + D, cache=cache)
+    say(f"cache_write_rotated {w.name}")
+    cdt, kc, vc, okc, ovc = _write_both(w, L, ks, vs)
+    assert np.array_equal(to_host_bits(kc), okc), "key cache bytes differ"
+    assert np.array_equal(to_host_bits(vc), ovc), "value cache bytes differ"
+
+
+def _decode(w, L, ks, vs, kc, vc, cdt, out_f32=False, num_splits=0):
+    dev = DeviceInputs(w)
+    B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+    win = L.sliding_window
+    nbytes = F.fp8kv_paged_decode_rotated_workspace_size(B, Hq, Hkv, D, 16, w.max_context_len, win,
+                                                        num_splits)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    out = torch.empty(B * Hq * D, dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
+    F.fp8kv_paged_decode_rotated(out, F.FP8KV_F32 if out_f32 else F.FP8KV_BF16, dev.q, kc, vc, cdt,
+                                 dev.bt, w.max_blocks_per_seq, dev.cl, w.max_context_len, B, Hq, Hkv,
+                                 D, 16, w.num_blocks, ks, vs, win, num_splits, ws, nbytes)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D)
+
+
+def _check_decode(w, L, ks, vs, out_f32=False, num_splits=0):
+    cdt, kc, vc, okc, ovc = _write_both(w, L, ks, vs)
+    got = _decode(w, L, ks, vs, kc, vc, cdt, out_f32=out_f32, num_splits=num_splits)
+    ref = oracle.paged_decode_rotated(w.q, okc, ovc, cdt, w.block_tables, w.context_lens,
+                                      w.num_q_heads, w.num_kv_heads, w.head_dim, 16, ks, vs,
+                                      L.sliding_window)
+    tol = dict(atol=2e-4, rtol=2e-3) if out_f32 else {}
+    assert_close(got, ref, what=w.name, **tol)
+
+
+SHAPES = [(4, 1, 64), (32, 8, 128), (64, 8, 128), (64, 8, 64), (16, 1, 256)]
+
+
+@pytest.mark.parametrize("cache", [syn.E4M3, syn.BF16])
+@pytest.mark.parametrize("Hq,Hkv,D", SHAPES)
+def test_rotated_decode_matches_oracle(Hq, Hkv, D, cache):
+    w, L, ks, vs = _mk(Hq, Hkv, D, [1, 16, 17, 300, 1027, 0], cid=190 + Hq + D, cache=cache)
+    say(f"paged_decode_rotated {w.name}")
+    _check_decode(w, L, ks, vs)
+
+
+@pytest.mark.parametrize("num_splits", [1, 5, 129])
+def test_rotated_decode_split_counts(num_splits):
+    w, L, ks, vs = _mk(32, 8, 128, [5, 700, 2049, 16], cid=200)
+    say(f"paged_decode_rotated splits={num_splits}")
+    _check_decode(w, L, ks, vs, out_f32=True, num_splits=num_splits)
+
+
+@pytest.mark.parametrize("window", [17, 512])
+def test_rotated_decode_windows(window):
+    w, L, ks, vs = _mk(64, 8, 64, [1, 20, 200, 1100], cid=201, window=window)
+    say(f"paged_decode_rotated window={window}")
+    _check_decode(w, L, ks, vs)
