@@ -441,6 +441,9 @@ def main(argv=None):
     ap.add_argument("--prefill-workload", default="llama8b-8k,d256-8k",
                     help="comma-separated: " + ", ".join(sorted(PREFILL_WORKLOADS)))
     ap.add_argument("--prefill-caches", default="e4m3,bf16", help="cache dtypes to time")
+    ap.add_argument("--rotated", action="store_true",
+                    help="only time the Hadamard-rotated path (rotated write of the step token + "
+                         "rotated decode) against the plain two-call path on --workload")
     ap.add_argument("--slope", action="store_true",
                     help="only sweep the context length at the 8B shape (B = 1, fp8 and bf16 KV) and fit "
                          "us/step = slope * L + intercept")
@@ -469,6 +472,9 @@ def main(argv=None):
 
     if args.slope:
         print(json.dumps(slope_sweep(F, torch, syn, args)), flush=True)
+        return 0
+    if args.rotated:
+        print(json.dumps(_finite(rotated_bench(F, torch, syn, args))), flush=True)
         return 0
     if args.prefill:
         for name in args.prefill_workload.split(","):
@@ -682,6 +688,40 @@ def prefill_bench(F, torch, syn, name: str, args) -> dict:
                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(res["e4m3"]["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4)}
     return res
+
+
+def rotated_bench(F, torch, syn, args) -> dict:
+    """Per-step time of the rotated path (fp8kv_cache_write_rotated of each sequence's token,
+    then fp8kv_paged_decode_rotated: query rotation, decode, output rotation) next to the
+    plain two-call path (fp8kv_cache_write + fp8kv_paged_decode), HIP events over
+    back-to-back steps on rotated cache instances."""
+    w = WORKLOADS[args.workload](syn)
+    layer = w.layers[args.layer]
+    one = 2 * w.num_blocks * w.num_kv_heads * BLOCK * w.head_dim
+    R = max(1, math.ceil(args.rotate_bytes * (1 << 30) / one))
+    b = DecodeBench(F, torch, w, layer, R, args.num_splits)
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    nbytes = F.fp8kv_paged_decode_rotated_workspace_size(w.num_seqs, Hq, Hkv, D, BLOCK, b.maxl,
+                                                        b.win, args.num_splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def rotated_step(i):
+        F.fp8kv_cache_write_rotated(b.k_new, b.v_new, b.kc[i], b.vc[i], b.cdt, b.slots_new, b.T_new,
+                                    Hkv, D, BLOCK, w.num_blocks, layer.k_scale, layer.v_scale,
+                                    b.stream)
+        F.fp8kv_paged_decode_rotated(b.out, F.FP8KV_BF16, b.q, b.kc[i], b.vc[i], b.cdt, b.bt,
+                                     w.max_blocks_per_seq, b.cl, b.maxl, w.num_seqs, Hq, Hkv, D,
+                                     BLOCK, w.num_blocks, layer.k_scale, layer.v_scale, b.win,
+                                     args.num_splits, ws, nbytes, b.stream)
+    ms_rot, _ = b.time_steps(args.steps, min(args.warmup, 200), rotated_step)
+    ms_two, _ = b.time_steps(args.steps, min(args.warmup, 200), b.two_call_step)
+    ms_fused, _ = b.time_steps(args.steps, min(args.warmup, 200))
+    return {"metric": "Hadamard-rotated decode step: us per step",
+            "workload": f"{args.workload}: {w.name}",
+            "rotated_step_us": round(ms_rot * 1e3, 2), "two_call_step_us": round(ms_two * 1e3, 2),
+            "fused_step_us": round(ms_fused * 1e3, 2),
+            "rotated_over_two_call": round(ms_rot / ms_two, 4),
+            "GBps_rotated": round(b.bytes["step"] / (ms_rot * 1e-3) / 1e9, 1)}
 
 
 def _finite(x):
