@@ -28,6 +28,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 CACHE_E4M3 = 0
 CACHE_BF16 = 1
+CACHE_E5M2 = 3
+CACHE_INT8 = 4
 
 GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
              "-fno-fast-math", "-Wall", "-Wextra"]
@@ -76,6 +78,10 @@ def _bind(path: str) -> ctypes.CDLL:
         "oracle_paged_prefill_pairs": [P, P, i32, P, P, i32, P, P, i32, P, i32, P, i32, i32, i32,
                                        i32, f64, f64, i32],
         "oracle_hadamard_f32": [P, i32],
+        "oracle_e5m2_decode_n": [P, P, i64],
+        "oracle_e5m2_encode_n": [P, P, i64],
+        "oracle_int8_encode_n": [P, P, i64],
+        "oracle_cache_write_codec": [P, P, P, P, i32, P, i32, i32, i32, i32, i32, f32, f32],
         "oracle_hadamard_f64": [P, i32],
         "oracle_cache_write_rotated": [P, P, P, P, i32, P, i32, i32, i32, i32, i32, f32, f32],
         "oracle_paged_decode_rotated_pairs": [P, P, i32, P, P, P, i32, P, i32, P, i32, i32, i32,
@@ -145,7 +151,7 @@ def cache_write(key, value, key_cache: np.ndarray, value_cache: np.ndarray, cach
     T = sm.shape[0]
     assert k.size == T * num_kv_heads * head_dim and v.size == k.size
     assert head_dim % 4 == 0 and block_size == 16, "the paged layout needs head_dim % 4 == 0, 16-slot blocks"
-    want = np.uint8 if cache_dtype == CACHE_E4M3 else np.uint16
+    want = np.uint16 if cache_dtype == CACHE_BF16 else np.uint8
     for c in (key_cache, value_cache):
         assert c.dtype == want and c.flags["C_CONTIGUOUS"]
         assert c.size == num_blocks * num_kv_heads * block_size * head_dim
@@ -167,7 +173,7 @@ def cache_write_per_head(key, value, key_cache: np.ndarray, value_cache: np.ndar
     assert k.size == T * num_kv_heads * head_dim and v.size == k.size
     assert ks.shape == (num_kv_heads,) and vs.shape == (num_kv_heads,)
     assert head_dim % 4 == 0 and block_size == 16, "the paged layout needs head_dim % 4 == 0, 16-slot blocks"
-    want = np.uint8 if cache_dtype == CACHE_E4M3 else np.uint16
+    want = np.uint16 if cache_dtype == CACHE_BF16 else np.uint8
     for c in (key_cache, value_cache):
         assert c.dtype == want and c.flags["C_CONTIGUOUS"]
         assert c.size == num_blocks * num_kv_heads * block_size * head_dim
@@ -196,7 +202,7 @@ def _decode_common(q, key_cache, value_cache, cache_dtype, block_tables, context
     assert q.shape[-1] % 4 == 0, "the paged layout needs head_dim % 4 == 0"
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     cl = np.ascontiguousarray(context_lens, dtype=np.int32)
-    want = np.uint8 if cache_dtype == CACHE_E4M3 else np.uint16
+    want = np.uint16 if cache_dtype == CACHE_BF16 else np.uint8
     assert key_cache.dtype == want and value_cache.dtype == want
     assert key_cache.flags["C_CONTIGUOUS"] and value_cache.flags["C_CONTIGUOUS"]
     return q, bt, cl
@@ -338,7 +344,7 @@ def cache_write_rotated(key, value, key_cache: np.ndarray, value_cache: np.ndarr
     T = sm.shape[0]
     assert k.size == T * num_kv_heads * head_dim and v.size == k.size
     assert head_dim & (head_dim - 1) == 0 and block_size == 16
-    want = np.uint8 if cache_dtype == CACHE_E4M3 else np.uint16
+    want = np.uint16 if cache_dtype == CACHE_BF16 else np.uint8
     assert key_cache.dtype == want and value_cache.dtype == want
     assert key_cache.flags["C_CONTIGUOUS"] and value_cache.flags["C_CONTIGUOUS"]
     lib().oracle_cache_write_rotated(_ptr(k), _ptr(v), _ptr(key_cache), _ptr(value_cache),
@@ -373,3 +379,47 @@ def paged_decode_rotated(q, key_cache, value_cache, cache_dtype: int, block_tabl
                                      context_lens, num_q_heads, num_kv_heads, head_dim, block_size,
                                      k_scale, v_scale, sliding_window)
     return out.reshape(B, num_q_heads, head_dim)
+
+
+# -------------------------------------------------------- other codecs ----
+
+def e5m2_decode(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    lib().oracle_e5m2_decode_n(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def e5m2_encode(y) -> np.ndarray:
+    v = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().oracle_e5m2_encode_n(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def int8_encode(y) -> np.ndarray:
+    v = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().oracle_int8_encode_n(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def int8_decode(codes) -> np.ndarray:
+    return np.ascontiguousarray(codes, dtype=np.uint8).view(np.int8).astype(np.float64)
+
+
+def cache_write_codec(key, value, key_cache: np.ndarray, value_cache: np.ndarray, codec: int,
+                      slot_mapping, num_kv_heads: int, head_dim: int, block_size: int,
+                      num_blocks: int, k_scale: float, v_scale: float) -> None:
+    """cache_write with a one-byte codec (CACHE_E4M3, CACHE_E5M2 or CACHE_INT8)."""
+    assert codec in (CACHE_E4M3, CACHE_E5M2, CACHE_INT8)
+    k = np.ascontiguousarray(key, dtype=np.uint16)
+    v = np.ascontiguousarray(value, dtype=np.uint16)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    T = sm.shape[0]
+    assert k.size == T * num_kv_heads * head_dim and v.size == k.size
+    assert key_cache.dtype == np.uint8 and value_cache.dtype == np.uint8
+    assert key_cache.flags["C_CONTIGUOUS"] and value_cache.flags["C_CONTIGUOUS"]
+    lib().oracle_cache_write_codec(_ptr(k), _ptr(v), _ptr(key_cache), _ptr(value_cache), codec,
+                                   _ptr(sm), T, num_kv_heads, head_dim, block_size, num_blocks,
+                                   float(k_scale), float(v_scale))

@@ -52,6 +52,8 @@
 
 #define ORACLE_CACHE_E4M3 0
 #define ORACLE_CACHE_BF16 1
+#define ORACLE_CACHE_E5M2 3
+#define ORACLE_CACHE_INT8 4
 
 /* ---------------------------------------------------------------- bf16 --- */
 
@@ -125,6 +127,80 @@ uint8_t oracle_quantize(uint16_t x_bf16, float scale) {
     return oracle_e4m3_encode((double)y);
 }
 
+/* ------------------------------------------------------ other codecs --- */
+
+/*
+ * The two other one-byte codecs the pages name for the KV cache: E5M2 (two mantissa
+ * bits, largest finite 57344 [FLOPS "Workarounds"; CAP "What FP8 KV changes" / E4M3 vs
+ * E5M2]) and INT8 (a near-identical story with no separate measurement [FLOPS "notes"]).
+ * The pages give neither codec's rounding; the readings mirror the E4M3 ones:
+ *   E5M2 (OCP): sign bit 7, exponent bits 6..2 (bias 15), mantissa bits 1..0;
+ *     E = 31 is infinity (M = 0) or NaN; E = 0 is subnormal, M * 2^-16.  Encoding rounds
+ *     to nearest with ties to the even code, saturates magnitudes >= 57344 (and
+ *     infinities) to +-57344, keeps the sign of zero, and maps NaN to 0x7F | sign.
+ *   INT8: symmetric; the code is the f32 quotient rounded to the nearest integer (ties to
+ *     even) and clamped to [-127, 127], stored as a two's-complement byte; NaN -> 0.
+ */
+double oracle_e5m2_decode(uint8_t c) {
+    int sign = c >> 7, E = (c >> 2) & 0x1F, M = c & 3;
+    double mag;
+    if (E == 31)
+        mag = M == 0 ? INFINITY : NAN;
+    else if (E == 0)
+        mag = ldexp((double)M, -16);
+    else
+        mag = ldexp(1.0 + (double)M / 4.0, E - 15);
+    return sign ? -mag : mag;
+}
+
+uint8_t oracle_e5m2_encode(double y) {
+    uint8_t sgn = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y)) return (uint8_t)(0x7F | sgn);
+    double a = fabs(y);
+    if (a >= 57344.0) return (uint8_t)(sgn | 0x7B);          /* saturate */
+    if (a < ldexp(1.0, -14)) {                                /* subnormal range */
+        double m = rint(ldexp(a, 16));                        /* m = 4 is the smallest normal */
+        return (uint8_t)(sgn | (uint8_t)m);
+    }
+    int e = (int)floor(log2(a));
+    if (ldexp(1.0, e) > a) e -= 1;                            /* guard log2 rounding */
+    if (ldexp(1.0, e + 1) <= a) e += 1;
+    double mq = rint((ldexp(a, -e) - 1.0) * 4.0);
+    if (mq == 4.0) {
+        mq = 0.0;
+        e += 1;
+    }
+    return (uint8_t)(sgn | ((e + 15) << 2) | (int)mq);
+}
+
+double oracle_int8_decode(uint8_t c) { return (double)(int8_t)c; }
+
+uint8_t oracle_int8_encode(double y) {
+    if (isnan(y)) return 0;
+    double r = rint(y);                                       /* ties to even */
+    if (r > 127.0) r = 127.0;
+    if (r < -127.0) r = -127.0;
+    return (uint8_t)(int8_t)r;
+}
+
+/* The f32 quotient of a bf16 element and the scale, cast once to the codec. */
+static uint8_t quantize_codec(uint16_t x_bf16, float scale, int codec) {
+    float y = oracle_bf16_to_f32(x_bf16) / scale;
+    if (codec == ORACLE_CACHE_E5M2) return oracle_e5m2_encode((double)y);
+    if (codec == ORACLE_CACHE_INT8) return oracle_int8_encode((double)y);
+    return oracle_e4m3_encode((double)y);
+}
+
+void oracle_e5m2_decode_n(const uint8_t* c, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e5m2_decode(c[i]);
+}
+void oracle_e5m2_encode_n(const double* y, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e5m2_encode(y[i]);
+}
+void oracle_int8_encode_n(const double* y, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_int8_encode(y[i]);
+}
+
 /* Array helpers so callers can sweep whole domains in one call. */
 void oracle_e4m3_decode_n(const uint8_t* c, double* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(c[i]);
@@ -186,7 +262,7 @@ void oracle_cache_write(const uint16_t* key, const uint16_t* value,
                 uint16_t xk = key[((int64_t)t * Hkv + h) * D + i];
                 uint16_t xv = value[((int64_t)t * Hkv + h) * D + i];
                 int64_t ki = key_index(blk, h, off, i, Hkv, bs, D,
-                                       cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2);
+                                       cache_dtype == ORACLE_CACHE_BF16 ? 2 : 1);
                 int64_t vi = value_index(blk, h, off, i, Hkv, bs, D);
                 if (cache_dtype == ORACLE_CACHE_E4M3) {
                     ((uint8_t*)key_cache)[ki] = oracle_quantize(xk, k_scale);
@@ -219,7 +295,7 @@ void oracle_cache_write_per_head(const uint16_t* key, const uint16_t* value,
                 uint16_t xk = key[((int64_t)t * Hkv + h) * D + i];
                 uint16_t xv = value[((int64_t)t * Hkv + h) * D + i];
                 int64_t ki = key_index(blk, h, off, i, Hkv, bs, D,
-                                       cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2);
+                                       cache_dtype == ORACLE_CACHE_BF16 ? 2 : 1);
                 int64_t vi = value_index(blk, h, off, i, Hkv, bs, D);
                 if (cache_dtype == ORACLE_CACHE_E4M3) {
                     ((uint8_t*)key_cache)[ki] = oracle_quantize(xk, k_scales[h]);
@@ -233,8 +309,36 @@ void oracle_cache_write_per_head(const uint16_t* key, const uint16_t* value,
     }
 }
 
-/* Dequantised cache element: e4m3 value times scale, or the bf16 value. */
+/*
+ * The cache write with a one-byte codec (ORACLE_CACHE_E4M3, _E5M2 or _INT8): the same
+ * slots and tile layout as oracle_cache_write, each element cast by quantize_codec.
+ */
+void oracle_cache_write_codec(const uint16_t* key, const uint16_t* value,
+                              void* key_cache, void* value_cache, int codec,
+                              const int64_t* slot_mapping, int T, int Hkv, int D,
+                              int bs, int NB, float k_scale, float v_scale) {
+    for (int t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= (int64_t)NB * bs) continue;
+        int64_t blk = slot / bs;
+        int in_blk = (int)(slot % bs);
+        for (int h = 0; h < Hkv; ++h)
+            for (int i = 0; i < D; ++i) {
+                int64_t src = ((int64_t)t * Hkv + h) * D + i;
+                ((uint8_t*)key_cache)[key_index(blk, h, in_blk, i, Hkv, bs, D, 1)] =
+                    quantize_codec(key[src], k_scale, codec);
+                ((uint8_t*)value_cache)[value_index(blk, h, in_blk, i, Hkv, bs, D)] =
+                    quantize_codec(value[src], v_scale, codec);
+            }
+    }
+}
+
+/* Dequantised cache element: the code's value times scale, or the bf16 value. */
 static double cache_value(const void* cache, int cache_dtype, int64_t idx, double scale) {
+    if (cache_dtype == ORACLE_CACHE_E5M2)
+        return oracle_e5m2_decode(((const uint8_t*)cache)[idx]) * scale;
+    if (cache_dtype == ORACLE_CACHE_INT8)
+        return oracle_int8_decode(((const uint8_t*)cache)[idx]) * scale;
     if (cache_dtype == ORACLE_CACHE_E4M3)
         return oracle_e4m3_decode(((const uint8_t*)cache)[idx]) * scale;
     return (double)oracle_bf16_to_f32(((const uint16_t*)cache)[idx]);
@@ -294,7 +398,7 @@ void oracle_paged_decode_head(double* out, const uint16_t* q,
     int64_t L = context_lens[b];
     int64_t lo = (window > 0 && L > window) ? L - window : 0;
     int64_t n = L > lo ? L - lo : 0;
-    int eb = cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2;
+    int eb = cache_dtype == ORACLE_CACHE_BF16 ? 2 : 1;
     double* qv = (double*)malloc(sizeof(double) * (size_t)D);
     double* K = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
     double* V = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
@@ -389,7 +493,7 @@ void oracle_paged_prefill_pairs(double* out, const int32_t* pairs, int npairs,
                                 const int32_t* context_lens, int Hq, int Hkv, int D, int bs,
                                 double k_scale, double v_scale, int window) {
     int group = Hq / Hkv;
-    int eb = cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2;
+    int eb = cache_dtype == ORACLE_CACHE_BF16 ? 2 : 1;
     for (int p = 0; p < npairs; ++p) {
         int64_t row = pairs[2 * p];
         int hq = pairs[2 * p + 1];
@@ -506,7 +610,7 @@ void oracle_cache_write_rotated(const uint16_t* key, const uint16_t* value,
             oracle_hadamard_f32(rv, D);
             for (int i = 0; i < D; ++i) {
                 int64_t ki = key_index(blk, h, in_block, i, Hkv, bs, D,
-                                       cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2);
+                                       cache_dtype == ORACLE_CACHE_BF16 ? 2 : 1);
                 int64_t vi = value_index(blk, h, in_block, i, Hkv, bs, D);
                 if (cache_dtype == ORACLE_CACHE_E4M3) {
                     ((uint8_t*)key_cache)[ki] = quantize_f32(rk[i], k_scale);
@@ -534,7 +638,7 @@ void oracle_paged_decode_rotated_pairs(double* out, const int32_t* pairs, int np
                                        const int32_t* context_lens, int Hq, int Hkv, int D,
                                        int bs, double k_scale, double v_scale, int window) {
     int g = Hq / Hkv;
-    int eb = cache_dtype == ORACLE_CACHE_E4M3 ? 1 : 2;
+    int eb = cache_dtype == ORACLE_CACHE_BF16 ? 2 : 1;
     double* qr = (double*)malloc(sizeof(double) * (size_t)D);
     for (int p = 0; p < npairs; ++p) {
         int b = pairs[2 * p], hq = pairs[2 * p + 1];

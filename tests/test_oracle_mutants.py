@@ -19,7 +19,8 @@ PINS = [os.path.join(ROOT, "tests", "test_oracle_codec.py"),
         os.path.join(ROOT, "tests", "test_oracle_attention.py"),
         os.path.join(ROOT, "tests", "test_oracle_per_head.py"),
         os.path.join(ROOT, "tests", "test_oracle_prefill.py"),
-        os.path.join(ROOT, "tests", "test_oracle_rotation.py")]
+        os.path.join(ROOT, "tests", "test_oracle_rotation.py"),
+        os.path.join(ROOT, "tests", "test_oracle_codecs.py")]
 
 MUTANTS = {
     "subnormal_ties_away": ("double m = rint(a * 512.0);", "double m = round(a * 512.0);"),
@@ -80,6 +81,18 @@ MUTANTS = {
         "(void)o;"),
     "rotated_decode_query_not_rotated": ("oracle_hadamard_f64(qr, D);", "(void)qr;"),
     "rotated_write_values_unrotated": ("oracle_hadamard_f32(rv, D);", "(void)rv;"),
+    "e5m2_exponent_bias": ("mag = ldexp(1.0 + (double)M / 4.0, E - 15);",
+                           "mag = ldexp(1.0 + (double)M / 4.0, E - 16);"),
+    "e5m2_subnormal_step": ("mag = ldexp((double)M, -16);", "mag = ldexp((double)M, -15);"),
+    "e5m2_saturates_to_infinity": ("if (a >= 57344.0) return (uint8_t)(sgn | 0x7B);",
+                                   "if (a >= 57344.0) return (uint8_t)(sgn | 0x7C);"),
+    "e5m2_ties_up": ("double mq = rint((ldexp(a, -e) - 1.0) * 4.0);",
+                     "double mq = floor((ldexp(a, -e) - 1.0) * 4.0 + 0.5);"),
+    "int8_round_half_up": ("double r = rint(y);                                       /* ties to even */",
+                           "double r = floor(y + 0.5);"),
+    "int8_asymmetric_clamp": ("if (r < -127.0) r = -127.0;", "if (r < -128.0) r = -128.0;"),
+    "int8_cache_decoded_as_e4m3": ("return oracle_int8_decode(((const uint8_t*)cache)[idx]) * scale;",
+                                   "return oracle_e4m3_decode(((const uint8_t*)cache)[idx]) * scale * 0.0 + oracle_int8_decode(((const uint8_t*)cache)[idx]);"),
 }
 
 
