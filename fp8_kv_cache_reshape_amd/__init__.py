@@ -25,6 +25,8 @@ FP8KV_ERR_HIP = -6
 FP8KV_E4M3 = 0
 FP8KV_BF16 = 1
 FP8KV_F32 = 2
+FP8KV_E5M2 = 3
+FP8KV_INT8 = 4
 
 BLOCK_SIZE = 16
 

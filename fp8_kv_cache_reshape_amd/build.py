@@ -1,10 +1,13 @@
 """Build libfp8kv.so (HIP for gfx950) in-tree with hipcc."""
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -24,16 +27,34 @@ def sources():
 PROBE_LIB = os.path.join(HERE, "libfp8kv_probe.so")
 
 
-def _compile(srcs, out, includes, verbose):
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *HIP_FLAGS, *[a for inc in includes for a in ("-I", inc)], *srcs, "-o", tmp]
+def _run(cmd, verbose, what):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building " + os.path.basename(out))
-    os.replace(tmp, out)
+        raise RuntimeError("hipcc failed building " + what)
+
+
+def _compile(srcs, out, includes, verbose):
+    """Compile each source to an object in parallel (they are independent translation
+    units), then link the shared library; the result replaces `out` atomically."""
+    inc = [a for d in includes for a in ("-I", d)]
+    tmpdir = tempfile.mkdtemp(prefix="fp8kv_build_")
+    try:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in srcs]
+        flags = [f for f in HIP_FLAGS if f != "-shared"]
+        jobs = [([HIPCC, *flags, *inc, "-c", src, "-o", obj], os.path.basename(src))
+                for src, obj in zip(srcs, objs)]
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+            for f in [pool.submit(_run, cmd, verbose, what) for cmd, what in jobs]:
+                f.result()
+        tmp = out + ".tmp%d" % os.getpid()
+        _run([HIPCC, *HIP_FLAGS, *objs, "-o", tmp], verbose, os.path.basename(out))
+        os.replace(tmp, out)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
 
 
 def build(verbose: bool = False) -> str:

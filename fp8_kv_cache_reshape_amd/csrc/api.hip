@@ -22,6 +22,14 @@ inline int target_workgroups(int head_dim) { return head_dim <= 64 ? 512 : 256; 
 constexpr int kMinBlocksPerSplit = 16;    // one wave step (4 blocks) for each of 4 waves
 
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+bool cache_dtype_ok(int d) {
+    return d == FP8KV_E4M3 || d == FP8KV_BF16 || d == FP8KV_E5M2 || d == FP8KV_INT8;
+}
+// The C-ABI element codes are the kernels' codec values.
+fp8kv::Codec codec_of(int cache_dtype) { return static_cast<fp8kv::Codec>(cache_dtype); }
+static_assert(FP8KV_E4M3 == fp8kv::kCodecE4M3 && FP8KV_BF16 == fp8kv::kCodecBF16 &&
+                  FP8KV_E5M2 == fp8kv::kCodecE5M2 && FP8KV_INT8 == fp8kv::kCodecINT8,
+              "element codes and codecs must agree");
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
 
@@ -153,8 +161,8 @@ int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const voi
                                 max_context_len, sliding_window, num_splits);
     if (st != FP8KV_OK) return st;
     if (max_blocks_per_seq < 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
-    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
-    fp8 = cache_dtype == FP8KV_E4M3;
+    if (!cache_dtype_ok(cache_dtype)) return FP8KV_ERR_UNSUPPORTED;
+    fp8 = cache_dtype != FP8KV_BF16;   // one-byte codes (E4M3, E5M2, INT8)
     if (fp8) {
         st = check_scales(sc, per_head_call);
         if (st != FP8KV_OK) return st;
@@ -217,8 +225,8 @@ int cache_write_impl(const void* key, const void* value, void* key_cache, void* 
                      const Scales& sc, bool per_head_call, void* stream) {
     if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
     if (!head_dim_ok(head_dim) || block_size != kBlockSize) return FP8KV_ERR_UNSUPPORTED;
-    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
-    const bool fp8 = cache_dtype == FP8KV_E4M3;
+    if (!cache_dtype_ok(cache_dtype)) return FP8KV_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype != FP8KV_BF16;   // one-byte codes (E4M3, E5M2, INT8)
     if (fp8) {
         const int st = check_scales(sc, per_head_call);
         if (st != FP8KV_OK) return st;
@@ -240,7 +248,7 @@ int cache_write_impl(const void* key, const void* value, void* key_cache, void* 
     p.v_scale = sc.v;
     p.k_scales = fp8 && per_head_call ? sc.ks : nullptr;
     p.v_scales = fp8 && per_head_call ? sc.vs : nullptr;
-    return hip_status(fp8kv::launch_cache_write(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
+    return hip_status(fp8kv::launch_cache_write(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
 }
 
 int paged_decode_impl(void* out, int out_dtype, const void* query, const void* key_cache,
@@ -265,7 +273,7 @@ int paged_decode_impl(void* out, int out_dtype, const void* query, const void* k
     p.out = out;
     p.out_f32 = out_dtype == FP8KV_F32;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
+    st = hip_status(fp8kv::launch_decode_partial(p, codec_of(cache_dtype), head_dim, s));
     if (st != FP8KV_OK || p.write_final) return st;
     return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
 }
@@ -312,7 +320,7 @@ int decode_step_impl(void* out, int out_dtype, const void* query, const void* ke
     p.k_scale_q = fp8 && !per_head_call ? sc.k : 1.0f;
     p.v_scale_q = fp8 && !per_head_call ? sc.v : 1.0f;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
+    st = hip_status(fp8kv::launch_decode_partial(p, codec_of(cache_dtype), head_dim, s));
     if (st != FP8KV_OK || p.write_final || fused) return st;
     return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
 }
@@ -329,8 +337,8 @@ int paged_prefill_impl(void* out, int out_dtype, const void* query,
                                 max_context_len, sliding_window, 0);
     if (st != FP8KV_OK) return st;
     if (max_query_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
-    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
-    const bool fp8 = cache_dtype == FP8KV_E4M3;
+    if (!cache_dtype_ok(cache_dtype)) return FP8KV_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype != FP8KV_BF16;   // one-byte codes (E4M3, E5M2, INT8)
     if (fp8) {
         st = check_scales(sc, per_head_call);
         if (st != FP8KV_OK) return st;
@@ -366,7 +374,7 @@ int paged_prefill_impl(void* out, int out_dtype, const void* query,
     p.v_scale = fp8 && !heads ? sc.v : 1.0f;
     p.k_scales = heads ? sc.ks : nullptr;
     p.v_scales = heads ? sc.vs : nullptr;
-    return hip_status(fp8kv::launch_prefill(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
+    return hip_status(fp8kv::launch_prefill(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
 }
 
 // The rotated decode's workspace: the decode's own (split partials), then the rotated
@@ -396,7 +404,7 @@ const char* fp8kv_status_string(int status) {
         case FP8KV_ERR_NULL: return "a required pointer is NULL";
         case FP8KV_ERR_SHAPE: return "a size is negative or inconsistent, or a buffer is misaligned";
         case FP8KV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, group ratio, split count or dtype";
-        case FP8KV_ERR_SCALE: return "an fp8 scale is not finite and positive";
+        case FP8KV_ERR_SCALE: return "a scale of a one-byte cache is not finite and positive";
         case FP8KV_ERR_WORKSPACE: return "workspace is NULL, too small, or not 256-byte aligned";
         case FP8KV_ERR_HIP: return "a HIP kernel launch failed";
         default: return "unknown status";
@@ -532,7 +540,7 @@ int fp8kv_paged_decode_partial(const void* query, const void* key_cache, const v
                           tensor_scales(k_scale, 1.0f), false, sliding_window, num_splits,
                           workspace, workspace_bytes, true);
     if (st != FP8KV_OK || num_seqs == 0) return st;
-    return hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
+    return hip_status(fp8kv::launch_decode_partial(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
 }
 
 int fp8kv_paged_decode_merge(void* out, int out_dtype, const int32_t* context_lens,
@@ -608,7 +616,7 @@ int fp8kv_cache_write_rotated(const void* key, const void* value, void* key_cach
     if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
     if (!head_dim_ok(head_dim) || block_size != kBlockSize) return FP8KV_ERR_UNSUPPORTED;
     if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
-    const bool fp8 = cache_dtype == FP8KV_E4M3;
+    const bool fp8 = cache_dtype != FP8KV_BF16;   // one-byte codes (E4M3, E5M2, INT8)
     if (fp8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return FP8KV_ERR_SCALE;
     if (num_tokens == 0) return FP8KV_OK;
     if (!key || !value || !key_cache || !value_cache || !slot_mapping) return FP8KV_ERR_NULL;
@@ -625,7 +633,7 @@ int fp8kv_cache_write_rotated(const void* key, const void* value, void* key_cach
     p.num_blocks = num_blocks;
     p.k_scale = fp8 ? k_scale : 1.0f;
     p.v_scale = fp8 ? v_scale : 1.0f;
-    return hip_status(fp8kv::launch_rotate_write(p, fp8, head_dim, static_cast<hipStream_t>(stream)));
+    return hip_status(fp8kv::launch_rotate_write(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
 }
 
 size_t fp8kv_paged_decode_rotated_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
@@ -648,6 +656,8 @@ int fp8kv_paged_decode_rotated(void* out, int out_dtype, const void* query, cons
                                int num_splits, void* workspace, size_t workspace_bytes,
                                void* stream) {
     if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    // the rotated path is defined for the E4M3 and BF16 caches
+    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
     int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_context_len, sliding_window, num_splits);
     if (st != FP8KV_OK) return st;
@@ -681,7 +691,7 @@ int fp8kv_paged_decode_rotated(void* out, int out_dtype, const void* query, cons
     p.query_lo = q_lo;
     p.out = out_rot;
     p.out_f32 = 1;
-    st = hip_status(fp8kv::launch_decode_partial(p, fp8, head_dim, s));
+    st = hip_status(fp8kv::launch_decode_partial(p, codec_of(cache_dtype), head_dim, s));
     if (st != FP8KV_OK) return st;
     if (!p.write_final) {
         st = hip_status(fp8kv::launch_decode_merge(p, head_dim, s));

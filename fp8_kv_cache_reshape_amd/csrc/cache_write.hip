@@ -57,8 +57,9 @@ __device__ inline uint32_t dword(const u32x4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <int D, bool FP8>
+template <int D, int C>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
+    constexpr bool FP8 = C != kCodecBF16;         // one-byte codes (E4M3, E5M2 or INT8)
     constexpr int CH = D / 8;                     // 8-channel chunks per row
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t T = p.num_tokens;
@@ -96,8 +97,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
         uint2 qk[4], qv[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            qk[k] = quantize8(make_uint4(xk[k].x, xk[k].y, xk[k].z, xk[k].w), ks);
-            qv[k] = quantize8(make_uint4(xv[k].x, xv[k].y, xv[k].z, xv[k].w), vs);
+            qk[k] = quantize8<C>(make_uint4(xk[k].x, xk[k].y, xk[k].z, xk[k].w), ks);
+            qv[k] = quantize8<C>(make_uint4(xv[k].x, xv[k].y, xv[k].z, xv[k].w), vs);
         }
         if (fast) {
             const int64_t blk = sl[0] / kBlockSize;
@@ -174,23 +175,29 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
 }
 
 template <int D>
-hipError_t launch_d(const CacheWriteParams& p, bool fp8, hipStream_t s) {
+hipError_t launch_d(const CacheWriteParams& p, Codec codec, hipStream_t s) {
     const int64_t total = (((int64_t)p.num_tokens + 15) / 16) * p.num_kv_heads * (D / 8) * 4;
     const int threads = 256;
     const int64_t blocks = (total + threads - 1) / threads;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const void* fn = fp8 ? reinterpret_cast<const void*>(&cache_write_kernel<D, true>)
-                         : reinterpret_cast<const void*>(&cache_write_kernel<D, false>);
+    const void* fn;
+    switch (codec) {
+        case kCodecE4M3: fn = reinterpret_cast<const void*>(&cache_write_kernel<D, kCodecE4M3>); break;
+        case kCodecBF16: fn = reinterpret_cast<const void*>(&cache_write_kernel<D, kCodecBF16>); break;
+        case kCodecE5M2: fn = reinterpret_cast<const void*>(&cache_write_kernel<D, kCodecE5M2>); break;
+        case kCodecINT8: fn = reinterpret_cast<const void*>(&cache_write_kernel<D, kCodecINT8>); break;
+        default: return hipErrorInvalidValue;
+    }
     return launch_kernel(fn, dim3((unsigned)blocks), dim3(threads), 0, s, p);
 }
 
 }  // namespace
 
-hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, int head_dim, hipStream_t s) {
+hipError_t launch_cache_write(const CacheWriteParams& p, Codec codec, int head_dim, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_d<64>(p, fp8, s);
-        case 128: return launch_d<128>(p, fp8, s);
-        case 256: return launch_d<256>(p, fp8, s);
+        case 64: return launch_d<64>(p, codec, s);
+        case 128: return launch_d<128>(p, codec, s);
+        case 256: return launch_d<256>(p, codec, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "codec.h"
+
 namespace fp8kv {
 
 constexpr int kBlockSize = 16;     // tokens per cache block (the only supported size)
@@ -152,17 +154,18 @@ inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, size_t ld
     return hipLaunchKernel(fn, grid, block, args, lds, s);
 }
 
-hipError_t launch_cache_write(const CacheWriteParams& p, bool fp8, int head_dim, hipStream_t s);
-hipError_t launch_decode_partial(const DecodeParams& p, bool fp8, int head_dim, hipStream_t s);
+// `codec`: the cache element codec (kCodecBF16 or a one-byte codec).
+hipError_t launch_cache_write(const CacheWriteParams& p, Codec codec, int head_dim, hipStream_t s);
+hipError_t launch_decode_partial(const DecodeParams& p, Codec codec, int head_dim, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t s);
 // Whether the decode kernel can merge the `splits` partials of a (sequence, kv head) group
 // of `group` query heads itself, in at most two batched round trips to memory; larger
 // merges run in the separate merge kernel.
 bool fused_merge_fits(int group, int head_dim, int splits);
-hipError_t launch_prefill(const PrefillParams& p, bool fp8, int head_dim, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, Codec codec, int head_dim, hipStream_t s);
 // Hadamard rotation (rotation.hip): the rotated cache write (CacheWriteParams' per-tensor
 // scales), the query rotation into hi + lo bf16 terms, and the output rotation back.
-hipError_t launch_rotate_write(const CacheWriteParams& p, bool fp8, int head_dim, hipStream_t s);
+hipError_t launch_rotate_write(const CacheWriteParams& p, Codec codec, int head_dim, hipStream_t s);
 hipError_t launch_rotate_query(const uint16_t* q, uint16_t* q_hi, uint16_t* q_lo, int64_t rows,
                                int head_dim, hipStream_t s);
 hipError_t launch_rotate_out(const float* in, void* out, int out_f32, int64_t rows, int head_dim,

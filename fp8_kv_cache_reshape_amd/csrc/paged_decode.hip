@@ -32,8 +32,8 @@
 //               tokens 8u..8u+7), exactly the 8 value bytes that one channel row of a
 //               channel-major value tile holds there, so each lane loads one 16-byte row
 //               per 16-channel output tile and no LDS transpose is needed.
-// fp8 codes become bf16 exactly (E4M3 is a subset of bf16) with the native gfx950
-// conversion; k_scale/sqrt(d)*log2(e) scales the fp32 scores and v_scale is applied at
+// One-byte codes (E4M3, and the E5M2 / INT8 variants) become bf16 exactly with the native
+// gfx950 conversions (INT8 through f32); k_scale/sqrt(d)*log2(e) scales the fp32 scores and v_scale is applied at
 // the final normalisation, since the hardware's scaled conversions only take powers of 2.
 //
 // Memory pipeline: the KV stream is read once, so it uses nontemporal 16-byte loads.  The
@@ -57,16 +57,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFlushSteps = 4;         // wave steps summed in the matrix-core accumulator
 constexpr float kRescaleLog2 = 8.0f;   // reference max moves only when a score exceeds it by 2^8
-
-// 8 E4M3 codes (bytes of lo then hi, in memory order) -> 8 bf16, exactly.
-__device__ inline bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-    bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-    return r;
-}
 
 __device__ inline f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -273,13 +263,17 @@ __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) 
 // 2-byte caches need more and run one wave per SIMD.
 // The variant with a second (low) query term -- the rotated query, carried as two bf16
 // terms -- runs one wave per SIMD.
-template <int D, bool FP8, bool QLO>
-constexpr int partial_waves_per_eu() { return QLO ? 1 : ((D <= 128 && FP8) || D == 64 ? 2 : 1); }
+template <int D, int C, bool QLO>
+constexpr int partial_waves_per_eu() {
+    return QLO ? 1 : ((D <= 128 && C != kCodecBF16) || D == 64 ? 2 : 1);
+}
 
-template <int D, bool FP8, bool QLO>
+// C: the cache codec (kCodecBF16, or a one-byte codec: E4M3, E5M2, INT8).
+template <int D, int C, bool QLO>
 __global__ __launch_bounds__(64 * kDecodeWaves)
-__attribute__((amdgpu_waves_per_eu(partial_waves_per_eu<D, FP8, QLO>(), 8)))
+__attribute__((amdgpu_waves_per_eu(partial_waves_per_eu<D, C, QLO>(), 8)))
 void decode_partial_kernel(DecodeParams p) {
+    constexpr bool FP8 = C != kCodecBF16;         // one-byte codes
     constexpr int ES = FP8 ? 1 : 2;               // bytes per cache element
     constexpr int DG = D / 4;                     // channels per lane group in S = K.q^T
     constexpr int KK = D / 32;                    // MFMA k-steps for S
@@ -464,7 +458,7 @@ void decode_partial_kernel(DecodeParams p) {
                     bf16x8 a;
                     if constexpr (FP8) {
                         const uint4 u = bf.k[s][kk >> 1];
-                        a = (kk & 1) ? e4m3x8_to_bf16x8(u.z, u.w) : e4m3x8_to_bf16x8(u.x, u.y);
+                        a = (kk & 1) ? codes8_to_bf16x8<C>(u.z, u.w) : codes8_to_bf16x8<C>(u.x, u.y);
                     } else {
                         a = __builtin_bit_cast(bf16x8, bf.k[s][kk]);
                     }
@@ -565,7 +559,7 @@ void decode_partial_kernel(DecodeParams p) {
                     bf16x8 vb8;
                     if constexpr (FP8) {
                         const uint4 v = bf.v[t][0];
-                        vb8 = u ? e4m3x8_to_bf16x8(v.z, v.w) : e4m3x8_to_bf16x8(v.x, v.y);
+                        vb8 = u ? codes8_to_bf16x8<C>(v.z, v.w) : codes8_to_bf16x8<C>(v.x, v.y);
                     } else {
                         vb8 = __builtin_bit_cast(bf16x8, bf.v[t][u]);
                     }
@@ -616,7 +610,7 @@ void decode_partial_kernel(DecodeParams p) {
             char* tile = static_cast<char*>(const_cast<void*>(val ? p.value_cache : p.key_cache))
                          + ((int64_t)tok_blk * p.num_kv_heads + h) * TILE_BYTES;
             if constexpr (FP8) {
-                const uint2 q8 = quantize8(tok, val ? head_scale(p.v_scales, h, p.v_scale_q)
+                const uint2 q8 = quantize8<C>(tok, val ? head_scale(p.v_scales, h, p.v_scale_q)
                                                     : head_scale(p.k_scales, h, p.k_scale_q));
                 if (!val) {
                     *reinterpret_cast<uint2*>(tile + key_chunk_offset<D, 1>(off, c * 8)) = q8;
@@ -909,7 +903,7 @@ size_t partial_lds_bytes(int G) {
 
 // Kernels whose dynamic LDS can exceed 64 KiB (g = 16 at head_dim 256) get their limit
 // raised once, to the largest size any group ratio needs.
-template <int D, bool FP8, bool QLO>
+template <int D, int C, bool QLO>
 hipError_t allow_lds(size_t need) {
     if (need <= 65536) return hipSuccess;
     // raise this kernel's limit once, to what the device allows (up to kMaxPartialLds)
@@ -919,7 +913,7 @@ hipError_t allow_lds(size_t need) {
             hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
             return 65536;
         if ((size_t)lim > kMaxPartialLds) lim = (int)kMaxPartialLds;
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, FP8, QLO>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, C, QLO>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, lim) != hipSuccess)
             return 65536;
         return lim;
@@ -927,33 +921,43 @@ hipError_t allow_lds(size_t need) {
     return need <= (size_t)allowed ? hipSuccess : hipErrorInvalidValue;
 }
 
+template <int D, int C, bool QLO>
+hipError_t launch_partial_dc(const DecodeParams& p, size_t lds, dim3 grid, dim3 block, hipStream_t s) {
+    const hipError_t e = allow_lds<D, C, QLO>(lds);
+    if (e != hipSuccess) return e;
+    return launch_kernel(reinterpret_cast<const void*>(&decode_partial_kernel<D, C, QLO>), grid, block,
+                         lds, s, p);
+}
+
+template <int D, int C>
+hipError_t launch_partial_c(const DecodeParams& p, size_t lds, dim3 grid, dim3 block, hipStream_t s) {
+    return p.query_lo != nullptr ? launch_partial_dc<D, C, true>(p, lds, grid, block, s)
+                                 : launch_partial_dc<D, C, false>(p, lds, grid, block, s);
+}
+
 template <int D>
-hipError_t launch_partial_d(const DecodeParams& p, bool fp8, hipStream_t s) {
+hipError_t launch_partial_d(const DecodeParams& p, Codec codec, hipStream_t s) {
     const int G = p.num_q_heads / p.num_kv_heads;
     const size_t lds = partial_lds_bytes<D>(G);
-
     const dim3 grid = kHeadsFastest ? dim3(p.num_kv_heads, p.splits, p.num_seqs)
                                     : dim3(p.splits, p.num_kv_heads, p.num_seqs);
     const dim3 block(64 * kDecodeWaves);
-    const bool qlo = p.query_lo != nullptr;
-    hipError_t e = fp8 ? (qlo ? allow_lds<D, true, true>(lds) : allow_lds<D, true, false>(lds))
-                       : (qlo ? allow_lds<D, false, true>(lds) : allow_lds<D, false, false>(lds));
-    if (e != hipSuccess) return e;
-    const void* fn =
-        fp8 ? (qlo ? reinterpret_cast<const void*>(&decode_partial_kernel<D, true, true>)
-                   : reinterpret_cast<const void*>(&decode_partial_kernel<D, true, false>))
-            : (qlo ? reinterpret_cast<const void*>(&decode_partial_kernel<D, false, true>)
-                   : reinterpret_cast<const void*>(&decode_partial_kernel<D, false, false>));
-    return launch_kernel(fn, grid, block, lds, s, p);
+    switch (codec) {
+        case kCodecE4M3: return launch_partial_c<D, kCodecE4M3>(p, lds, grid, block, s);
+        case kCodecBF16: return launch_partial_c<D, kCodecBF16>(p, lds, grid, block, s);
+        case kCodecE5M2: return launch_partial_c<D, kCodecE5M2>(p, lds, grid, block, s);
+        case kCodecINT8: return launch_partial_c<D, kCodecINT8>(p, lds, grid, block, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_decode_partial(const DecodeParams& p, bool fp8, int head_dim, hipStream_t s) {
+hipError_t launch_decode_partial(const DecodeParams& p, Codec codec, int head_dim, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_partial_d<64>(p, fp8, s);
-        case 128: return launch_partial_d<128>(p, fp8, s);
-        case 256: return launch_partial_d<256>(p, fp8, s);
+        case 64: return launch_partial_d<64>(p, codec, s);
+        case 128: return launch_partial_d<128>(p, codec, s);
+        case 256: return launch_partial_d<256>(p, codec, s);
         default: return hipErrorInvalidValue;
     }
 }

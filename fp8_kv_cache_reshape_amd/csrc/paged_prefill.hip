@@ -34,12 +34,13 @@
 //               the 8 (or 16, bf16)
 //               contiguous bytes of channel l%32's row in the channel-major value tile
 //               that hold tokens 8h..8h+7 -- no transpose.
-// fp8 codes become bf16 exactly (E4M3 is a subset of bf16).  Scores are kept in base-2
+// One-byte codes (E4M3, E5M2, INT8) become bf16 exactly.  Scores are kept in base-2
 // units (k_scale log2(e)/sqrt(d) folded into one multiply); v_scale multiplies the final
 // normalisation.  The running maximum of a column is only moved when a score exceeds it
 // by 2^8, so probabilities stay below 256 and the accumulators are rarely rescaled.
 #include <type_traits>
 
+#include "codec.h"
 #include "internal.h"
 
 namespace fp8kv {
@@ -57,15 +58,6 @@ constexpr int kCols = 32;                  // query columns per wave
 constexpr int kStep = 32;                  // key tokens per wave step (two cache blocks)
 constexpr int kFlushSteps = 8;             // key steps summed in the matrix-core accumulator
 constexpr float kRescaleLog2 = 8.0f;
-
-__device__ inline bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-    bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-    return r;
-}
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -102,8 +94,10 @@ __device__ inline void comp_add(float& hi, float& lo, float x) {
     hi = s;
 }
 
-template <int D, bool FP8>
+// C: the cache codec (kCodecBF16, or a one-byte codec: E4M3, E5M2, INT8).
+template <int D, int C>
 __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
+    constexpr bool FP8 = C != kCodecBF16;  // one-byte codes
     constexpr int ES = FP8 ? 1 : 2;
     constexpr int NK = D / 16;             // contraction slices of S (16 channels each)
     constexpr int NT = D / 32;             // 32-channel output tiles of O
@@ -279,11 +273,11 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
                 for (int kk = 0; kk < NK; kk += 2) {
                     const u32x4 v = *reinterpret_cast<const u32x4*>(
                         ktile + key_chunk_offset<D, 1>(slot, key_slice_channel<D, 1>(half, kk)));
-                    s0 = mfma32(e4m3x8_to_bf16x8(v[0], v[1]), qb[kk], s0);
+                    s0 = mfma32(codes8_to_bf16x8<C>(v[0], v[1]), qb[kk], s0);
                     if constexpr (D <= 128)
-                        s1 = mfma32(e4m3x8_to_bf16x8(v[2], v[3]), qb[kk + 1], s1);
+                        s1 = mfma32(codes8_to_bf16x8<C>(v[2], v[3]), qb[kk + 1], s1);
                     else    // (head_dim 256: one chain, to stay within the registers)
-                        s0 = mfma32(e4m3x8_to_bf16x8(v[2], v[3]), qb[kk + 1], s0);
+                        s0 = mfma32(codes8_to_bf16x8<C>(v[2], v[3]), qb[kk + 1], s0);
                 }
             } else {
 #pragma unroll
@@ -369,7 +363,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
                 bf16x8 vb;
                 if constexpr (ES == 1) {
                     const u32x2 v = *reinterpret_cast<const u32x2*>(vtile + ch * kBlockSize + 8 * half);
-                    vb = e4m3x8_to_bf16x8(v[0], v[1]);
+                    vb = codes8_to_bf16x8<C>(v[0], v[1]);
                 } else {
                     vb = as_bf16x8(*reinterpret_cast<const u32x4*>(vtile + (ch * kBlockSize + 8 * half) * 2));
                 }
@@ -453,24 +447,30 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
 }
 
 template <int D>
-hipError_t launch_d(const PrefillParams& p, bool fp8, hipStream_t s) {
+hipError_t launch_d(const PrefillParams& p, Codec codec, hipStream_t s) {
     const int G = p.num_q_heads / p.num_kv_heads;
     const int64_t tiles = ((int64_t)p.max_query_len * G + kWaves * kCols - 1) / (kWaves * kCols);
     if (tiles <= 0 || p.num_seqs <= 0) return hipSuccess;
     if (tiles > 0x7FFFFFFF || p.num_seqs > 65535 || p.num_kv_heads > 65535) return hipErrorInvalidValue;
-    const void* fn = fp8 ? reinterpret_cast<const void*>(&prefill_kernel<D, true>)
-                         : reinterpret_cast<const void*>(&prefill_kernel<D, false>);
+    const void* fn;
+    switch (codec) {
+        case kCodecE4M3: fn = reinterpret_cast<const void*>(&prefill_kernel<D, kCodecE4M3>); break;
+        case kCodecBF16: fn = reinterpret_cast<const void*>(&prefill_kernel<D, kCodecBF16>); break;
+        case kCodecE5M2: fn = reinterpret_cast<const void*>(&prefill_kernel<D, kCodecE5M2>); break;
+        case kCodecINT8: fn = reinterpret_cast<const void*>(&prefill_kernel<D, kCodecINT8>); break;
+        default: return hipErrorInvalidValue;
+    }
     return launch_kernel(fn, dim3((unsigned)tiles, p.num_kv_heads, p.num_seqs), dim3(64 * kWaves),
                          0, s, p);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& p, bool fp8, int head_dim, hipStream_t s) {
+hipError_t launch_prefill(const PrefillParams& p, Codec codec, int head_dim, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_d<64>(p, fp8, s);
-        case 128: return launch_d<128>(p, fp8, s);
-        case 256: return launch_d<256>(p, fp8, s);
+        case 64: return launch_d<64>(p, codec, s);
+        case 128: return launch_d<128>(p, codec, s);
+        case 256: return launch_d<256>(p, codec, s);
         default: return hipErrorInvalidValue;
     }
 }

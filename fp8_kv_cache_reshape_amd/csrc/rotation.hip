@@ -59,8 +59,9 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 }
 
 // ---- rotated cache write: one lane per (token, kv head, 8 channels), d/8 lanes per row
-template <int D, bool FP8>
+template <int D, int C>
 __global__ __launch_bounds__(256) void rotate_write_kernel(CacheWriteParams p, float rscale) {
+    constexpr bool FP8 = C != kCodecBF16;  // one-byte codes
     constexpr int CH = D / 8;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * CH;
@@ -86,8 +87,8 @@ __global__ __launch_bounds__(256) void rotate_write_kernel(CacheWriteParams p, f
         uint32_t ck[4], cv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {   // IEEE f32 division by the scale, then the cast
-            ck[j] = e4m3_pack2(k[2 * j] / p.k_scale, k[2 * j + 1] / p.k_scale);
-            cv[j] = e4m3_pack2(v[2 * j] / p.v_scale, v[2 * j + 1] / p.v_scale);
+            ck[j] = pack2<C>(k[2 * j] / p.k_scale, k[2 * j + 1] / p.k_scale);
+            cv[j] = pack2<C>(v[2 * j] / p.v_scale, v[2 * j + 1] / p.v_scale);
         }
         *reinterpret_cast<uint2*>(kc + tile + key_chunk_offset<D, 1>(off, c * 8)) =
             make_uint2(ck[0] | (ck[1] << 16), ck[2] | (ck[3] << 16));
@@ -176,16 +177,25 @@ hipError_t launch_rows(void (*kernel)(A...), int64_t threads_total, hipStream_t 
 
 }  // namespace
 
-hipError_t launch_rotate_write(const CacheWriteParams& p, bool fp8, int head_dim, hipStream_t s) {
+template <int D>
+hipError_t launch_rotate_write_d(const CacheWriteParams& p, Codec codec, int64_t total, float rs,
+                                 hipStream_t s) {
+    switch (codec) {
+        case kCodecE4M3: return launch_rows(rotate_write_kernel<D, kCodecE4M3>, total, s, p, rs);
+        case kCodecBF16: return launch_rows(rotate_write_kernel<D, kCodecBF16>, total, s, p, rs);
+        case kCodecE5M2: return launch_rows(rotate_write_kernel<D, kCodecE5M2>, total, s, p, rs);
+        case kCodecINT8: return launch_rows(rotate_write_kernel<D, kCodecINT8>, total, s, p, rs);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_rotate_write(const CacheWriteParams& p, Codec codec, int head_dim, hipStream_t s) {
     const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * (head_dim / 8);
     const float rs = rotation_scale(head_dim);
     switch (head_dim) {
-        case 64: return fp8 ? launch_rows(rotate_write_kernel<64, true>, total, s, p, rs)
-                            : launch_rows(rotate_write_kernel<64, false>, total, s, p, rs);
-        case 128: return fp8 ? launch_rows(rotate_write_kernel<128, true>, total, s, p, rs)
-                             : launch_rows(rotate_write_kernel<128, false>, total, s, p, rs);
-        case 256: return fp8 ? launch_rows(rotate_write_kernel<256, true>, total, s, p, rs)
-                             : launch_rows(rotate_write_kernel<256, false>, total, s, p, rs);
+        case 64: return launch_rotate_write_d<64>(p, codec, total, rs, s);
+        case 128: return launch_rotate_write_d<128>(p, codec, total, rs, s);
+        case 256: return launch_rotate_write_d<256>(p, codec, total, rs, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -37,7 +37,8 @@
  *   query:                            [num_seqs][num_q_heads][head_dim] bf16
  *   output:                           [num_seqs][num_q_heads][head_dim] bf16 or f32
  *   key_cache, value_cache: [num_blocks][num_kv_heads] tiles of block_size*head_dim
- *     elements (u8 E4M3 codes for FP8KV_E4M3, bf16 for FP8KV_BF16), each contiguous.
+ *     elements (one-byte codes for FP8KV_E4M3 / FP8KV_E5M2 / FP8KV_INT8, bf16 for
+ *     FP8KV_BF16), each contiguous.
  *     value tile: channel-major, element (slot t, channel i) at i*block_size + t.
  *     key tile: 16-byte chunks ordered (slot quad, chunk, slot within quad, channel
  *       quarter).  With e = element bytes, q = head_dim/4, g = i/q, w = (i%q)*e and
@@ -78,6 +79,14 @@ extern "C" {
 #define FP8KV_E4M3 0   /* OCP FP8 E4M3 ("fn"): bias 7, max 448, no infinities, NaN = S.1111.111 */
 #define FP8KV_BF16 1
 #define FP8KV_F32  2   /* output only */
+/* The other one-byte cache codecs the pages name (page "ctx-fp8-kv-cache-long-context-
+ * accuracy", "Workarounds" and "notes": E5M2 and INT8 KV, no measured advantage).  Every
+ * entry point that takes a cache_dtype accepts them wherever it accepts FP8KV_E4M3, with
+ * the same layout, scales and error behaviour. */
+#define FP8KV_E5M2 3   /* OCP FP8 E5M2: bias 15, max 57344; encoded like E4M3 (RNE, ties to even,
+                          saturating at +-57344, NaN -> 0x7F | sign) */
+#define FP8KV_INT8 4   /* symmetric INT8: nearest integer to x/scale, ties to even, clamped to
+                          [-127, 127], NaN -> 0; two's-complement byte */
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* fp8kv_status_string(int status);
@@ -99,6 +108,7 @@ const char* fp8kv_last_hip_error(void);
  *     maps NaN to 0x7F | sign.  k uses k_scale, v uses v_scale (page "FP8 KV Cache
  *     Quantization: Capacity Gains and Accuracy Risk", "Scales and calibration": one
  *     scale per tensor, elements divided by it before the cast).
+ *   E5M2 / INT8 caches: the same f32 division, then that codec's cast (see the codes).
  *   BF16 caches: the bf16 bits are stored unchanged; the scales are ignored.
  * Bytes of the caches that no valid slot addresses are left untouched.  Two tokens that
  * name the same slot race; the result is one of the two rows.
@@ -108,7 +118,7 @@ const char* fp8kv_last_hip_error(void);
  *   value_cache     device caches in the layout above, of cache_dtype elements
  *   slot_mapping    device int64 [num_tokens]
  *   num_tokens      >= 0 (0 enqueues nothing)
- *   k_scale,v_scale finite and > 0 for FP8KV_E4M3 (else FP8KV_ERR_SCALE)
+ *   k_scale,v_scale finite and > 0 for the one-byte codecs (else FP8KV_ERR_SCALE)
  */
 int fp8kv_cache_write(const void* key, const void* value,
                       void* key_cache, void* value_cache, int cache_dtype,
@@ -381,7 +391,8 @@ int fp8kv_paged_prefill_per_head(void* out, int out_dtype, const void* query,
  * is rotated back.  Dot products are unchanged; outliers spread across coordinates, which
  * lowers the quantisation error of per-tensor scales.  A cache written by
  * fp8kv_cache_write_rotated must be read by fp8kv_paged_decode_rotated (and vice versa);
- * scales should be calibrated on the rotated rows.
+ * scales should be calibrated on the rotated rows.  Cache dtypes: FP8KV_E4M3 and FP8KV_BF16
+ * (others: FP8KV_ERR_UNSUPPORTED).
  *
  * fp8kv_cache_write_rotated -- fp8kv_cache_write of rotated rows.  Each row x (d elements
  * of one token and kv head, widened to f32) becomes y = R(x): the fast Walsh-Hadamard
