@@ -79,13 +79,22 @@ def algorithmic_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_di
 class DecodeBench:
     """Device buffers for one workload layer and the calls of one decode step."""
 
-    def __init__(self, F, torch, w, layer, instances: int, num_splits: int, heads=None):
+    def __init__(self, F, torch, w, layer, instances: int, num_splits: int, heads=None, codec=None):
         """heads: None (the layer's per-tensor scales) or float32 [Hkv] (k_scales, v_scales)
-        for the per-head entry points."""
+        for the per-head entry points.  codec: a one-byte cache code (FP8KV_E5M2 /
+        FP8KV_INT8) in place of the layer's E4M3 (with scales rescaled to its range)."""
         self.F, self.torch, self.w, self.layer = F, torch, w, layer
         dev = "cuda"
         self.cdt = F.FP8KV_E4M3 if layer.cache_dtype == "e4m3" else F.FP8KV_BF16
-        self.ebytes = 1 if self.cdt == F.FP8KV_E4M3 else 2
+        if codec is not None:
+            assert self.cdt == F.FP8KV_E4M3
+            top = {F.FP8KV_E5M2: 57344.0, F.FP8KV_INT8: 127.0}[codec]
+            import dataclasses
+            layer = dataclasses.replace(layer, k_scale=float(np.float32(layer.k_scale) * 448 / top),
+                                        v_scale=float(np.float32(layer.v_scale) * 448 / top))
+            self.layer = layer
+            self.cdt = codec
+        self.ebytes = 2 if self.cdt == F.FP8KV_BF16 else 1
         B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
         n = w.num_blocks * Hkv * BLOCK * D
         u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
@@ -283,7 +292,8 @@ class DecodeBench:
 
 PROFILE_SUMMARY = "profiles/decode_llama8b_b1_128k.txt"
 KERNEL_SOURCES = ["fp8_kv_cache_reshape_amd/csrc/paged_decode.hip",
-                  "fp8_kv_cache_reshape_amd/csrc/internal.h"]
+                  "fp8_kv_cache_reshape_amd/csrc/internal.h",
+                  "fp8_kv_cache_reshape_amd/csrc/codec.h"]
 
 
 def measured_traffic(root: str):
@@ -298,7 +308,7 @@ def measured_traffic(root: str):
     for f in KERNEL_SOURCES:
         h.update(open(os.path.join(root, f), "rb").read())
     text = open(path).read()
-    if f"(paged_decode.hip + internal.h): {h.hexdigest()[:16]}" not in text:
+    if f"(paged_decode.hip + internal.h + codec.h): {h.hexdigest()[:16]}" not in text:
         return None
     for line in text.splitlines():
         if line.startswith("decode_partial_traffic_bytes_per_launch"):
@@ -441,6 +451,8 @@ def main(argv=None):
     ap.add_argument("--prefill-workload", default="llama8b-8k,d256-8k",
                     help="comma-separated: " + ", ".join(sorted(PREFILL_WORKLOADS)))
     ap.add_argument("--prefill-caches", default="e4m3,bf16", help="cache dtypes to time")
+    ap.add_argument("--codec", choices=["e4m3", "e5m2", "int8"], default="e4m3",
+                    help="one-byte cache codec of the timed fp8 layer (default e4m3)")
     ap.add_argument("--rotated", action="store_true",
                     help="only time the Hadamard-rotated path (rotated write of the step token + "
                          "rotated decode) against the plain two-call path on --workload")
@@ -491,7 +503,10 @@ def main(argv=None):
     gen_s = time.perf_counter() - t0
     one = 2 * w.num_blocks * w.num_kv_heads * BLOCK * w.head_dim * (1 if layer.cache_dtype == "e4m3" else 2)
     R = max(1, math.ceil(args.rotate_bytes * (1 << 30) / one))
-    bench = DecodeBench(F, torch, w, layer, R, args.num_splits, heads)
+    codec = {"e4m3": None, "e5m2": F.FP8KV_E5M2, "int8": F.FP8KV_INT8}[args.codec]
+    if codec is not None and layer.cache_dtype != "e4m3":
+        codec = None
+    bench = DecodeBench(F, torch, w, layer, R, args.num_splits, heads, codec)
     ms_step, ms_enqueue = bench.time_steps(args.steps, args.warmup)
     # under a profiler (--profile) only the fused step runs, so every dispatch of the decode
     # kernel in the trace is a fused step
@@ -512,10 +527,12 @@ def main(argv=None):
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_step": round(ms_step * 1e3, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "e4m3 KV -> bf16 MFMA, f32 accumulate" if bench.ebytes == 1 else "bf16 KV, f32 accumulate",
+        "dtype": (f"{args.codec if codec is not None else 'e4m3'} KV -> bf16 MFMA, f32 accumulate"
+                  if bench.ebytes == 1 else "bf16 KV, f32 accumulate"),
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {w.name}, layer {layer.name} "
-                               f"({layer.cache_dtype} cache, window {layer.sliding_window}"
+                               f"({layer.cache_dtype if codec is None else args.codec} cache, "
+                               f"window {layer.sliding_window}"
                                f"{', per-head scales' if heads is not None else ''})",
                    "num_seqs": w.num_seqs, "context_lens": sorted(set(int(x) for x in w.context_lens))[:4],
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
@@ -525,7 +542,7 @@ def main(argv=None):
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (measured_traffic(root) if args.workload == "llama8b-b1-128k"
                                  and layer.cache_dtype == "e4m3" and args.num_splits == 0
-                                 and heads is None else None),
+                                 and heads is None and codec is None else None),
                      "kernel": "decode_partial_kernel (fp8kv_decode_step: write + decode + merge)",
                      "bytes_per_launch": by["step"],
                      "avg_launch_us": round(kern["step_ms"] * 1e3, 3)},
@@ -551,7 +568,8 @@ def main(argv=None):
         result["pct_of_read_ceiling"] = round(100 * value / rc["GBps"], 2)
         torch.cuda.empty_cache()
 
-    if not (args.no_bf16 or args.profile or heads is not None) and layer.cache_dtype == "e4m3":
+    if not (args.no_bf16 or args.profile or heads is not None or codec is not None) \
+            and layer.cache_dtype == "e4m3":
         import dataclasses
         bl = dataclasses.replace(layer, cache_dtype="bf16", k_scale=1.0, v_scale=1.0)
         R2 = max(1, math.ceil(args.rotate_bytes * (1 << 30) / (2 * one)))
@@ -565,7 +583,8 @@ def main(argv=None):
         del b2
         torch.cuda.empty_cache()
 
-    if not (args.no_cpu_baseline or args.profile or heads is not None) and layer.cache_dtype == "e4m3":
+    if not (args.no_cpu_baseline or args.profile or heads is not None or codec is not None) \
+            and layer.cache_dtype == "e4m3":
         result["cpu_baseline"] = cpu_baseline(w, layer)
 
     print(json.dumps(_finite(result)), flush=True)
