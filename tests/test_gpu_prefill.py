@@ -20,8 +20,27 @@ def _mk(Hq, Hkv, D, lens, chunks, cid, cache=syn.E4M3, window=0):
     return w, syn.prefill_queries(w, chunks, cid)
 
 
+MAX_FULL_PAIRS = 3000   # beyond this many (row, head) pairs the oracle runs on a sample
+
+
+def _sample_pairs(w, pq, seed):
+    """Every row for the first and the last query head (all tiles, all tails), and every
+    head for the first, the last and three random rows of each sequence."""
+    rng = np.random.default_rng(seed)
+    Hq = w.num_q_heads
+    pairs = {(r, hq) for r in range(pq.num_tokens) for hq in (0, Hq - 1)}
+    for b in range(w.num_seqs):
+        a, e = int(pq.query_start_loc[b]), int(pq.query_start_loc[b + 1])
+        if e > a:
+            for r in {a, e - 1, *rng.integers(a, e, 3).tolist()}:
+                pairs |= {(r, hq) for hq in range(Hq)}
+    return np.array(sorted(pairs), np.int32)
+
+
 def _check(w, pq, out_f32=False, heads=None, pairs=None, context_lens=None, max_query_len=None):
     layer = w.layers[0]
+    if pairs is None and pq.num_tokens * w.num_q_heads > MAX_FULL_PAIRS:
+        pairs = _sample_pairs(w, pq, 170)
     cdt = E4M3 if layer.cache_dtype == syn.E4M3 else BF16
     kc, vc = dev_caches(w, cdt)
     gpu_write(w, layer, kc, vc, heads=heads)
