@@ -1,5 +1,4 @@
-// paged_prefill.hip -- prefill / chunked-prefill attention over the paged fp8 (or bf16) KV
-// cache.
+// paged_prefill.hip -- prefill / chunked-prefill attention over the paged KV cache.
 //
 // What is computed (header fp8kv.h has the exact definition): the chunk of n_b new query
 // tokens of sequence b sits at the last n_b positions of its context; the token at
@@ -15,29 +14,31 @@
 //
 // Work mapping.  A query "column" is one (chunk token, query head of the group) pair; the
 // columns of a (sequence, kv head) are numbered token-major, head fastest, so the g heads
-// of one token -- which read the same keys -- sit side by side.  A workgroup of 4 waves
-// owns 128 consecutive columns of one (sequence, kv head); each wave owns 32 and walks
-// the keys its columns need, 32 tokens (two cache blocks) per step, straight from the
-// paged cache (no LDS staging: a step's K and V bytes are read once per wave, and the
-// waves and workgroups of one kv head share them through the L2).  Both products run on
-// v_mfma_f32_32x32x16_bf16:
-//   S = K.Q^T : A = 32 key rows x 16 channels, B = 16 channels x 32 columns.  The result
-//               lands with lane l holding column l%32 and 16 key rows, so the softmax
-//               max and sum of a column stay inside the lane pair (l, l^32).  Key row r
-//               reads token tau(r) = r with bits 2 and 3 swapped: that makes the 8
-//               probabilities a lane feeds to P.V tokens 8h..8h+7 of one block (h = l/32).
-//               Each lane reads half of its key row's channels, as the key tile's
-//               16-byte chunks of quarters 2h and 2h+1; the query operand follows the
-//               same channel order.
-//   O += P.V  : A = 32 columns x 16 tokens (the lane's own probabilities, as a high and a
-//               low bf16 term: two products), B = 16 tokens x 32 channels: lane l reads
-//               the 8 (or 16, bf16)
-//               contiguous bytes of channel l%32's row in the channel-major value tile
-//               that hold tokens 8h..8h+7 -- no transpose.
-// One-byte codes (E4M3, E5M2, INT8) become bf16 exactly.  Scores are kept in base-2
-// units (k_scale log2(e)/sqrt(d) folded into one multiply); v_scale multiplies the final
-// normalisation.  The running maximum of a column is only moved when a score exceeds it
-// by 2^8, so probabilities stay below 256 and the accumulators are rarely rescaled.
+// of one token -- which read the same keys -- sit side by side.  A workgroup of 8 waves
+// owns 128 consecutive columns of one (sequence, kv head), 16 per wave, and walks the keys
+// they need 32 tokens (two cache blocks) at a time.
+//
+// Staging.  Each step's K and V tiles are loaded once per workgroup (two waves per tile),
+// widened to bf16 on the way (one-byte codes are a subset of bf16), and written into a
+// double-buffered LDS tile; the loads run two steps ahead in registers.  The matrix cores
+// then read bf16 operands straight from LDS, so no wave converts codes itself.  The LDS
+// tiles have their own order, chosen so that every operand read instruction covers
+// contiguous 256-byte runs (no bank conflicts): keys [group][slice][slot][8 channels],
+// values [16-channel tile][group][channel][4 slots].
+//
+// Both products run on v_mfma_f32_16x16x32_bf16 (16 columns per wave keeps the two
+// accumulator levels and the query operand small enough for two waves per SIMD):
+//   S = K.Q^T per block : A = 16 key slots x 32 channels, B = 32 channels x 16 columns.
+//               Lane l (column l%16, group g = l/16) gets slots 4g..4g+3 of the block; the
+//               32-channel slice kk of group g is channels [g*d/4 + 8kk, +8) -- one 16-byte
+//               chunk of the key tile.
+//   O += P.V  : A = 16 columns x 32 keys, B = 32 keys x 16 channels.  Group g's contraction
+//               slot is slots 4g..4g+3 of both blocks: exactly the 8 probabilities the lane
+//               holds, and two 8-byte reads of a channel row of the value tiles.
+// Probabilities enter P.V as a high (truncated) and a low bf16 term.  Scores are kept in
+// base-2 units (k_scale log2(e)/sqrt(d) is applied inside the exponent's FMA); v_scale
+// multiplies the final normalisation.  The running maximum of a column only moves when a
+// score exceeds it by 2^8, so the accumulators are rarely rescaled.
 #include <type_traits>
 
 #include "codec.h"
@@ -47,36 +48,20 @@ namespace fp8kv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
 
-constexpr int kWaves = 4;
-constexpr int kCols = 32;                  // query columns per wave
-constexpr int kStep = 32;                  // key tokens per wave step (two cache blocks)
+constexpr int kWaves = 8;
+constexpr int kCols = 16;                  // query columns per wave
+constexpr int kStep = 32;                  // key tokens per step (two cache blocks)
 constexpr int kFlushSteps = 8;             // key steps summed in the matrix-core accumulator
 constexpr float kRescaleLog2 = 8.0f;
 
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-// First channel of the 8 channels a lane of half h feeds to contraction slice kk of the
-// S product (see the key layout in internal.h: the lane reads quarters 2h and 2h+1).
-template <int D, int ES>
-__device__ constexpr int key_slice_channel(int h, int kk) {
-    if constexpr (ES == 1)      // a 16-byte chunk holds 16 channels: two slices
-        return (2 * h + (kk % 4) / 2) * (D / 4) + 16 * (kk / 4) + 8 * (kk % 2);
-    else                        // a 16-byte chunk holds 8 channels: one slice
-        return (2 * h + kk % 2) * (D / 4) + 8 * (kk / 2);
-}
-
-// Key row r of a step reads token tau(r): bits 2 and 3 of r swapped.
-__device__ inline int key_token(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 __device__ inline void store_out(void* out, int out_f32, int64_t idx, float v) {
     if (out_f32)
@@ -94,25 +79,50 @@ __device__ inline void comp_add(float& hi, float& lo, float x) {
     hi = s;
 }
 
-// C: the cache codec (kCodecBF16, or a one-byte codec: E4M3, E5M2, INT8).
+// LDS byte offset of key element (slot, channel) of a staged block: [group g = ch/(D/4)]
+// [slice kk = (ch % (D/4))/8][slot ^ 4g][channel % 8], bf16.  The XOR keeps each 16-slot
+// row a permutation (reads stay conflict-free) and spreads the staging stores, whose
+// lanes hold the same slot in different groups, over different banks.
+template <int D>
+__device__ constexpr int lds_key(int slot, int ch) {
+    const int g = ch / (D / 4);
+    return ((g * (D / 32) + (ch % (D / 4)) / 8) * kBlockSize + (slot ^ ((4 * g) & 15))) * 16 + (ch % 8) * 2;
+}
+
+// LDS byte offset of value element (channel, slot) of a staged block: [tile t = ch/16]
+// [group = slot/4][channel % 16][slot % 4], bf16.
+__device__ constexpr int lds_value(int ch, int slot) {
+    return (((ch / 16) * 4 + slot / 4) * 16 + ch % 16) * 8 + (slot % 4) * 2;
+}
+
+// Staging geometry: a step is 4 cache tiles (keys of blocks 0 and 1, then their values),
+// each moved by 2 waves; a lane moves PER source bytes of one tile.
 template <int D, int C>
-__global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
-    constexpr bool FP8 = C != kCodecBF16;  // one-byte codes
-    constexpr int ES = FP8 ? 1 : 2;
-    constexpr int NK = D / 16;             // contraction slices of S (16 channels each)
-    constexpr int NT = D / 32;             // 32-channel output tiles of O
-    constexpr int TILE = kBlockSize * D * ES;   // bytes of one (block, kv head) tile
-    constexpr int NV = TILE / 64 / 16;     // 16-byte pieces per lane of one staged tile
-    // a staged step: key tiles of its two blocks, then their value tiles
-    __shared__ __attribute__((aligned(16))) uint8_t sm_kv[2][4 * TILE];
-    __shared__ float sm_f[kWaves][kCols];
+struct Stage {
+    static constexpr int ES = C == kCodecBF16 ? 2 : 1;       // source bytes per element
+    static constexpr int TILE_SRC = kBlockSize * D * ES;     // bytes of a cache tile
+    static constexpr int TILE_LDS = kBlockSize * D * 2;      // bytes of its bf16 copy
+    static constexpr int PER = TILE_SRC / 128;               // source bytes per lane
+    static constexpr int NW = PER / 4;                       // dwords per lane
+};
+
+template <int D, int C>
+__global__ __launch_bounds__(64 * kWaves)
+__attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, 8)))
+void prefill_kernel(PrefillParams p) {
+    using S = Stage<D, C>;
+    constexpr int NK = D / 32;             // 32-channel contraction slices of S
+    constexpr int NT = D / 16;             // 16-channel output tiles of O
+    constexpr int TL = S::TILE_LDS;
+    // a staged step in bf16: key tiles of blocks 0 and 1, then their value tiles
+    __shared__ __attribute__((aligned(16))) uint8_t sm_kv[2][4 * TL];
 
     const int lane = threadIdx.x & 63;
-    // wave-uniform (kept in a scalar register: block ids then come from scalar loads, whose
-    // waits do not drain the vector loads in flight)
+    // wave-uniform (a scalar register: block ids come from scalar loads, whose waits do not
+    // drain the vector loads in flight)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int col = lane & 31;             // this lane's query column (S layout)
-    const int half = lane >> 5;            // contraction half
+    const int col = lane & 15;             // this lane's query column
+    const int grp = lane >> 4;             // contraction group
     const int h = blockIdx.y;              // kv head
     const int b = blockIdx.z;
     const int G = p.num_q_heads / p.num_kv_heads;
@@ -154,16 +164,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
     const int lomax = lo_of(pmax);
     const int lomin = lo_of(pmin);
 
-    // query operand of S: slice kk = q[hq][key_slice_channel(half, kk) .. +8)
+    // query operand of S: slice kk = q[hq][grp*D/4 + 8kk .. +8)
     bf16x8 qb[NK];
     {
-        const uint16_t* qrow = p.query + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * D;
+        const uint16_t* qrow = p.query + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * D + grp * (D / 4);
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (cvalid && pos >= 0)
-                v = *reinterpret_cast<const u32x4*>(qrow + key_slice_channel<D, ES>(half, kk));
-            qb[kk] = as_bf16x8(v);
+            if (cvalid && pos >= 0) v = *reinterpret_cast<const u32x4*>(qrow + 8 * kk);
+            qb[kk] = __builtin_bit_cast(bf16x8, v);
         }
     }
 
@@ -181,147 +190,133 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
         return (id >= 0 && id < p.num_blocks && kb + c * kBlockSize < kend) ? id : -1;
     };
 
-    // ---- staging: wave w moves piece w of a step (key block 0, key block 1, value block 0,
-    // value block 1).  The loads are always issued (a missing block or a step past the end
-    // reads block 0 of the cache, in bounds) so that no branch sits between a load and
-    // its use; missing blocks become zeros and value slots at or past kend are zeroed when
-    // the piece is written to LDS, where the wait for the data happens anyway.
-    const int part_c = wave & 1;
-    const bool part_v = wave >= 2;
+    // ---- staging: waves 2t, 2t+1 move tile t of a step (key block 0, key block 1, value
+    // block 0, value block 1), PER source bytes per lane.  The loads are always issued (a
+    // missing block or a step past the end reads block 0, in bounds) so that no branch sits
+    // between a load and its use; missing blocks become zeros and value slots at or past
+    // kend are zeroed when the piece is widened and written to LDS.
+    const int part = wave >> 1;                                   // 0..3
+    const int part_c = part & 1;
+    const bool part_v = part >= 2;
+    const int src_off = ((wave & 1) * 64 + lane) * S::PER;        // byte offset in the tile
     const uint8_t* part_src = static_cast<const uint8_t*>(part_v ? p.value_cache : p.key_cache);
-    auto stage_load = [&](int st, u32x4 (&r)[NV]) {
+    typedef uint32_t stage_t __attribute__((ext_vector_type(S::NW)));
+    auto stage_load = [&](int st, stage_t& r) {
         const int kb = kfirst + (st < nsteps ? st : 0) * kStep;
         const int id = block_of(kb, part_c);
-        const uint8_t* src = part_src + ((int64_t)(id >= 0 ? id : 0) * p.num_kv_heads + h) * TILE +
-                             lane * (NV * 16);
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            r[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16 * i));
+        const uint8_t* src = part_src + ((int64_t)(id >= 0 ? id : 0) * p.num_kv_heads + h) * S::TILE_SRC + src_off;
+        r = __builtin_nontemporal_load(reinterpret_cast<const stage_t*>(src));
     };
-    auto stage_store = [&](int buf, int st, const u32x4 (&r)[NV]) {
+    auto stage_store = [&](int buf, int st, const stage_t& r) {
         const int kb = kfirst + st * kStep;
-        const bool ok = block_of(kb, part_c) >= 0;
-        // value slots kept: a 16-byte piece holds 16 slots (fp8) or 8 slots (bf16) of one row
-        const int nvalid = part_v ? kend - (kb + part_c * kBlockSize) : kBlockSize;
-        uint8_t* dst = &sm_kv[buf][wave * TILE + lane * (NV * 16)];
+        const uint32_t okm = block_of(kb, part_c) >= 0 ? 0xFFFFFFFFu : 0u;
+        uint8_t* dst = sm_kv[buf] + part * TL;
+        constexpr int EPL = S::PER / S::ES;                       // elements per lane
+        constexpr int DW8 = 2 * S::ES;                            // source dwords per 8 elements
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            u32x4 v = r[i];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t m = ok ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-                for (int k = 0; k < 4 / ES; ++k) {
-                    const int slot = ((lane * NV + i) * (16 / ES) + e * (4 / ES) + k) % kBlockSize;
-                    if (slot >= nvalid) m &= ~((ES == 1 ? 0xFFu : 0xFFFFu) << (8 * ES * k));
-                }
-                v[e] &= m;
+        for (int j = 0; j < EPL / 8; ++j) {
+            const int e0 = src_off / S::ES + 8 * j;               // element index in the tile
+            u32x4 v;
+            if constexpr (C == kCodecBF16) {
+                v = u32x4{r[4 * j] & okm, r[4 * j + 1] & okm, r[4 * j + 2] & okm, r[4 * j + 3] & okm};
+            } else {
+                v = __builtin_bit_cast(u32x4, codes8_to_bf16x8<C>(r[DW8 * j] & okm, r[DW8 * j + 1] & okm));
             }
-            *reinterpret_cast<u32x4*>(dst + 16 * i) = v;
+            if (!part_v) {
+                // element e0 of the source key tile: invert the chunk layout to (slot, channel)
+                const int o = e0 * S::ES;                         // source byte offset
+                constexpr int C1 = D * S::ES / 64;                // chunks per quarter of a slot
+                const int slot = 4 * ((o / 256) / C1) + (o / 64) % 4;
+                const int ch = ((o % 64) / 16) * (D / 4) + (16 * ((o / 256) % C1) + o % 16) / S::ES;
+                *reinterpret_cast<u32x4*>(dst + lds_key<D>(slot, ch)) = v;
+            } else {
+                // value tile: channel-major rows of 16 slots; zero the slots at or past kend
+                const int slot0 = e0 % kBlockSize;
+                const int nvalid = kend - (kb + part_c * kBlockSize);
+                if (slot0 + 8 > nvalid) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t lo = slot0 + 2 * k < nvalid ? 0x0000FFFFu : 0u;
+                        const uint32_t hi = slot0 + 2 * k + 1 < nvalid ? 0xFFFF0000u : 0u;
+                        v[k] &= lo | hi;
+                    }
+                }
+                // slots slot0 .. slot0+7 of channel e0 / 16: two 4-slot groups
+                const int ch = e0 / kBlockSize;
+                *reinterpret_cast<u32x2*>(dst + lds_value(ch, slot0)) = u32x2{v[0], v[1]};
+                *reinterpret_cast<u32x2*>(dst + lds_value(ch, slot0 + 4)) = u32x2{v[2], v[3]};
+            }
         }
     };
 
-    f32x16 oacc[NT], osum[NT];
+    f32x4 oacc[NT], osum[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        oacc[t] = f32x16{};
-        osum[t] = f32x16{};
+        oacc[t] = f32x4{};
+        osum[t] = f32x4{};
     }
     float mref = -INFINITY;                // running reference maximum of this column
-    float l_hi = 0.0f, l_lo = 0.0f;        // sum of this lane's half of the probabilities
+    float l_hi = 0.0f, l_lo = 0.0f;        // sum of this lane's share of the probabilities
     int flush = 0;
 
-    // rescale the O rows (columns 8j + 4*half + i) by the per-column factors in sm_f
+    // multiply the O rows (columns 4*grp + i) by their columns' factors
     auto rescale_rows = [&](float f) {
-        if (half == 0) sm_f[wave][col] = f;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float fr[16];
+        float fr[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) fr[r] = sm_f[wave][(r / 4) * 8 + 4 * half + (r % 4)];
+        for (int i = 0; i < 4; ++i) fr[i] = __shfl(f, 4 * grp + i);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                oacc[t][r] *= fr[r];
-                osum[t][r] *= fr[r];
+            for (int i = 0; i < 4; ++i) {
+                oacc[t][i] *= fr[i];
+                osum[t][i] *= fr[i];
             }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
     };
 
-    const int kt = key_token(col);         // token (within the step) of this lane's key row
-    // one step of the wave from staged buffer `buf`
     // whether step st holds any key this wave's columns attend to
     auto visible = [&](int st) {
         const int kb = kfirst + st * kStep;
         return st < nsteps && wactive && kb <= pmax && kb + kStep > lomin;
     };
-    // S = K.Q^T of the step staged in buffer `buf`
-    auto s_product = [&](int buf) {
-        const uint8_t* sk = sm_kv[buf];
-        // ---- S = K.Q^T, as two independent accumulator chains (even and odd slices) up to
-        // head_dim 128
-        f32x16 s;
-        {
-            f32x16 s0 = f32x16{}, s1 = f32x16{};
-            const uint8_t* ktile = sk + (kt / kBlockSize) * TILE;
-            const int slot = kt % kBlockSize;
-            if constexpr (ES == 1) {
-#pragma unroll
-                for (int kk = 0; kk < NK; kk += 2) {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(
-                        ktile + key_chunk_offset<D, 1>(slot, key_slice_channel<D, 1>(half, kk)));
-                    s0 = mfma32(codes8_to_bf16x8<C>(v[0], v[1]), qb[kk], s0);
-                    if constexpr (D <= 128)
-                        s1 = mfma32(codes8_to_bf16x8<C>(v[2], v[3]), qb[kk + 1], s1);
-                    else    // (head_dim 256: one chain, to stay within the registers)
-                        s0 = mfma32(codes8_to_bf16x8<C>(v[2], v[3]), qb[kk + 1], s0);
-                }
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < NK; kk += 2) {
-                    const u32x4 v0 = *reinterpret_cast<const u32x4*>(
-                        ktile + key_chunk_offset<D, 2>(slot, key_slice_channel<D, 2>(half, kk)));
-                    const u32x4 v1 = *reinterpret_cast<const u32x4*>(
-                        ktile + key_chunk_offset<D, 2>(slot, key_slice_channel<D, 2>(half, kk + 1)));
-                    s0 = mfma32(as_bf16x8(v0), qb[kk], s0);
-                    if constexpr (D <= 128)
-                        s1 = mfma32(as_bf16x8(v1), qb[kk + 1], s1);
-                    else
-                        s0 = mfma32(as_bf16x8(v1), qb[kk + 1], s0);
-                }
-            }
-            if constexpr (D <= 128)
-                s = s0 + s1;
-            else
-                s = s0;
-        }
-        return s;
-    };
-    // softmax update and O += P.V of step st, whose scores are s, staged in buffer `buf`
-    auto finish = [&](int st, f32x16 s, int buf) {
+
+    auto compute = [&](int st, int buf) {
+        if (!visible(st)) return;
         const int kb = kfirst + st * kStep;
         const bool bok0 = block_of(kb, 0) >= 0, bok1 = block_of(kb, 1) >= 0;
         const uint8_t* sk = sm_kv[buf];
+
+        // ---- S = K.Q^T for each block: lane holds slots 4*grp + i of its column
+        f32x4 s[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            f32x4 a = f32x4{};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(
+                    sk + c * TL + lds_key<D>(col, grp * (D / 4) + 8 * kk));
+                a = mfma16(__builtin_bit_cast(bf16x8, v), qb[kk], a);
+            }
+            s[c] = a;
+        }
 
         // ---- raw scores masked outside [clo, pos] and outside valid blocks; the base-2
         // scale (> 0) is applied to the maximum and inside the exponent's FMA
         const bool edge = kb + kStep > pmin + 1 || kb < lomax || !bok0 || !bok1;
         float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float v = s[r];
-            if (edge) {
-                const int tr = key_token((r / 4) * 8 + 4 * half + (r % 4));
-                const int kp = kb + tr;
-                const bool ok = kp >= clo && kp <= pos && (tr < kBlockSize ? bok0 : bok1);
-                v = ok ? v : -INFINITY;
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = s[c][i];
+                if (edge) {
+                    const int kp = kb + c * kBlockSize + 4 * grp + i;
+                    const bool ok = kp >= clo && kp <= pos && (c == 0 ? bok0 : bok1);
+                    v = ok ? v : -INFINITY;
+                }
+                s[c][i] = v;
+                mx = fmaxf(mx, v);
             }
-            s[r] = v;
-            mx = fmaxf(mx, v);
-        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * sscale;
         // lazy reference move: only when a score exceeds it by 2^8 (or on the first keys)
         const bool move = mx > mref + kRescaleLog2;
@@ -336,40 +331,32 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
         }
         const float mu = mref == -INFINITY ? 0.0f : mref;
 
-        // ---- probabilities as the sum of two bf16 terms (about 16 significant bits: one
-        // bf16 term alone moves a weighted average by up to 2^-9 of the value spread)
-        // (the high term is pf truncated to bf16, so pf - hi is exact; the low term is
-        // that remainder rounded to bf16)
-        bf16x8 pa[2], pb[2];
+        // ---- probabilities as a high (pf truncated to bf16, so pf - hi is exact) and a low
+        // bf16 term; element 4c + i is slot 4*grp + i of block c
+        bf16x8 pa, pb;
         float psum = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sscale, -mu));
-            const float hf = __uint_as_float(__float_as_uint(pf) & 0xFFFF0000u);
-            pa[r / 8][r % 8] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(pf) >> 16));
-            pb[r / 8][r % 8] = (__bf16)(pf - hf);
-            psum += pf;
-        }
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][i], sscale, -mu));
+                const float hf = __uint_as_float(__float_as_uint(pf) & 0xFFFF0000u);
+                pa[4 * c + i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(pf) >> 16));
+                pb[4 * c + i] = (__bf16)(pf - hf);
+                psum += pf;
+            }
         comp_add(l_hi, l_lo, psum);
 
-        // ---- O += P.V: chunk c = block c of the step, lane reads tokens 8*half .. +7
-        // (value slots past the context were zeroed when staged)
+        // ---- O += P.V: channel tile t, lane reads slots 4*grp .. +3 of both blocks (value
+        // slots past the context were zeroed when staged)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const uint8_t* vtile = sk + (2 + c) * TILE;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int ch = 32 * t + col;
-                bf16x8 vb;
-                if constexpr (ES == 1) {
-                    const u32x2 v = *reinterpret_cast<const u32x2*>(vtile + ch * kBlockSize + 8 * half);
-                    vb = codes8_to_bf16x8<C>(v[0], v[1]);
-                } else {
-                    vb = as_bf16x8(*reinterpret_cast<const u32x4*>(vtile + (ch * kBlockSize + 8 * half) * 2));
-                }
-                oacc[t] = mfma32(pa[c], vb, oacc[t]);
-                oacc[t] = mfma32(pb[c], vb, oacc[t]);
-            }
+        for (int t = 0; t < NT; ++t) {
+            const int ch = 16 * t + col;
+            const u32x2 v0 = *reinterpret_cast<const u32x2*>(sk + 2 * TL + lds_value(ch, 4 * grp));
+            const u32x2 v1 = *reinterpret_cast<const u32x2*>(sk + 3 * TL + lds_value(ch, 4 * grp));
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+            oacc[t] = mfma16(pa, vb, oacc[t]);
+            oacc[t] = mfma16(pb, vb, oacc[t]);
         }
 
         // ---- second level: move the matrix-core partial sums into fp32 registers
@@ -378,71 +365,52 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 osum[t] += oacc[t];
-                oacc[t] = f32x16{};
+                oacc[t] = f32x4{};
             }
         }
     };
-    auto compute = [&](int st, int buf) {
-        if (visible(st)) finish(st, s_product(buf), buf);
-    };
 
-    if constexpr (D <= 128) {
-        // ---- the pipeline: step s+2 is loaded into registers while step s is computed
-        // from one LDS buffer and step s+1 is written into the other; one barrier per step
-        u32x4 ra[NV], rb[NV];
-        stage_load(0, ra);
-        stage_load(1, rb);
-        stage_store(0, 0, ra);
+    // ---- the pipeline: step s+2 is loaded into registers while step s is computed from
+    // one LDS buffer and step s+1 is written into the other; one barrier per step
+    stage_t ra, rb;
+    stage_load(0, ra);
+    stage_load(1, rb);
+    stage_store(0, 0, ra);
+    __syncthreads();
+    for (int st = 0; st < nsteps; st += 2) {
+        stage_load(st + 2, ra);
+        compute(st, 0);
+        stage_store(1, st + 1, rb);
         __syncthreads();
-        for (int st = 0; st < nsteps; st += 2) {
-            stage_load(st + 2, ra);
-            compute(st, 0);
-            stage_store(1, st + 1, rb);
-            __syncthreads();
-            if (st + 1 >= nsteps) break;
-            stage_load(st + 3, rb);
-            compute(st + 1, 1);
-            stage_store(0, st + 2, ra);
-            __syncthreads();
-        }
-    } else {
-        // ---- head_dim 256 (twice the accumulators): one register set, step s+1 loaded
-        // while step s is computed
-        u32x4 ra[NV];
-        stage_load(0, ra);
-        for (int st = 0; st < nsteps; ++st) {
-            stage_store(st & 1, st, ra);
-            __syncthreads();
-            stage_load(st + 1, ra);
-            compute(st, st & 1);
-        }
+        if (st + 1 >= nsteps) break;
+        stage_load(st + 3, rb);
+        compute(st + 1, 1);
+        stage_store(0, st + 2, ra);
+        __syncthreads();
     }
     if (!wactive) return;
 #pragma unroll
     for (int t = 0; t < NT; ++t) osum[t] += oacc[t];
 
-    // ---- normalise: the column's probability sum over both halves, then v_scale / l
+    // ---- normalise: the column's probability sum over its four groups, then v_scale / l
     float l_tot = l_hi + l_lo;
+    l_tot += __shfl_xor(l_tot, 16);
     l_tot += __shfl_xor(l_tot, 32);
     const float vscale = p.v_scales != nullptr
                              ? ((const __attribute__((address_space(4))) float*)p.v_scales)[h]
                              : p.v_scale;
     const float inv = l_tot > 0.0f ? vscale / l_tot : 0.0f;   // no attended key: zero row
-    if (half == 0) sm_f[wave][col] = inv;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int orow = (r / 4) * 8 + 4 * half + (r % 4);    // the column this row holds
+    for (int i = 0; i < 4; ++i) {
+        const int orow = 4 * grp + i;                          // the column this row holds
+        const float f = __shfl(inv, orow);
         const int64_t oc = c0 + orow;
         if (oc >= ncols) continue;
-        const float f = sm_f[wave][orow];
         const int otok = (int)(oc / G);
         const int ohq = h * G + (int)(oc % G);
         const int64_t base = ((int64_t)(q0 + otok) * p.num_q_heads + ohq) * D;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) store_out(p.out, p.out_f32, base + 32 * t + col, osum[t][r] * f);
+        for (int t = 0; t < NT; ++t) store_out(p.out, p.out_f32, base + 16 * t + col, osum[t][i] * f);
     }
 }
 
