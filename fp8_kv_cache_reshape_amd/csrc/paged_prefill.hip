@@ -9,7 +9,7 @@
 // "Arithmetic intensity").  Prefill is the pass whose contraction runs over the whole
 // context, so it keeps the two-level accumulation of page "The State of FP8 KV-Cache and
 // Attention Quantization in vLLM", "ACCURACY AT LONG CONTEXT": the matrix-core
-// accumulator sums at most kFlushSteps key steps, then its partial sums move into plain
+// accumulator sums at most kFlushKeys keys, then its partial sums move into plain
 // fp32 registers.
 //
 // Work mapping.  A query "column" is one (chunk token, query head of the group) pair; the
@@ -55,8 +55,7 @@ typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
 
 constexpr int kWaves = 8;
 constexpr int kCols = 16;                  // query columns per wave
-constexpr int kStep = 32;                  // key tokens per step (two cache blocks)
-constexpr int kFlushSteps = 8;             // key steps summed in the matrix-core accumulator
+constexpr int kFlushKeys = 256;            // keys summed in the matrix-core accumulator
 constexpr float kRescaleLog2 = 8.0f;
 
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -95,15 +94,23 @@ __device__ constexpr int lds_value(int ch, int slot) {
     return (((ch / 16) * 4 + slot / 4) * 16 + ch % 16) * 8 + (slot % 4) * 2;
 }
 
-// Staging geometry: a step is 4 cache tiles (keys of blocks 0 and 1, then their values),
-// each moved by 2 waves; a lane moves PER source bytes of one tile.
+// Staging geometry.  A step covers NB cache blocks (64 keys for d <= 128, 32 for d = 256,
+// so that the double-buffered step stays within 64 KB of LDS); its 2*NB cache tiles (keys
+// of blocks 0..NB-1, then their values) are moved by the 8 waves, each wave WAVE_SRC
+// contiguous source bytes of one tile and each lane PER bytes of those.
 template <int D, int C>
 struct Stage {
+    static constexpr int NB = D <= 128 ? 4 : 2;               // cache blocks per step
+    static constexpr int STEP = NB * kBlockSize;              // keys per step
     static constexpr int ES = C == kCodecBF16 ? 2 : 1;       // source bytes per element
     static constexpr int TILE_SRC = kBlockSize * D * ES;     // bytes of a cache tile
     static constexpr int TILE_LDS = kBlockSize * D * 2;      // bytes of its bf16 copy
-    static constexpr int PER = TILE_SRC / 128;               // source bytes per lane
+    static constexpr int WAVE_SRC = 2 * NB * TILE_SRC / kWaves;
+    static constexpr int PER = WAVE_SRC / 64;                // source bytes per lane
     static constexpr int NW = PER / 4;                       // dwords per lane
+    static constexpr int FLUSH = kFlushKeys / STEP;          // steps per accumulator flush
+    static_assert(WAVE_SRC <= TILE_SRC && TILE_SRC % WAVE_SRC == 0, "a wave stays in one tile");
+    static_assert(PER % 16 == 0 && FLUSH >= 1, "staging geometry");
 };
 
 template <int D, int C>
@@ -111,15 +118,17 @@ __global__ __launch_bounds__(64 * kWaves)
 __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, 8)))
 void prefill_kernel(PrefillParams p) {
     using S = Stage<D, C>;
+    constexpr int NB = S::NB;
+    constexpr int STEP = S::STEP;
     constexpr int NK = D / 32;             // 32-channel contraction slices of S
     constexpr int NT = D / 16;             // 16-channel output tiles of O
     constexpr int TL = S::TILE_LDS;
-    // a staged step in bf16: key tiles of blocks 0 and 1, then their value tiles
-    __shared__ __attribute__((aligned(16))) uint8_t sm_kv[2][4 * TL];
+    constexpr uint32_t kAllBlocks = (1u << NB) - 1;
+    // a staged step in bf16: key tiles of blocks 0..NB-1, then their value tiles
+    __shared__ __attribute__((aligned(16))) uint8_t sm_kv[2][2 * NB * TL];
 
     const int lane = threadIdx.x & 63;
-    // wave-uniform (a scalar register: block ids come from scalar loads, whose waits do not
-    // drain the vector loads in flight)
+    // wave-uniform (a scalar register, so that the staging addresses stay scalar)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;             // this lane's query column
     const int grp = lane >> 4;             // contraction group
@@ -156,8 +165,8 @@ void prefill_kernel(PrefillParams p) {
     const int64_t cwlast = (cw0 + kWaves * kCols <= ncols ? cw0 + kWaves * kCols : ncols) - 1;
     const int pwmin = L - nq + (int)(cw0 / G);
     const int kend = L - nq + (int)(cwlast / G) + 1;                  // exclusive, <= L
-    const int kfirst = pwmin >= 0 ? (lo_of(pwmin) / kStep) * kStep : 0;
-    const int nsteps = kend > kfirst ? (kend - kfirst + kStep - 1) / kStep : 0;
+    const int kfirst = pwmin >= 0 ? (lo_of(pwmin) / STEP) * STEP : 0;
+    const int nsteps = kend > kfirst ? (kend - kfirst + STEP - 1) / STEP : 0;
     const int64_t clast = wactive ? (c0 + kCols <= ncols ? c0 + kCols : ncols) - 1 : c0;
     const int pmin = L - nq + (int)(c0 / G);
     const int pmax = L - nq + (int)(clast / G);
@@ -182,34 +191,64 @@ void prefill_kernel(PrefillParams p) {
     const float sscale = p.score_scale * kscale;
     const ConstI32Ptr bt = (ConstI32Ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
 
-    // block c of the step at kb: valid id, or -1 (past the table, outside [0, num_blocks),
-    // or starting at or after kend)
-    auto block_of = [&](int kb, int c) {
-        const int n = kb / kBlockSize + c;
-        const int id = n < p.max_blocks_per_seq ? bt[n] : -1;
-        return (id >= 0 && id < p.num_blocks && kb + c * kBlockSize < kend) ? id : -1;
+    f32x4 oacc[NT], osum[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        oacc[t] = f32x4{};
+        osum[t] = f32x4{};
+    }
+    float mref = -INFINITY;                // running reference maximum of this column
+    float l_hi = 0.0f, l_lo = 0.0f;        // sum of this lane's share of the probabilities
+
+    if (nsteps > 0) {   // (then L >= 1, so the table and the cache hold at least one block)
+    // ---- block ids.  The NB raw ids of a step are read (scalar loads at clamped indices)
+    // one step before the step is staged, ahead of a barrier, so the loads never stall the
+    // matrix-core work; ok_mask turns them into a bit per block: a valid id (inside the
+    // table and [0, num_blocks)) whose first key lies before kend.
+    typedef int ids_t __attribute__((ext_vector_type(NB)));
+    auto load_ids = [&](int st) {
+        const int n0 = (kfirst + (st < nsteps ? st : 0) * STEP) / kBlockSize;
+        ids_t ids;
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+            const int n = n0 + c < p.max_blocks_per_seq ? n0 + c : p.max_blocks_per_seq - 1;
+            ids[c] = bt[n];
+        }
+        return ids;
+    };
+    auto ok_mask = [&](int st, ids_t ids) {
+        const int kb = kfirst + st * STEP;
+        uint32_t m = 0;
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+            const bool ok = kb / kBlockSize + c < p.max_blocks_per_seq && ids[c] >= 0 &&
+                            ids[c] < p.num_blocks && kb + c * kBlockSize < kend;
+            m |= ok ? 1u << c : 0u;
+        }
+        return m;
     };
 
-    // ---- staging: waves 2t, 2t+1 move tile t of a step (key block 0, key block 1, value
-    // block 0, value block 1), PER source bytes per lane.  The loads are always issued (a
-    // missing block or a step past the end reads block 0, in bounds) so that no branch sits
-    // between a load and its use; missing blocks become zeros and value slots at or past
-    // kend are zeroed when the piece is widened and written to LDS.
-    const int part = wave >> 1;                                   // 0..3
-    const int part_c = part & 1;
-    const bool part_v = part >= 2;
-    const int src_off = ((wave & 1) * 64 + lane) * S::PER;        // byte offset in the tile
+    // ---- staging: wave w moves source bytes [w*WAVE_SRC, +WAVE_SRC) of the step's tiles.
+    // The loads are always issued (a missing block reads block 0, in bounds) so that no
+    // branch sits between a load and its use; missing blocks become zeros and value slots
+    // at or past kend are zeroed when the piece is widened and written to LDS.
+    const int part = wave * S::WAVE_SRC / S::TILE_SRC;            // tile of the step
+    const int part_c = part % NB;
+    const bool part_v = part >= NB;
+    const int src_off = (wave * S::WAVE_SRC) % S::TILE_SRC + lane * S::PER;   // byte offset in the tile
     const uint8_t* part_src = static_cast<const uint8_t*>(part_v ? p.value_cache : p.key_cache);
     typedef uint32_t stage_t __attribute__((ext_vector_type(S::NW)));
-    auto stage_load = [&](int st, stage_t& r) {
-        const int kb = kfirst + (st < nsteps ? st : 0) * kStep;
-        const int id = block_of(kb, part_c);
-        const uint8_t* src = part_src + ((int64_t)(id >= 0 ? id : 0) * p.num_kv_heads + h) * S::TILE_SRC + src_off;
+    auto stage_load = [&](ids_t ids, uint32_t okm, stage_t& r) {
+        int id = ids[0];
+#pragma unroll
+        for (int c = 1; c < NB; ++c) id = part_c == c ? ids[c] : id;
+        id = (okm >> part_c) & 1u ? id : 0;
+        const uint8_t* src = part_src + ((int64_t)id * p.num_kv_heads + h) * S::TILE_SRC + src_off;
         r = __builtin_nontemporal_load(reinterpret_cast<const stage_t*>(src));
     };
-    auto stage_store = [&](int buf, int st, const stage_t& r) {
-        const int kb = kfirst + st * kStep;
-        const uint32_t okm = block_of(kb, part_c) >= 0 ? 0xFFFFFFFFu : 0u;
+    auto stage_store = [&](int buf, int st, uint32_t okmask, const stage_t& r) {
+        const int kb = kfirst + st * STEP;
+        const uint32_t okm = (okmask >> part_c) & 1u ? 0xFFFFFFFFu : 0u;
         uint8_t* dst = sm_kv[buf] + part * TL;
         constexpr int EPL = S::PER / S::ES;                       // elements per lane
         constexpr int DW8 = 2 * S::ES;                            // source dwords per 8 elements
@@ -249,16 +288,7 @@ void prefill_kernel(PrefillParams p) {
         }
     };
 
-    f32x4 oacc[NT], osum[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        oacc[t] = f32x4{};
-        osum[t] = f32x4{};
-    }
-    float mref = -INFINITY;                // running reference maximum of this column
-    float l_hi = 0.0f, l_lo = 0.0f;        // sum of this lane's share of the probabilities
     int flush = 0;
-
     // multiply the O rows (columns 4*grp + i) by their columns' factors
     auto rescale_rows = [&](float f) {
         float fr[4];
@@ -273,22 +303,16 @@ void prefill_kernel(PrefillParams p) {
             }
     };
 
-    // whether step st holds any key this wave's columns attend to
-    auto visible = [&](int st) {
-        const int kb = kfirst + st * kStep;
-        return st < nsteps && wactive && kb <= pmax && kb + kStep > lomin;
-    };
-
-    auto compute = [&](int st, int buf) {
-        if (!visible(st)) return;
-        const int kb = kfirst + st * kStep;
-        const bool bok0 = block_of(kb, 0) >= 0, bok1 = block_of(kb, 1) >= 0;
+    auto compute = [&](int st, int buf, uint32_t okmask) {
+        const int kb = kfirst + st * STEP;
+        // whether the step holds any key this wave's columns attend to
+        if (!(st < nsteps && wactive && kb <= pmax && kb + STEP > lomin)) return;
         const uint8_t* sk = sm_kv[buf];
 
         // ---- S = K.Q^T for each block: lane holds slots 4*grp + i of its column
-        f32x4 s[2];
+        f32x4 s[NB];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NB; ++c) {
             f32x4 a = f32x4{};
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
@@ -301,21 +325,22 @@ void prefill_kernel(PrefillParams p) {
 
         // ---- raw scores masked outside [clo, pos] and outside valid blocks; the base-2
         // scale (> 0) is applied to the maximum and inside the exponent's FMA
-        const bool edge = kb + kStep > pmin + 1 || kb < lomax || !bok0 || !bok1;
+        if (kb + STEP > pmin + 1 || kb < lomax || okmask != kAllBlocks) {
+            const int k0 = kb + 4 * grp;
+#pragma unroll
+            for (int c = 0; c < NB; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kp = k0 + c * kBlockSize + i;
+                    const bool ok = kp >= clo && kp <= pos && ((okmask >> c) & 1u);
+                    s[c][i] = ok ? s[c][i] : -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < NB; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = s[c][i];
-                if (edge) {
-                    const int kp = kb + c * kBlockSize + 4 * grp + i;
-                    const bool ok = kp >= clo && kp <= pos && (c == 0 ? bok0 : bok1);
-                    v = ok ? v : -INFINITY;
-                }
-                s[c][i] = v;
-                mx = fmaxf(mx, v);
-            }
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[c][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * sscale;
         // lazy reference move: only when a score exceeds it by 2^8 (or on the first keys)
@@ -332,35 +357,39 @@ void prefill_kernel(PrefillParams p) {
         const float mu = mref == -INFINITY ? 0.0f : mref;
 
         // ---- probabilities as a high (pf truncated to bf16, so pf - hi is exact) and a low
-        // bf16 term; element 4c + i is slot 4*grp + i of block c
-        bf16x8 pa, pb;
+        // bf16 term; pair r holds blocks 2r and 2r+1, element 4c' + i of it is slot
+        // 4*grp + i of block 2r + c'
+        bf16x8 pa[NB / 2], pb[NB / 2];
         float psum = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < NB; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][i], sscale, -mu));
                 const float hf = __uint_as_float(__float_as_uint(pf) & 0xFFFF0000u);
-                pa[4 * c + i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(pf) >> 16));
-                pb[4 * c + i] = (__bf16)(pf - hf);
+                pa[c / 2][4 * (c % 2) + i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(pf) >> 16));
+                pb[c / 2][4 * (c % 2) + i] = (__bf16)(pf - hf);
                 psum += pf;
             }
         comp_add(l_hi, l_lo, psum);
 
-        // ---- O += P.V: channel tile t, lane reads slots 4*grp .. +3 of both blocks (value
-        // slots past the context were zeroed when staged)
+        // ---- O += P.V: channel tile t, lane reads slots 4*grp .. +3 of both blocks of a
+        // pair (value slots past the context were zeroed when staged)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int ch = 16 * t + col;
-            const u32x2 v0 = *reinterpret_cast<const u32x2*>(sk + 2 * TL + lds_value(ch, 4 * grp));
-            const u32x2 v1 = *reinterpret_cast<const u32x2*>(sk + 3 * TL + lds_value(ch, 4 * grp));
-            const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
-            oacc[t] = mfma16(pa, vb, oacc[t]);
-            oacc[t] = mfma16(pb, vb, oacc[t]);
+#pragma unroll
+            for (int r = 0; r < NB / 2; ++r) {
+                const u32x2 v0 = *reinterpret_cast<const u32x2*>(sk + (NB + 2 * r) * TL + lds_value(ch, 4 * grp));
+                const u32x2 v1 = *reinterpret_cast<const u32x2*>(sk + (NB + 2 * r + 1) * TL + lds_value(ch, 4 * grp));
+                const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+                oacc[t] = mfma16(pa[r], vb, oacc[t]);
+                oacc[t] = mfma16(pb[r], vb, oacc[t]);
+            }
         }
 
         // ---- second level: move the matrix-core partial sums into fp32 registers
-        if (++flush == kFlushSteps) {
+        if (++flush == S::FLUSH) {
             flush = 0;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -371,23 +400,38 @@ void prefill_kernel(PrefillParams p) {
     };
 
     // ---- the pipeline: step s+2 is loaded into registers while step s is computed from
-    // one LDS buffer and step s+1 is written into the other; one barrier per step
+    // one LDS buffer and step s+1 is written into the other; one barrier per step.  The
+    // ids of step s+3 are read before that barrier.  The loop always runs both halves (a
+    // half past the last step computes nothing and fills a buffer no one reads), so its
+    // body has no early exit between a load and its use.
+    ids_t ids = load_ids(0);
+    const uint32_t ok0 = ok_mask(0, ids);
     stage_t ra, rb;
-    stage_load(0, ra);
-    stage_load(1, rb);
-    stage_store(0, 0, ra);
+    stage_load(ids, ok0, ra);
+    ids = load_ids(1);
+    uint32_t ok1 = ok_mask(1, ids);
+    stage_load(ids, ok1, rb);
+    ids = load_ids(2);                     // ids of step st + 2 at the top of the loop
+    stage_store(0, 0, ok0, ra);
+    uint32_t okc = ok0;                    // mask of step st
     __syncthreads();
     for (int st = 0; st < nsteps; st += 2) {
-        stage_load(st + 2, ra);
-        compute(st, 0);
-        stage_store(1, st + 1, rb);
+        uint32_t ok2 = ok_mask(st + 2, ids);
+        stage_load(ids, ok2, ra);
+        compute(st, 0, okc);
+        stage_store(1, st + 1, ok1, rb);
+        const ids_t ids_next = load_ids(st + 3);
         __syncthreads();
-        if (st + 1 >= nsteps) break;
-        stage_load(st + 3, rb);
-        compute(st + 1, 1);
-        stage_store(0, st + 2, ra);
+        const uint32_t ok3 = ok_mask(st + 3, ids_next);
+        stage_load(ids_next, ok3, rb);
+        compute(st + 1, 1, ok1);
+        stage_store(0, st + 2, ok2, ra);
+        ids = load_ids(st + 4);
         __syncthreads();
+        okc = ok2;
+        ok1 = ok3;
     }
+    }   // nsteps > 0
     if (!wactive) return;
 #pragma unroll
     for (int t = 0; t < NT; ++t) osum[t] += oacc[t];
