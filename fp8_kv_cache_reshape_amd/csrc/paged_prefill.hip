@@ -16,15 +16,15 @@
 // columns of a (sequence, kv head) are numbered token-major, head fastest, so the g heads
 // of one token -- which read the same keys -- sit side by side.  A workgroup of 8 waves
 // owns 128 consecutive columns of one (sequence, kv head), 16 per wave, and walks the keys
-// they need 32 tokens (two cache blocks) at a time.
+// they need one step at a time: 64 tokens (four cache blocks) for d <= 128, 32 for d = 256.
 //
-// Staging.  Each step's K and V tiles are loaded once per workgroup (two waves per tile),
+// Staging.  Each step's K and V tiles are loaded once per workgroup (spread over the waves),
 // widened to bf16 on the way (one-byte codes are a subset of bf16), and written into a
 // double-buffered LDS tile; the loads run two steps ahead in registers.  The matrix cores
 // then read bf16 operands straight from LDS, so no wave converts codes itself.  The LDS
 // tiles have their own order, chosen so that every operand read instruction covers
 // contiguous 256-byte runs (no bank conflicts): keys [group][slice][slot][8 channels],
-// values [16-channel tile][group][channel][4 slots].
+// values of a block pair [16-channel tile][group][channel][block][4 slots].
 //
 // Both products run on v_mfma_f32_16x16x32_bf16 (16 columns per wave keeps the two
 // accumulator levels and the query operand small enough for two waves per SIMD):
@@ -32,9 +32,9 @@
 //               Lane l (column l%16, group g = l/16) gets slots 4g..4g+3 of the block; the
 //               32-channel slice kk of group g is channels [g*d/4 + 8kk, +8) -- one 16-byte
 //               chunk of the key tile.
-//   O += P.V  : A = 16 columns x 32 keys, B = 32 keys x 16 channels.  Group g's contraction
-//               slot is slots 4g..4g+3 of both blocks: exactly the 8 probabilities the lane
-//               holds, and two 8-byte reads of a channel row of the value tiles.
+//   O += P.V  : A = 16 columns x 32 keys, B = 32 keys x 16 channels, per pair of blocks.
+//               Group g's contraction slot is slots 4g..4g+3 of both blocks of the pair:
+//               8 of the probabilities the lane holds, and one 16-byte LDS read.
 // Probabilities enter P.V as a high (truncated) and a low bf16 term.  Scores are kept in
 // base-2 units (k_scale log2(e)/sqrt(d) is applied inside the exponent's FMA); v_scale
 // multiplies the final normalisation.  The running maximum of a column only moves when a
@@ -69,6 +69,16 @@ __device__ inline void store_out(void* out, int out_f32, int64_t idx, float v) {
         static_cast<__bf16*>(out)[idx] = (__bf16)v;   // round to nearest even
 }
 
+// Maximum over the four lanes l, l^16, l^32, l^48 (the four contraction groups of a
+// column), with the VALU row swaps of gfx950: after a swap the two results hold the values
+// of lane l and its partner, in some order, so their maximum is the pair's.
+__device__ inline float max_over_groups(float m) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Compensated add (Knuth's TwoSum) of x into (hi, lo).
 __device__ inline void comp_add(float& hi, float& lo, float x) {
     const float s = hi + x;
@@ -88,10 +98,11 @@ __device__ constexpr int lds_key(int slot, int ch) {
     return ((g * (D / 32) + (ch % (D / 4)) / 8) * kBlockSize + (slot ^ ((4 * g) & 15))) * 16 + (ch % 8) * 2;
 }
 
-// LDS byte offset of value element (channel, slot) of a staged block: [tile t = ch/16]
-// [group = slot/4][channel % 16][slot % 4], bf16.
-__device__ constexpr int lds_value(int ch, int slot) {
-    return (((ch / 16) * 4 + slot / 4) * 16 + ch % 16) * 8 + (slot % 4) * 2;
+// LDS byte offset of value element (channel, slot) of block cb (0 or 1) of a staged block
+// pair: [tile t = ch/16][group = slot/4][channel % 16][cb][slot % 4], bf16 -- the 4 slots
+// of a group in both blocks of the pair are one 16-byte operand read.
+__device__ constexpr int lds_value(int ch, int slot, int cb) {
+    return ((((ch / 16) * 4 + slot / 4) * 16 + ch % 16) * 2 + cb) * 8 + (slot % 4) * 2;
 }
 
 // Staging geometry.  A step covers NB cache blocks (64 keys for d <= 128, 32 for d = 256,
@@ -249,7 +260,8 @@ void prefill_kernel(PrefillParams p) {
     auto stage_store = [&](int buf, int st, uint32_t okmask, const stage_t& r) {
         const int kb = kfirst + st * STEP;
         const uint32_t okm = (okmask >> part_c) & 1u ? 0xFFFFFFFFu : 0u;
-        uint8_t* dst = sm_kv[buf] + part * TL;
+        // keys: tile part; values: the pair region of blocks 2*(c/2), 2*(c/2)+1
+        uint8_t* dst = sm_kv[buf] + (part_v ? NB + 2 * (part_c / 2) : part) * TL;
         constexpr int EPL = S::PER / S::ES;                       // elements per lane
         constexpr int DW8 = 2 * S::ES;                            // source dwords per 8 elements
 #pragma unroll
@@ -282,8 +294,8 @@ void prefill_kernel(PrefillParams p) {
                 }
                 // slots slot0 .. slot0+7 of channel e0 / 16: two 4-slot groups
                 const int ch = e0 / kBlockSize;
-                *reinterpret_cast<u32x2*>(dst + lds_value(ch, slot0)) = u32x2{v[0], v[1]};
-                *reinterpret_cast<u32x2*>(dst + lds_value(ch, slot0 + 4)) = u32x2{v[2], v[3]};
+                *reinterpret_cast<u32x2*>(dst + lds_value(ch, slot0, part_c % 2)) = u32x2{v[0], v[1]};
+                *reinterpret_cast<u32x2*>(dst + lds_value(ch, slot0 + 4, part_c % 2)) = u32x2{v[2], v[3]};
             }
         }
     };
@@ -341,8 +353,7 @@ void prefill_kernel(PrefillParams p) {
         for (int c = 0; c < NB; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[c][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sscale;
+        mx = max_over_groups(mx) * sscale;
         // lazy reference move: only when a score exceeds it by 2^8 (or on the first keys)
         const bool move = mx > mref + kRescaleLog2;
         if (__ballot(move) != 0) {
@@ -380,9 +391,7 @@ void prefill_kernel(PrefillParams p) {
             const int ch = 16 * t + col;
 #pragma unroll
             for (int r = 0; r < NB / 2; ++r) {
-                const u32x2 v0 = *reinterpret_cast<const u32x2*>(sk + (NB + 2 * r) * TL + lds_value(ch, 4 * grp));
-                const u32x2 v1 = *reinterpret_cast<const u32x2*>(sk + (NB + 2 * r + 1) * TL + lds_value(ch, 4 * grp));
-                const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+                const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sk + (NB + 2 * r) * TL + lds_value(ch, 4 * grp, 0));
                 oacc[t] = mfma16(pa[r], vb, oacc[t]);
                 oacc[t] = mfma16(pb[r], vb, oacc[t]);
             }
