@@ -135,14 +135,13 @@ constexpr int kMergeLaneBatch = 16;
 // under the bf16 rounding of the output (the merge kernel, which takes up to kMaxSplits
 // partials, compensates its sums).
 //
-// Two passes over the quads with at most 2 * kMergeLaneBatch splits (group ratio 8 at
-// head_dim 128): each lane takes both of its quads at once -- every load of both is issued
-// before the first wait, unconditionally (absent splits read the last split and weigh 0) so
-// the compiler can count them -- one round trip instead of two.
-template <int D>
-__device__ void merge_two_quads(const DecodeParams& p, int64_t hq0, int NQ, int ns, float vsc) {
-    constexpr int Q = 2;
-    constexpr int S = kMergeLaneBatch;
+// Q passes over the quads with at most 2 * S splits (Q = 2, S = 16: group ratio 8 at
+// head_dim 128; Q = 4, S = 8: group ratio 8 at head_dim 256): each lane takes all Q of its
+// quads at once -- every load is issued before the first wait, unconditionally (absent
+// splits read the last split and weigh 0) so the compiler can count them -- one round trip
+// instead of Q.
+template <int D, int Q, int S>
+__device__ void merge_quads(const DecodeParams& p, int64_t hq0, int NQ, int ns, float vsc) {
     const int par = threadIdx.x & 1;
     float2 mv[Q][S];
     float4 xv[Q][S];
@@ -202,8 +201,14 @@ __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) 
     const int NQ = G * D / 4;                                  // channel quads of the group
     const int64_t hq0 = (int64_t)b * p.num_q_heads + (int64_t)h * G;
     if (NQ > 32 * kDecodeWaves && NQ <= 64 * kDecodeWaves && ns <= 2 * kMergeLaneBatch) {
-        merge_two_quads<D>(p, hq0, NQ, ns, vsc);
+        merge_quads<D, 2, kMergeLaneBatch>(p, hq0, NQ, ns, vsc);
         return;
+    }
+    if constexpr (D == 256) {   // one wave per SIMD: room for 4 x 8 partials per lane
+        if (NQ > 64 * kDecodeWaves && NQ <= 128 * kDecodeWaves && ns <= kMergeLaneBatch) {
+            merge_quads<D, 4, kMergeLaneBatch / 2>(p, hq0, NQ, ns, vsc);
+            return;
+        }
     }
     for (int q = threadIdx.x >> 1; q < NQ; q += 32 * kDecodeWaves) {   // lane pairs of the workgroup
         const int hh = q / (D / 4), c4 = q % (D / 4);
@@ -963,9 +968,12 @@ hipError_t launch_decode_partial(const DecodeParams& p, Codec codec, int head_di
 }
 
 bool fused_merge_fits(int group, int head_dim, int splits) {
-    // every lane reads at most kMergeLaneSplits splits, in at most two passes over the quads
+    // every lane reads at most kMergeLaneSplits splits, in at most two passes over the
+    // quads; at head_dim 256, four passes (one round trip) when a lane reads at most 8
     const int pairs = 64 * kDecodeWaves / 2;
-    return splits <= 2 * kMergeLaneSplits && group * head_dim / 4 <= 2 * pairs;
+    const int quads = group * head_dim / 4;
+    return (splits <= 2 * kMergeLaneSplits && quads <= 2 * pairs) ||
+           (head_dim == 256 && splits <= kMergeLaneBatch && quads <= 4 * pairs);
 }
 
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t s) {

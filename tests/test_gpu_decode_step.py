@@ -59,6 +59,16 @@ def test_step_split_counts(num_splits):
     _check_step(w, num_splits=num_splits, out_f32=True)
 
 
+# head_dim 256, group 8: up to 16 splits merge inside the kernel in one round trip (four
+# passes over the channel quads per lane); 17 splits queue the merge kernel
+@pytest.mark.parametrize("num_splits", [1, 3, 16, 17])
+@pytest.mark.parametrize("window", [0, 512])
+def test_step_d256_group8_merge(num_splits, window):
+    w = _mk(8, 1, 256, [5, 700, 4100, 16, 1500], cid=65, window=window)
+    say(f"decode_step d256 g8 splits={num_splits} window={window}")
+    _check_step(w, num_splits=num_splits, out_f32=True)
+
+
 @pytest.mark.parametrize("window", [1, 17, 128, 512])
 def test_step_windows(window):
     w = _mk(64, 8, 64, [1, 20, 200, 1100], cid=62, window=window)
