@@ -57,6 +57,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFlushSteps = 4;         // wave steps summed in the matrix-core accumulator
 constexpr float kRescaleLog2 = 8.0f;   // reference max moves only when a score exceeds it by 2^8
+#ifndef FP8KV_CLAIM_TAIL
+#define FP8KV_CLAIM_TAIL 2
+#endif
+constexpr int kClaimTail = FP8KV_CLAIM_TAIL;   // pool entries per workgroup claimed at the end
 
 __device__ inline f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -651,7 +655,7 @@ void decode_partial_kernel(DecodeParams p) {
     // after that step's loads, and read at the end of the next one.
     const bool dyn = claim != nullptr;
     const int slot_entries = np > wave ? (np - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
-    const int e_static = dyn ? max(3, slot_entries / ns - 2) : INT_MAX;
+    const int e_static = dyn ? max(3, slot_entries / ns - kClaimTail) : INT_MAX;
     int cur = writer ? nsteps - 1 : pool_step(split);
     int e_nxt = writer ? 0 : 1;                   // pool entry that `nxt` is
     int nxt = cur >= 0 ? pool_step(split + e_nxt * ns) : -1;

@@ -126,7 +126,7 @@ struct Stage {
 
 template <int D, int C>
 __global__ __launch_bounds__(64 * kWaves)
-__attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, 8)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams p) {
     using S = Stage<D, C>;
     constexpr int NB = S::NB;
@@ -321,6 +321,22 @@ void prefill_kernel(PrefillParams p) {
         if (!(st < nsteps && wactive && kb <= pmax && kb + STEP > lomin)) return;
         const uint8_t* sk = sm_kv[buf];
 
+        // ---- value operands of P.V (lane: slots 4*grp .. +3 of both blocks of a pair, channel
+        // 16t + col).  They do not depend on the scores: for d <= 128 (64 registers) they are
+        // read first, so their LDS latency hides behind S and the softmax; at d = 256 they
+        // would not fit beside the rest, and each is read just before its products.
+        auto read_v = [&](int t, int r) {
+            return *reinterpret_cast<const bf16x8*>(sk + (NB + 2 * r) * TL + lds_value(16 * t + col, 4 * grp, 0));
+        };
+        constexpr bool kEarlyV = D <= 128;
+        bf16x8 vb[kEarlyV ? NT : 1][NB / 2];
+        if constexpr (kEarlyV) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < NB / 2; ++r) vb[t][r] = read_v(t, r);
+        }
+
         // ---- S = K.Q^T for each block: lane holds slots 4*grp + i of its column
         f32x4 s[NB];
 #pragma unroll
@@ -384,16 +400,14 @@ void prefill_kernel(PrefillParams p) {
             }
         comp_add(l_hi, l_lo, psum);
 
-        // ---- O += P.V: channel tile t, lane reads slots 4*grp .. +3 of both blocks of a
-        // pair (value slots past the context were zeroed when staged)
+        // ---- O += P.V per channel tile (value slots past the context were zeroed when staged)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int ch = 16 * t + col;
 #pragma unroll
             for (int r = 0; r < NB / 2; ++r) {
-                const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sk + (NB + 2 * r) * TL + lds_value(ch, 4 * grp, 0));
-                oacc[t] = mfma16(pa[r], vb, oacc[t]);
-                oacc[t] = mfma16(pb[r], vb, oacc[t]);
+                const bf16x8 v = kEarlyV ? vb[kEarlyV ? t : 0][r] : read_v(t, r);
+                oacc[t] = mfma16(pa[r], v, oacc[t]);
+                oacc[t] = mfma16(pb[r], v, oacc[t]);
             }
         }
 
