@@ -89,13 +89,17 @@ __device__ inline void comp_add(float& hi, float& lo, float x) {
 }
 
 // LDS byte offset of key element (slot, channel) of a staged block: [group g = ch/(D/4)]
-// [slice kk = (ch % (D/4))/8][slot ^ 4g][channel % 8], bf16.  The XOR keeps each 16-slot
-// row a permutation (reads stay conflict-free) and spreads the staging stores, whose
-// lanes hold the same slot in different groups, over different banks.
+// [slice kk = (ch % (D/4))/8][slot ^ swz(g, kk)][channel % 8], bf16.  The XOR keeps each
+// 16-slot row a permutation, so the operand reads stay conflict-free; swz (bit 2: bit 1
+// of g ^ bit 0 of kk, bit 3: bit 0 ^ bit 1 of kk) gives the lanes of one staging store --
+// the same slot in different (group, slice) rows -- different banks, 8 and 16 lanes at a
+// time, at head_dim 128 and 256.
 template <int D>
 __device__ constexpr int lds_key(int slot, int ch) {
     const int g = ch / (D / 4);
-    return ((g * (D / 32) + (ch % (D / 4)) / 8) * kBlockSize + (slot ^ ((4 * g) & 15))) * 16 + (ch % 8) * 2;
+    const int kk = (ch % (D / 4)) / 8;
+    const int swz = 4 * (((g >> 1) ^ kk) & 1) + 8 * ((kk ^ (kk >> 1)) & 1);
+    return ((g * (D / 32) + kk) * kBlockSize + (slot ^ swz)) * 16 + (ch % 8) * 2;
 }
 
 // LDS byte offset of value element (channel, slot) of block cb (0 or 1) of a staged block
