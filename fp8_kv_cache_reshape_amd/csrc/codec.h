@@ -107,4 +107,40 @@ __device__ inline codec_bf16x8 codes8_to_bf16x8(uint32_t lo, uint32_t hi) {
     }
 }
 
+// ---- 8 one-byte codes (bytes of lo then hi, memory order) -> 8 fp16, exactly: every E4M3
+// value (|x| <= 448, steps >= 2^-9), every E5M2 value (E5M2 is fp16 with the low 8 bits
+// dropped) and every INT8 value is an fp16 value.
+typedef _Float16 codec_f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 codec_f16x2 __attribute__((ext_vector_type(2)));
+
+template <int C>
+__device__ inline codec_f16x8 codes8_to_f16x8(uint32_t lo, uint32_t hi) {
+    static_assert(C != kCodecBF16, "one-byte codecs only");
+    codec_f16x2 a, b, c, d;
+    if constexpr (C == kCodecINT8) {
+        const uint32_t src[2] = {lo, hi};
+        codec_f16x2 w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t v = src[k / 2] >> (16 * (k % 2));
+            const float f0 = (float)(int)(int8_t)v;              // exact
+            const float f1 = (float)(int)(int8_t)(v >> 8);
+            w[k] = codec_f16x2{(_Float16)f0, (_Float16)f1};      // exact (|x| <= 128)
+        }
+        a = w[0]; b = w[1]; c = w[2]; d = w[3];
+    } else if constexpr (C == kCodecE5M2) {
+        a = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(lo, 1.0f, false);
+        b = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(lo, 1.0f, true);
+        c = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(hi, 1.0f, false);
+        d = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(hi, 1.0f, true);
+    } else {
+        a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+        b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+        c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+        d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+    }
+    codec_f16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return r;
+}
+
 }  // namespace fp8kv

@@ -19,14 +19,15 @@
 // they need one step at a time: 64 tokens (four cache blocks) for d <= 128, 32 for d = 256.
 //
 // Staging.  Each step's K and V tiles are loaded once per workgroup (spread over the waves),
-// widened to bf16 on the way (one-byte codes are a subset of bf16), and written into a
-// double-buffered LDS tile; the loads run two steps ahead in registers.  The matrix cores
-// then read bf16 operands straight from LDS, so no wave converts codes itself.  The LDS
+// widened on the way -- keys to bf16, values to fp16 (bf16 for the bf16 cache); one-byte
+// codes are exact in both -- and written into a double-buffered LDS tile; the loads run
+// two steps ahead in registers.  The matrix cores then read their operands straight from
+// LDS, so no wave converts codes itself.  The LDS
 // tiles have their own order, chosen so that every operand read instruction covers
 // contiguous 256-byte runs (no bank conflicts): keys [group][slice][slot][8 channels],
 // values of a block pair [16-channel tile][group][channel][block][4 slots].
 //
-// Both products run on v_mfma_f32_16x16x32_bf16 (16 columns per wave keeps the two
+// Both products run on 16x16x32 matrix-core tiles (16 columns per wave keeps the two
 // accumulator levels and the query operand small enough for two waves per SIMD):
 //   S = K.Q^T per block : A = 16 key slots x 32 channels, B = 32 channels x 16 columns.
 //               Lane l (column l%16, group g = l/16) gets slots 4g..4g+3 of the block; the
@@ -35,7 +36,11 @@
 //   O += P.V  : A = 16 columns x 32 keys, B = 32 keys x 16 channels, per pair of blocks.
 //               Group g's contraction slot is slots 4g..4g+3 of both blocks of the pair:
 //               8 of the probabilities the lane holds, and one 16-byte LDS read.
-// Probabilities enter P.V as a high (truncated) and a low bf16 term.  Scores are kept in
+// S runs in bf16 (q is bf16).  With a one-byte cache P.V runs in fp16: each probability is
+// rounded once to fp16 (relative error <= 2^-12, eight times below a bf16 rounding), after
+// a 2^7 scaling that keeps small probabilities out of the fp16 subnormal range (the
+// normaliser carries the same factor).  With the bf16 cache, whose values are not fp16
+// values, probabilities enter P.V as a high (truncated) and a low bf16 term.  Scores are kept in
 // base-2 units (k_scale log2(e)/sqrt(d) is applied inside the exponent's FMA); v_scale
 // multiplies the final normalisation.  The running maximum of a column only moves when a
 // score exceeds it by 2^8, so the accumulators are rarely rescaled.
@@ -48,6 +53,7 @@ namespace fp8kv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -57,9 +63,13 @@ constexpr int kWaves = 8;
 constexpr int kCols = 16;                  // query columns per wave
 constexpr int kFlushKeys = 256;            // keys summed in the matrix-core accumulator
 constexpr float kRescaleLog2 = 8.0f;
+constexpr int kPShift = 7;                 // fp16 probabilities are scaled by 2^7 (<= 2^15)
 
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ inline void store_out(void* out, int out_f32, int64_t idx, float v) {
@@ -139,7 +149,11 @@ void prefill_kernel(PrefillParams p) {
     constexpr int NT = D / 16;             // 16-channel output tiles of O
     constexpr int TL = S::TILE_LDS;
     constexpr uint32_t kAllBlocks = (1u << NB) - 1;
-    // a staged step in bf16: key tiles of blocks 0..NB-1, then their value tiles
+    // P.V operands: fp16 for the one-byte codecs (their codes are exact fp16 values), bf16
+    // for the bf16 cache
+    constexpr bool kF16 = C != kCodecBF16;
+    using pv_t = std::conditional_t<kF16, f16x8, bf16x8>;
+    // a staged step: key tiles of blocks 0..NB-1 in bf16, then their value tiles (pv_t)
     __shared__ __attribute__((aligned(16))) uint8_t sm_kv[2][2 * NB * TL];
 
     const int lane = threadIdx.x & 63;
@@ -274,8 +288,10 @@ void prefill_kernel(PrefillParams p) {
             u32x4 v;
             if constexpr (C == kCodecBF16) {
                 v = u32x4{r[4 * j] & okm, r[4 * j + 1] & okm, r[4 * j + 2] & okm, r[4 * j + 3] & okm};
-            } else {
+            } else if (!part_v) {
                 v = __builtin_bit_cast(u32x4, codes8_to_bf16x8<C>(r[DW8 * j] & okm, r[DW8 * j + 1] & okm));
+            } else {
+                v = __builtin_bit_cast(u32x4, codes8_to_f16x8<C>(r[DW8 * j] & okm, r[DW8 * j + 1] & okm));
             }
             if (!part_v) {
                 // element e0 of the source key tile: invert the chunk layout to (slot, channel)
@@ -330,10 +346,10 @@ void prefill_kernel(PrefillParams p) {
         // read first, so their LDS latency hides behind S and the softmax; at d = 256 they
         // would not fit beside the rest, and each is read just before its products.
         auto read_v = [&](int t, int r) {
-            return *reinterpret_cast<const bf16x8*>(sk + (NB + 2 * r) * TL + lds_value(16 * t + col, 4 * grp, 0));
+            return *reinterpret_cast<const pv_t*>(sk + (NB + 2 * r) * TL + lds_value(16 * t + col, 4 * grp, 0));
         };
         constexpr bool kEarlyV = D <= 128;
-        bf16x8 vb[kEarlyV ? NT : 1][NB / 2];
+        pv_t vb[kEarlyV ? NT : 1][NB / 2];
         if constexpr (kEarlyV) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
@@ -387,19 +403,26 @@ void prefill_kernel(PrefillParams p) {
         }
         const float mu = mref == -INFINITY ? 0.0f : mref;
 
-        // ---- probabilities as a high (pf truncated to bf16, so pf - hi is exact) and a low
-        // bf16 term; pair r holds blocks 2r and 2r+1, element 4c' + i of it is slot
-        // 4*grp + i of block 2r + c'
-        bf16x8 pa[NB / 2], pb[NB / 2];
+        // ---- probabilities; pair r holds blocks 2r and 2r+1, element 4c' + i of it is slot
+        // 4*grp + i of block 2r + c'.  One-byte caches: one fp16 term, every probability
+        // (and the normaliser with it) scaled by 2^kPShift so that small ones stay normal
+        // fp16 numbers.  bf16 cache: a high (pf truncated to bf16, so pf - hi is exact) and
+        // a low bf16 term.
+        const float mus = kF16 ? mu - (float)kPShift : mu;
+        pv_t pa[NB / 2], pb[kF16 ? 1 : NB / 2];
         float psum = 0.0f;
 #pragma unroll
         for (int c = 0; c < NB; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][i], sscale, -mu));
-                const float hf = __uint_as_float(__float_as_uint(pf) & 0xFFFF0000u);
-                pa[c / 2][4 * (c % 2) + i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(pf) >> 16));
-                pb[c / 2][4 * (c % 2) + i] = (__bf16)(pf - hf);
+                const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][i], sscale, -mus));
+                if constexpr (kF16) {
+                    pa[c / 2][4 * (c % 2) + i] = (_Float16)pf;   // round to nearest even
+                } else {
+                    const float hf = __uint_as_float(__float_as_uint(pf) & 0xFFFF0000u);
+                    pa[c / 2][4 * (c % 2) + i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(pf) >> 16));
+                    pb[c / 2][4 * (c % 2) + i] = (__bf16)(pf - hf);
+                }
                 psum += pf;
             }
         comp_add(l_hi, l_lo, psum);
@@ -409,9 +432,9 @@ void prefill_kernel(PrefillParams p) {
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
             for (int r = 0; r < NB / 2; ++r) {
-                const bf16x8 v = kEarlyV ? vb[kEarlyV ? t : 0][r] : read_v(t, r);
+                const pv_t v = kEarlyV ? vb[kEarlyV ? t : 0][r] : read_v(t, r);
                 oacc[t] = mfma16(pa[r], v, oacc[t]);
-                oacc[t] = mfma16(pb[r], v, oacc[t]);
+                if constexpr (!kF16) oacc[t] = mfma16(pb[kF16 ? 0 : r], v, oacc[t]);
             }
         }
 

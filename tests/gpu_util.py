@@ -152,6 +152,8 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, atol=ATOL, rtol=RTOL, what=""
     err = np.abs(gpu - ref)
     bound = atol + rtol * np.abs(ref)
     bad = err > bound
+    if err.size:
+        say(f"{what}: max abs err {err.max():.3g}, worst err/bound {(err / bound).max():.3f}")
     if bad.any():
         idx = np.unravel_index(np.argmax(err - bound), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst at {idx}: "
