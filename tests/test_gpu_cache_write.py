@@ -143,3 +143,50 @@ def test_slot_patterns_bit_exact(pattern, cache, D):
     okc, ovc = oracle_write(w, layer)
     assert np.array_equal(to_host_bits(kc), okc), "key cache bytes differ"
     assert np.array_equal(to_host_bits(vc), ovc), "value cache bytes differ"
+
+
+def _bf16_bits(x: float) -> int:
+    b = int(np.array(x, np.float32).view(np.uint32))
+    assert b & 0xFFFF == 0, x                   # exactly a bf16 value
+    return b >> 16
+
+
+def test_quotients_near_rounding_boundaries():
+    """Scales s = x0 / m, and the floats either side of it, for every E4M3 rounding midpoint m
+    (and the saturation threshold 464): x0 / s lands on or a few binary32 steps from a
+    boundary of the cast, where the write's multiply-by-reciprocal shortcut must hand over to
+    the division.  Per-head scales give 8 key and 8 value scales per call; every byte must
+    equal the oracle's (correctly rounded division, then one cast)."""
+    Hkv, D, T = 8, 64, 16
+    vals = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = list((vals[:-1] + vals[1:]) / 2) + [464.0]
+    combos = []
+    for x0 in (1.5, 3.0, -0.3125, 7.0, 100.0):
+        for m in mids:
+            s0 = np.float32(abs(x0) / m)
+            for s in (s0, np.nextafter(s0, np.float32(0)), np.nextafter(s0, np.float32(np.inf))):
+                combos.append((x0, np.float32(s)))
+    rng = np.random.default_rng(31)
+    rng.shuffle(combos)
+    slots = np.arange(T, dtype=np.int64)
+    w = syn.Workload(name="boundaries", num_seqs=0, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D,
+                     block_size=16, num_blocks=1, context_lens=np.zeros(0, np.int32),
+                     block_tables=np.zeros((0, 1), np.int32), seq_offsets=np.zeros(1, np.int64),
+                     slot_mapping=slots, q=np.zeros((0, Hkv, D), np.uint16), layers=[])
+    say(f"cache_write boundaries: {len(combos)} scales")
+    sign = np.where(np.arange(D) % 2 == 0, 0, 0x8000).astype(np.uint16)   # alternate signs
+    for i in range(0, len(combos) - 2 * Hkv + 1, 2 * Hkv):
+        kx, ks = zip(*combos[i:i + Hkv])
+        vx, vs = zip(*combos[i + Hkv:i + 2 * Hkv])
+        keys = np.empty((T, Hkv, D), np.uint16)
+        vals_ = np.empty((T, Hkv, D), np.uint16)
+        for h in range(Hkv):
+            keys[:, h, :] = _bf16_bits(kx[h]) ^ sign
+            vals_[:, h, :] = _bf16_bits(vx[h]) ^ sign
+        layer = syn.Layer(k=keys, v=vals_, cache_dtype=syn.E4M3, k_scale=1.0, v_scale=1.0)
+        heads = (np.array(ks, np.float32), np.array(vs, np.float32))
+        kc, vc = dev_caches(w, E4M3)
+        gpu_write(w, layer, kc, vc, heads=heads)
+        okc, ovc = oracle_write(w, layer, heads=heads)
+        assert np.array_equal(to_host_bits(kc), okc), f"key bytes differ, scales {ks}"
+        assert np.array_equal(to_host_bits(vc), ovc), f"value bytes differ, scales {vs}"
