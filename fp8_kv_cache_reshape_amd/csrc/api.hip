@@ -20,6 +20,13 @@ using fp8kv::kMaxSplits;
 // (d 64, 8 x 20K) 35.2 us at 256 workgroups, 33.9 us at 512.
 inline int target_workgroups(int head_dim) { return head_dim <= 64 ? 512 : 256; }
 constexpr int kMinBlocksPerSplit = 16;    // one wave step (4 blocks) for each of 4 waves
+// Automatic planning keeps one split up to this many blocks per (sequence, kv head): a
+// 512-position window straddles at most 33 blocks, at most 3 wave steps per wave of one
+// workgroup.  A second split costs a merge -- the arrival count, then one round trip for
+// partials written on other XCDs -- measured at 2.5-4.6 us on such layers (d256 512-window
+// layer 13.1 us per step with one split, 17.7 with three), while at 64 blocks the best
+// count depends on the batch.
+constexpr int kSingleSplitBlocks = 2 * kMinBlocksPerSplit + 1;
 
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool cache_dtype_ok(int d) {
@@ -103,7 +110,7 @@ Plan make_plan(int num_seqs, int num_kv_heads, int head_dim, int max_context_len
     } else {
         const long long units = (long long)(num_seqs > 0 ? num_seqs : 1) * num_kv_heads;
         long long s = (target_workgroups(head_dim) + units - 1) / units;
-        if (s < 1) s = 1;
+        if (s < 1 || nb <= kSingleSplitBlocks) s = 1;
         if (s > nb) s = nb;
         bps = (int)((nb + s - 1) / s);
         bps = (bps + kMinBlocksPerSplit - 1) / kMinBlocksPerSplit * kMinBlocksPerSplit;

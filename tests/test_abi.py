@@ -163,6 +163,10 @@ def test_split_planning():
     assert ns(1, 8, 128, 16, 131072, 0, 0) * 8 >= 256        # B=1 long context: a workgroup per CU
     assert ns(1, 8, 128, 16, 131072, 0, 16) == 16            # requested count
     assert ns(8, 8, 64, 16, 20480, 128, 0) == 1              # 128-token window: one split
+    assert ns(16, 1, 256, 16, 65536, 512, 0) == 1            # 512-token window (33 blocks): one split
+    assert ns(1, 8, 128, 16, 528, 0, 0) == 1                 # 33 blocks of context: one split
+    assert ns(1, 8, 128, 16, 529, 0, 0) > 1                  # 34 blocks: split
+    assert ns(16, 1, 256, 16, 65536, 1024, 0) > 1            # 1024-token window (65 blocks)
     assert ns(8, 8, 64, 16, 20480, 0, 0) == 8                # head_dim 64: two workgroups per CU
     assert ns(4, 8, 128, 16, 0, 0, 0) == 1                   # empty contexts
     assert ns(1, 1, 256, 16, 65536, 0, 4) == 4
