@@ -366,6 +366,7 @@ def cpu_baseline(w, layer, pairs_kv_heads: int = 2) -> dict:
     """The oracle (plain C, fp64, single thread) on a bounded sample of the same workload:
     every query head of the first `pairs_kv_heads` KV heads over the full context."""
     import oracle
+    pairs_kv_heads = min(pairs_kv_heads, w.num_kv_heads)
     okc = np.zeros(w.num_blocks * w.num_kv_heads * BLOCK * w.head_dim, np.uint8)
     ovc = np.zeros_like(okc)
     oracle.cache_write(layer.k, layer.v, okc, ovc, oracle.CACHE_E4M3, w.slot_mapping, w.num_kv_heads,
@@ -395,9 +396,11 @@ def cpu_baseline(w, layer, pairs_kv_heads: int = 2) -> dict:
                                    layer.sliding_window)["pass1"]
     return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 3),
-            "sample": f"fp64 C oracle decode of query heads 0..{len(pairs) - 1} (KV heads 0..{pairs_kv_heads - 1} "
-                      f"of {w.num_kv_heads}) over the full {int(w.context_lens[0])}-token context, single thread; "
-                      f"GB/s = the sample's algorithmic KV+q+table bytes / time",
+            "sample": f"fp64 C oracle decode of query heads 0..{pairs_kv_heads * g - 1} (KV heads "
+                      f"0..{pairs_kv_heads - 1} of {w.num_kv_heads}) of each of the {w.num_seqs} sequences over "
+                      f"its whole window (contexts {int(w.context_lens.min())}..{int(w.context_lens.max())}, "
+                      f"window {layer.sliding_window}), single thread; GB/s = the sample's algorithmic "
+                      f"KV+q+table bytes / time",
             "multi_thread": {"value": round(full_bytes / dt_mt / 1e9, 4), "unit": "GB/s", "cores": threads,
                              "seconds": round(dt_mt, 3), "ms_per_step": round(dt_mt * 1e3, 1),
                              "sample": f"every query head ({len(all_pairs)} (sequence, head) tasks) of the "

@@ -53,3 +53,13 @@ def test_algorithmic_bytes_per_step():
 
 def test_gpus_above_one_exits():
     assert bench.main(["--gpus", "2"]) == 2
+
+
+def test_cpu_baseline_with_one_kv_head():
+    """The oracle sample takes at most the workload's kv heads (the tiny shape has one)."""
+    import synthetic as syn
+    w = syn.tiny()
+    r = bench.cpu_baseline(w, w.layers[0])
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
+    assert "query heads 0..3 (KV heads 0..0 of 1)" in r["sample"]
+    assert r["multi_thread"]["value"] > 0
