@@ -346,9 +346,12 @@ int fp8kv_decode_step_per_head(void* out, int out_dtype, const void* query,
  *   out = sum_j exp(s_j - max s) V_j / sum_j exp(s_j - max s);   out = 0 if p < 0.
  * K_j and V_j as in fp8kv_paged_decode.  The chunk's own K/V must already be in the cache
  * (fp8kv_cache_write first, on the same stream).  Arithmetic: S = K.Q^T and O = P.V on
- * the matrix cores (bf16 operands, fp32 accumulation); probabilities enter P.V as the sum
- * of two bf16 values (about 16 significant bits); the matrix-core accumulator holds at most
- * 256 keys before its sums move into fp32 registers.
+ * the matrix cores with fp32 accumulation.  S takes bf16 operands.  With a one-byte cache
+ * P.V takes fp16 operands: the codes are exact fp16 values and each probability is
+ * rounded once to fp16 (11 significant bits); with the bf16 cache P.V takes bf16 operands
+ * and each probability enters as the sum of two bf16 values (about 16 significant bits).
+ * The matrix-core accumulator holds at most 256 keys before its sums move into fp32
+ * registers.
  *
  *   out              device [num_query_tokens][num_q_heads][head_dim] of out_dtype
  *   query            device bf16 [num_query_tokens][num_q_heads][head_dim]
