@@ -267,7 +267,7 @@ void prefill_kernel(PrefillParams p) {
     const int src_off = (wave * S::WAVE_SRC) % S::TILE_SRC + lane * S::PER;   // byte offset in the tile
     const uint8_t* part_src = static_cast<const uint8_t*>(part_v ? p.value_cache : p.key_cache);
     typedef uint32_t stage_t __attribute__((ext_vector_type(S::NW)));
-    auto stage_load = [&](ids_t ids, uint32_t okm, stage_t& r) {
+    auto stage_load = [&](ids_t ids, uint32_t okm, stage_t& r) __attribute__((always_inline)) {
         int id = ids[0];
 #pragma unroll
         for (int c = 1; c < NB; ++c) id = part_c == c ? ids[c] : id;
@@ -275,7 +275,7 @@ void prefill_kernel(PrefillParams p) {
         const uint8_t* src = part_src + ((int64_t)id * p.num_kv_heads + h) * S::TILE_SRC + src_off;
         r = __builtin_nontemporal_load(reinterpret_cast<const stage_t*>(src));
     };
-    auto stage_store = [&](int buf, int st, uint32_t okmask, const stage_t& r) {
+    auto stage_store = [&](int buf, int st, uint32_t okmask, const stage_t& r) __attribute__((always_inline)) {
         const int kb = kfirst + st * STEP;
         const uint32_t okm = (okmask >> part_c) & 1u ? 0xFFFFFFFFu : 0u;
         // keys: tile part; values: the pair region of blocks 2*(c/2), 2*(c/2)+1
@@ -322,7 +322,7 @@ void prefill_kernel(PrefillParams p) {
 
     int flush = 0;
     // multiply the O rows (columns 4*grp + i) by their columns' factors
-    auto rescale_rows = [&](float f) {
+    auto rescale_rows = [&](float f) __attribute__((always_inline)) {
         float fr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) fr[i] = __shfl(f, 4 * grp + i);
@@ -335,7 +335,7 @@ void prefill_kernel(PrefillParams p) {
             }
     };
 
-    auto compute = [&](int st, int buf, uint32_t okmask) {
+    auto compute = [&](int st, int buf, uint32_t okmask) __attribute__((always_inline)) {
         const int kb = kfirst + st * STEP;
         // whether the step holds any key this wave's columns attend to
         if (!(st < nsteps && wactive && kb <= pmax && kb + STEP > lomin)) return;
@@ -465,22 +465,34 @@ void prefill_kernel(PrefillParams p) {
     stage_store(0, 0, ok0, ra);
     uint32_t okc = ok0;                    // mask of step st
     __syncthreads();
-    for (int st = 0; st < nsteps; st += 2) {
-        uint32_t ok2 = ok_mask(st + 2, ids);
-        stage_load(ids, ok2, ra);
-        compute(st, 0, okc);
-        stage_store(1, st + 1, ok1, rb);
-        const ids_t ids_next = load_ids(st + 3);
-        __syncthreads();
-        const uint32_t ok3 = ok_mask(st + 3, ids_next);
-        stage_load(ids_next, ok3, rb);
-        compute(st + 1, 1, ok1);
-        stage_store(0, st + 2, ok2, ra);
-        ids = load_ids(st + 4);
-        __syncthreads();
-        okc = ok2;
-        ok1 = ok3;
-    }
+    // Waves 4-7 stage the next step before computing this one, waves 0-3 after it.  Both
+    // orders are legal between two barriers (the staged buffer is not the one being computed
+    // from).  Waves w and w + 4 share a SIMD, so one's staging (vector ALU work) runs beside
+    // the other's S products, and its P.V products beside the other's staging.  The loop is
+    // written out once per order (E), so that no branch sits inside it.
+    auto run = [&](auto stage_first) __attribute__((always_inline)) {
+        constexpr bool E = decltype(stage_first)::value;
+        for (int st = 0; st < nsteps; st += 2) {
+            uint32_t ok2 = ok_mask(st + 2, ids);
+            stage_load(ids, ok2, ra);
+            if constexpr (E) stage_store(1, st + 1, ok1, rb);
+            compute(st, 0, okc);
+            if constexpr (!E) stage_store(1, st + 1, ok1, rb);
+            const ids_t ids_next = load_ids(st + 3);
+            __syncthreads();
+            const uint32_t ok3 = ok_mask(st + 3, ids_next);
+            stage_load(ids_next, ok3, rb);
+            if constexpr (E) stage_store(0, st + 2, ok2, ra);
+            compute(st + 1, 1, ok1);
+            if constexpr (!E) stage_store(0, st + 2, ok2, ra);
+            ids = load_ids(st + 4);
+            __syncthreads();
+            okc = ok2;
+            ok1 = ok3;
+        }
+    };
+    if (wave >= kWaves / 2) run(std::true_type{});
+    else run(std::false_type{});
     }   // nsteps > 0
     if (!wactive) return;
 #pragma unroll
