@@ -130,3 +130,15 @@ def test_step_headline_128k():
     w = syn.llama8b_long(131072, "amax")
     say(f"decode_step {w.name}")
     _check_step(w)
+
+
+@pytest.mark.parametrize("L,window", [(528, 0), (529, 0), (4000, 512), (4000, 513)])
+def test_step_at_single_split_threshold(L, window):
+    """The planner keeps one split up to 33 blocks per (sequence, kv head) and splits beyond:
+    both sides of that threshold (context and window) against the oracle."""
+    w = _mk(32, 8, 128, [L, L - 7, 16], cid=66, window=window)
+    ns = F.fp8kv_paged_decode_num_splits(w.num_seqs, w.num_kv_heads, w.head_dim, 16,
+                                         w.max_context_len, window, 0)
+    assert (ns == 1) == ((L <= 528) if window == 0 else (window <= 512))
+    say(f"decode_step threshold L={L} window={window} splits={ns}")
+    _check_step(w, out_f32=True)
