@@ -11,7 +11,8 @@
 // key load instruction of the decode kernel reads whole 256-byte runs of a tile.
 //
 // One thread handles 8 consecutive channels of 4 consecutive input tokens of one kv head:
-// four 16-byte bf16 loads per tensor, 64 f32 divisions, then the stores.  When the four
+// four 16-byte bf16 loads per tensor, 64 f32 divisions (multiplies when both scales are
+// powers of two, with the same result), then the stores.  When the four
 // tokens go to four consecutive slots starting at a multiple of 4 (what a prefill or any
 // in-order write of a sequence produces, except at its two ends) the four value bytes of
 // one channel are adjacent in the channel-major tile: a 4 x 8 byte transpose in registers
@@ -57,6 +58,27 @@ __device__ inline uint32_t dword(const u32x4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// A scale that is a power of two, s = 2^k with s normal, has an exact reciprocal (2^-k,
+// possibly subnormal), so x * (1 / s) and x / s are the same real number and IEEE
+// rounding gives the same binary32 result, overflow and underflow included: the codes can
+// be formed with a multiply.  Other scales take the division.
+__device__ inline bool exact_reciprocal(float s) {
+    const uint32_t b = __float_as_uint(s);
+    return (b & 0x007FFFFFu) == 0 && (b & 0x7F800000u) != 0 && (b & 0x7F800000u) != 0x7F800000u;
+}
+
+// Eight bf16 (as 4 dwords) multiplied by the exact reciprocal of a power-of-two scale and
+// cast: the same 8 codes as quantize8 with that scale.
+template <int C>
+__device__ inline uint2 quantize8_pow2(uint4 x, float rcp) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        c[k] = pack2<C>(bf16_bits_to_f32(w[k] & 0xFFFFu) * rcp, bf16_bits_to_f32(w[k] >> 16) * rcp);
+    return make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
+}
+
 template <int D, int C>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
     constexpr bool FP8 = C != kCodecBF16;         // one-byte codes (E4M3, E5M2 or INT8)
@@ -95,10 +117,19 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
         const float ks = p.k_scales != nullptr ? p.k_scales[h] : p.k_scale;
         const float vs = p.v_scales != nullptr ? p.v_scales[h] : p.v_scale;
         uint2 qk[4], qv[4];
+        if (exact_reciprocal(ks) && exact_reciprocal(vs)) {
+            const float rk = 1.0f / ks, rv = 1.0f / vs;   // exact
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            qk[k] = quantize8<C>(make_uint4(xk[k].x, xk[k].y, xk[k].z, xk[k].w), ks);
-            qv[k] = quantize8<C>(make_uint4(xv[k].x, xv[k].y, xv[k].z, xv[k].w), vs);
+            for (int k = 0; k < 4; ++k) {
+                qk[k] = quantize8_pow2<C>(make_uint4(xk[k].x, xk[k].y, xk[k].z, xk[k].w), rk);
+                qv[k] = quantize8_pow2<C>(make_uint4(xv[k].x, xv[k].y, xv[k].z, xv[k].w), rv);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                qk[k] = quantize8<C>(make_uint4(xk[k].x, xk[k].y, xk[k].z, xk[k].w), ks);
+                qv[k] = quantize8<C>(make_uint4(xv[k].x, xv[k].y, xv[k].z, xv[k].w), vs);
+            }
         }
         if (fast) {
             const int64_t blk = sl[0] / kBlockSize;
