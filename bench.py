@@ -638,6 +638,11 @@ PREFILL_WORKLOADS = {
     "d256-8k": (lambda syn: syn.make_workload("d256-b1-L8192", 5, num_q_heads=8, num_kv_heads=1,
                                               head_dim=256, context_lens=[8192], std=0.5),
                 8192),
+    "gptoss-8k": (lambda syn: syn.make_workload("gptoss-b1-L8192", 4, num_q_heads=64, num_kv_heads=8,
+                                                head_dim=64, context_lens=[8192]), 8192),
+    "gptoss-8k-sw128": (lambda syn: syn.make_workload("gptoss-b1-L8192-sw128", 4, num_q_heads=64,
+                                                      num_kv_heads=8, head_dim=64, context_lens=[8192],
+                                                      layers=(("sw128", 128, syn.E4M3),)), 8192),
 }
 
 
@@ -660,7 +665,7 @@ def prefill_bench(F, torch, syn, name: str, args) -> dict:
     w = build(syn)
     layer = w.layers[0]
     pq = syn.prefill_queries(w, [chunk] * w.num_seqs, 170)
-    flops = prefill_flops(w.context_lens, pq.chunk_lens, w.num_q_heads, w.head_dim)
+    flops = prefill_flops(w.context_lens, pq.chunk_lens, w.num_q_heads, w.head_dim, layer.sliding_window)
     dev = "cuda"
     u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
     q, qsl = u16(pq.q), torch.from_numpy(pq.query_start_loc).to(dev)
@@ -672,7 +677,8 @@ def prefill_bench(F, torch, syn, name: str, args) -> dict:
     n = w.num_blocks * Hkv * BLOCK * D
     out = torch.empty(pq.num_tokens * Hq * D, dtype=torch.bfloat16, device=dev)
     res = {"metric": "prefill attention over the paged cache: TFLOP/s (% of bf16 MFMA peak)",
-           "workload": f"{name}: {w.name}, chunk {chunk}, Hq {Hq}, Hkv {Hkv}, d {D}",
+           "workload": f"{name}: {w.name}, chunk {chunk}, Hq {Hq}, Hkv {Hkv}, d {D}, "
+                       f"window {layer.sliding_window}",
            "flops_per_call": flops}
     launches = 20
     for cache in args.prefill_caches.split(","):
@@ -687,7 +693,7 @@ def prefill_bench(F, torch, syn, name: str, args) -> dict:
         def call():
             F.fp8kv_paged_prefill(out, F.FP8KV_BF16, q, qsl, kc, vc, cdt, bt, w.max_blocks_per_seq,
                                   cl, w.max_context_len, w.num_seqs, pq.max_query_len, Hq, Hkv, D,
-                                  BLOCK, w.num_blocks, ks, vs, 0)
+                                  BLOCK, w.num_blocks, ks, vs, layer.sliding_window)
         for _ in range(3):
             call()
         torch.cuda.synchronize()
