@@ -30,29 +30,36 @@ FP8KV_INT8 = 4
 
 BLOCK_SIZE = 16
 
+# bits of the device error word (fp8kv_set_error_word)
+FP8KV_DEVERR_BLOCK_ID = 1
+FP8KV_DEVERR_SLOT = 2
+FP8KV_DEVERR_CONTEXT_LEN = 4
+FP8KV_DEVERR_QUERY_LEN = 8
+
 # Every symbol include/fp8kv.h declares, with its ctypes signature.
 _P, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "fp8kv_status_string": (ctypes.c_char_p, [_I]),
     "fp8kv_version": (_I, []),
     "fp8kv_last_hip_error": (ctypes.c_char_p, []),
+    "fp8kv_set_error_word": (_I, [_P]),
+    "fp8kv_decode_counters_size": (_SZ, [_I, _I]),
     "fp8kv_cache_write": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _F, _P]),
     "fp8kv_cache_write_per_head": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "fp8kv_paged_decode_num_splits": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "fp8kv_paged_decode_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "fp8kv_paged_decode": (_I, [_P, _I, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
-                                _F, _F, _I, _I, _P, _SZ, _P]),
+                                _F, _F, _I, _I, _P, _SZ, _P, _SZ, _P]),
     "fp8kv_paged_decode_per_head": (_I, [_P, _I, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I,
-                                         _I, _I, _P, _P, _I, _I, _P, _SZ, _P]),
+                                         _I, _I, _P, _P, _I, _I, _P, _SZ, _P, _SZ, _P]),
     "fp8kv_paged_decode_partial": (_I, [_P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
                                         _F, _I, _I, _P, _SZ, _P]),
     "fp8kv_paged_decode_merge": (_I, [_P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P,
                                       _SZ, _P]),
-    "fp8kv_decode_step_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "fp8kv_decode_step": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I,
-                               _I, _F, _F, _I, _I, _P, _SZ, _P]),
+                               _I, _F, _F, _I, _I, _P, _SZ, _P, _SZ, _P]),
     "fp8kv_decode_step_per_head": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I,
-                                        _I, _I, _I, _I, _P, _P, _I, _I, _P, _SZ, _P]),
+                                        _I, _I, _I, _I, _P, _P, _I, _I, _P, _SZ, _P, _SZ, _P]),
     "fp8kv_paged_prefill": (_I, [_P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I,
                                  _I, _I, _F, _F, _I, _P]),
     "fp8kv_paged_prefill_per_head": (_I, [_P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
@@ -125,6 +132,14 @@ def fp8kv_last_hip_error() -> str:
     return lib.fp8kv_last_hip_error().decode()
 
 
+def fp8kv_set_error_word(word) -> int:
+    return _check(lib.fp8kv_set_error_word(_addr(word)), "fp8kv_set_error_word")
+
+
+def fp8kv_decode_counters_size(max_num_seqs, num_kv_heads) -> int:
+    return int(lib.fp8kv_decode_counters_size(max_num_seqs, num_kv_heads))
+
+
 def fp8kv_cache_write(key, value, key_cache, value_cache, cache_dtype, slot_mapping, num_tokens,
                       num_kv_heads, head_dim, block_size, num_blocks, k_scale, v_scale,
                       stream=None) -> int:
@@ -162,13 +177,15 @@ def fp8kv_paged_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_
 def fp8kv_paged_decode(out, out_dtype, query, key_cache, value_cache, cache_dtype, block_tables,
                        max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
                        num_kv_heads, head_dim, block_size, num_blocks, k_scale, v_scale,
-                       sliding_window, num_splits, workspace, workspace_bytes, stream=None) -> int:
+                       sliding_window, num_splits, counters, counters_bytes, workspace,
+                       workspace_bytes, stream=None) -> int:
     return _check(lib.fp8kv_paged_decode(_addr(out), out_dtype, _addr(query), _addr(key_cache),
                                          _addr(value_cache), cache_dtype, _addr(block_tables),
                                          max_blocks_per_seq, _addr(context_lens), max_context_len,
                                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                          num_blocks, k_scale, v_scale, sliding_window, num_splits,
-                                         _addr(workspace), workspace_bytes, _stream(stream)),
+                                         _addr(counters), counters_bytes, _addr(workspace),
+                                         workspace_bytes, _stream(stream)),
                   "fp8kv_paged_decode")
 
 
@@ -176,14 +193,16 @@ def fp8kv_paged_decode_per_head(out, out_dtype, query, key_cache, value_cache, c
                                 block_tables, max_blocks_per_seq, context_lens, max_context_len,
                                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 num_blocks, k_scales, v_scales, sliding_window, num_splits,
-                                workspace, workspace_bytes, stream=None) -> int:
+                                counters, counters_bytes, workspace, workspace_bytes,
+                                stream=None) -> int:
     return _check(lib.fp8kv_paged_decode_per_head(_addr(out), out_dtype, _addr(query),
                                                   _addr(key_cache), _addr(value_cache), cache_dtype,
                                                   _addr(block_tables), max_blocks_per_seq,
                                                   _addr(context_lens), max_context_len, num_seqs,
                                                   num_q_heads, num_kv_heads, head_dim, block_size,
                                                   num_blocks, _addr(k_scales), _addr(v_scales),
-                                                  sliding_window, num_splits, _addr(workspace),
+                                                  sliding_window, num_splits, _addr(counters),
+                                                  counters_bytes, _addr(workspace),
                                                   workspace_bytes, _stream(stream)),
                   "fp8kv_paged_decode_per_head")
 
@@ -214,25 +233,19 @@ def fp8kv_paged_decode_merge(out, out_dtype, context_lens, max_context_len, max_
                   "fp8kv_paged_decode_merge")
 
 
-def fp8kv_decode_step_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                     max_context_len, sliding_window, num_splits) -> int:
-    return int(lib.fp8kv_decode_step_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                    block_size, max_context_len, sliding_window,
-                                                    num_splits))
-
-
 def fp8kv_decode_step(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
                       cache_dtype, block_tables, max_blocks_per_seq, context_lens,
                       max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                      num_blocks, k_scale, v_scale, sliding_window, num_splits, workspace,
-                      workspace_bytes, stream=None) -> int:
+                      num_blocks, k_scale, v_scale, sliding_window, num_splits, counters,
+                      counters_bytes, workspace, workspace_bytes, stream=None) -> int:
     return _check(lib.fp8kv_decode_step(_addr(out), out_dtype, _addr(query), _addr(key_new),
                                         _addr(value_new), _addr(key_cache), _addr(value_cache),
                                         cache_dtype, _addr(block_tables), max_blocks_per_seq,
                                         _addr(context_lens), max_context_len, num_seqs,
                                         num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                                         k_scale, v_scale, sliding_window, num_splits,
-                                        _addr(workspace), workspace_bytes, _stream(stream)),
+                                        _addr(counters), counters_bytes, _addr(workspace),
+                                        workspace_bytes, _stream(stream)),
                   "fp8kv_decode_step")
 
 
@@ -240,7 +253,8 @@ def fp8kv_decode_step_per_head(out, out_dtype, query, key_new, value_new, key_ca
                                cache_dtype, block_tables, max_blocks_per_seq, context_lens,
                                max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                block_size, num_blocks, k_scales, v_scales, sliding_window,
-                               num_splits, workspace, workspace_bytes, stream=None) -> int:
+                               num_splits, counters, counters_bytes, workspace, workspace_bytes,
+                               stream=None) -> int:
     return _check(lib.fp8kv_decode_step_per_head(_addr(out), out_dtype, _addr(query),
                                                  _addr(key_new), _addr(value_new),
                                                  _addr(key_cache), _addr(value_cache), cache_dtype,
@@ -248,7 +262,8 @@ def fp8kv_decode_step_per_head(out, out_dtype, query, key_new, value_new, key_ca
                                                  _addr(context_lens), max_context_len, num_seqs,
                                                  num_q_heads, num_kv_heads, head_dim, block_size,
                                                  num_blocks, _addr(k_scales), _addr(v_scales),
-                                                 sliding_window, num_splits, _addr(workspace),
+                                                 sliding_window, num_splits, _addr(counters),
+                                                 counters_bytes, _addr(workspace),
                                                  workspace_bytes, _stream(stream)),
                   "fp8kv_decode_step_per_head")
 

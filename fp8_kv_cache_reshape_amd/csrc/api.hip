@@ -134,27 +134,31 @@ WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int head_dim, in
     return l;
 }
 
-// The fused decode step keeps its counters at the start of its workspace (a fixed place,
-// whatever split plan a call uses): one arrival counter per (sequence, kv head), padded to
-// 256 bytes, then one step claim counter per (sequence, kv head, wave) every 256 bytes.
-// The split partials follow.
-size_t arrival_bytes(int num_seqs, int num_kv_heads) {
-    return ((size_t)num_seqs * num_kv_heads * sizeof(unsigned int) + 255) / 256 * 256;
-}
-static_assert(fp8kv::kDecodeWaves * fp8kv::kClaimStride * sizeof(unsigned int) == 1024,
-              "the public header documents 1024 claim-counter bytes per (sequence, kv head)");
-size_t step_counter_bytes(int num_seqs, int num_kv_heads) {
-    return arrival_bytes(num_seqs, num_kv_heads) +
-           (size_t)num_seqs * num_kv_heads * fp8kv::kDecodeWaves * fp8kv::kClaimStride * sizeof(unsigned int);
+// The counter buffer holds one record per (sequence, kv head) group, group b*Hkv + h at
+// byte (b*Hkv + h) * kCounterRecordBytes: the split arrival counter and one step-claim
+// counter per decode wave, each in a 256-byte line of its own.
+constexpr size_t kCounterRecordBytes = fp8kv::kCounterRecordWords * sizeof(unsigned int);
+static_assert(kCounterRecordBytes == 1280, "the public header documents 1280-byte counter records");
+
+size_t counter_bytes(int num_seqs, int num_kv_heads) {
+    return (size_t)num_seqs * num_kv_heads * kCounterRecordBytes;
 }
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
+// device error word of the calling thread's launches (fp8kv_set_error_word), or null
+thread_local unsigned int* g_error_word = nullptr;
 
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return FP8KV_OK;
     g_last_hip_error = e;
     return FP8KV_ERR_HIP;
 }
+
+}  // namespace
+
+void fp8kv::record_hip_error(hipError_t e) { g_last_hip_error = e; }
+
+namespace {
 
 // Shared validation and parameter setup of the decode entry points.
 int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const void* key_cache,
@@ -221,9 +225,28 @@ int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const voi
     p.k_scale_q = 1.0f;
     p.v_scale_q = 1.0f;
     p.counters = nullptr;
-    p.claims = nullptr;
+    p.use_claims = 0;
     p.merge_in_kernel = 0;
+    p.err = g_error_word;
     return FP8KV_OK;
+}
+
+// Attach the caller's counter buffer to a decode with several splits: the last workgroup of
+// each (sequence, kv head) merges the partials inside the decode kernel when one workgroup
+// merges a group cheaply (else the merge kernel still runs), and with the automatic split
+// plan the last steps of each group are claimed at run time.  Returns whether the merge is
+// fused, or a negative status for a buffer that is too small or misaligned.
+int attach_counters(fp8kv::DecodeParams& p, int head_dim, void* counters, size_t counters_bytes,
+                    int num_splits) {
+    if (p.write_final || p.num_seqs == 0) return 0;
+    if (!counters || counters_bytes < counter_bytes(p.num_seqs, p.num_kv_heads))
+        return FP8KV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(counters) & 255u) != 0) return FP8KV_ERR_WORKSPACE;
+    const bool fused = fp8kv::fused_merge_fits(p.num_q_heads / p.num_kv_heads, head_dim, p.splits);
+    p.counters = static_cast<unsigned int*>(counters);
+    p.use_claims = num_splits == 0 ? 1 : 0;
+    p.merge_in_kernel = fused ? 1 : 0;
+    return fused ? 1 : 0;
 }
 
 int cache_write_impl(const void* key, const void* value, void* key_cache, void* value_cache,
@@ -255,6 +278,7 @@ int cache_write_impl(const void* key, const void* value, void* key_cache, void* 
     p.v_scale = sc.v;
     p.k_scales = fp8 && per_head_call ? sc.ks : nullptr;
     p.v_scales = fp8 && per_head_call ? sc.vs : nullptr;
+    p.err = g_error_word;
     return hip_status(fp8kv::launch_cache_write(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
 }
 
@@ -263,8 +287,8 @@ int paged_decode_impl(void* out, int out_dtype, const void* query, const void* k
                       int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                       int block_size, int num_blocks, const Scales& sc, bool per_head_call,
-                      int sliding_window, int num_splits, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      int sliding_window, int num_splits, void* counters, size_t counters_bytes,
+                      void* workspace, size_t workspace_bytes, void* stream) {
     if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
     fp8kv::DecodeParams p;
     bool fp8 = true;
@@ -277,11 +301,15 @@ int paged_decode_impl(void* out, int out_dtype, const void* query, const void* k
     if (num_seqs == 0) return FP8KV_OK;
     if (!out) return FP8KV_ERR_NULL;
     if (!aligned16(out)) return FP8KV_ERR_SHAPE;
+    // optional counters: the in-kernel merge
+    const int fused = counters != nullptr
+                          ? attach_counters(p, head_dim, counters, counters_bytes, num_splits) : 0;
+    if (fused < 0) return fused;
     p.out = out;
     p.out_f32 = out_dtype == FP8KV_F32;
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = hip_status(fp8kv::launch_decode_partial(p, codec_of(cache_dtype), head_dim, s));
-    if (st != FP8KV_OK || p.write_final) return st;
+    if (st != FP8KV_OK || p.write_final || fused) return st;
     return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
 }
 
@@ -291,35 +319,23 @@ int decode_step_impl(void* out, int out_dtype, const void* query, const void* ke
                      const int32_t* context_lens, int max_context_len, int num_seqs,
                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                      int num_blocks, const Scales& sc, bool per_head_call, int sliding_window,
-                     int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+                     int num_splits, void* counters, size_t counters_bytes, void* workspace,
+                     size_t workspace_bytes, void* stream) {
     if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
-    if (num_seqs < 0 || num_kv_heads <= 0) return FP8KV_ERR_SHAPE;
-    // counters first, then the partials (checked by setup_decode)
-    const size_t cbytes = step_counter_bytes(num_seqs, num_kv_heads);
-    const bool have_ws = workspace != nullptr && workspace_bytes >= cbytes;
     fp8kv::DecodeParams p;
     bool fp8 = true;
     int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
                           max_blocks_per_seq, context_lens, max_context_len, num_seqs,
                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, sc,
-                          per_head_call, sliding_window, num_splits,
-                          have_ws ? static_cast<char*>(workspace) + cbytes : nullptr,
-                          have_ws ? workspace_bytes - cbytes : 0, false);
+                          per_head_call, sliding_window, num_splits, workspace, workspace_bytes,
+                          false);
     if (st != FP8KV_OK) return st;
     if (num_seqs == 0) return FP8KV_OK;
     if (!out || !key_new || !value_new) return FP8KV_ERR_NULL;
     if (!aligned16(out) || !aligned16(key_new) || !aligned16(value_new)) return FP8KV_ERR_SHAPE;
-    // several splits: workgroups claim steps from counters (load balance) and the last one
-    // of each group merges inside the decode kernel when one workgroup merges a group
-    // cheaply, else the merge kernel queued behind it does
-    const bool fused = !p.write_final &&
-                       fp8kv::fused_merge_fits(num_q_heads / num_kv_heads, head_dim, p.splits);
-    if (!p.write_final) {
-        p.counters = static_cast<unsigned int*>(workspace);
-        p.claims = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) +
-                                                   arrival_bytes(num_seqs, num_kv_heads));
-        p.merge_in_kernel = fused ? 1 : 0;
-    }
+    // several splits: the counters are required (arrival, and claims with the automatic plan)
+    const int fused = attach_counters(p, head_dim, counters, counters_bytes, num_splits);
+    if (fused < 0) return fused;
     p.out = out;
     p.out_f32 = out_dtype == FP8KV_F32;
     p.k_new = static_cast<const uint16_t*>(key_new);
@@ -381,6 +397,7 @@ int paged_prefill_impl(void* out, int out_dtype, const void* query,
     p.v_scale = fp8 && !heads ? sc.v : 1.0f;
     p.k_scales = heads ? sc.ks : nullptr;
     p.v_scales = heads ? sc.vs : nullptr;
+    p.err = g_error_word;
     return hip_status(fp8kv::launch_prefill(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
 }
 
@@ -421,6 +438,17 @@ const char* fp8kv_status_string(int status) {
 int fp8kv_version(void) { return 200; }
 
 const char* fp8kv_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
+
+int fp8kv_set_error_word(unsigned int* word) {
+    if (word != nullptr && !aligned4(word)) return FP8KV_ERR_SHAPE;
+    g_error_word = word;
+    return FP8KV_OK;
+}
+
+size_t fp8kv_decode_counters_size(int max_num_seqs, int num_kv_heads) {
+    if (max_num_seqs < 0 || num_kv_heads <= 0) return 0;
+    return counter_bytes(max_num_seqs, num_kv_heads);
+}
 
 int fp8kv_cache_write(const void* key, const void* value, void* key_cache, void* value_cache,
                       int cache_dtype, const int64_t* slot_mapping, int num_tokens,
@@ -465,13 +493,14 @@ int fp8kv_paged_decode(void* out, int out_dtype, const void* query, const void* 
                        int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                        int block_size, int num_blocks, float k_scale, float v_scale,
-                       int sliding_window, int num_splits, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       int sliding_window, int num_splits, void* counters, size_t counters_bytes,
+                       void* workspace, size_t workspace_bytes, void* stream) {
     return paged_decode_impl(out, out_dtype, query, key_cache, value_cache, cache_dtype,
                              block_tables, max_blocks_per_seq, context_lens, max_context_len,
                              num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                              num_blocks, tensor_scales(k_scale, v_scale), false, sliding_window,
-                             num_splits, workspace, workspace_bytes, stream);
+                             num_splits, counters, counters_bytes, workspace, workspace_bytes,
+                             stream);
 }
 
 int fp8kv_paged_decode_per_head(void* out, int out_dtype, const void* query,
@@ -480,26 +509,17 @@ int fp8kv_paged_decode_per_head(void* out, int out_dtype, const void* query,
                                 const int32_t* context_lens, int max_context_len, int num_seqs,
                                 int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                                 int num_blocks, const float* k_scales, const float* v_scales,
-                                int sliding_window, int num_splits, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                int sliding_window, int num_splits, void* counters,
+                                size_t counters_bytes, void* workspace, size_t workspace_bytes,
+                                void* stream) {
     return paged_decode_impl(out, out_dtype, query, key_cache, value_cache, cache_dtype,
                              block_tables, max_blocks_per_seq, context_lens, max_context_len,
                              num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                              num_blocks, head_scales(k_scales, v_scales), true, sliding_window,
-                             num_splits, workspace, workspace_bytes, stream);
+                             num_splits, counters, counters_bytes, workspace, workspace_bytes,
+                             stream);
 }
 
-
-size_t fp8kv_decode_step_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
-                                        int head_dim, int block_size, int max_context_len,
-                                        int sliding_window, int num_splits) {
-    if (check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                           max_context_len, sliding_window, num_splits) != FP8KV_OK)
-        return 0;
-    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, max_context_len, sliding_window, num_splits);
-    return step_counter_bytes(num_seqs, num_kv_heads) +
-           workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits).total;
-}
 
 int fp8kv_decode_step(void* out, int out_dtype, const void* query, const void* key_new,
                       const void* value_new, void* key_cache, void* value_cache, int cache_dtype,
@@ -507,12 +527,14 @@ int fp8kv_decode_step(void* out, int out_dtype, const void* query, const void* k
                       const int32_t* context_lens, int max_context_len, int num_seqs,
                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                       int num_blocks, float k_scale, float v_scale, int sliding_window,
-                      int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+                      int num_splits, void* counters, size_t counters_bytes, void* workspace,
+                      size_t workspace_bytes, void* stream) {
     return decode_step_impl(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
                             cache_dtype, block_tables, max_blocks_per_seq, context_lens,
                             max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
                             block_size, num_blocks, tensor_scales(k_scale, v_scale), false,
-                            sliding_window, num_splits, workspace, workspace_bytes, stream);
+                            sliding_window, num_splits, counters, counters_bytes, workspace,
+                            workspace_bytes, stream);
 }
 
 int fp8kv_decode_step_per_head(void* out, int out_dtype, const void* query, const void* key_new,
@@ -522,13 +544,14 @@ int fp8kv_decode_step_per_head(void* out, int out_dtype, const void* query, cons
                                int max_context_len, int num_seqs, int num_q_heads,
                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                const float* k_scales, const float* v_scales, int sliding_window,
-                               int num_splits, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               int num_splits, void* counters, size_t counters_bytes,
+                               void* workspace, size_t workspace_bytes, void* stream) {
     return decode_step_impl(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
                             cache_dtype, block_tables, max_blocks_per_seq, context_lens,
                             max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
                             block_size, num_blocks, head_scales(k_scales, v_scales), true,
-                            sliding_window, num_splits, workspace, workspace_bytes, stream);
+                            sliding_window, num_splits, counters, counters_bytes, workspace,
+                            workspace_bytes, stream);
 }
 
 
@@ -640,6 +663,7 @@ int fp8kv_cache_write_rotated(const void* key, const void* value, void* key_cach
     p.num_blocks = num_blocks;
     p.k_scale = fp8 ? k_scale : 1.0f;
     p.v_scale = fp8 ? v_scale : 1.0f;
+    p.err = g_error_word;
     return hip_status(fp8kv::launch_rotate_write(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
 }
 

@@ -108,6 +108,15 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
         sl[k] = p.slot_mapping[tk];
     });
     const int64_t nslots = (int64_t)p.num_blocks * kBlockSize;
+    // a slot past the cache is skipped, and reported (negative slots are padding by design)
+    if (p.err != nullptr && c == 0 && h == 0) {
+        bool bad = false;
+        for4([&](auto kk) {
+            constexpr int k = decltype(kk)::value;
+            bad |= t0 + k < T && sl[k] >= nslots;
+        });
+        if (bad) report_error(p.err, kErrSlot);
+    }
     const bool fast = t0 + 3 < T && sl[0] >= 0 && sl[0] < nslots && (sl[0] & 3) == 0 &&
                       sl[1] == sl[0] + 1 && sl[2] == sl[0] + 2 && sl[3] == sl[0] + 3;
 

@@ -36,6 +36,7 @@ struct CacheWriteParams {
     float v_scale;
     const float* k_scales;         // per-kv-head scales [Hkv] (device), or null: k_scale
     const float* v_scales;         // ... or null: v_scale
+    unsigned int* err;             // device error word (FP8KV_DEVERR_* bits), or null
 };
 
 struct DecodeParams {
@@ -66,15 +67,16 @@ struct DecodeParams {
     const uint16_t* v_new;
     float k_scale_q;               // quantisation scales of the step token (fp8 caches)
     float v_scale_q;
-    unsigned int* counters;        // [B][Hkv] split arrival counters (zero between calls), or null
-    unsigned int* claims;          // [B][Hkv][waves] step claim counters, kClaimStride apart
-                                   // (zero between calls), or null; needs `counters`
+    unsigned int* counters;        // [B][Hkv] counter records of kCounterRecordWords words (zero
+                                   // between calls), or null
+    int use_claims;                // with `counters`: the last pool steps are claimed at run time
     int merge_in_kernel;           // with `counters`: the last workgroup of a group merges
     // per-attention-head scales [Hkv] (device), or null for the per-tensor values above;
     // with them score_scale excludes the key scale and v_scale / k_scale_q / v_scale_q are
     // unused
     const float* k_scales;
     const float* v_scales;
+    unsigned int* err;             // device error word (FP8KV_DEVERR_* bits), or null
 };
 
 struct PrefillParams {
@@ -98,7 +100,19 @@ struct PrefillParams {
     float v_scale;
     const float* k_scales;         // per-kv-head scales [Hkv] (device), or null
     const float* v_scales;
+    unsigned int* err;             // device error word (FP8KV_DEVERR_* bits), or null
 };
+
+// Bits of the device error word (the public FP8KV_DEVERR_* values).
+constexpr unsigned int kErrBlockId = 1u;      // a block id of an attended block is out of range
+constexpr unsigned int kErrSlot = 2u;         // a slot at or past num_blocks * block_size
+constexpr unsigned int kErrContextLen = 4u;   // a context length that had to be clamped
+constexpr unsigned int kErrQueryLen = 8u;     // a prefill chunk that does not fit its bounds
+
+// Record a device-side input error (a vector atomic OR into the caller's word).
+__device__ inline void report_error(unsigned int* err, unsigned int bits) {
+    if (err != nullptr) __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // The scale of kv head h: from a per-head array (a wave-uniform scalar load), or the
 // per-tensor value when there is no array.
@@ -107,9 +121,12 @@ __device__ inline float head_scale(const float* per_head, int h, float per_tenso
     return per_head != nullptr ? ((ConstF32Ptr)per_head)[h] : per_tensor;
 }
 
-// Claim counters sit this many 32-bit words (256 bytes) apart, so that the counters of
-// different waves and groups never share a line.
-constexpr int kClaimStride = 64;
+// Counter record of one (sequence, kv head) group in the caller's counter buffer: the
+// split arrival counter, then one step-claim counter per decode wave, each in a 256-byte
+// line of its own so that no two counters share a line.  Group b*Hkv + h's record sits at
+// a fixed place whatever the batch or split plan of a call.
+constexpr int kCounterLineWords = 64;
+constexpr int kCounterRecordWords = kCounterLineWords * (1 + kDecodeWaves);
 
 // Context window of one sequence in blocks: positions [lo, L), blocks [blk0, blk0+nblk).
 struct SeqWindow {
@@ -153,6 +170,9 @@ inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, size_t ld
     void* args[] = {const_cast<P*>(&p)};
     return hipLaunchKernel(fn, grid, block, args, lds, s);
 }
+
+// Remember a HIP error for fp8kv_last_hip_error (the calling thread's most recent).
+void record_hip_error(hipError_t e);
 
 // `codec`: the cache element codec (kCodecBF16 or a one-byte codec).
 hipError_t launch_cache_write(const CacheWriteParams& p, Codec codec, int head_dim, hipStream_t s);

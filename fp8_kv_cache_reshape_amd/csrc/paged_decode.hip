@@ -297,12 +297,12 @@ void decode_partial_kernel(DecodeParams p) {
     // in series before the first KV load.
     asm volatile("" :: "s"(p.out), "s"(p.query), "s"(p.key_cache), "s"(p.value_cache),
                  "s"(p.block_tables), "s"(p.context_lens), "s"(p.ws_ml), "s"(p.ws_acc));
-    asm volatile("" :: "s"(p.k_new), "s"(p.v_new), "s"(p.counters), "s"(p.claims),
+    asm volatile("" :: "s"(p.k_new), "s"(p.v_new), "s"(p.counters), "s"(p.use_claims),
                  "s"(p.max_blocks_per_seq), "s"(p.max_context_len), "s"(p.num_q_heads),
                  "s"(p.num_kv_heads), "s"(p.num_blocks), "s"(p.sliding_window));
     asm volatile("" :: "s"(p.score_scale), "s"(p.v_scale), "s"(p.splits), "s"(p.blocks_per_split),
                  "s"(p.write_final), "s"(p.k_scale_q), "s"(p.v_scale_q), "s"(p.merge_in_kernel),
-                 "s"(p.k_scales), "s"(p.v_scales),
+                 "s"(p.k_scales), "s"(p.v_scales), "s"(p.err),
                  "s"(p.out_f32));
     const int split = kHeadsFastest ? blockIdx.y : blockIdx.x;
     const int h = kHeadsFastest ? blockIdx.x : blockIdx.y;
@@ -329,8 +329,11 @@ void decode_partial_kernel(DecodeParams p) {
         }
     }
     // (a scalar load, like the block ids)
-    const SeqWindow w = seq_window(((ConstI32Ptr)p.context_lens)[b], p.max_context_len,
-                                   p.max_blocks_per_seq, p.sliding_window);
+    const int len_in = ((ConstI32Ptr)p.context_lens)[b];
+    const SeqWindow w = seq_window(len_in, p.max_context_len, p.max_blocks_per_seq, p.sliding_window);
+    if (p.err != nullptr && split == 0 && h == 0 && threadIdx.x == 0 &&
+        (len_in < 0 || len_in != w.L))
+        report_error(p.err, kErrContextLen);
     const int ns = (w.nblk + p.blocks_per_split - 1) / p.blocks_per_split;   // workgroups taking part
     const int64_t out_row0 = ((int64_t)b * p.num_q_heads + (int64_t)h * G) * D;
     if (split >= ns) {
@@ -384,10 +387,19 @@ void decode_partial_kernel(DecodeParams p) {
         if ((unsigned)kid >= (unsigned)p.num_blocks) kid = -1;
         if ((unsigned)vid >= (unsigned)p.num_blocks) vid = -1;
     };
+    // Any id of an attended block outside [0, num_blocks) (a wave-uniform flag, reported once
+    // at the end; the block reads as empty).
+    bool bad_id = false;
+    auto note_ids = [&](const int* id, int stp) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            bad_id |= 4 * stp + x < nblk && (unsigned)id[x] >= (unsigned)p.num_blocks;
+    };
     auto step_ids = [&](int stp, int& kid, int& vid) {
         int id[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) id[x] = (4 * stp + x < nblk) ? bt[4 * stp + x] : -1;
+        note_ids(id, stp);
         pick_ids(id, kid, vid);
     };
     // Loads are unconditional (branch-free, so the compiler can count them in flight): a
@@ -601,8 +613,9 @@ void decode_partial_kernel(DecodeParams p) {
         const int st = kDecodeWaves * k + wave;
         return st < np ? st : -1;
     };
-    unsigned int* claim = p.claims == nullptr ? nullptr
-        : p.claims + (((int64_t)b * p.num_kv_heads + h) * kDecodeWaves + wave) * kClaimStride;
+    unsigned int* const rec = p.counters == nullptr ? nullptr
+        : p.counters + ((int64_t)b * p.num_kv_heads + h) * kCounterRecordWords;
+    unsigned int* claim = rec != nullptr && p.use_claims ? rec + (1 + wave) * kCounterLineWords : nullptr;
 
     // Fused decode step: lanes [0, D/8) write 8 key channels of the token each, lanes
     // [32, 32 + D/8) 8 value channels.  Load and store sit in one branch: a token load left
@@ -613,6 +626,7 @@ void decode_partial_kernel(DecodeParams p) {
         const uint4 tok = load16((lane >= 32 ? p.v_new : p.k_new) + ((int64_t)b * p.num_kv_heads + h) * D +
                                  min(lane & 31, D / 8 - 1) * 8);
         const int c = lane & 31;
+        if ((unsigned)tok_blk >= (unsigned)p.num_blocks && lane == 0) report_error(p.err, kErrBlockId);
         if ((unsigned)tok_blk < (unsigned)p.num_blocks && c < D / 8) {
             const bool val = lane >= 32;
             const int off = (w.L - 1) % kBlockSize;
@@ -666,6 +680,7 @@ void decode_partial_kernel(DecodeParams p) {
             int id[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) id[x] = (4 * cur + x < nblk) ? id_early[x] : -1;
+            note_ids(id, cur);
             pick_ids(id, buf.kid, buf.vid);
         } else {
             step_ids(cur, buf.kid, buf.vid);
@@ -701,6 +716,7 @@ void decode_partial_kernel(DecodeParams p) {
         process(buf, cur, -1, std::false_type{});
     }
     flush();
+    if (bad_id && lane == 0) report_error(p.err, kErrBlockId);
 
     // ---- combine the waves of this workgroup in LDS
     float l_tot = l_hi + l_lo;
@@ -782,16 +798,15 @@ void decode_partial_kernel(DecodeParams p) {
         if (p.merge_in_kernel) __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores done
         __syncthreads();                                         // ... and every thread's
         if (threadIdx.x == 0) {
-            unsigned int* cnt = p.counters + (int64_t)b * p.num_kv_heads + h;
-            const unsigned int old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned int old = __hip_atomic_fetch_add(rec, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const bool last = old + 1 == (unsigned int)ns;
             if (last) {
                 // every wave of the group has made its last claim
-                __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (p.claims != nullptr)
+                __hip_atomic_store(rec, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (p.use_claims)
                     for (int v = 0; v < kDecodeWaves; ++v)
-                        __hip_atomic_store(p.claims + (((int64_t)b * p.num_kv_heads + h) * kDecodeWaves + v) * kClaimStride,
-                                           0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(rec + (1 + v) * kCounterLineWords, 0u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                 // drop stale copies of the partials from this CU's L1 and this XCD's L2;
                 // the barrier below orders the other threads' loads after it
                 if (p.merge_in_kernel) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");

@@ -170,6 +170,12 @@ void prefill_kernel(PrefillParams p) {
     const int tile = (int)gridDim.x - 1 - (int)blockIdx.x;             // heaviest tiles first
     const int64_t ncols = (int64_t)(nq > 0 ? nq : 0) * G;
     const int64_t cw0 = (int64_t)tile * (kWaves * kCols);             // first column of the workgroup
+    if (p.err != nullptr && tile == 0 && h == 0 && threadIdx.x == 0) {
+        const int len_in = ((ConstI32Ptr)p.context_lens)[b];
+        if (nq < 0 || nq > p.max_query_len) report_error(p.err, kErrQueryLen);
+        if (len_in < 0 || len_in > p.max_context_len || len_in > p.max_blocks_per_seq * kBlockSize)
+            report_error(p.err, kErrContextLen);
+    }
     if (cw0 >= ncols) return;                                         // (whole workgroup)
     const int64_t c0 = cw0 + wave * kCols;                            // first column of the wave
     const bool wactive = c0 < ncols;
@@ -494,6 +500,16 @@ void prefill_kernel(PrefillParams p) {
     if (wave >= kWaves / 2) run(std::true_type{});
     else run(std::false_type{});
     }   // nsteps > 0
+    // With an error word: wave 0 checks the ids of every block some column of the workgroup
+    // attends to (staged blocks with a bad id read as empty).
+    if (p.err != nullptr && wave == 0 && kend > 0) {
+        const ConstI32Ptr row = (ConstI32Ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
+        const int n_end = (kend - 1) / kBlockSize;
+        bool bad = false;
+        for (int n = (pwmin >= 0 ? lo_of(pwmin) : 0) / kBlockSize + lane; n <= n_end; n += 64)
+            bad |= (unsigned)row[n] >= (unsigned)p.num_blocks;
+        if (__any(bad) && lane == 0) report_error(p.err, kErrBlockId);
+    }
     if (!wactive) return;
 #pragma unroll
     for (int t = 0; t < NT; ++t) osum[t] += oacc[t];

@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void rotate_write_kernel(CacheWriteParams p, f
     hadamard_row<D>(k, c, rscale);
     hadamard_row<D>(v, c, rscale);
     const int64_t slot = p.slot_mapping[t];
+    if (slot >= (int64_t)p.num_blocks * kBlockSize && c == 0 && h == 0) report_error(p.err, kErrSlot);
     if (slot < 0 || slot >= (int64_t)p.num_blocks * kBlockSize) return;
     const int64_t blk = slot / kBlockSize;
     const int off = (int)(slot % kBlockSize);

@@ -8,46 +8,56 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;                 // independent 16-byte loads in flight per thread
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// U: independent 16-byte loads in flight per thread.
+template <int U>
 __global__ __launch_bounds__(kThreads) void read_ceiling_kernel(const u32x4* p, size_t n16, unsigned* sink) {
     const size_t tid = (size_t)blockIdx.x * kThreads + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * kThreads;
     u32x4 acc = {0u, 0u, 0u, 0u};
-    // the host guarantees n16 is a multiple of kUnroll * stride: every index below is < n16
-    for (size_t base = tid; base < n16; base += kUnroll * stride) {
-        u32x4 v[kUnroll];
+    // the host guarantees n16 is a multiple of U * stride: every index below is < n16
+    for (size_t base = tid; base < n16; base += U * stride) {
+        u32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(p + base + u * stride);
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + base + u * stride);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+        for (int u = 0; u < U; ++u) acc ^= v[u];
     }
     if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = 1u;   // keeps the loads
 }
+
+bool unroll_ok(int u) { return u == 4 || u == 8 || u == 16; }
 
 }  // namespace
 
 extern "C" {
 
-// Bytes per launch must be a positive multiple of this, for a launch of `grid` workgroups.
-size_t fp8kv_probe_read_granule(int grid) { return (size_t)16 * kUnroll * kThreads * (size_t)(grid > 0 ? grid : 0); }
+// Bytes per launch must be a positive multiple of this, for a launch of `grid` workgroups
+// with `unroll` loads in flight per thread (4, 8 or 16; else 0).
+size_t fp8kv_probe_read_granule(int grid, int unroll) {
+    if (!unroll_ok(unroll)) return 0;
+    return (size_t)16 * unroll * kThreads * (size_t)(grid > 0 ? grid : 0);
+}
 
 // Reads `bytes` of device memory at `buf` (16-byte aligned) once, with `grid` workgroups of 256
-// threads.  `sink` is a device word the kernel may write.  Returns 0, -2 for a bad size, grid
-// or alignment, -6 for a launch error.
-int fp8kv_probe_read(const void* buf, size_t bytes, int grid, void* sink, void* stream) {
-    if (grid <= 0 || grid > 65536) return -2;
-    const size_t g = fp8kv_probe_read_granule(grid);
+// threads, each thread keeping `unroll` loads in flight.  `sink` is a device word the kernel
+// may write.  Returns 0, -2 for a bad size, grid, unroll or alignment, -6 for a launch error.
+int fp8kv_probe_read(const void* buf, size_t bytes, int grid, int unroll, void* sink, void* stream) {
+    if (grid <= 0 || grid > 65536 || !unroll_ok(unroll)) return -2;
+    const size_t g = fp8kv_probe_read_granule(grid, unroll);
     if (!buf || !sink || bytes == 0 || bytes % g != 0 || (reinterpret_cast<uintptr_t>(buf) & 15u) != 0)
         return -2;
     const u32x4* p = static_cast<const u32x4*>(buf);
     size_t n16 = bytes / 16;
     unsigned* s = static_cast<unsigned*>(sink);
     void* args[] = {&p, &n16, &s};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&read_ceiling_kernel), dim3(grid), dim3(kThreads),
-                           args, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : -6;
+    const void* fn = unroll == 4 ? reinterpret_cast<const void*>(&read_ceiling_kernel<4>)
+                   : unroll == 8 ? reinterpret_cast<const void*>(&read_ceiling_kernel<8>)
+                                 : reinterpret_cast<const void*>(&read_ceiling_kernel<16>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess ? 0 : -6;
 }
 
 }  // extern "C"

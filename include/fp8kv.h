@@ -10,8 +10,9 @@
  *   - decode attention softmax(q K^T / sqrt(d)) V that reads the fp8 blocks directly,
  *     dequantising inside the kernel (same page, "Attention backend interactions"),
  *     with GQA group ratio g = Hq / Hkv (page "ctx-fp8-kv-cache-long-context-accuracy",
- *     "Arithmetic intensity"), an optional sliding window (first page, "Accuracy risks
- *     to test for"), and fp32 partial results merged across context splits: the
+ *     "Arithmetic intensity"), an optional sliding window (page "FP8 KV Cache
+ *     Quantization: Capacity Gains and Accuracy Risk", "Accuracy risks to test for"), and
+ *     fp32 partial results merged across context splits: the
  *     two-level accumulation that keeps long contractions accurate (page "The State of
  *     FP8 KV-Cache and Attention Quantization in vLLM", "ACCURACY AT LONG CONTEXT").
  *   A bf16 cache variant of both calls keeps chosen layers in the native dtype (page
@@ -20,7 +21,8 @@
  *
  * Conventions for every call
  *   - All pointers except the scalars are DEVICE pointers the caller owns.  The library
- *     allocates nothing, keeps no state between calls, and is thread-safe.
+ *     allocates nothing and is thread-safe.  Its only state is, per host thread, the
+ *     optional device error word set by fp8kv_set_error_word.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
  *     returns without synchronising.
  *   - Arguments are validated on the host before any HIP call; a failed check returns a
@@ -30,7 +32,8 @@
  *     [0, num_blocks*block_size) is skipped, a block id outside [0, num_blocks) is read as
  *     an empty block, and a context length is clamped to
  *     min(max_context_len, max_blocks_per_seq*block_size).  Results for such inputs are
- *     otherwise unspecified.
+ *     otherwise unspecified; with an error word set (fp8kv_set_error_word) the kernels
+ *     report them there.
  *
  * Data layout (row-major, no padding)
  *   bf16 K/V rows written per token:  [num_tokens][num_kv_heads][head_dim]
@@ -98,6 +101,30 @@ int fp8kv_version(void);
  * thread ("hipSuccess" if none).  Static storage; never NULL. */
 const char* fp8kv_last_hip_error(void);
 
+/* Bits of the device error word (see fp8kv_set_error_word). */
+#define FP8KV_DEVERR_BLOCK_ID     1u  /* a block_tables entry of a block some query attends to is
+                                         outside [0, num_blocks): the block was read as empty (a
+                                         decode step's token was not written) */
+#define FP8KV_DEVERR_SLOT         2u  /* a slot_mapping entry >= num_blocks*block_size: that token
+                                         was not written (negative slots are skipped silently, as
+                                         padding) */
+#define FP8KV_DEVERR_CONTEXT_LEN  4u  /* a context length < 0 or above min(max_context_len,
+                                         max_blocks_per_seq*block_size): it was clamped */
+#define FP8KV_DEVERR_QUERY_LEN    8u  /* prefill: query_start_loc decreases, or a chunk is longer
+                                         than max_query_len (its rows past that are not computed) */
+
+/*
+ * fp8kv_set_error_word -- from now on, kernels enqueued by the calling host thread OR the
+ * FP8KV_DEVERR_* bits above into *word (a device uint32, 4-byte aligned, owned by the
+ * caller) when they meet device-resident inputs that break the preconditions stated below;
+ * NULL (the initial state) switches reporting off.  The library never clears the word:
+ * zero it, run the calls, then read it after the stream has reached that point.  Reports
+ * are atomic ORs made only when an error is found (prefill also reads the attended block
+ * ids once more per workgroup while a word is set).  The pointer is per host thread.
+ * Returns FP8KV_OK, or FP8KV_ERR_SHAPE for a misaligned word.
+ */
+int fp8kv_set_error_word(unsigned int* word);
+
 /*
  * fp8kv_cache_write -- quantise new K/V rows and scatter them into the paged caches.
  *
@@ -154,19 +181,44 @@ int fp8kv_cache_write_per_head(const void* key, const void* value,
  * accumulator acc[head_dim]) that a second pass merges.  num_splits > 0 requests at most
  * that many splits for the longest sequence; 0 lets the library choose.  Returns the
  * split count (>= 1) or a negative status.
+ *
+ * Reproducibility (decode calls that take a counter buffer): with num_splits > 0 every
+ * workgroup's share of the context is fixed by the arguments and every merge sums in a
+ * fixed order, so the output is bit-for-bit the same on every run.  With num_splits = 0 and
+ * a counter buffer the last context steps of each (sequence, kv head) are handed at run
+ * time to whichever workgroup is free (load balancing across compute units), so the fp32
+ * summation order, and the last bits of the output, may differ from run to run, within the
+ * accuracy stated for fp8kv_paged_decode.  Calls without a counter buffer are always
+ * reproducible.
  */
 int fp8kv_paged_decode_num_splits(int num_seqs, int num_kv_heads, int head_dim,
                                   int block_size, int max_context_len, int sliding_window,
                                   int num_splits);
 
 /*
- * fp8kv_paged_decode_workspace_size -- bytes of device workspace a decode with these
- * arguments needs (0 on invalid arguments).  The workspace holds the fp32 split
- * partials: num_seqs * num_q_heads * splits * (head_dim + 2) floats, rounded up.
+ * fp8kv_paged_decode_workspace_size -- bytes of device workspace a decode (or decode step)
+ * with these arguments needs (0 on invalid arguments).  The workspace holds the fp32 split
+ * partials: num_seqs * num_q_heads * splits * (head_dim + 2) floats, rounded up.  Its
+ * contents on entry never matter.
  */
 size_t fp8kv_paged_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                          int head_dim, int block_size, int max_context_len,
                                          int sliding_window, int num_splits);
+
+/*
+ * fp8kv_decode_counters_size -- bytes of the counter buffer that decode calls with up to
+ * max_num_seqs sequences of num_kv_heads kv heads use (0 on invalid arguments):
+ * max_num_seqs * num_kv_heads records of 1280 bytes.  The record of (sequence b, kv head h)
+ * sits at byte (b*num_kv_heads + h)*1280 whatever the batch, split plan or window of a call;
+ * it holds the split arrival counter and four step-claim counters, each in a 256-byte line.
+ *
+ * Contract: allocate the buffer once for the largest batch, 256-byte aligned, and zero it
+ * before its first use.  Every call leaves the records it used at zero again, so the buffer
+ * serves any later call with at most max_num_seqs sequences (of the same or fewer kv heads)
+ * with no clearing in between.  It holds counters only (no partials).  Calls that share a
+ * counter buffer must not run concurrently; give each stream its own.
+ */
+size_t fp8kv_decode_counters_size(int max_num_seqs, int num_kv_heads);
 
 /*
  * fp8kv_paged_decode -- one decode step of GQA attention over the paged cache.
@@ -193,9 +245,19 @@ size_t fp8kv_paged_decode_workspace_size(int num_seqs, int num_q_heads, int num_
  *   max_context_len  host upper bound on context_lens (sizes the grid and workspace)
  *   sliding_window   0 = full attention, W > 0 = the last W positions
  *   num_splits    0 = automatic, else requested split count (see above)
+ *   counters      optional (NULL: none).  A counter buffer (fp8kv_decode_counters_size,
+ *                 with its zero-on-entry contract) of at least num_seqs*num_kv_heads
+ *                 records: the last workgroup of each (sequence, kv head) to finish then
+ *                 merges the split partials inside the decode kernel, and no separate merge
+ *                 launch follows (except for groups with more partials than one workgroup
+ *                 merges quickly -- more than 64 splits, or more than 32 float4 per thread);
+ *                 see fp8kv_paged_decode_num_splits for reproducibility.  Without it the
+ *                 partials are merged by a second kernel launch on `stream`.
  *   workspace     device buffer of at least fp8kv_paged_decode_workspace_size() bytes,
  *                 256-byte aligned; may be NULL when that size is 0.  Its contents on
  *                 entry do not matter; on return it holds the split partials.
+ * Errors: FP8KV_ERR_WORKSPACE also for a counter buffer that is too small or not 256-byte
+ * aligned (checked only when the call uses more than one split).
  */
 int fp8kv_paged_decode(void* out, int out_dtype, const void* query,
                        const void* key_cache, const void* value_cache, int cache_dtype,
@@ -204,6 +266,7 @@ int fp8kv_paged_decode(void* out, int out_dtype, const void* query,
                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                        int block_size, int num_blocks,
                        float k_scale, float v_scale, int sliding_window, int num_splits,
+                       void* counters, size_t counters_bytes,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -213,7 +276,7 @@ int fp8kv_paged_decode(void* out, int out_dtype, const void* query,
  * calibration", per-attention-head granularity).  The key scale multiplies
  * log2(e)/sqrt(head_dim) (rounded to float) inside the kernel; the value scale multiplies
  * the merged output.  k_scales / v_scales as for fp8kv_cache_write_per_head; every other
- * argument, the workspace and the error behaviour as for fp8kv_paged_decode.
+ * argument, the counters, the workspace and the error behaviour as for fp8kv_paged_decode.
  */
 int fp8kv_paged_decode_per_head(void* out, int out_dtype, const void* query,
                                 const void* key_cache, const void* value_cache, int cache_dtype,
@@ -223,6 +286,7 @@ int fp8kv_paged_decode_per_head(void* out, int out_dtype, const void* query,
                                 int block_size, int num_blocks,
                                 const float* k_scales, const float* v_scales,
                                 int sliding_window, int num_splits,
+                                void* counters, size_t counters_bytes,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -258,31 +322,22 @@ int fp8kv_paged_decode_merge(void* out, int out_dtype,
                              const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fp8kv_decode_step_workspace_size -- bytes of device workspace fp8kv_decode_step needs
- * (0 on invalid arguments): first the counter region -- one 32-bit arrival counter per
- * (sequence, kv head), padded to a multiple of 256 bytes, then one 32-bit step claim
- * counter per (sequence, kv head, wave of a decode workgroup) every 256 bytes, that is
- * num_seqs*num_kv_heads*1024 bytes -- then the split partials of fp8kv_paged_decode.  The
- * counter region sits at the same place whatever split plan a call uses.
- */
-size_t fp8kv_decode_step_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
-                                        int head_dim, int block_size, int max_context_len,
-                                        int sliding_window, int num_splits);
-
-/*
  * fp8kv_decode_step -- one whole decode step: write each sequence's new token into the
  * cache, then decode attention over the cache, normally in a single kernel launch (when the
  * split partials of one (sequence, kv head) are too many for one workgroup to merge
- * quickly -- more than 32 float4 per thread -- a second, merge launch follows on `stream`).
+ * quickly -- more than 64 splits, or more than 32 float4 per thread -- a second, merge
+ * launch follows on `stream`).
  *
  * Equivalent to fp8kv_cache_write(key_new, value_new, ...) with num_tokens = num_seqs and
  * slot_mapping[b] = block_tables[b][(L_b-1)/16]*16 + (L_b-1)%16 for every sequence with
  * L_b >= 1 (L_b as clamped in fp8kv_paged_decode; sequences with L_b = 0 write nothing,
  * and a block id outside [0, num_blocks) writes nothing), followed by
- * fp8kv_paged_decode(...) with the same arguments.  The bytes written are identical; the
- * output agrees with the two-call path to within fp32 rounding (the split partials are
- * combined by the last workgroup of each (sequence, kv head) to finish, in a different
- * order from the merge kernel).
+ * fp8kv_paged_decode(...) with the same arguments and the counter buffer.  The bytes written
+ * are identical; the output agrees with the two-call path to within fp32 rounding (the split
+ * partials are combined by the last workgroup of each (sequence, kv head) to finish, in a
+ * different order from the merge kernel).  Reproducibility as stated at
+ * fp8kv_paged_decode_num_splits: bit-for-bit with num_splits > 0; with num_splits = 0 the
+ * run-time step claims may change the last bits from run to run.
  *
  *   key_new, value_new  device bf16 [num_seqs][num_kv_heads][head_dim]: the token at
  *                       position L_b - 1 of every sequence.  The block holding position
@@ -290,13 +345,11 @@ size_t fp8kv_decode_step_workspace_size(int num_seqs, int num_q_heads, int num_k
  *                       sequences may not write one slot).
  *   key_cache,
  *   value_cache         written and read
- *   workspace           at least fp8kv_decode_step_workspace_size() bytes, 256-byte
- *                       aligned.  Its counter region (the first
- *                       round_up(num_seqs*num_kv_heads*4, 256) + num_seqs*num_kv_heads*1024
- *                       bytes) must be zero before the first call (allocate the workspace
- *                       zero-filled); every call leaves it zero again, so consecutive steps
- *                       can reuse it even as the split plan changes.  One workspace serves
- *                       one call at a time.
+ *   counters            a counter buffer of at least num_seqs*num_kv_heads records (see
+ *                       fp8kv_decode_counters_size and its zero-on-entry contract); required
+ *                       when the call uses more than one split, else it may be NULL.
+ *   workspace           at least fp8kv_paged_decode_workspace_size() bytes, 256-byte
+ *                       aligned, contents on entry irrelevant (it receives the partials).
  * Other arguments, layout and error behaviour as for fp8kv_paged_decode.
  */
 int fp8kv_decode_step(void* out, int out_dtype, const void* query,
@@ -307,6 +360,7 @@ int fp8kv_decode_step(void* out, int out_dtype, const void* query,
                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                       int block_size, int num_blocks,
                       float k_scale, float v_scale, int sliding_window, int num_splits,
+                      void* counters, size_t counters_bytes,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -315,8 +369,8 @@ int fp8kv_decode_step(void* out, int out_dtype, const void* query,
  * fp8kv_cache_write_per_head does, and the attention dequantises as
  * fp8kv_paged_decode_per_head does (page "FP8 KV Cache Quantization: Capacity Gains and
  * Accuracy Risk", "Scales and calibration").  k_scales / v_scales as for
- * fp8kv_cache_write_per_head; everything else, the workspace and its counter region
- * included, as for fp8kv_decode_step.
+ * fp8kv_cache_write_per_head; everything else, the counters and workspace included, as for
+ * fp8kv_decode_step.
  */
 int fp8kv_decode_step_per_head(void* out, int out_dtype, const void* query,
                                const void* key_new, const void* value_new,
@@ -327,6 +381,7 @@ int fp8kv_decode_step_per_head(void* out, int out_dtype, const void* query,
                                int block_size, int num_blocks,
                                const float* k_scales, const float* v_scales,
                                int sliding_window, int num_splits,
+                               void* counters, size_t counters_bytes,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*

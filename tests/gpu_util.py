@@ -96,10 +96,19 @@ class DeviceInputs:
         self.cl = torch.from_numpy(np.ascontiguousarray(cl, dtype=np.int32)).to(DEV)
 
 
+def new_counters(num_seqs: int, num_kv_heads: int) -> torch.Tensor:
+    """A zero-filled counter buffer for decode calls of up to num_seqs sequences."""
+    n = F.fp8kv_decode_counters_size(num_seqs, num_kv_heads)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=DEV)
+
+
 def gpu_decode(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_splits=0,
                window=None, dev: DeviceInputs = None, max_context_len=None, split_api=False,
-               heads=None):
+               heads=None, counters=None):
+    """fp8kv_paged_decode (per-head variant with `heads`, the two split passes with
+    `split_api`); `counters` (a counter buffer) selects the in-kernel merge."""
     dev = dev or DeviceInputs(w)
+    cn = counters.numel() if counters is not None else 0
     win = layer.sliding_window if window is None else window
     maxl = w.max_context_len if max_context_len is None else max_context_len
     B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
@@ -112,8 +121,8 @@ def gpu_decode(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_spl
         assert not split_api, "the split passes take per-tensor scales only"
         F.fp8kv_paged_decode_per_head(out, odt, dev.q, kc, vc, cdt, dev.bt, w.max_blocks_per_seq,
                                       dev.cl, maxl, B, Hq, Hkv, D, w.block_size, w.num_blocks,
-                                      f32_dev(heads[0]), f32_dev(heads[1]), win, num_splits, ws,
-                                      ws_bytes)
+                                      f32_dev(heads[0]), f32_dev(heads[1]), win, num_splits,
+                                      counters, cn, ws, ws_bytes)
     elif split_api:
         F.fp8kv_paged_decode_partial(dev.q, kc, vc, cdt, dev.bt, w.max_blocks_per_seq, dev.cl, maxl,
                                      B, Hq, Hkv, D, w.block_size, w.num_blocks, layer.k_scale, win,
@@ -124,7 +133,7 @@ def gpu_decode(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_spl
     else:
         F.fp8kv_paged_decode(out, odt, dev.q, kc, vc, cdt, dev.bt, w.max_blocks_per_seq, dev.cl, maxl,
                              B, Hq, Hkv, D, w.block_size, w.num_blocks, layer.k_scale, layer.v_scale,
-                             win, num_splits, ws, ws_bytes)
+                             win, num_splits, counters, cn, ws, ws_bytes)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D)
 
@@ -144,6 +153,16 @@ def oracle_decode(w: syn.Workload, layer: syn.Layer, okc, ovc, pairs=None, windo
     if pairs is None:
         return oracle.paged_decode(*args)
     return oracle.paged_decode_pairs(pairs, *args)
+
+
+def oracle_decode_threaded(w: syn.Workload, layer: syn.Layer, okc, ovc, pairs, threads: int = 16):
+    """oracle_decode for (b, hq) pairs, one pair per task on a thread pool (the oracle's C
+    calls release the interpreter lock): [n][D]."""
+    from concurrent.futures import ThreadPoolExecutor
+    pairs = np.asarray(pairs, np.int32).reshape(-1, 2)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        rows = list(ex.map(lambda pr: oracle_decode(w, layer, okc, ovc, pairs=pr.reshape(1, 2)), pairs))
+    return np.concatenate(rows) if rows else np.zeros((0, w.head_dim))
 
 
 def assert_close(gpu: np.ndarray, ref: np.ndarray, atol=ATOL, rtol=RTOL, what=""):
@@ -186,15 +205,19 @@ def step_rows_by_seq(w: syn.Workload, layer: syn.Layer):
 
 
 def gpu_decode_step(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_splits=0,
-                    dev: DeviceInputs = None, workspace=None, heads=None):
-    """One fused step: writes each sequence's last token and decodes.  Returns (out, workspace)."""
+                    dev: DeviceInputs = None, counters=None, heads=None, workspace=None):
+    """One fused step: writes each sequence's last token and decodes.  Returns (out,
+    counters): the counter buffer given (zero on entry), or a new one for this batch."""
     dev = dev or DeviceInputs(w)
     B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
     win = layer.sliding_window
     maxl = w.max_context_len
-    ws_bytes = F.fp8kv_decode_step_workspace_size(B, Hq, Hkv, D, w.block_size, maxl, win, num_splits)
+    if counters is None:
+        counters = new_counters(B, Hkv)
+    ws_bytes = F.fp8kv_paged_decode_workspace_size(B, Hq, Hkv, D, w.block_size, maxl, win, num_splits)
     if workspace is None:
-        workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
+        # filled with NaN bytes: the partials the step reads must all be its own
+        workspace = torch.full((max(ws_bytes, 256),), 0xFF, dtype=torch.uint8, device=DEV)
     ws_bytes = workspace.numel()           # the library checks what it needs against this
     kn, vn = step_rows_by_seq(w, layer)
     out = torch.empty(B * Hq * D, dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
@@ -202,19 +225,21 @@ def gpu_decode_step(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, nu
     if heads is None:
         F.fp8kv_decode_step(out, odt, dev.q, u16_dev(kn), u16_dev(vn), kc, vc, code(layer), dev.bt,
                             w.max_blocks_per_seq, dev.cl, maxl, B, Hq, Hkv, D, w.block_size,
-                            w.num_blocks, layer.k_scale, layer.v_scale, win, num_splits, workspace,
-                            ws_bytes)
+                            w.num_blocks, layer.k_scale, layer.v_scale, win, num_splits, counters,
+                            counters.numel(), workspace, ws_bytes)
     else:
         F.fp8kv_decode_step_per_head(out, odt, dev.q, u16_dev(kn), u16_dev(vn), kc, vc, code(layer),
                                      dev.bt, w.max_blocks_per_seq, dev.cl, maxl, B, Hq, Hkv, D,
                                      w.block_size, w.num_blocks, f32_dev(heads[0]),
-                                     f32_dev(heads[1]), win, num_splits, workspace, ws_bytes)
+                                     f32_dev(heads[1]), win, num_splits, counters,
+                                     counters.numel(), workspace, ws_bytes)
     torch.cuda.synchronize()
-    return out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D), workspace
+    return out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D), counters
 
 
 def gpu_prefill(w: syn.Workload, layer: syn.Layer, kc, vc, pq: syn.PrefillQueries, out_f32=False,
-                window=None, heads=None, context_lens=None, max_query_len=None):
+                window=None, heads=None, context_lens=None, max_query_len=None,
+                max_context_len=None):
     """fp8kv_paged_prefill (or the per-head variant) over caches kc / vc: [Tq][Hq][D]."""
     win = layer.sliding_window if window is None else window
     dev = DeviceInputs(w, context_lens=context_lens)
@@ -227,6 +252,8 @@ def gpu_prefill(w: syn.Workload, layer: syn.Layer, kc, vc, pq: syn.PrefillQuerie
     mql = pq.max_query_len if max_query_len is None else max_query_len
     odt = F.FP8KV_F32 if out_f32 else F.FP8KV_BF16
     maxl = w.max_context_len if context_lens is None else int(np.max(context_lens))
+    if max_context_len is not None:
+        maxl = max_context_len
     if heads is None:
         F.fp8kv_paged_prefill(out, odt, q, qsl, kc, vc, code(layer), dev.bt, w.max_blocks_per_seq,
                               dev.cl, maxl, w.num_seqs, mql, Hq, Hkv, D, w.block_size,

@@ -98,9 +98,22 @@ def _decode(**kw):
              cache_dtype=F.FP8KV_E4M3, block_tables=FAKE, max_blocks_per_seq=64, context_lens=FAKE,
              max_context_len=1024, num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=128,
              block_size=16, num_blocks=200, k_scale=1.0, v_scale=1.0, sliding_window=0,
-             num_splits=4, workspace=FAKE, workspace_bytes=0, stream=0)
+             num_splits=4, counters=0, counters_bytes=0, workspace=FAKE, workspace_bytes=0,
+             stream=0)
     a.update(kw)
     return F.lib.fp8kv_paged_decode(*a.values())
+
+
+def _step(**kw):
+    """fp8kv_decode_step with the same arguments as _decode plus the token rows."""
+    a = dict(out=FAKE, out_dtype=F.FP8KV_BF16, query=FAKE, key_new=FAKE, value_new=FAKE,
+             key_cache=FAKE, value_cache=FAKE, cache_dtype=F.FP8KV_E4M3, block_tables=FAKE,
+             max_blocks_per_seq=64, context_lens=FAKE, max_context_len=1024, num_seqs=2,
+             num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=200,
+             k_scale=1.0, v_scale=1.0, sliding_window=0, num_splits=4, counters=FAKE,
+             counters_bytes=1 << 20, workspace=FAKE, workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return F.lib.fp8kv_decode_step(*a.values())
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -118,9 +131,44 @@ def _decode(**kw):
     (dict(k_scale=0.0), F.FP8KV_ERR_SCALE), (dict(v_scale=float("nan")), F.FP8KV_ERR_SCALE),
     (dict(workspace=0), F.FP8KV_ERR_WORKSPACE), (dict(workspace_bytes=100), F.FP8KV_ERR_WORKSPACE),
     (dict(workspace=FAKE + 16, workspace_bytes=1 << 30), F.FP8KV_ERR_WORKSPACE),
+    # optional counters: checked when given (2 sequences x 8 kv heads need 16 records)
+    (dict(workspace_bytes=1 << 30, counters=FAKE, counters_bytes=16 * 1280 - 1), F.FP8KV_ERR_WORKSPACE),
+    (dict(workspace_bytes=1 << 30, counters=FAKE + 64, counters_bytes=1 << 20), F.FP8KV_ERR_WORKSPACE),
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(key_new=0), F.FP8KV_ERR_NULL), (dict(value_new=0), F.FP8KV_ERR_NULL),
+    (dict(key_new=FAKE + 2), F.FP8KV_ERR_SHAPE),
+    # several splits: the counter buffer is required, large enough and 256-byte aligned
+    (dict(counters=0), F.FP8KV_ERR_WORKSPACE),
+    (dict(counters_bytes=16 * 1280 - 4), F.FP8KV_ERR_WORKSPACE),
+    (dict(counters=FAKE + 128), F.FP8KV_ERR_WORKSPACE),
+    (dict(workspace=0), F.FP8KV_ERR_WORKSPACE), (dict(out_dtype=0), F.FP8KV_ERR_UNSUPPORTED),
+])
+def test_decode_step_rejects(kw, status):
+    assert _step(**kw) == status
+
+
+def test_decode_step_counters_optional_for_one_split():
+    # one split (33 blocks or fewer): no counters and no workspace are needed; with no
+    # sequences nothing is launched
+    assert _step(num_seqs=0, counters=0, workspace=0) == F.FP8KV_OK
+
+
+def test_counter_buffer_size():
+    assert F.fp8kv_decode_counters_size(8, 8) == 64 * 1280
+    assert F.fp8kv_decode_counters_size(0, 8) == 0
+    assert F.lib.fp8kv_decode_counters_size(-1, 8) == 0
+    assert F.lib.fp8kv_decode_counters_size(4, 0) == 0
+
+
+def test_error_word_setter():
+    assert F.lib.fp8kv_set_error_word(FAKE + 2) == F.FP8KV_ERR_SHAPE
+    assert F.lib.fp8kv_set_error_word(FAKE + 4) == F.FP8KV_OK
+    assert F.lib.fp8kv_set_error_word(0) == F.FP8KV_OK
 
 
 def _decode_ph(step=False, **kw):
@@ -128,7 +176,8 @@ def _decode_ph(step=False, **kw):
              cache_dtype=F.FP8KV_E4M3, block_tables=FAKE, max_blocks_per_seq=64, context_lens=FAKE,
              max_context_len=1024, num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=128,
              block_size=16, num_blocks=200, k_scales=FAKE, v_scales=FAKE, sliding_window=0,
-             num_splits=4, workspace=FAKE, workspace_bytes=0, stream=0)
+             num_splits=4, counters=FAKE, counters_bytes=1 << 20, workspace=FAKE,
+             workspace_bytes=0, stream=0)
     a.update(kw)
     if step:
         v = list(a.values())

@@ -1,6 +1,7 @@
 """The benchmark's byte and intensity formulas against the pages' worked numbers (CPU)."""
 import os
 
+import numpy as np
 import pytest
 
 import bench
@@ -59,7 +60,9 @@ def test_cpu_baseline_with_one_kv_head():
     """The oracle sample takes at most the workload's kv heads (the tiny shape has one)."""
     import synthetic as syn
     w = syn.tiny()
-    r = bench.cpu_baseline(w, w.layers[0])
+    r, ref = bench.cpu_baseline(w, w.layers[0])
     assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
     assert "query heads 0..3 (KV heads 0..0 of 1)" in r["sample"]
     assert r["multi_thread"]["value"] > 0
+    # the whole step's oracle output, which the bench compares with the last timed step
+    assert ref.shape == (w.num_seqs, w.num_q_heads, w.head_dim) and np.all(np.isfinite(ref))

@@ -28,8 +28,13 @@ def _every_bf16_workload(Hkv=2, D=128, seed=0):
     return w, keys, vals
 
 
+# (1.0, 1.0) and the last three pairs are powers of two on both tensors: the kernel then
+# multiplies by the exact reciprocal instead of dividing (2^-126: the smallest normal scale;
+# 2^127: a subnormal reciprocal); the others divide
 @pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.125, 3.0), (0.1, 36.5 / 448.0),
-                                             (1e-3, 7.0), (4.40625 / 448.0, 0.0078125)])
+                                             (1e-3, 7.0), (4.40625 / 448.0, 0.0078125),
+                                             (0.125, 2.0 ** -7), (2.0 ** -126, 2.0 ** 20),
+                                             (2.0 ** 127, 2.0 ** -3)])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_every_bf16_input_bit_exact(k_scale, v_scale, D):
     say(f"cache_write every-bf16 D={D} scales={k_scale},{v_scale}")

@@ -8,7 +8,8 @@ import torch
 import fp8_kv_cache_reshape_amd as F
 import oracle
 import synthetic as syn
-from gpu_util import (DEV, DeviceInputs, assert_close, say, step_rows_by_seq, to_host_bits, u16_dev)
+from gpu_util import (DEV, DeviceInputs, assert_close, new_counters, say, step_rows_by_seq, to_host_bits,
+                      u16_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +51,10 @@ def _oracle_write(w, L, ocodec, ks, vs):
 
 
 @pytest.mark.parametrize("name", sorted(CODECS))
-@pytest.mark.parametrize("scale", [1.0, 0.0371, 250.0])
+# 0.125, 2^-7, 2^-126, 2^20 and 2^127 (a subnormal reciprocal) are powers of two: the
+# multiply-by-reciprocal path; 0.0371 and 250 divide
+@pytest.mark.parametrize("scale", [1.0, 0.0371, 250.0, 0.125, 2.0 ** -7, 2.0 ** -126, 2.0 ** 20,
+                                   2.0 ** 127])
 def test_codec_write_every_bf16_input(name, scale):
     """Every bf16 bit pattern once as a key and once as a value element, scattered to random
     slots (the per-token store path) and, in a second write, to in-order slots (the
@@ -85,7 +89,7 @@ def _decode_gpu(w, L, codec, kc, vc, ks, vs, num_splits=0):
     out = torch.empty(B * Hq * D, dtype=torch.bfloat16, device=DEV)
     F.fp8kv_paged_decode(out, F.FP8KV_BF16, dev.q, kc, vc, codec, dev.bt, w.max_blocks_per_seq, dev.cl,
                          w.max_context_len, B, Hq, Hkv, D, 16, w.num_blocks, ks, vs, L.sliding_window,
-                         num_splits, ws, nb)
+                         num_splits, None, 0, ws, nb)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D)
 
@@ -118,13 +122,14 @@ def test_codec_decode_step_matches_oracle(name):
     kc, vc = _gpu_write(w, L, codec, ks, vs, rows=w.prefix_token_rows())
     dev = DeviceInputs(w)
     B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
-    nb = F.fp8kv_decode_step_workspace_size(B, Hq, Hkv, D, 16, w.max_context_len, 0, 0)
-    ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=DEV)
+    nb = F.fp8kv_paged_decode_workspace_size(B, Hq, Hkv, D, 16, w.max_context_len, 0, 0)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=DEV)
+    cnt = new_counters(B, Hkv)
     kn, vn = step_rows_by_seq(w, L)
     out = torch.empty(B * Hq * D, dtype=torch.bfloat16, device=DEV)
     F.fp8kv_decode_step(out, F.FP8KV_BF16, dev.q, u16_dev(kn), u16_dev(vn), kc, vc, codec, dev.bt,
                         w.max_blocks_per_seq, dev.cl, w.max_context_len, B, Hq, Hkv, D, 16,
-                        w.num_blocks, ks, vs, 0, 0, ws, nb)
+                        w.num_blocks, ks, vs, 0, 0, cnt, cnt.numel(), ws, nb)
     torch.cuda.synchronize()
     okc, ovc = _oracle_write(w, L, ocodec, ks, vs)
     assert np.array_equal(to_host_bits(kc), okc) and np.array_equal(to_host_bits(vc), ovc)

@@ -1,14 +1,16 @@
 """GPU parity of fp8kv_paged_decode against the fp64 oracle on small, ragged inputs that span
 several blocks, splits and a partial tail block, for every supported head_dim, several group
-ratios, both cache dtypes, windows and split counts."""
+ratios, both cache dtypes, windows and split counts; with the separate merge kernel and with
+a counter buffer (the partials merged inside the decode kernel)."""
 import numpy as np
 import pytest
 import torch
 
 import fp8_kv_cache_reshape_amd as F
+import oracle
 import synthetic as syn
 from gpu_util import (BF16, E4M3, DeviceInputs, assert_close, dev_caches, gpu_decode, gpu_write,
-                      oracle_decode, oracle_write, say)
+                      new_counters, oracle_decode, oracle_write, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,15 +25,18 @@ def _mk(Hq, Hkv, D, lens=LENS, cache=syn.E4M3, window=0, cid=40, std=1.0, outlie
                              layers=(("l0", window, cache),))
 
 
-def _run(w, out_f32=False, num_splits=0, window=None, split_api=False):
+def _run(w, out_f32=False, num_splits=0, window=None, split_api=False, fused=False):
     layer = w.layers[0]
     cdt = E4M3 if layer.cache_dtype == syn.E4M3 else BF16
     kc, vc = dev_caches(w, cdt)
     gpu_write(w, layer, kc, vc)
     okc, ovc = oracle_write(w, layer)
+    cnt = new_counters(w.num_seqs, w.num_kv_heads) if fused else None
     got = gpu_decode(w, layer, kc, vc, out_f32=out_f32, num_splits=num_splits, window=window,
-                     split_api=split_api)
+                     split_api=split_api, counters=cnt)
     ref = oracle_decode(w, layer, okc, ovc, window=window)
+    if fused:
+        assert not cnt.cpu().numpy().any(), "counters were not returned to zero"
     return got, ref
 
 
@@ -39,21 +44,45 @@ SHAPES = [(4, 1, 64), (2, 2, 64), (32, 8, 128), (64, 8, 128), (12, 2, 128), (16,
           (64, 8, 64), (8, 1, 256), (16, 1, 256)]
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("cache", [syn.E4M3, syn.BF16])
 @pytest.mark.parametrize("Hq,Hkv,D", SHAPES)
-def test_decode_matches_oracle(Hq, Hkv, D, cache):
+def test_decode_matches_oracle(Hq, Hkv, D, cache, fused):
     w = _mk(Hq, Hkv, D, cache=cache)
-    say(f"decode {w.name}")
-    got, ref = _run(w)
+    say(f"decode {w.name} fused={fused}")
+    got, ref = _run(w, fused=fused)
     assert_close(got, ref, what=w.name)
 
 
-@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 64])
-def test_split_counts(num_splits):
+# with counters: 64 splits merge in the kernel in two batches per lane; 129 are more than it
+# merges, so the merge kernel follows the decode
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 64, 129])
+def test_split_counts(num_splits, fused):
     w = _mk(32, 8, 128, lens=[5, 700, 2049, 16], cid=41)
-    say(f"decode splits={num_splits}")
-    got, ref = _run(w, num_splits=num_splits)
-    assert_close(got, ref, what=f"splits={num_splits}")
+    say(f"decode splits={num_splits} fused={fused}")
+    got, ref = _run(w, num_splits=num_splits, fused=fused, out_f32=True)
+    assert_close(got, ref, atol=2e-4, rtol=2e-3, what=f"splits={num_splits}")
+
+
+def test_in_kernel_merge_equals_merge_kernel():
+    """The same split partials merged by the last workgroup (counters given, fixed split
+    count: no run-time claims) and by the merge kernel: both sum the same fp32 partials, so
+    they differ by fp32 rounding only (at most 64 plain fp32 terms against a compensated sum:
+    2 * 64 * 2^-24 * max|V|); two runs of the in-kernel merge are bit-identical."""
+    w = _mk(64, 8, 128, lens=[4000, 333, 2500], cid=49)
+    say("decode in-kernel merge vs merge kernel")
+    layer = w.layers[0]
+    kc, vc = dev_caches(w, E4M3)
+    gpu_write(w, layer, kc, vc)
+    cnt = new_counters(w.num_seqs, w.num_kv_heads)
+    a = gpu_decode(w, layer, kc, vc, out_f32=True, num_splits=9)
+    b = gpu_decode(w, layer, kc, vc, out_f32=True, num_splits=9, counters=cnt)
+    c = gpu_decode(w, layer, kc, vc, out_f32=True, num_splits=9, counters=cnt)
+    assert np.array_equal(b, c)
+    assert not cnt.cpu().numpy().any()
+    vmax = float(np.nanmax(np.abs(oracle.e4m3_decode(oracle_write(w, layer)[1])))) * layer.v_scale
+    assert np.abs(a - b).max() <= 2 * 64 * 2.0 ** -24 * vmax
 
 
 @pytest.mark.parametrize("window", [1, 2, 15, 16, 17, 128, 129, 512, 5000])

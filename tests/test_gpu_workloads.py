@@ -7,8 +7,9 @@ import pytest
 import torch
 
 import synthetic as syn
-from gpu_util import (BF16, E4M3, DeviceInputs, assert_close, dev_caches, gpu_decode, gpu_write,
-                      oracle_decode, oracle_write, sample_pairs, say, to_host_bits)
+from gpu_util import (BF16, E4M3, DeviceInputs, assert_close, dev_caches, gpu_decode, gpu_decode_step,
+                      gpu_write, new_counters, oracle_decode, oracle_decode_threaded, oracle_write,
+                      sample_pairs, say, to_host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +55,37 @@ def test_llama8b_headline_128k():
     w = syn.llama8b_long(131072, "amax")
     say(f"workload {w.name}")
     _layer_parity(w, w.layers[0], sample_pairs(w, 6))
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_headline_b8_128k():
+    """8 sequences x 131,072 tokens (2.15 GB of fp8 KV per step), in the benchmark's launch
+    configuration: the fused step (each sequence's token written, automatic splits, partials
+    merged in the kernel) against the oracle on sampled query heads of every sequence, the
+    whole caches byte for byte, and the two-call path with the in-kernel merge on the same
+    cache."""
+    w = syn.llama8b_long(131072, "amax", num_seqs=8)
+    layer = w.layers[0]
+    say(f"workload {w.name}: writing the context")
+    kc, vc = dev_caches(w, E4M3)
+    gpu_write(w, layer, kc, vc, rows=w.prefix_token_rows())
+    dev = DeviceInputs(w)
+    say("fused step")
+    got, cnt = gpu_decode_step(w, layer, kc, vc, dev=dev)
+    assert not cnt.cpu().numpy().any(), "counters were not returned to zero"
+    assert np.all(np.isfinite(got))
+    say("oracle write")
+    okc, ovc = oracle_write(w, layer)
+    assert np.array_equal(to_host_bits(kc), okc), "key cache bytes differ"
+    assert np.array_equal(to_host_bits(vc), ovc), "value cache bytes differ"
+    pairs = sample_pairs(w, 2)
+    say(f"oracle decode of {len(pairs)} (sequence, head) pairs")
+    ref = oracle_decode_threaded(w, layer, okc, ovc, pairs)
+    assert_close(got[pairs[:, 0], pairs[:, 1]], ref, what=f"{w.name} fused step")
+    two = gpu_decode(w, layer, kc, vc, dev=dev, counters=new_counters(w.num_seqs, w.num_kv_heads))
+    assert_close(two[pairs[:, 0], pairs[:, 1]], ref, what=f"{w.name} two-call path")
+    del kc, vc
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("skip_sw", [False, True])

@@ -77,6 +77,18 @@ def test_int8_encode_is_rint_and_clip():
                                   np.arange(256, dtype=np.uint8).view(np.int8).astype(np.float64))
 
 
+def test_int8_hand_ties_and_clamp():
+    """Hand values: halves round to the even integer (2.5 -> 2, 3.5 -> 4, -3.5 -> -4,
+    -2.5 -> -2, 0.5 -> 0, -0.5 -> 0), just off a half rounds to nearest, 126.5 -> 126 and
+    127.5 -> 127 (the even neighbour 128 clamps to 127), -127.5 and below clamp to -127
+    (never -128)."""
+    cases = {2.5: 2, 3.5: 4, -3.5: -4, -2.5: -2, 0.5: 0, -0.5: 0, 1.5: 2, -1.5: -2,
+             2.5000001: 3, 2.4999999: 2, 126.5: 126, 127.5: 127, 128.0: 127, -127.5: -127,
+             -128.0: -127, -1e30: -127, 0.0: 0, -0.0: 0}
+    got = oracle.int8_encode(np.array(list(cases), dtype=np.float64)).view(np.int8).tolist()
+    assert got == list(cases.values())
+
+
 def _small_integer_workload(cid):
     """Elements in {0, +-1, +-2, +-3, +-4}: with scale 1 every codec stores them exactly."""
     w = syn.make_workload(f"codec-{cid}", cid, num_q_heads=8, num_kv_heads=2, head_dim=64,
