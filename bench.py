@@ -320,18 +320,19 @@ def measured_traffic(root: str):
     return None
 
 
-def read_ceiling(torch, root: str, gib: int = 2, launches: int = 10) -> dict:
+def read_ceiling(torch, root: str, gib: int = 2, launches: int = 20) -> dict:
     """Streaming-read ceiling of this GPU: a plain kernel reading `gib` GiB once with 16-byte
     nontemporal loads (libfp8kv_probe.so), averaged over back-to-back launches, swept over grid
-    sizes and loads in flight per thread; the best rate is the ceiling.  `converged` says
-    whether the best rate is within 1 % of the best rate at half its grid (a plateau)."""
+    sizes, loads in flight per thread and two access patterns (grid-stride, and contiguous
+    runs per workgroup); the best rate is the ceiling.  `converged` says whether the same
+    pattern and loads in flight at half the best grid reach within 1 % of it (a plateau)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(root, "fp8_kv_cache_reshape_amd", "libfp8kv_probe.so"))
     lib.fp8kv_probe_read_granule.restype = ctypes.c_size_t
     lib.fp8kv_probe_read_granule.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.fp8kv_probe_read.restype = ctypes.c_int
     lib.fp8kv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
-                                     ctypes.c_void_p, ctypes.c_void_p]
+                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     grids = (1024, 2048, 4096, 8192, 16384, 32768)
     unrolls = (8, 16)
     g = max(lib.fp8kv_probe_read_granule(grid, u) for grid in grids for u in unrolls)
@@ -340,28 +341,31 @@ def read_ceiling(torch, root: str, gib: int = 2, launches: int = 10) -> dict:
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     stream = int(torch.cuda.current_stream().cuda_stream)
     rates = {}
-    for u in unrolls:
-        for grid in grids:
-            call = lambda: lib.fp8kv_probe_read(buf.data_ptr(), n, grid, u, sink.data_ptr(), stream)
-            for _ in range(2):
-                assert call() == 0, "read-ceiling probe launch failed"
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(launches):
-                call()
-            e1.record()
-            torch.cuda.synchronize()
-            rates[(grid, u)] = n / (e0.elapsed_time(e1) / launches * 1e-3) / 1e9
+    for pat in (0, 1):
+        for u in unrolls:
+            for grid in grids:
+                call = lambda: lib.fp8kv_probe_read(buf.data_ptr(), n, grid, u, pat, sink.data_ptr(), stream)
+                for _ in range(2):
+                    assert call() == 0, "read-ceiling probe launch failed"
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(launches):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
+                rates[(pat, grid, u)] = n / (e0.elapsed_time(e1) / launches * 1e-3) / 1e9
     del buf
     best = max(rates, key=rates.get)
-    half = (best[0] // 2, best[1])
+    half = (best[0], best[1] // 2, best[2])
     converged = half in rates and rates[half] >= 0.99 * rates[best]
-    return {"GBps": round(rates[best], 1), "bytes": n, "grid": best[0], "loads_in_flight": best[1],
-            "GBps_by_grid": {f"{grd}x{u}": round(r, 1) for (grd, u), r in rates.items()},
+    names = ("stride", "chunk")
+    return {"GBps": round(rates[best], 1), "bytes": n, "pattern": names[best[0]], "grid": best[1],
+            "loads_in_flight": best[2],
+            "GBps_by_config": {f"{names[p]}-{grd}x{u}": round(r, 1) for (p, grd, u), r in rates.items()},
             "converged": bool(converged),
-            "kernel": "grid-stride 16-byte nontemporal reads, 256 threads per workgroup; keys are "
-                      "grid x loads in flight per thread"}
+            "kernel": "16-byte nontemporal reads, 256 threads per workgroup; keys are pattern (grid-"
+                      "stride or contiguous runs per workgroup), grid x loads in flight per thread"}
 
 
 def _oracle_threads() -> int:
@@ -457,6 +461,7 @@ def main(argv=None):
     ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of rotated cache instances")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16-KV instantiation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read probe")
     ap.add_argument("--profile", action="store_true",
                     help="short run for a profiler: fused step only, no bf16 variant, no CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -593,7 +598,7 @@ def main(argv=None):
     del bench
     torch.cuda.empty_cache()
 
-    if not args.profile:
+    if not (args.profile or args.no_read_ceiling):
         rc = read_ceiling(torch, root)
         result["read_ceiling"] = rc
         result["pct_of_read_ceiling"] = round(100 * value / rc["GBps"], 2)

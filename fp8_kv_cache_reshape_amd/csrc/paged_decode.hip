@@ -272,8 +272,12 @@ __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) 
 // 2-byte caches need more and run one wave per SIMD.
 // The variant with a second (low) query term -- the rotated query, carried as two bf16
 // terms -- runs one wave per SIMD.
+#ifndef FP8KV_DECODE_WPE
+#define FP8KV_DECODE_WPE 0
+#endif
 template <int D, int C, bool QLO>
 constexpr int partial_waves_per_eu() {
+    if (FP8KV_DECODE_WPE > 0) return FP8KV_DECODE_WPE;
     return QLO ? 1 : ((D <= 128 && C != kCodecBF16) || D == 64 ? 2 : 1);
 }
 

@@ -11,21 +11,33 @@ constexpr int kThreads = 256;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// U: independent 16-byte loads in flight per thread.
-template <int U>
+// U: independent 16-byte loads in flight per thread.  CHUNK = false: grid-stride (load u of
+// a thread is u grid-widths after its first); CHUNK = true: each workgroup reads a contiguous
+// run of U * 4 KiB per iteration (load u is u * 4 KiB after the first), the next run a grid
+// of runs further on.
+template <int U, bool CHUNK>
 __global__ __launch_bounds__(kThreads) void read_ceiling_kernel(const u32x4* p, size_t n16, unsigned* sink) {
     const size_t tid = (size_t)blockIdx.x * kThreads + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * kThreads;
     u32x4 acc = {0u, 0u, 0u, 0u};
     // the host guarantees n16 is a multiple of U * stride: every index below is < n16
-    for (size_t base = tid; base < n16; base += U * stride) {
+    const size_t first = CHUNK ? (size_t)blockIdx.x * U * kThreads + threadIdx.x : tid;
+    const size_t step = CHUNK ? kThreads : stride;
+    for (size_t base = first; base < n16; base += U * stride) {
         u32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + base + u * stride);
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + base + u * step);
 #pragma unroll
         for (int u = 0; u < U; ++u) acc ^= v[u];
     }
     if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[0] = 1u;   // keeps the loads
+}
+
+template <bool CHUNK>
+const void* kernel_for(int u) {
+    return u == 4 ? reinterpret_cast<const void*>(&read_ceiling_kernel<4, CHUNK>)
+         : u == 8 ? reinterpret_cast<const void*>(&read_ceiling_kernel<8, CHUNK>)
+                  : reinterpret_cast<const void*>(&read_ceiling_kernel<16, CHUNK>);
 }
 
 bool unroll_ok(int u) { return u == 4 || u == 8 || u == 16; }
@@ -42,10 +54,12 @@ size_t fp8kv_probe_read_granule(int grid, int unroll) {
 }
 
 // Reads `bytes` of device memory at `buf` (16-byte aligned) once, with `grid` workgroups of 256
-// threads, each thread keeping `unroll` loads in flight.  `sink` is a device word the kernel
-// may write.  Returns 0, -2 for a bad size, grid, unroll or alignment, -6 for a launch error.
-int fp8kv_probe_read(const void* buf, size_t bytes, int grid, int unroll, void* sink, void* stream) {
-    if (grid <= 0 || grid > 65536 || !unroll_ok(unroll)) return -2;
+// threads, each thread keeping `unroll` loads in flight; pattern 0 = grid-stride, 1 =
+// contiguous runs per workgroup.  `sink` is a device word the kernel may write.  Returns 0,
+// -2 for a bad size, grid, unroll, pattern or alignment, -6 for a launch error.
+int fp8kv_probe_read(const void* buf, size_t bytes, int grid, int unroll, int pattern, void* sink,
+                     void* stream) {
+    if (grid <= 0 || grid > 65536 || !unroll_ok(unroll) || (pattern != 0 && pattern != 1)) return -2;
     const size_t g = fp8kv_probe_read_granule(grid, unroll);
     if (!buf || !sink || bytes == 0 || bytes % g != 0 || (reinterpret_cast<uintptr_t>(buf) & 15u) != 0)
         return -2;
@@ -53,9 +67,7 @@ int fp8kv_probe_read(const void* buf, size_t bytes, int grid, int unroll, void* 
     size_t n16 = bytes / 16;
     unsigned* s = static_cast<unsigned*>(sink);
     void* args[] = {&p, &n16, &s};
-    const void* fn = unroll == 4 ? reinterpret_cast<const void*>(&read_ceiling_kernel<4>)
-                   : unroll == 8 ? reinterpret_cast<const void*>(&read_ceiling_kernel<8>)
-                                 : reinterpret_cast<const void*>(&read_ceiling_kernel<16>);
+    const void* fn = pattern == 1 ? kernel_for<true>(unroll) : kernel_for<false>(unroll);
     return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, static_cast<hipStream_t>(stream)) ==
                    hipSuccess ? 0 : -6;
 }
