@@ -21,6 +21,7 @@ FP8KV_ERR_UNSUPPORTED = -3
 FP8KV_ERR_SCALE = -4
 FP8KV_ERR_WORKSPACE = -5
 FP8KV_ERR_HIP = -6
+FP8KV_ERR_SCRATCH = -7
 
 FP8KV_E4M3 = 0
 FP8KV_BF16 = 1
@@ -29,6 +30,10 @@ FP8KV_E5M2 = 3
 FP8KV_INT8 = 4
 
 BLOCK_SIZE = 16
+
+# limits of fp8kv_decode_step_noalloc's fixed device array
+FP8KV_NOALLOC_MAX_GROUPS = 2048
+FP8KV_NOALLOC_MAX_PARTIAL_BYTES = 14155776
 
 # bits of the device error word (fp8kv_set_error_word)
 FP8KV_DEVERR_BLOCK_ID = 1
@@ -60,6 +65,8 @@ SIGNATURES = {
                                _I, _F, _F, _I, _I, _P, _SZ, _P, _SZ, _P]),
     "fp8kv_decode_step_per_head": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I,
                                         _I, _I, _I, _I, _P, _P, _I, _I, _P, _SZ, _P, _SZ, _P]),
+    "fp8kv_decode_step_noalloc": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
+                                       _I, _I, _I, _F, _F, _I, _I, _P]),
     "fp8kv_paged_prefill": (_I, [_P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I,
                                  _I, _I, _F, _F, _I, _P]),
     "fp8kv_paged_prefill_per_head": (_I, [_P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
@@ -266,6 +273,22 @@ def fp8kv_decode_step_per_head(out, out_dtype, query, key_new, value_new, key_ca
                                                  counters_bytes, _addr(workspace),
                                                  workspace_bytes, _stream(stream)),
                   "fp8kv_decode_step_per_head")
+
+
+def fp8kv_decode_step_noalloc(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
+                              cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                              max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              block_size, num_blocks, k_scale, v_scale, sliding_window, num_splits,
+                              stream=None) -> int:
+    return _check(lib.fp8kv_decode_step_noalloc(_addr(out), out_dtype, _addr(query), _addr(key_new),
+                                                _addr(value_new), _addr(key_cache),
+                                                _addr(value_cache), cache_dtype,
+                                                _addr(block_tables), max_blocks_per_seq,
+                                                _addr(context_lens), max_context_len, num_seqs,
+                                                num_q_heads, num_kv_heads, head_dim, block_size,
+                                                num_blocks, k_scale, v_scale, sliding_window,
+                                                num_splits, _stream(stream)),
+                  "fp8kv_decode_step_noalloc")
 
 
 def fp8kv_paged_prefill(out, out_dtype, query, query_start_loc, key_cache, value_cache,

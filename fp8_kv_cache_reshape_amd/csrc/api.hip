@@ -320,7 +320,7 @@ int decode_step_impl(void* out, int out_dtype, const void* query, const void* ke
                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                      int num_blocks, const Scales& sc, bool per_head_call, int sliding_window,
                      int num_splits, void* counters, size_t counters_bytes, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     size_t workspace_bytes, void* stream, bool launch = true) {
     if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
     fp8kv::DecodeParams p;
     bool fp8 = true;
@@ -336,6 +336,7 @@ int decode_step_impl(void* out, int out_dtype, const void* query, const void* ke
     // several splits: the counters are required (arrival, and claims with the automatic plan)
     const int fused = attach_counters(p, head_dim, counters, counters_bytes, num_splits);
     if (fused < 0) return fused;
+    if (!launch) return FP8KV_OK;   // validation only
     p.out = out;
     p.out_f32 = out_dtype == FP8KV_F32;
     p.k_new = static_cast<const uint16_t*>(key_new);
@@ -420,6 +421,23 @@ RotatedLayout rotated_layout(size_t decode_bytes, int num_seqs, int num_q_heads,
 
 }  // namespace
 
+int fp8kv::decode_step_check(void* out, int out_dtype, const void* query, const void* key_new,
+                             const void* value_new, void* key_cache, void* value_cache,
+                             int cache_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len, int num_seqs,
+                             int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                             int num_blocks, float k_scale, float v_scale, int sliding_window,
+                             int num_splits, size_t counters_bytes, size_t workspace_bytes) {
+    // placeholder buffers of the given sizes (256-byte aligned, never dereferenced here)
+    void* const buf = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+    return decode_step_impl(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
+                            cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                            max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            block_size, num_blocks, tensor_scales(k_scale, v_scale), false,
+                            sliding_window, num_splits, buf, counters_bytes, buf, workspace_bytes,
+                            nullptr, false);
+}
+
 extern "C" {
 
 const char* fp8kv_status_string(int status) {
@@ -431,6 +449,7 @@ const char* fp8kv_status_string(int status) {
         case FP8KV_ERR_SCALE: return "a scale of a one-byte cache is not finite and positive";
         case FP8KV_ERR_WORKSPACE: return "workspace is NULL, too small, or not 256-byte aligned";
         case FP8KV_ERR_HIP: return "a HIP kernel launch failed";
+        case FP8KV_ERR_SCRATCH: return "the call needs more than the fixed device array of fp8kv_decode_step_noalloc holds";
         default: return "unknown status";
     }
 }

@@ -174,6 +174,16 @@ inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, size_t ld
 // Remember a HIP error for fp8kv_last_hip_error (the calling thread's most recent).
 void record_hip_error(hipError_t e);
 
+// Every host check fp8kv_decode_step makes, for counter and workspace buffers of the given
+// sizes, without any HIP call: FP8KV_OK or the status the step would return.
+int decode_step_check(void* out, int out_dtype, const void* query, const void* key_new,
+                      const void* value_new, void* key_cache, void* value_cache, int cache_dtype,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int max_context_len, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, float k_scale, float v_scale, int sliding_window,
+                      int num_splits, size_t counters_bytes, size_t workspace_bytes);
+
 // `codec`: the cache element codec (kCodecBF16 or a one-byte codec).
 hipError_t launch_cache_write(const CacheWriteParams& p, Codec codec, int head_dim, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeParams& p, Codec codec, int head_dim, hipStream_t s);

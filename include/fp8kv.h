@@ -22,7 +22,8 @@
  * Conventions for every call
  *   - All pointers except the scalars are DEVICE pointers the caller owns.  The library
  *     allocates nothing and is thread-safe.  Its only state is, per host thread, the
- *     optional device error word set by fp8kv_set_error_word.
+ *     optional device error word set by fp8kv_set_error_word (and the fixed device array of
+ *     fp8kv_decode_step_noalloc, the one entry point that takes no caller buffers).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
  *     returns without synchronising.
  *   - Arguments are validated on the host before any HIP call; a failed check returns a
@@ -77,6 +78,8 @@ extern "C" {
 #define FP8KV_ERR_SCALE       (-4)  /* an fp8 scale is not finite and positive            */
 #define FP8KV_ERR_WORKSPACE   (-5)  /* workspace NULL, too small, or not 256-byte aligned */
 #define FP8KV_ERR_HIP         (-6)  /* a kernel launch failed                             */
+#define FP8KV_ERR_SCRATCH     (-7)  /* fp8kv_decode_step_noalloc: the call needs more than
+                                       its fixed device array holds                       */
 
 /* Element type codes. */
 #define FP8KV_E4M3 0   /* OCP FP8 E4M3 ("fn"): bias 7, max 448, no infinities, NaN = S.1111.111 */
@@ -383,6 +386,36 @@ int fp8kv_decode_step_per_head(void* out, int out_dtype, const void* query,
                                int sliding_window, int num_splits,
                                void* counters, size_t counters_bytes,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8kv_decode_step_noalloc -- fp8kv_decode_step with no counter buffer and no workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The split counters and partials live in a fixed
+ * 16 MiB device array of the library, one per GPU, held until the process ends: counter
+ * records for up to FP8KV_NOALLOC_MAX_GROUPS (sequence, kv head) groups and up to
+ * FP8KV_NOALLOC_MAX_PARTIAL_BYTES of partials (fp8kv_paged_decode_workspace_size of the
+ * call).  A call over either limit returns FP8KV_ERR_SCRATCH and enqueues nothing.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ * The array belongs to the current device (hipGetDevice) of the calling thread; `stream`
+ * must be a stream of that device.  The first call on a device looks up the array's address
+ * and enqueues a clear of its counter region on `stream`, before its own kernel; every call
+ * leaves the counters zero again.  All calls on one device share the array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give wrong results --
+ * serialise them (one stream), or use fp8kv_decode_step with buffers of their own.
+ * Arguments, results, reproducibility and errors otherwise as for fp8kv_decode_step.
+ */
+#define FP8KV_NOALLOC_MAX_GROUPS        2048
+#define FP8KV_NOALLOC_MAX_PARTIAL_BYTES ((size_t)14155776)   /* 16 MiB - 2048 * 1280 */
+int fp8kv_decode_step_noalloc(void* out, int out_dtype, const void* query,
+                              const void* key_new, const void* value_new,
+                              void* key_cache, void* value_cache, int cache_dtype,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* context_lens, int max_context_len,
+                              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks,
+                              float k_scale, float v_scale, int sliding_window, int num_splits,
+                              void* stream);
 
 /*
  * fp8kv_paged_prefill -- prefill / chunked-prefill attention over the paged cache: the

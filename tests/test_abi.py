@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert F.fp8kv_status_string(st) and F.fp8kv_status_string(st) != "unknown status"
     assert F.fp8kv_status_string(-99) == "unknown status"
     assert F.fp8kv_version() >= 100
@@ -238,3 +238,31 @@ def test_single_hip_runtime_in_process():
             "print(len(set(l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l)))\n")
     out = subprocess.check_output([sys.executable, "-c", code], cwd=ROOT, text=True)
     assert out.strip() == "1"
+
+
+def _noalloc(**kw):
+    a = dict(out=FAKE, out_dtype=F.FP8KV_BF16, query=FAKE, key_new=FAKE, value_new=FAKE,
+             key_cache=FAKE, value_cache=FAKE, cache_dtype=F.FP8KV_E4M3, block_tables=FAKE,
+             max_blocks_per_seq=1 << 14, context_lens=FAKE, max_context_len=4096, num_seqs=2,
+             num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=1 << 20,
+             k_scale=1.0, v_scale=1.0, sliding_window=0, num_splits=0, stream=0)
+    a.update(kw)
+    return F.lib.fp8kv_decode_step_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    # more (sequence, kv head) groups than the array has counter records for, in a call that
+    # needs counters (two splits); a one-split call needs neither counters nor partials
+    (dict(num_seqs=F.FP8KV_NOALLOC_MAX_GROUPS // 8 + 1, num_splits=2), F.FP8KV_ERR_SCRATCH),
+    # 1024 splits x 32 heads x 130 floats of partials: more than the array's 13.5 MiB
+    (dict(num_seqs=1, max_context_len=1 << 18, num_splits=1024), F.FP8KV_ERR_SCRATCH),
+    # the step's own checks, before the array is touched
+    (dict(head_dim=96), F.FP8KV_ERR_UNSUPPORTED), (dict(num_q_heads=30), F.FP8KV_ERR_SHAPE),
+    (dict(k_scale=0.0), F.FP8KV_ERR_SCALE),
+])
+def test_decode_step_noalloc_rejects_on_the_host(kw, status):
+    assert _noalloc(**kw) == status
+
+
+def test_decode_step_noalloc_empty_batch_is_a_no_op():
+    assert _noalloc(num_seqs=0, query=0, out=0) == F.FP8KV_OK
