@@ -61,6 +61,10 @@ SIGNATURES = {
                                         _F, _I, _I, _P, _SZ, _P]),
     "fp8kv_paged_decode_merge": (_I, [_P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P,
                                       _SZ, _P]),
+    "fp8kv_paged_decode_partial_per_head": (_I, [_P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I,
+                                                 _I, _I, _P, _I, _I, _P, _SZ, _P]),
+    "fp8kv_paged_decode_merge_per_head": (_I, [_P, _I, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P,
+                                               _I, _I, _P, _SZ, _P]),
     "fp8kv_decode_step": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I,
                                _I, _F, _F, _I, _I, _P, _SZ, _P, _SZ, _P]),
     "fp8kv_decode_step_per_head": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I,
@@ -238,6 +242,30 @@ def fp8kv_paged_decode_merge(out, out_dtype, context_lens, max_context_len, max_
                                                v_scale, sliding_window, num_splits, _addr(workspace),
                                                workspace_bytes, _stream(stream)),
                   "fp8kv_paged_decode_merge")
+
+
+def fp8kv_paged_decode_partial_per_head(query, key_cache, value_cache, cache_dtype, block_tables,
+                                        max_blocks_per_seq, context_lens, max_context_len,
+                                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                        num_blocks, k_scales, sliding_window, num_splits,
+                                        workspace, workspace_bytes, stream=None) -> int:
+    return _check(lib.fp8kv_paged_decode_partial_per_head(
+        _addr(query), _addr(key_cache), _addr(value_cache), cache_dtype, _addr(block_tables),
+        max_blocks_per_seq, _addr(context_lens), max_context_len, num_seqs, num_q_heads,
+        num_kv_heads, head_dim, block_size, num_blocks, _addr(k_scales), sliding_window,
+        num_splits, _addr(workspace), workspace_bytes, _stream(stream)),
+        "fp8kv_paged_decode_partial_per_head")
+
+
+def fp8kv_paged_decode_merge_per_head(out, out_dtype, cache_dtype, context_lens, max_context_len,
+                                      max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads,
+                                      head_dim, block_size, v_scales, sliding_window, num_splits,
+                                      workspace, workspace_bytes, stream=None) -> int:
+    return _check(lib.fp8kv_paged_decode_merge_per_head(
+        _addr(out), out_dtype, cache_dtype, _addr(context_lens), max_context_len,
+        max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+        _addr(v_scales), sliding_window, num_splits, _addr(workspace), workspace_bytes,
+        _stream(stream)), "fp8kv_paged_decode_merge_per_head")
 
 
 def fp8kv_decode_step(out, out_dtype, query, key_new, value_new, key_cache, value_cache,

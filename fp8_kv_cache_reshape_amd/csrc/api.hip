@@ -402,6 +402,61 @@ int paged_prefill_impl(void* out, int out_dtype, const void* query,
     return hip_status(fp8kv::launch_prefill(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
 }
 
+int partial_impl(const void* query, const void* key_cache, const void* value_cache,
+                 int cache_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+                 const int32_t* context_lens, int max_context_len, int num_seqs, int num_q_heads,
+                 int num_kv_heads, int head_dim, int block_size, int num_blocks, const Scales& sc,
+                 bool per_head_call, int sliding_window, int num_splits, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    fp8kv::DecodeParams p;
+    bool fp8 = true;
+    // the per-head call's key array stands in for both arrays in the shared checks
+    int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
+                          max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, sc,
+                          per_head_call, sliding_window, num_splits, workspace, workspace_bytes,
+                          true);
+    if (st != FP8KV_OK || num_seqs == 0) return st;
+    p.v_scales = nullptr;   // the merge applies the value scales
+    return hip_status(fp8kv::launch_decode_partial(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int merge_impl(void* out, int out_dtype, const int32_t* context_lens, int max_context_len,
+               int max_blocks_per_seq, int num_seqs, int num_q_heads, int num_kv_heads,
+               int head_dim, int block_size, float v_scale, const float* v_scales,
+               int sliding_window, int num_splits, const void* workspace, size_t workspace_bytes,
+               void* stream) {
+    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_context_len, sliding_window, num_splits);
+    if (st != FP8KV_OK) return st;
+    if (max_blocks_per_seq < 0) return FP8KV_ERR_SHAPE;
+    if (num_seqs == 0) return FP8KV_OK;
+    if (!out || !context_lens) return FP8KV_ERR_NULL;
+    if (!aligned16(out)) return FP8KV_ERR_SHAPE;
+    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, max_context_len, sliding_window, num_splits);
+    const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits);
+    if (!workspace || workspace_bytes < wl.total) return FP8KV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP8KV_ERR_WORKSPACE;
+    fp8kv::DecodeParams p = {};
+    p.out = out;
+    p.out_f32 = out_dtype == FP8KV_F32;
+    p.context_lens = context_lens;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_context_len = max_context_len;
+    p.num_seqs = num_seqs;
+    p.num_q_heads = num_q_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.sliding_window = sliding_window;
+    p.v_scale = v_scale;
+    p.v_scales = v_scales;
+    p.splits = pl.splits;
+    p.blocks_per_split = pl.blocks_per_split;
+    p.ws_ml = reinterpret_cast<float*>(const_cast<void*>(workspace));
+    p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) + wl.acc_offset);
+    return hip_status(fp8kv::launch_decode_merge(p, head_dim, static_cast<hipStream_t>(stream)));
+}
+
 // The rotated decode's workspace: the decode's own (split partials), then the rotated
 // query as two bf16 terms, then the f32 output before it is rotated back; each 256-aligned.
 struct RotatedLayout {
@@ -581,15 +636,29 @@ int fp8kv_paged_decode_partial(const void* query, const void* key_cache, const v
                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                float k_scale, int sliding_window, int num_splits, void* workspace,
                                size_t workspace_bytes, void* stream) {
-    fp8kv::DecodeParams p;
-    bool fp8 = true;
-    int st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
-                          max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                          tensor_scales(k_scale, 1.0f), false, sliding_window, num_splits,
-                          workspace, workspace_bytes, true);
-    if (st != FP8KV_OK || num_seqs == 0) return st;
-    return hip_status(fp8kv::launch_decode_partial(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
+    return partial_impl(query, key_cache, value_cache, cache_dtype, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                        num_kv_heads, head_dim, block_size, num_blocks, tensor_scales(k_scale, 1.0f),
+                        false, sliding_window, num_splits, workspace, workspace_bytes, stream);
+}
+
+int fp8kv_paged_decode_partial_per_head(const void* query, const void* key_cache,
+                                        const void* value_cache, int cache_dtype,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* context_lens, int max_context_len,
+                                        int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int num_blocks,
+                                        const float* k_scales, int sliding_window, int num_splits,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    // the value scales belong to the merge: only the key array is checked here
+    if (cache_dtype != FP8KV_BF16) {
+        if (!k_scales) return FP8KV_ERR_NULL;
+        if (!aligned4(k_scales)) return FP8KV_ERR_SHAPE;
+    }
+    return partial_impl(query, key_cache, value_cache, cache_dtype, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                        num_kv_heads, head_dim, block_size, num_blocks, head_scales(k_scales, k_scales),
+                        true, sliding_window, num_splits, workspace, workspace_bytes, stream);
 }
 
 int fp8kv_paged_decode_merge(void* out, int out_dtype, const int32_t* context_lens,
@@ -597,35 +666,29 @@ int fp8kv_paged_decode_merge(void* out, int out_dtype, const int32_t* context_le
                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                              float v_scale, int sliding_window, int num_splits,
                              const void* workspace, size_t workspace_bytes, void* stream) {
-    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
-    int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                max_context_len, sliding_window, num_splits);
-    if (st != FP8KV_OK) return st;
-    if (max_blocks_per_seq < 0) return FP8KV_ERR_SHAPE;
     if (!scale_ok(v_scale)) return FP8KV_ERR_SCALE;
-    if (num_seqs == 0) return FP8KV_OK;
-    if (!out || !context_lens) return FP8KV_ERR_NULL;
-    if (!aligned16(out)) return FP8KV_ERR_SHAPE;
-    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, max_context_len, sliding_window, num_splits);
-    const WorkspaceLayout wl = workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits);
-    if (!workspace || workspace_bytes < wl.total) return FP8KV_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP8KV_ERR_WORKSPACE;
-    fp8kv::DecodeParams p = {};   // per-tensor: no scale arrays
-    p.out = out;
-    p.out_f32 = out_dtype == FP8KV_F32;
-    p.context_lens = context_lens;
-    p.max_blocks_per_seq = max_blocks_per_seq;
-    p.max_context_len = max_context_len;
-    p.num_seqs = num_seqs;
-    p.num_q_heads = num_q_heads;
-    p.num_kv_heads = num_kv_heads;
-    p.sliding_window = sliding_window;
-    p.v_scale = v_scale;
-    p.splits = pl.splits;
-    p.blocks_per_split = pl.blocks_per_split;
-    p.ws_ml = reinterpret_cast<float*>(const_cast<void*>(workspace));
-    p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) + wl.acc_offset);
-    return hip_status(fp8kv::launch_decode_merge(p, head_dim, static_cast<hipStream_t>(stream)));
+    return merge_impl(out, out_dtype, context_lens, max_context_len, max_blocks_per_seq, num_seqs,
+                      num_q_heads, num_kv_heads, head_dim, block_size, v_scale, nullptr,
+                      sliding_window, num_splits, workspace, workspace_bytes, stream);
+}
+
+int fp8kv_paged_decode_merge_per_head(void* out, int out_dtype, int cache_dtype,
+                                      const int32_t* context_lens, int max_context_len,
+                                      int max_blocks_per_seq, int num_seqs, int num_q_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      const float* v_scales, int sliding_window, int num_splits,
+                                      const void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+    if (!cache_dtype_ok(cache_dtype)) return FP8KV_ERR_UNSUPPORTED;
+    const bool fp8 = cache_dtype != FP8KV_BF16;
+    if (fp8) {
+        if (!v_scales) return FP8KV_ERR_NULL;
+        if (!aligned4(v_scales)) return FP8KV_ERR_SHAPE;
+    }
+    return merge_impl(out, out_dtype, context_lens, max_context_len, max_blocks_per_seq, num_seqs,
+                      num_q_heads, num_kv_heads, head_dim, block_size, 1.0f,
+                      fp8 ? v_scales : nullptr, sliding_window, num_splits, workspace,
+                      workspace_bytes, stream);
 }
 
 int fp8kv_paged_prefill(void* out, int out_dtype, const void* query,

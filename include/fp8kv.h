@@ -299,8 +299,8 @@ int fp8kv_paged_decode_per_head(void* out, int out_dtype, const void* query,
  * like splits, so a sequence whose blocks are spread over several devices can run this
  * pass per device, gather the partials, and finish with fp8kv_paged_decode_merge.
  * Arguments as for fp8kv_paged_decode (v_scale is applied by the merge).  The partial
- * m is kept in base-2 units: m = max_j s_j * log2(e).  This pass and the merge below take
- * per-tensor scales only.
+ * m is kept in base-2 units: m = max_j s_j * log2(e).  The _per_head variants below take
+ * one key (partial pass) and one value (merge) scale per kv head.
  */
 int fp8kv_paged_decode_partial(const void* query,
                                const void* key_cache, const void* value_cache, int cache_dtype,
@@ -323,6 +323,33 @@ int fp8kv_paged_decode_merge(void* out, int out_dtype,
                              int num_kv_heads, int head_dim, int block_size,
                              float v_scale, int sliding_window, int num_splits,
                              const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8kv_paged_decode_partial_per_head / fp8kv_paged_decode_merge_per_head -- the two passes
+ * with per-kv-head scales (page "FP8 KV Cache Quantization: Capacity Gains and Accuracy
+ * Risk", "Scales and calibration"): the partial pass dequantises the keys of kv head h with
+ * k_scales[h], the merge multiplies the merged output of query head hq by v_scales[hq / g].
+ * Together they equal fp8kv_paged_decode_per_head without a counter buffer.  k_scales /
+ * v_scales: device float32 [num_kv_heads], 4-byte aligned, read on `stream` (for one-byte
+ * caches the array must be non-NULL and its entries finite and > 0; ignored for
+ * FP8KV_BF16).  Everything else as for the per-tensor passes.
+ */
+int fp8kv_paged_decode_partial_per_head(const void* query,
+                                        const void* key_cache, const void* value_cache,
+                                        int cache_dtype, const int32_t* block_tables,
+                                        int max_blocks_per_seq, const int32_t* context_lens,
+                                        int max_context_len, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, const float* k_scales,
+                                        int sliding_window, int num_splits,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+int fp8kv_paged_decode_merge_per_head(void* out, int out_dtype, int cache_dtype,
+                                      const int32_t* context_lens, int max_context_len,
+                                      int max_blocks_per_seq, int num_seqs, int num_q_heads,
+                                      int num_kv_heads, int head_dim, int block_size,
+                                      const float* v_scales, int sliding_window, int num_splits,
+                                      const void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /*
  * fp8kv_decode_step -- one whole decode step: write each sequence's new token into the

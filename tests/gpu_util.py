@@ -117,8 +117,14 @@ def gpu_decode(w: syn.Workload, layer: syn.Layer, kc, vc, out_f32=False, num_spl
     out = torch.empty(B * Hq * D, dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
     odt = F.FP8KV_F32 if out_f32 else F.FP8KV_BF16
     cdt = code(layer)
-    if heads is not None:
-        assert not split_api, "the split passes take per-tensor scales only"
+    if heads is not None and split_api:
+        F.fp8kv_paged_decode_partial_per_head(dev.q, kc, vc, cdt, dev.bt, w.max_blocks_per_seq, dev.cl,
+                                              maxl, B, Hq, Hkv, D, w.block_size, w.num_blocks,
+                                              f32_dev(heads[0]), win, num_splits, ws, ws_bytes)
+        F.fp8kv_paged_decode_merge_per_head(out, odt, cdt, dev.cl, maxl, w.max_blocks_per_seq, B, Hq,
+                                            Hkv, D, w.block_size, f32_dev(heads[1]), win, num_splits,
+                                            ws, ws_bytes)
+    elif heads is not None:
         F.fp8kv_paged_decode_per_head(out, odt, dev.q, kc, vc, cdt, dev.bt, w.max_blocks_per_seq,
                                       dev.cl, maxl, B, Hq, Hkv, D, w.block_size, w.num_blocks,
                                       f32_dev(heads[0]), f32_dev(heads[1]), win, num_splits,

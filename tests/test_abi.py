@@ -266,3 +266,26 @@ def test_decode_step_noalloc_rejects_on_the_host(kw, status):
 
 def test_decode_step_noalloc_empty_batch_is_a_no_op():
     assert _noalloc(num_seqs=0, query=0, out=0) == F.FP8KV_OK
+
+
+def test_split_passes_per_head_reject():
+    f = F.lib.fp8kv_paged_decode_partial_per_head
+    args = [FAKE, FAKE, FAKE, F.FP8KV_E4M3, FAKE, 64, FAKE, 1024, 2, 32, 8, 128, 16, 200, FAKE, 0, 4,
+            FAKE, 1 << 30, 0]
+    bad = list(args); bad[14] = 0
+    assert f(*bad) == F.FP8KV_ERR_NULL                      # key scales missing
+    bad = list(args); bad[14] = FAKE + 2
+    assert f(*bad) == F.FP8KV_ERR_SHAPE                     # misaligned
+    bad = list(args); bad[17] = FAKE + 16
+    assert f(*bad) == F.FP8KV_ERR_WORKSPACE
+    m = F.lib.fp8kv_paged_decode_merge_per_head
+    margs = [FAKE, F.FP8KV_BF16, F.FP8KV_E4M3, FAKE, 1024, 64, 2, 32, 8, 128, 16, FAKE, 0, 4, FAKE,
+             1 << 30, 0]
+    bad = list(margs); bad[11] = 0
+    assert m(*bad) == F.FP8KV_ERR_NULL                      # value scales missing
+    bad = list(margs); bad[2] = 9
+    assert m(*bad) == F.FP8KV_ERR_UNSUPPORTED
+    bad = list(margs); bad[15] = 100
+    assert m(*bad) == F.FP8KV_ERR_WORKSPACE
+    bad = list(margs); bad[0] = 0
+    assert m(*bad) == F.FP8KV_ERR_NULL

@@ -156,3 +156,22 @@ def test_step_per_head_headline_128k():
     w, scales = syn.with_head_magnitudes(w, 140)
     say(f"decode_step_per_head {w.name}")
     _check_step(w, scales[0])
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 64])
+def test_split_passes_per_head_equal_one_call(num_splits):
+    """fp8kv_paged_decode_partial_per_head + fp8kv_paged_decode_merge_per_head run the same
+    kernels as fp8kv_paged_decode_per_head without a counter buffer: the same bits, and the
+    oracle's per-head decode within the f32 tolerance (the passes a context-parallel decode
+    would run on each device and after the gather)."""
+    w, heads = _mk(32, 8, 128, [2000, 100, 4099], cid=150)
+    say(f"per-head split passes splits={num_splits}")
+    layer = w.layers[0]
+    kc, vc = dev_caches(w, E4M3)
+    gpu_write(w, layer, kc, vc, heads=heads)
+    a = gpu_decode(w, layer, kc, vc, out_f32=True, num_splits=num_splits, heads=heads)
+    b = gpu_decode(w, layer, kc, vc, out_f32=True, num_splits=num_splits, heads=heads, split_api=True)
+    assert np.array_equal(a, b)
+    okc, ovc = oracle_write(w, layer, heads=heads)
+    assert_close(b, oracle_decode(w, layer, okc, ovc, heads=heads), atol=2e-4, rtol=2e-3,
+                 what="per-head split passes")
