@@ -119,22 +119,32 @@ __device__ constexpr int lds_value(int ch, int slot, int cb) {
     return ((((ch / 16) * 4 + slot / 4) * 16 + ch % 16) * 2 + cb) * 8 + (slot % 4) * 2;
 }
 
-// Staging geometry.  A step covers NB cache blocks (64 keys for d <= 128, 32 for d = 256,
-// so that the double-buffered step stays within 64 KB of LDS); its 2*NB cache tiles (keys
-// of blocks 0..NB-1, then their values) are moved by the 8 waves, each wave WAVE_SRC
-// contiguous source bytes of one tile and each lane PER bytes of those.
+// Staging geometry.  A step covers NB cache blocks: 128 keys (8 blocks) for one-byte caches
+// at d <= 128 and for d = 64, whose double-buffered widened tiles (2 x 2 x NB) fill 128 KB
+// of the 160 KB LDS, so each step's fixed work (block ids, masks, barrier) is spread over
+// twice the matrix-core products; 64 keys for the bf16 cache at d = 128 and 32 at d = 256,
+// where the larger step would not fit the registers of two waves per SIMD.  Its 2*NB cache
+// tiles (keys of blocks 0..NB-1, then their values) are moved by the 8 waves: each wave
+// WAVE_SRC contiguous source bytes, in PIECES pieces of PIECE_SRC bytes that each lie in one
+// tile, each lane PER bytes of a piece.
+#ifndef FP8KV_PREFILL_STEP_SCALE
+#define FP8KV_PREFILL_STEP_SCALE 2
+#endif
 template <int D, int C>
 struct Stage {
-    static constexpr int NB = D <= 128 ? 4 : 2;               // cache blocks per step
+    static constexpr bool WIDE = D == 64 || (D == 128 && C != kCodecBF16);
+    static constexpr int NB = (D <= 128 ? 4 : 2) * (WIDE ? FP8KV_PREFILL_STEP_SCALE : 1);   // blocks per step
     static constexpr int STEP = NB * kBlockSize;              // keys per step
     static constexpr int ES = C == kCodecBF16 ? 2 : 1;       // source bytes per element
     static constexpr int TILE_SRC = kBlockSize * D * ES;     // bytes of a cache tile
     static constexpr int TILE_LDS = kBlockSize * D * 2;      // bytes of its bf16 copy
     static constexpr int WAVE_SRC = 2 * NB * TILE_SRC / kWaves;
-    static constexpr int PER = WAVE_SRC / 64;                // source bytes per lane
-    static constexpr int NW = PER / 4;                       // dwords per lane
+    static constexpr int PIECE_SRC = WAVE_SRC < TILE_SRC ? WAVE_SRC : TILE_SRC;
+    static constexpr int PIECES = WAVE_SRC / PIECE_SRC;
+    static constexpr int PER = PIECE_SRC / 64;               // source bytes per lane and piece
+    static constexpr int NW = PER / 4;                       // dwords per lane and piece
     static constexpr int FLUSH = kFlushKeys / STEP;          // steps per accumulator flush
-    static_assert(WAVE_SRC <= TILE_SRC && TILE_SRC % WAVE_SRC == 0, "a wave stays in one tile");
+    static_assert(TILE_SRC % PIECE_SRC == 0 && WAVE_SRC % PIECE_SRC == 0, "a piece stays in one tile");
     static_assert(PER % 16 == 0 && FLUSH >= 1, "staging geometry");
 };
 
@@ -236,18 +246,24 @@ void prefill_kernel(PrefillParams p) {
     float l_hi = 0.0f, l_lo = 0.0f;        // sum of this lane's share of the probabilities
 
     if (nsteps > 0) {   // (then L >= 1, so the table and the cache hold at least one block)
-    // ---- block ids.  The NB raw ids of a step are read (scalar loads at clamped indices)
-    // one step before the step is staged, ahead of a barrier, so the loads never stall the
-    // matrix-core work; ok_mask turns them into a bit per block: a valid id (inside the
-    // table and [0, num_blocks)) whose first key lies before kend.
+    // ---- block ids.  The NB ids of a step are read one step before the step is staged,
+    // ahead of a barrier, so the loads never stall the matrix-core work.  When the step's NB
+    // table entries all lie inside the row (every step but at most the row's last) they are
+    // one NB-dword scalar load; otherwise each index is clamped to the row.  ok_mask turns
+    // them into a bit per block, without branches: a valid id (inside [0, num_blocks)) whose
+    // first key lies before kend (such a block is inside the row, as kend <= L).
     typedef int ids_t __attribute__((ext_vector_type(NB)));
+    typedef const __attribute__((address_space(4))) ids_t* ConstIdsPtr;
+    const int nrow = p.max_blocks_per_seq;
     auto load_ids = [&](int st) {
         const int n0 = (kfirst + (st < nsteps ? st : 0) * STEP) / kBlockSize;
         ids_t ids;
+        if (n0 + NB <= nrow) {
+            // NB consecutive dwords of the row (dword-aligned: one scalar load)
+            ids = *(ConstIdsPtr)(bt + n0);
+        } else {
 #pragma unroll
-        for (int c = 0; c < NB; ++c) {
-            const int n = n0 + c < p.max_blocks_per_seq ? n0 + c : p.max_blocks_per_seq - 1;
-            ids[c] = bt[n];
+            for (int c = 0; c < NB; ++c) ids[c] = bt[n0 + c < nrow ? n0 + c : nrow - 1];
         }
         return ids;
     };
@@ -255,35 +271,53 @@ void prefill_kernel(PrefillParams p) {
         const int kb = kfirst + st * STEP;
         uint32_t m = 0;
 #pragma unroll
-        for (int c = 0; c < NB; ++c) {
-            const bool ok = kb / kBlockSize + c < p.max_blocks_per_seq && ids[c] >= 0 &&
-                            ids[c] < p.num_blocks && kb + c * kBlockSize < kend;
-            m |= ok ? 1u << c : 0u;
-        }
+        for (int c = 0; c < NB; ++c)
+            m |= ((uint32_t)((unsigned)ids[c] < (unsigned)p.num_blocks) &
+                  (uint32_t)(kb + c * kBlockSize < kend)) << c;
         return m;
     };
 
-    // ---- staging: wave w moves source bytes [w*WAVE_SRC, +WAVE_SRC) of the step's tiles.
-    // The loads are always issued (a missing block reads block 0, in bounds) so that no
-    // branch sits between a load and its use; missing blocks become zeros and value slots
-    // at or past kend are zeroed when the piece is widened and written to LDS.
-    const int part = wave * S::WAVE_SRC / S::TILE_SRC;            // tile of the step
-    const int part_c = part % NB;
-    const bool part_v = part >= NB;
-    const int src_off = (wave * S::WAVE_SRC) % S::TILE_SRC + lane * S::PER;   // byte offset in the tile
-    const uint8_t* part_src = static_cast<const uint8_t*>(part_v ? p.value_cache : p.key_cache);
-    typedef uint32_t stage_t __attribute__((ext_vector_type(S::NW)));
-    auto stage_load = [&](ids_t ids, uint32_t okm, stage_t& r) __attribute__((always_inline)) {
-        int id = ids[0];
-#pragma unroll
-        for (int c = 1; c < NB; ++c) id = part_c == c ? ids[c] : id;
-        id = (okm >> part_c) & 1u ? id : 0;
-        const uint8_t* src = part_src + ((int64_t)id * p.num_kv_heads + h) * S::TILE_SRC + src_off;
-        r = __builtin_nontemporal_load(reinterpret_cast<const stage_t*>(src));
+    // ---- staging: wave w moves source bytes [w*WAVE_SRC, +WAVE_SRC) of the step's tiles, in
+    // PIECES pieces that each lie in one tile.  The loads are always issued (a missing block
+    // reads block 0, in bounds) so that no branch sits between a load and its use; missing
+    // blocks become zeros and value slots at or past kend are zeroed when a piece is widened
+    // and written to LDS.
+    typedef uint32_t piece_t __attribute__((ext_vector_type(S::NW)));
+    struct stage_t { piece_t pc[S::PIECES]; };
+    // geometry of piece i of this wave (wave-uniform except the lane's byte offset)
+    auto piece_part = [&](int i) { return (wave * S::WAVE_SRC + i * S::PIECE_SRC) / S::TILE_SRC; };
+    auto piece_off = [&](int i) {        // byte offset of this lane's bytes in the piece's tile
+        return (wave * S::WAVE_SRC + i * S::PIECE_SRC) % S::TILE_SRC + lane * S::PER;
     };
-    auto stage_store = [&](int buf, int st, uint32_t okmask, const stage_t& r) __attribute__((always_inline)) {
+    auto stage_load = [&](ids_t ids, uint32_t okm, stage_t& r) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < S::PIECES; ++i) {
+            const int part = piece_part(i);
+            const int part_c = part % NB;
+            int id = ids[0];
+#pragma unroll
+            for (int c = 1; c < NB; ++c) id = part_c == c ? ids[c] : id;
+            id = (okm >> part_c) & 1u ? id : 0;
+            const uint8_t* src = static_cast<const uint8_t*>(part >= NB ? p.value_cache : p.key_cache) +
+                                 ((int64_t)id * p.num_kv_heads + h) * S::TILE_SRC + piece_off(i);
+            r.pc[i] = __builtin_nontemporal_load(reinterpret_cast<const piece_t*>(src));
+        }
+    };
+    auto stage_store = [&](int buf, int st, uint32_t okmask, const stage_t& r0) __attribute__((always_inline)) {
         const int kb = kfirst + st * STEP;
-        const uint32_t okm = (okmask >> part_c) & 1u ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int i = 0; i < S::PIECES; ++i) {
+        const int part = piece_part(i);
+        const int part_c = part % NB;
+        const bool part_v = part >= NB;
+        const int src_off = piece_off(i);
+        // a missing block stages zeros (a wave-uniform test: no per-lane masking in the
+        // common case)
+        piece_t r = r0.pc[i];
+        if (!((okmask >> part_c) & 1u)) r = piece_t{};
+        // value slots at or past kend are zeroed below, only in a block that reaches kend
+        const int nvalid = kend - (kb + part_c * kBlockSize);
+        const bool tail = nvalid < kBlockSize;
         // keys: tile part; values: the pair region of blocks 2*(c/2), 2*(c/2)+1
         uint8_t* dst = sm_kv[buf] + (part_v ? NB + 2 * (part_c / 2) : part) * TL;
         constexpr int EPL = S::PER / S::ES;                       // elements per lane
@@ -293,11 +327,11 @@ void prefill_kernel(PrefillParams p) {
             const int e0 = src_off / S::ES + 8 * j;               // element index in the tile
             u32x4 v;
             if constexpr (C == kCodecBF16) {
-                v = u32x4{r[4 * j] & okm, r[4 * j + 1] & okm, r[4 * j + 2] & okm, r[4 * j + 3] & okm};
+                v = u32x4{r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]};
             } else if (!part_v) {
-                v = __builtin_bit_cast(u32x4, codes8_to_bf16x8<C>(r[DW8 * j] & okm, r[DW8 * j + 1] & okm));
+                v = __builtin_bit_cast(u32x4, codes8_to_bf16x8<C>(r[DW8 * j], r[DW8 * j + 1]));
             } else {
-                v = __builtin_bit_cast(u32x4, codes8_to_f16x8<C>(r[DW8 * j] & okm, r[DW8 * j + 1] & okm));
+                v = __builtin_bit_cast(u32x4, codes8_to_f16x8<C>(r[DW8 * j], r[DW8 * j + 1]));
             }
             if (!part_v) {
                 // element e0 of the source key tile: invert the chunk layout to (slot, channel)
@@ -309,8 +343,7 @@ void prefill_kernel(PrefillParams p) {
             } else {
                 // value tile: channel-major rows of 16 slots; zero the slots at or past kend
                 const int slot0 = e0 % kBlockSize;
-                const int nvalid = kend - (kb + part_c * kBlockSize);
-                if (slot0 + 8 > nvalid) {
+                if (tail && slot0 + 8 > nvalid) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const uint32_t lo = slot0 + 2 * k < nvalid ? 0x0000FFFFu : 0u;
@@ -323,6 +356,7 @@ void prefill_kernel(PrefillParams p) {
                 *reinterpret_cast<u32x2*>(dst + lds_value(ch, slot0, part_c % 2)) = u32x2{v[0], v[1]};
                 *reinterpret_cast<u32x2*>(dst + lds_value(ch, slot0 + 4, part_c % 2)) = u32x2{v[2], v[3]};
             }
+        }
         }
     };
 
@@ -343,18 +377,18 @@ void prefill_kernel(PrefillParams p) {
 
     auto compute = [&](int st, int buf, uint32_t okmask) __attribute__((always_inline)) {
         const int kb = kfirst + st * STEP;
-        // whether the step holds any key this wave's columns attend to
-        if (!(st < nsteps && wactive && kb <= pmax && kb + STEP > lomin)) return;
+        // whether the step holds any key this wave's columns attend to (one uniform test)
+        if (!((st < nsteps) & wactive & (kb <= pmax) & (kb + STEP > lomin))) return;
         const uint8_t* sk = sm_kv[buf];
 
         // ---- value operands of P.V (lane: slots 4*grp .. +3 of both blocks of a pair, channel
-        // 16t + col).  They do not depend on the scores: for d <= 128 (64 registers) they are
-        // read first, so their LDS latency hides behind S and the softmax; at d = 256 they
-        // would not fit beside the rest, and each is read just before its products.
+        // 16t + col).  They do not depend on the scores: when they fit in 64 registers they
+        // are read first, so their LDS latency hides behind S and the softmax; otherwise each
+        // is read just before its products.
         auto read_v = [&](int t, int r) {
             return *reinterpret_cast<const pv_t*>(sk + (NB + 2 * r) * TL + lds_value(16 * t + col, 4 * grp, 0));
         };
-        constexpr bool kEarlyV = D <= 128;
+        constexpr bool kEarlyV = D <= 128 && NT * (NB / 2) <= 16;
         pv_t vb[kEarlyV ? NT : 1][NB / 2];
         if constexpr (kEarlyV) {
 #pragma unroll
@@ -379,7 +413,7 @@ void prefill_kernel(PrefillParams p) {
 
         // ---- raw scores masked outside [clo, pos] and outside valid blocks; the base-2
         // scale (> 0) is applied to the maximum and inside the exponent's FMA
-        if (kb + STEP > pmin + 1 || kb < lomax || okmask != kAllBlocks) {
+        if ((kb + STEP > pmin + 1) | (kb < lomax) | (okmask != kAllBlocks)) {
             const int k0 = kb + 4 * grp;
 #pragma unroll
             for (int c = 0; c < NB; ++c)
