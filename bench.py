@@ -762,9 +762,10 @@ def prefill_bench(F, torch, syn, name: str, args) -> dict:
 
 
 def rotated_bench(F, torch, syn, args) -> dict:
-    """Per-step time of the rotated path (fp8kv_cache_write_rotated of each sequence's token,
-    then fp8kv_paged_decode_rotated: query rotation, decode, output rotation) next to the
-    plain two-call path (fp8kv_cache_write + fp8kv_paged_decode), HIP events over
+    """Per-step time of the rotated path, as two calls (fp8kv_cache_write_rotated of each
+    sequence's token, then fp8kv_paged_decode_rotated: query rotation, decode, output rotation)
+    and as the fused fp8kv_decode_step_rotated, next to the plain two-call path
+    (fp8kv_cache_write + fp8kv_paged_decode) and the plain fused step; HIP events over
     back-to-back steps on rotated cache instances."""
     w = WORKLOADS[args.workload](syn)
     layer = w.layers[args.layer]
@@ -784,15 +785,26 @@ def rotated_bench(F, torch, syn, args) -> dict:
                                      w.max_blocks_per_seq, b.cl, b.maxl, w.num_seqs, Hq, Hkv, D,
                                      BLOCK, w.num_blocks, layer.k_scale, layer.v_scale, b.win,
                                      args.num_splits, ws, nbytes, b.stream)
+    def rotated_fused_step(i):
+        F.fp8kv_decode_step_rotated(b.out, F.FP8KV_BF16, b.q, b.k_new, b.v_new, b.kc[i], b.vc[i],
+                                    b.cdt, b.bt, w.max_blocks_per_seq, b.cl, b.maxl, w.num_seqs, Hq,
+                                    Hkv, D, BLOCK, w.num_blocks, layer.k_scale, layer.v_scale,
+                                    b.win, args.num_splits, b.cnt, b.cnt_bytes, ws, nbytes,
+                                    b.stream)
     ms_rot, _ = b.time_steps(args.steps, min(args.warmup, 200), rotated_step)
+    ms_rot_fused, _ = b.time_steps(args.steps, min(args.warmup, 200), rotated_fused_step)
     ms_two, _ = b.time_steps(args.steps, min(args.warmup, 200), b.two_call_step)
     ms_fused, _ = b.time_steps(args.steps, min(args.warmup, 200))
     return {"metric": "Hadamard-rotated decode step: us per step",
             "workload": f"{args.workload}: {w.name}",
-            "rotated_step_us": round(ms_rot * 1e3, 2), "two_call_step_us": round(ms_two * 1e3, 2),
+            "rotated_step_us": round(ms_rot * 1e3, 2),
+            "rotated_fused_step_us": round(ms_rot_fused * 1e3, 2),
+            "two_call_step_us": round(ms_two * 1e3, 2),
             "fused_step_us": round(ms_fused * 1e3, 2),
             "rotated_over_two_call": round(ms_rot / ms_two, 4),
-            "GBps_rotated": round(b.bytes["step"] / (ms_rot * 1e-3) / 1e9, 1)}
+            "rotated_fused_over_fused": round(ms_rot_fused / ms_fused, 4),
+            "GBps_rotated": round(b.bytes["step"] / (ms_rot * 1e-3) / 1e9, 1),
+            "GBps_rotated_fused": round(b.bytes["step"] / (ms_rot_fused * 1e-3) / 1e9, 1)}
 
 
 def _finite(x):

@@ -79,6 +79,8 @@ SIGNATURES = {
     "fp8kv_paged_decode_rotated_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "fp8kv_paged_decode_rotated": (_I, [_P, _I, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I,
                                         _I, _F, _F, _I, _I, _P, _SZ, _P]),
+    "fp8kv_decode_step_rotated": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
+                                       _I, _I, _I, _F, _F, _I, _I, _P, _SZ, _P, _SZ, _P]),
 }
 
 if not os.path.exists(LIBRARY_PATH):
@@ -383,3 +385,21 @@ def fp8kv_paged_decode_rotated(out, out_dtype, query, key_cache, value_cache, ca
                                                  num_splits, _addr(workspace), workspace_bytes,
                                                  _stream(stream)),
                   "fp8kv_paged_decode_rotated")
+
+
+def fp8kv_decode_step_rotated(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
+                              cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                              max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              block_size, num_blocks, k_scale, v_scale, sliding_window, num_splits,
+                              counters, counters_bytes, workspace, workspace_bytes,
+                              stream=None) -> int:
+    return _check(lib.fp8kv_decode_step_rotated(_addr(out), out_dtype, _addr(query), _addr(key_new),
+                                                _addr(value_new), _addr(key_cache),
+                                                _addr(value_cache), cache_dtype,
+                                                _addr(block_tables), max_blocks_per_seq,
+                                                _addr(context_lens), max_context_len, num_seqs,
+                                                num_q_heads, num_kv_heads, head_dim, block_size,
+                                                num_blocks, k_scale, v_scale, sliding_window,
+                                                num_splits, _addr(counters), counters_bytes,
+                                                _addr(workspace), workspace_bytes, _stream(stream)),
+                  "fp8kv_decode_step_rotated")

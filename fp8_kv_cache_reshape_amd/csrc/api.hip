@@ -228,6 +228,7 @@ int setup_decode(fp8kv::DecodeParams& p, bool& fp8, const void* query, const voi
     p.use_claims = 0;
     p.merge_in_kernel = 0;
     p.err = g_error_word;
+    p.rot_scale = 1.0f;
     return FP8KV_OK;
 }
 
@@ -811,6 +812,58 @@ int fp8kv_paged_decode_rotated(void* out, int out_dtype, const void* query, cons
         if (st != FP8KV_OK) return st;
     }
     return hip_status(fp8kv::launch_rotate_out(out_rot, out, out_dtype == FP8KV_F32, rows, head_dim, s));
+}
+
+int fp8kv_decode_step_rotated(void* out, int out_dtype, const void* query, const void* key_new,
+                              const void* value_new, void* key_cache, void* value_cache,
+                              int cache_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* context_lens, int max_context_len, int num_seqs,
+                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, float k_scale, float v_scale, int sliding_window,
+                              int num_splits, void* counters, size_t counters_bytes,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    // the rotated path is defined for the E4M3 and BF16 caches
+    if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
+    int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_context_len, sliding_window, num_splits);
+    if (st != FP8KV_OK) return st;
+    const Plan pl = make_plan(num_seqs, num_kv_heads, head_dim, max_context_len, sliding_window, num_splits);
+    const size_t dec = workspace_layout(num_seqs, num_q_heads, head_dim, pl.splits).total;
+    const RotatedLayout rl = rotated_layout(dec, num_seqs, num_q_heads, head_dim);
+    fp8kv::DecodeParams p;
+    bool fp8 = true;
+    st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
+                      max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, tensor_scales(k_scale, v_scale),
+                      false, sliding_window, num_splits, workspace,
+                      workspace_bytes < dec ? workspace_bytes : dec, false);
+    if (st != FP8KV_OK) return st;
+    if (num_seqs == 0) return FP8KV_OK;
+    if (!out || !key_new || !value_new) return FP8KV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(key_new) || !aligned16(value_new)) return FP8KV_ERR_SHAPE;
+    const int fused = attach_counters(p, head_dim, counters, counters_bytes, num_splits);
+    if (fused < 0) return fused;
+    const bool one_launch = p.write_final || fused;
+    if (!one_launch) {   // the merge kernel writes f32 rows that one more launch rotates back
+        if (!workspace || workspace_bytes < rl.total) return FP8KV_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FP8KV_ERR_WORKSPACE;
+    }
+    float* out_rot = one_launch ? nullptr : reinterpret_cast<float*>(static_cast<char*>(workspace) + rl.out);
+    p.out = one_launch ? out : out_rot;
+    p.out_f32 = one_launch ? (out_dtype == FP8KV_F32) : 1;
+    p.k_new = static_cast<const uint16_t*>(key_new);
+    p.v_new = static_cast<const uint16_t*>(value_new);
+    p.k_scale_q = fp8 ? k_scale : 1.0f;
+    p.v_scale_q = fp8 ? v_scale : 1.0f;
+    p.rot_scale = (float)(1.0 / sqrt((double)head_dim));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(fp8kv::launch_decode_partial_rotated(p, codec_of(cache_dtype), head_dim, s));
+    if (st != FP8KV_OK || one_launch) return st;
+    st = hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
+    if (st != FP8KV_OK) return st;
+    return hip_status(fp8kv::launch_rotate_out(out_rot, out, out_dtype == FP8KV_F32,
+                                               (int64_t)num_seqs * num_q_heads, head_dim, s));
 }
 
 }  // extern "C"

@@ -77,6 +77,8 @@ struct DecodeParams {
     const float* k_scales;
     const float* v_scales;
     unsigned int* err;             // device error word (FP8KV_DEVERR_* bits), or null
+    // rotated cache (the rotated decode step): (float)(1/sqrt(D)), the Hadamard normaliser
+    float rot_scale;
 };
 
 struct PrefillParams {
@@ -187,6 +189,12 @@ int decode_step_check(void* out, int out_dtype, const void* query, const void* k
 // `codec`: the cache element codec (kCodecBF16 or a one-byte codec).
 hipError_t launch_cache_write(const CacheWriteParams& p, Codec codec, int head_dim, hipStream_t s);
 hipError_t launch_decode_partial(const DecodeParams& p, Codec codec, int head_dim, hipStream_t s);
+// The decode kernel over a Hadamard-rotated cache (E4M3 or BF16): the query is rotated in the
+// kernel, the step token (when given) rotated before it is quantised, and a merged output
+// rotated back before it is stored.  Without an in-kernel merge (or a single split) the
+// partials go to the workspace as usual.
+hipError_t launch_decode_partial_rotated(const DecodeParams& p, Codec codec, int head_dim,
+                                         hipStream_t s);
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, hipStream_t s);
 // Whether the decode kernel can merge the `splits` partials of a (sequence, kv head) group
 // of `group` query heads itself, in at most two batched round trips to memory; larger

@@ -45,6 +45,7 @@
 #include <type_traits>
 
 #include "codec.h"
+#include "hadamard.h"
 #include "internal.h"
 
 namespace fp8kv {
@@ -144,8 +145,22 @@ constexpr int kMergeLaneBatch = 16;
 // quads at once -- every load is issued before the first wait, unconditionally (absent
 // splits read the last split and weigh 0) so the compiler can count them -- one round trip
 // instead of Q.
-template <int D, int Q, int S>
-__device__ void merge_quads(const DecodeParams& p, int64_t hq0, int NQ, int ns, float vsc) {
+// Two output values of head hh of the group (channels ch, ch + 1): to `out`, or -- for the
+// rotated cache -- to the group's f32 rows in LDS, rotated back before they are stored.
+template <bool ROT, int D>
+__device__ inline void emit2(const DecodeParams& p, float* rot, int64_t hq0, int hh, int ch, float a, float b) {
+    if constexpr (ROT) {
+        rot[hh * D + ch] = a;
+        rot[hh * D + ch + 1] = b;
+    } else {
+        const int64_t o = (hq0 + hh) * D + ch;
+        store_out(p.out, p.out_f32, o, a);
+        store_out(p.out, p.out_f32, o + 1, b);
+    }
+}
+
+template <int D, int Q, int S, bool ROT>
+__device__ void merge_quads(const DecodeParams& p, int64_t hq0, int NQ, int ns, float vsc, float* rot) {
     const int par = threadIdx.x & 1;
     float2 mv[Q][S];
     float4 xv[Q][S];
@@ -191,26 +206,24 @@ __device__ void merge_quads(const DecodeParams& p, int64_t hq0, int NQ, int ns, 
         const int q = (int)(threadIdx.x >> 1) + j * 32 * kDecodeWaves;
         if (q < NQ) {
             const int hh = q / (D / 4), c4 = q % (D / 4);
-            const int64_t o = (hq0 + hh) * D + 4 * c4 + 2 * par;
-            store_out(p.out, p.out_f32, o, scale * (par ? r2 : r0));
-            store_out(p.out, p.out_f32, o + 1, scale * (par ? r3 : r1));
+            emit2<ROT, D>(p, rot, hq0, hh, 4 * c4 + 2 * par, scale * (par ? r2 : r0), scale * (par ? r3 : r1));
         }
     }
 }
 
-template <int D>
-__device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) {
+template <int D, bool ROT>
+__device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns, float* rot) {
     const float vsc = head_scale(p.v_scales, h, p.v_scale);
     const int par = threadIdx.x & 1;
     const int NQ = G * D / 4;                                  // channel quads of the group
     const int64_t hq0 = (int64_t)b * p.num_q_heads + (int64_t)h * G;
     if (NQ > 32 * kDecodeWaves && NQ <= 64 * kDecodeWaves && ns <= 2 * kMergeLaneBatch) {
-        merge_quads<D, 2, kMergeLaneBatch>(p, hq0, NQ, ns, vsc);
+        merge_quads<D, 2, kMergeLaneBatch, ROT>(p, hq0, NQ, ns, vsc, rot);
         return;
     }
     if constexpr (D == 256) {   // one wave per SIMD: room for 4 x 8 partials per lane
         if (NQ > 64 * kDecodeWaves && NQ <= 128 * kDecodeWaves && ns <= kMergeLaneBatch) {
-            merge_quads<D, 4, kMergeLaneBatch / 2>(p, hq0, NQ, ns, vsc);
+            merge_quads<D, 4, kMergeLaneBatch / 2, ROT>(p, hq0, NQ, ns, vsc, rot);
             return;
         }
     }
@@ -262,9 +275,28 @@ __device__ void merge_group(const DecodeParams& p, int b, int h, int G, int ns) 
         const float scale = lam > 0.0f ? vsc / lam : 0.0f;
         const float r0 = a.x + pair_swap(a.x), r1 = a.y + pair_swap(a.y);
         const float r2 = a.z + pair_swap(a.z), r3 = a.w + pair_swap(a.w);
-        const int64_t o = (hq0 + hh) * D + 4 * c4 + 2 * par;
-        store_out(p.out, p.out_f32, o, scale * (par ? r2 : r0));
-        store_out(p.out, p.out_f32, o + 1, scale * (par ? r3 : r1));
+        emit2<ROT, D>(p, rot, hq0, hh, 4 * c4 + 2 * par, scale * (par ? r2 : r0), scale * (par ? r3 : r1));
+    }
+}
+
+// The rotated cache: the G merged f32 rows of the group, held in LDS, rotated back (D/8
+// lanes per row, the butterflies of hadamard_row) and stored to `out`.  Every thread of the
+// workgroup calls this (it starts with a barrier).
+template <int D>
+__device__ void rotate_rows_out(const DecodeParams& p, const float* rot, int G, int64_t out_row0) {
+    __syncthreads();
+    constexpr int CH = D / 8;
+    for (int base = 0; base < G * CH; base += 64 * kDecodeWaves) {
+        const int li = base + (int)threadIdx.x;           // (row, chunk) of this lane
+        const int lc = li < G * CH ? li : G * CH - 1;    // clamped: every lane shuffles
+        const int row = lc / CH, c = lc % CH;
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = rot[row * D + c * 8 + j];
+        hadamard_row<D>(v, c, p.rot_scale);
+        if (li < G * CH)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) store_out(p.out, p.out_f32, out_row0 + (int64_t)row * D + c * 8 + j, v[j]);
     }
 }
 
@@ -281,11 +313,14 @@ constexpr int partial_waves_per_eu() {
     return QLO ? 1 : ((D <= 128 && C != kCodecBF16) || D == 64 ? 2 : 1);
 }
 
-// C: the cache codec (kCodecBF16, or a one-byte codec: E4M3, E5M2, INT8).
-template <int D, int C, bool QLO>
+// C: the cache codec (kCodecBF16, or a one-byte codec: E4M3, E5M2, INT8).  ROT: a
+// Hadamard-rotated cache; the kernel rotates the query into its two bf16 terms (so QLO),
+// rotates the step token before quantising it, and rotates a merged output back.
+template <int D, int C, bool QLO, bool ROT = false>
 __global__ __launch_bounds__(64 * kDecodeWaves)
 __attribute__((amdgpu_waves_per_eu(partial_waves_per_eu<D, C, QLO>(), 8)))
 void decode_partial_kernel(DecodeParams p) {
+    static_assert(!ROT || QLO, "the rotated query is carried as two bf16 terms");
     constexpr bool FP8 = C != kCodecBF16;         // one-byte codes
     constexpr int ES = FP8 ? 1 : 2;               // bytes per cache element
     constexpr int DG = D / 4;                     // channels per lane group in S = K.q^T
@@ -351,7 +386,53 @@ void decode_partial_kernel(DecodeParams p) {
     // [grp*DG + 8kk, +8) for kk = 0..KK-1; heads >= G are zero columns.
     bf16x8 qop[KK];
     bf16x8 qlo[QLO ? KK : 1];                     // the query's low bf16 term (QLO only)
-    {
+    if constexpr (ROT) {
+        // the lane's quarter of head n's row in f32, rotated in place with the butterflies of
+        // hadamard_row (h = 1, 2, ..., D/2: inside the lane for h < DG, then with the lanes
+        // of groups grp ^ 1 and grp ^ 2), times (float)(1/sqrt(D)), then split into a high
+        // and a low bf16 term
+        const int64_t qoff = out_row0 + (int64_t)(n < G ? n : 0) * D + grp * DG;
+        float x[DG];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            uint4 u = load16(p.query + qoff + 8 * kk);
+            if (n >= G) u = make_uint4(0, 0, 0, 0);
+            float f[8];
+            bf16x8_to_f32(u, f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[8 * kk + e] = f[e];
+        }
+#pragma unroll
+        for (int hh = 1; hh < DG; hh *= 2)
+#pragma unroll
+            for (int j = 0; j < DG; ++j)
+                if ((j & hh) == 0) {
+                    const float a = x[j], c = x[j + hh];
+                    x[j] = a + c;
+                    x[j + hh] = a - c;
+                }
+#pragma unroll
+        for (int m = 1; m <= 2; m *= 2) {             // h = m * DG: lane groups grp and grp ^ m
+            const bool upper = (grp & m) != 0;
+#pragma unroll
+            for (int j = 0; j < DG; ++j) {
+                const float other = __shfl_xor(x[j], 16 * m);
+                x[j] = upper ? other - x[j] : x[j] + other;
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = x[8 * kk + 2 * j] * p.rot_scale, c = x[8 * kk + 2 * j + 1] * p.rot_scale;
+                hi[j] = pack_bf16x2(a, c);
+                lo[j] = pack_bf16x2(a - __uint_as_float(hi[j] << 16), c - __uint_as_float(hi[j] & 0xFFFF0000u));
+            }
+            qop[kk] = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+            qlo[kk] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+        }
+    } else {
         // heads n >= G read head 0's row (in bounds) and are zeroed: no branch around the loads
         const int64_t qoff = out_row0 + (int64_t)(n < G ? n : 0) * D + grp * DG;
         const uint16_t* qrow = p.query + qoff;
@@ -631,12 +712,47 @@ void decode_partial_kernel(DecodeParams p) {
                                  min(lane & 31, D / 8 - 1) * 8);
         const int c = lane & 31;
         if ((unsigned)tok_blk >= (unsigned)p.num_blocks && lane == 0) report_error(p.err, kErrBlockId);
+        // the rotated cache: each row (lanes [0, D/8) keys, [32, 32 + D/8) values) rotated in
+        // f32 by every lane of the wave (the shuffles stay inside each half), exactly as the
+        // rotated cache write does
+        float rv[8];
+        if constexpr (ROT) {
+            bf16x8_to_f32(tok, rv);
+            hadamard_row<D>(rv, c, p.rot_scale);
+        }
         if ((unsigned)tok_blk < (unsigned)p.num_blocks && c < D / 8) {
             const bool val = lane >= 32;
             const int off = (w.L - 1) % kBlockSize;
             char* tile = static_cast<char*>(const_cast<void*>(val ? p.value_cache : p.key_cache))
                          + ((int64_t)tok_blk * p.num_kv_heads + h) * TILE_BYTES;
-            if constexpr (FP8) {
+            if constexpr (ROT) {
+                if constexpr (FP8) {
+                    // IEEE f32 division by the scale, then the cast
+                    const float sc = val ? p.v_scale_q : p.k_scale_q;
+                    uint32_t cw[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) cw[j] = pack2<C>(rv[2 * j] / sc, rv[2 * j + 1] / sc);
+                    const uint2 q8 = make_uint2(cw[0] | (cw[1] << 16), cw[2] | (cw[3] << 16));
+                    if (!val) {
+                        *reinterpret_cast<uint2*>(tile + key_chunk_offset<D, 1>(off, c * 8)) = q8;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            tile[(c * 8 + i) * kBlockSize + off] = (char)(((i < 4 ? q8.x : q8.y) >> (8 * (i & 3))) & 0xFF);
+                    }
+                } else {
+                    if (!val) {
+                        *reinterpret_cast<uint4*>(tile + key_chunk_offset<D, 2>(off, c * 8)) =
+                            make_uint4(pack_bf16x2(rv[0], rv[1]), pack_bf16x2(rv[2], rv[3]),
+                                       pack_bf16x2(rv[4], rv[5]), pack_bf16x2(rv[6], rv[7]));
+                    } else {
+                        uint16_t* vt16 = reinterpret_cast<uint16_t*>(tile);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            vt16[(c * 8 + i) * kBlockSize + off] = __builtin_bit_cast(uint16_t, (__bf16)rv[i]);
+                    }
+                }
+            } else if constexpr (FP8) {
                 const uint2 q8 = quantize8<C>(tok, val ? head_scale(p.v_scales, h, p.v_scale_q)
                                                     : head_scale(p.k_scales, h, p.k_scale_q));
                 if (!val) {
@@ -748,6 +864,7 @@ void decode_partial_kernel(DecodeParams p) {
     float* sm_s = sm_w + kDecodeWaves * 16;                              // [16] v_scale / Lambda
     float* sm_M = sm_s + 16;                                             // [16] M
     float* sm_L = sm_M + 16;                                             // [16] Lambda
+    float* sm_rot = sm_L + 16;                                           // [16][D] rotated cache only
     if (threadIdx.x < G) {
         const int hd = threadIdx.x;
         float M = -INFINITY;
@@ -776,7 +893,8 @@ void decode_partial_kernel(DecodeParams p) {
         for (int v = 0; v < kDecodeWaves; ++v) comp_add(a, a_c, sm_w[v * 16 + head] * sm_a[(v * 16 + head) * D + i]);
         a += a_c;
         if (p.write_final) {
-            store_out(p.out, p.out_f32, out_row0 + (int64_t)head * D + i, sm_s[head] * a);
+            if constexpr (ROT) sm_rot[head * D + i] = sm_s[head] * a;
+            else store_out(p.out, p.out_f32, out_row0 + (int64_t)head * D + i, sm_s[head] * a);
         } else {
             const int64_t row = ((int64_t)b * p.num_q_heads + (int64_t)h * G + head) * p.splits + split;
             store_device(p.ws_acc + row * D + i, a);
@@ -785,6 +903,9 @@ void decode_partial_kernel(DecodeParams p) {
                 store_device(p.ws_ml + row * 2 + 1, sm_L[head]);
             }
         }
+    }
+    if constexpr (ROT) {
+        if (p.write_final) rotate_rows_out<D>(p, sm_rot, G, out_row0);   // (uniform branch)
     }
 
     // Arrival: the last workgroup of this (sequence, kv head) to finish resets the group's
@@ -818,7 +939,10 @@ void decode_partial_kernel(DecodeParams p) {
             s_last = (int)last;
         }
         __syncthreads();
-        if (s_last && p.merge_in_kernel) merge_group<D>(p, b, h, G, ns);
+        if (s_last && p.merge_in_kernel) {
+            merge_group<D, ROT>(p, b, h, G, ns, sm_rot);
+            if constexpr (ROT) rotate_rows_out<D>(p, sm_rot, G, out_row0);
+        }
     }
 }
 
@@ -918,43 +1042,64 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
 }
 
 // Largest dynamic LDS a partial-kernel launch may request (head_dim 256 keeps all 16 MFMA
-// rows of 4 waves: about 65 KB).  Launches above 64 KB also need the device to allow it.
-constexpr size_t kMaxPartialLds = 80 * 1024;
+// rows of 4 waves: about 65 KB; the rotated variant adds 16 KB of output rows).  Launches
+// above 64 KB also need the device to allow it (gfx950 has 160 KB per workgroup).
+constexpr size_t kMaxPartialLds = 160 * 1024;
 
 // Dynamic LDS of the partial kernel: per-wave (m, l), every wave's accumulators over all 16
-// MFMA rows, and the per-head wave weights, scale, max and normaliser.
-template <int D>
+// MFMA rows, and the per-head wave weights, scale, max and normaliser; the rotated variant
+// adds the 16 output rows it rotates back.
+template <int D, bool ROT = false>
 size_t partial_lds_bytes(int G) {
     (void)G;
-    return sizeof(float) * (2 * kDecodeWaves * 16 + (size_t)kDecodeWaves * 16 * D + kDecodeWaves * 16 + 48);
+    return sizeof(float) * (2 * kDecodeWaves * 16 + (size_t)kDecodeWaves * 16 * D + kDecodeWaves * 16 + 48 +
+                            (ROT ? 16 * D : 0));
 }
 
 // Kernels whose dynamic LDS can exceed 64 KiB (g = 16 at head_dim 256) get their limit
 // raised once, to the largest size any group ratio needs.
-template <int D, int C, bool QLO>
+template <int D, int C, bool QLO, bool ROT = false>
 hipError_t allow_lds(size_t need) {
     if (need <= 65536) return hipSuccess;
     // raise this kernel's limit once, to what the device allows (up to kMaxPartialLds)
+    // (the kernel's static LDS counts against the same per-workgroup maximum)
     static const int allowed = [] {
+        const void* fn = reinterpret_cast<const void*>(&decode_partial_kernel<D, C, QLO, ROT>);
         int dev = 0, lim = 65536;
+        hipFuncAttributes fa{};
         if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            hipFuncGetAttributes(&fa, fn) != hipSuccess)
             return 65536;
+        lim -= (int)fa.sharedSizeBytes;
         if ((size_t)lim > kMaxPartialLds) lim = (int)kMaxPartialLds;
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partial_kernel<D, C, QLO>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lim) != hipSuccess)
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lim) != hipSuccess)
             return 65536;
         return lim;
     }();
     return need <= (size_t)allowed ? hipSuccess : hipErrorInvalidValue;
 }
 
-template <int D, int C, bool QLO>
+template <int D, int C, bool QLO, bool ROT = false>
 hipError_t launch_partial_dc(const DecodeParams& p, size_t lds, dim3 grid, dim3 block, hipStream_t s) {
-    const hipError_t e = allow_lds<D, C, QLO>(lds);
+    const hipError_t e = allow_lds<D, C, QLO, ROT>(lds);
     if (e != hipSuccess) return e;
-    return launch_kernel(reinterpret_cast<const void*>(&decode_partial_kernel<D, C, QLO>), grid, block,
+    return launch_kernel(reinterpret_cast<const void*>(&decode_partial_kernel<D, C, QLO, ROT>), grid, block,
                          lds, s, p);
+}
+
+template <int D>
+hipError_t launch_rotated_d(const DecodeParams& p, Codec codec, hipStream_t s) {
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const size_t lds = partial_lds_bytes<D, true>(G);
+    const dim3 grid = kHeadsFastest ? dim3(p.num_kv_heads, p.splits, p.num_seqs)
+                                    : dim3(p.splits, p.num_kv_heads, p.num_seqs);
+    const dim3 block(64 * kDecodeWaves);
+    switch (codec) {
+        case kCodecE4M3: return launch_partial_dc<D, kCodecE4M3, true, true>(p, lds, grid, block, s);
+        case kCodecBF16: return launch_partial_dc<D, kCodecBF16, true, true>(p, lds, grid, block, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int D, int C>
@@ -986,6 +1131,15 @@ hipError_t launch_decode_partial(const DecodeParams& p, Codec codec, int head_di
         case 64: return launch_partial_d<64>(p, codec, s);
         case 128: return launch_partial_d<128>(p, codec, s);
         case 256: return launch_partial_d<256>(p, codec, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_partial_rotated(const DecodeParams& p, Codec codec, int head_dim, hipStream_t s) {
+    switch (head_dim) {
+        case 64: return launch_rotated_d<64>(p, codec, s);
+        case 128: return launch_rotated_d<128>(p, codec, s);
+        case 256: return launch_rotated_d<256>(p, codec, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -556,6 +556,33 @@ int fp8kv_paged_decode_rotated(void* out, int out_dtype, const void* query,
                                float k_scale, float v_scale, int sliding_window, int num_splits,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fp8kv_decode_step_rotated -- one whole decode step over a rotated cache, normally in a
+ * single kernel launch: each sequence's new K/V token is rotated and written exactly as
+ * fp8kv_cache_write_rotated writes it (same f32 butterflies, same division and cast), the
+ * query is rotated inside the kernel into the same two bf16 terms fp8kv_paged_decode_rotated
+ * uses, and the merged output is rotated back before it is stored:
+ *   out = H/sqrt(d) . Attention(H/sqrt(d) . q, K_rot, V_rot).
+ * When the split partials of a (sequence, kv head) are more than one workgroup merges
+ * quickly (as in fp8kv_decode_step), the merge kernel writes f32 rows into the workspace and
+ * one more launch rotates them back.  Token rows, slots, counters, reproducibility and errors
+ * as for fp8kv_decode_step; per-tensor scales; cache dtypes FP8KV_E4M3 and FP8KV_BF16 (else
+ * FP8KV_ERR_UNSUPPORTED).
+ *
+ *   workspace  at least fp8kv_paged_decode_rotated_workspace_size() bytes, 256-byte aligned,
+ *              contents on entry irrelevant.
+ */
+int fp8kv_decode_step_rotated(void* out, int out_dtype, const void* query,
+                              const void* key_new, const void* value_new,
+                              void* key_cache, void* value_cache, int cache_dtype,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* context_lens, int max_context_len,
+                              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks,
+                              float k_scale, float v_scale, int sliding_window, int num_splits,
+                              void* counters, size_t counters_bytes,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

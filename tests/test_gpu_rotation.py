@@ -1,7 +1,8 @@
 """GPU parity of the Hadamard-rotation entry points: the rotated cache write is bit-exact
 against the oracle's rotated write (rotation in f32 in the same butterfly order, then the
 same quantiser), and the rotated decode (query rotation, decode, output rotated back)
-matches the oracle's rotated decode within the decode tolerance."""
+matches the oracle's rotated decode within the decode tolerance; the fused rotated step writes
+the step token's bytes exactly as the rotated write does and decodes within that tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -9,8 +10,8 @@ import torch
 import fp8_kv_cache_reshape_amd as F
 import oracle
 import synthetic as syn
-from gpu_util import (BF16, DEV, E4M3, DeviceInputs, assert_close, dev_caches, host_caches, say,
-                      to_host_bits, u16_dev)
+from gpu_util import (BF16, DEV, E4M3, DeviceInputs, assert_close, dev_caches, host_caches,
+                      new_counters, say, step_rows_by_seq, to_host_bits, u16_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,3 +100,92 @@ def test_rotated_decode_windows(window):
     w, L, ks, vs = _mk(64, 8, 64, [1, 20, 200, 1100], cid=201, window=window)
     say(f"paged_decode_rotated window={window}")
     _check_decode(w, L, ks, vs)
+
+
+# ---- the fused rotated step: write the step token rotated + decode + rotate back
+
+def _step(w, L, ks, vs, kc, vc, cdt, out_f32=False, num_splits=0, counters=None):
+    dev = DeviceInputs(w)
+    B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+    win = L.sliding_window
+    if counters is None:
+        counters = new_counters(B, Hkv)
+    nbytes = F.fp8kv_paged_decode_rotated_workspace_size(B, Hq, Hkv, D, 16, w.max_context_len, win,
+                                                        num_splits)
+    # NaN bytes: every partial and rotated row the step reads must be its own
+    ws = torch.full((max(nbytes, 256),), 0xFF, dtype=torch.uint8, device=DEV)
+    kn, vn = step_rows_by_seq(w, L)
+    kd, vd = u16_dev(kn), u16_dev(vn)
+    out = torch.empty(B * Hq * D, dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
+    F.fp8kv_decode_step_rotated(out, F.FP8KV_F32 if out_f32 else F.FP8KV_BF16, dev.q, kd, vd, kc, vc,
+                                cdt, dev.bt, w.max_blocks_per_seq, dev.cl, w.max_context_len, B, Hq,
+                                Hkv, D, 16, w.num_blocks, ks, vs, win, num_splits, counters,
+                                counters.numel(), ws, ws.numel())
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D), counters
+
+
+def _check_step(w, L, ks, vs, out_f32=False, num_splits=0):
+    """Context rows written by the rotated cache write, the step token by the rotated step:
+    the cache bytes equal the oracle's rotated write of every row, the output matches the
+    oracle's rotated decode over that cache, and the counters are back at zero."""
+    cdt = E4M3 if L.cache_dtype == syn.E4M3 else BF16
+    kc, vc = dev_caches(w, cdt)
+    rows = w.prefix_token_rows()
+    slots = torch.from_numpy(np.ascontiguousarray(w.slot_mapping[rows])).to(DEV)
+    kp, vp = u16_dev(L.k[rows]), u16_dev(L.v[rows])
+    F.fp8kv_cache_write_rotated(kp, vp, kc, vc, cdt, slots, len(rows), w.num_kv_heads, w.head_dim,
+                                16, w.num_blocks, ks, vs)
+    got, cnt = _step(w, L, ks, vs, kc, vc, cdt, out_f32=out_f32, num_splits=num_splits)
+    okc, ovc = host_caches(w, cdt)
+    oracle.cache_write_rotated(L.k, L.v, okc, ovc, cdt, w.slot_mapping, w.num_kv_heads, w.head_dim,
+                               16, w.num_blocks, ks, vs)
+    assert np.array_equal(to_host_bits(kc), okc), "key cache bytes differ after the rotated step"
+    assert np.array_equal(to_host_bits(vc), ovc), "value cache bytes differ after the rotated step"
+    ref = oracle.paged_decode_rotated(w.q, okc, ovc, cdt, w.block_tables, w.context_lens,
+                                      w.num_q_heads, w.num_kv_heads, w.head_dim, 16, ks, vs,
+                                      L.sliding_window)
+    tol = dict(atol=2e-4, rtol=2e-3) if out_f32 else {}
+    assert_close(got, ref, what=w.name, **tol)
+    assert not cnt.cpu().numpy().any(), "counters were not returned to zero"
+    return got
+
+
+@pytest.mark.parametrize("cache", [syn.E4M3, syn.BF16])
+@pytest.mark.parametrize("Hq,Hkv,D", SHAPES + [(8, 1, 256)])
+def test_rotated_step_matches_oracle(Hq, Hkv, D, cache):
+    w, L, ks, vs = _mk(Hq, Hkv, D, [1, 16, 17, 300, 1027, 0], cid=210 + Hq + D, cache=cache)
+    say(f"decode_step_rotated {w.name}")
+    _check_step(w, L, ks, vs)
+
+
+# 1: the kernel writes final rows itself; 64: in-kernel merge over two batches; 129: more
+# partials than the in-kernel merge takes, so the merge kernel and the rotate-back launch run
+@pytest.mark.parametrize("num_splits", [0, 1, 5, 64, 129])
+def test_rotated_step_split_counts(num_splits):
+    w, L, ks, vs = _mk(32, 8, 128, [5, 700, 2049, 16], cid=220)
+    say(f"decode_step_rotated splits={num_splits}")
+    _check_step(w, L, ks, vs, out_f32=True, num_splits=num_splits)
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 16, 17])
+def test_rotated_step_d256_group8(num_splits):
+    w, L, ks, vs = _mk(8, 1, 256, [5, 700, 4100, 16, 1500], cid=221)
+    say(f"decode_step_rotated d256 g8 splits={num_splits}")
+    _check_step(w, L, ks, vs, out_f32=True, num_splits=num_splits)
+
+
+@pytest.mark.parametrize("window", [1, 17, 512])
+def test_rotated_step_windows(window):
+    w, L, ks, vs = _mk(64, 8, 64, [1, 20, 200, 1100], cid=222, window=window)
+    say(f"decode_step_rotated window={window}")
+    _check_step(w, L, ks, vs)
+
+
+def test_rotated_step_fixed_splits_reproducible():
+    """A fixed split count: two steps over the same cache give the same output, bit for bit."""
+    w, L, ks, vs = _mk(32, 8, 128, [3000, 900, 40], cid=223)
+    say("decode_step_rotated reproducibility")
+    a = _check_step(w, L, ks, vs, out_f32=True, num_splits=7)
+    b = _check_step(w, L, ks, vs, out_f32=True, num_splits=7)
+    assert np.array_equal(a, b)
