@@ -297,7 +297,8 @@ class DecodeBench:
 PROFILE_SUMMARY = "profiles/decode_llama8b_b1_128k.txt"
 KERNEL_SOURCES = ["fp8_kv_cache_reshape_amd/csrc/paged_decode.hip",
                   "fp8_kv_cache_reshape_amd/csrc/internal.h",
-                  "fp8_kv_cache_reshape_amd/csrc/codec.h"]
+                  "fp8_kv_cache_reshape_amd/csrc/codec.h",
+                  "fp8_kv_cache_reshape_amd/csrc/hadamard.h"]
 
 
 def measured_traffic(root: str):
@@ -312,7 +313,7 @@ def measured_traffic(root: str):
     for f in KERNEL_SOURCES:
         h.update(open(os.path.join(root, f), "rb").read())
     text = open(path).read()
-    if f"(paged_decode.hip + internal.h + codec.h): {h.hexdigest()[:16]}" not in text:
+    if f"(paged_decode.hip + internal.h + codec.h + hadamard.h): {h.hexdigest()[:16]}" not in text:
         return None
     for line in text.splitlines():
         if line.startswith("decode_partial_traffic_bytes_per_launch"):
