@@ -127,13 +127,22 @@ __device__ constexpr int lds_value(int ch, int slot, int cb) {
 // tiles (keys of blocks 0..NB-1, then their values) are moved by the 8 waves: each wave
 // WAVE_SRC contiguous source bytes, in PIECES pieces of PIECE_SRC bytes that each lie in one
 // tile, each lane PER bytes of a piece.
-#ifndef FP8KV_PREFILL_STEP_SCALE
-#define FP8KV_PREFILL_STEP_SCALE 2
+#ifndef FP8KV_PREFILL_TILES
+#define FP8KV_PREFILL_TILES 2
 #endif
+// Column tiles per wave: two 16-column tiles at d <= 128, whose products share every key and
+// value operand read from LDS; one at d = 256, whose accumulators would not fit twice in the
+// registers of two waves per SIMD.
+__host__ __device__ constexpr int col_tiles(int d) { return d <= 128 && FP8KV_PREFILL_TILES >= 2 ? 2 : 1; }
+
 template <int D, int C>
 struct Stage {
+    static constexpr int CT = col_tiles(D);
     static constexpr bool WIDE = D == 64 || (D == 128 && C != kCodecBF16);
-    static constexpr int NB = (D <= 128 ? 4 : 2) * (WIDE ? FP8KV_PREFILL_STEP_SCALE : 1);   // blocks per step
+    // blocks per step (a two-byte cache stages twice the bytes and needs the low P term, so
+    // its steps are half as long at two column tiles)
+    static constexpr int NB = CT == 2 ? (D == 64 ? 8 : 4) / (C == kCodecBF16 ? 2 : 1)
+                                      : (D <= 128 ? 4 : 2) * (WIDE ? 2 : 1);
     static constexpr int STEP = NB * kBlockSize;              // keys per step
     static constexpr int ES = C == kCodecBF16 ? 2 : 1;       // source bytes per element
     static constexpr int TILE_SRC = kBlockSize * D * ES;     // bytes of a cache tile
@@ -153,6 +162,8 @@ __global__ __launch_bounds__(64 * kWaves)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams p) {
     using S = Stage<D, C>;
+    constexpr int CT = S::CT;
+    constexpr int WCOLS = kCols * CT;      // query columns per wave
     constexpr int NB = S::NB;
     constexpr int STEP = S::STEP;
     constexpr int NK = D / 32;             // 32-channel contraction slices of S
@@ -165,21 +176,30 @@ void prefill_kernel(PrefillParams p) {
     using pv_t = std::conditional_t<kF16, f16x8, bf16x8>;
     // a staged step: key tiles of blocks 0..NB-1 in bf16, then their value tiles (pv_t)
     __shared__ __attribute__((aligned(16))) uint8_t sm_kv[2][2 * NB * TL];
+    // with two column tiles the query operands live in LDS (each wave's own region, 16-byte
+    // pieces [tile][slice][lane]), read again for every step: registers are what bounds
+    // this kernel
+    constexpr bool kQLds = CT == 2;
+    __shared__ __attribute__((aligned(16))) uint8_t sm_q[kQLds ? kWaves * CT * NK * 64 * 16 : 16];
 
     const int lane = threadIdx.x & 63;
     // wave-uniform (a scalar register, so that the staging addresses stay scalar)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;             // this lane's query column
     const int grp = lane >> 4;             // contraction group
-    const int h = blockIdx.y;              // kv head
-    const int b = blockIdx.z;
+    // grid x = (column tile, sequence, kv head), tile slowest: workgroups start in index order,
+    // so the heaviest tiles of every sequence and head go first (longest first over the grid)
+    const int hb = (int)blockIdx.x % (p.num_seqs * p.num_kv_heads);
+    const int h = hb % p.num_kv_heads;     // kv head
+    const int b = hb / p.num_kv_heads;
     const int G = p.num_q_heads / p.num_kv_heads;
 
     const int q0 = ((ConstI32Ptr)p.query_start_loc)[b];
     const int nq = ((ConstI32Ptr)p.query_start_loc)[b + 1] - q0;       // chunk tokens
-    const int tile = (int)gridDim.x - 1 - (int)blockIdx.x;             // heaviest tiles first
+    const int tile = (int)gridDim.x / (p.num_seqs * p.num_kv_heads) - 1 -
+                     (int)blockIdx.x / (p.num_seqs * p.num_kv_heads);  // heaviest tiles first
     const int64_t ncols = (int64_t)(nq > 0 ? nq : 0) * G;
-    const int64_t cw0 = (int64_t)tile * (kWaves * kCols);             // first column of the workgroup
+    const int64_t cw0 = (int64_t)tile * (kWaves * WCOLS);            // first column of the workgroup
     if (p.err != nullptr && tile == 0 && h == 0 && threadIdx.x == 0) {
         const int len_in = ((ConstI32Ptr)p.context_lens)[b];
         if (nq < 0 || nq > p.max_query_len) report_error(p.err, kErrQueryLen);
@@ -187,7 +207,7 @@ void prefill_kernel(PrefillParams p) {
             report_error(p.err, kErrContextLen);
     }
     if (cw0 >= ncols) return;                                         // (whole workgroup)
-    const int64_t c0 = cw0 + wave * kCols;                            // first column of the wave
+    const int64_t c0 = cw0 + wave * WCOLS;                            // first column of the wave
     const bool wactive = c0 < ncols;
 
     int L = ((ConstI32Ptr)p.context_lens)[b];
@@ -197,38 +217,54 @@ void prefill_kernel(PrefillParams p) {
     const int W = p.sliding_window;
     auto lo_of = [&](int pos) { return (W > 0 && pos + 1 > W) ? pos + 1 - W : 0; };
 
-    // this lane's column
-    const int64_t cg = c0 + col;
-    const bool cvalid = cg < ncols;
-    const int tok = cvalid ? (int)(cg / G) : 0;
-    const int hq = h * G + (cvalid ? (int)(cg % G) : 0);
-    const int pos = L - nq + tok;          // < 0: the column attends to nothing
-    const int clo = lo_of(pos);
+    // this lane's column in tile j: c0 + 16 j + col
+    bool cvalid[CT];
+    int tok[CT], hq[CT], pos[CT], clo[CT];
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+        const int64_t cg = c0 + kCols * j + col;
+        cvalid[j] = cg < ncols;
+        tok[j] = cvalid[j] ? (int)(cg / G) : 0;
+        hq[j] = h * G + (cvalid[j] ? (int)(cg % G) : 0);
+        pos[j] = L - nq + tok[j];          // < 0: the column attends to nothing
+        clo[j] = lo_of(pos[j]);
+    }
 
     // key ranges: the workgroup stages [lo of its first position, its last position]; a
     // wave computes only the steps its own columns can see
-    const int64_t cwlast = (cw0 + kWaves * kCols <= ncols ? cw0 + kWaves * kCols : ncols) - 1;
+    const int64_t cwlast = (cw0 + kWaves * WCOLS <= ncols ? cw0 + kWaves * WCOLS : ncols) - 1;
     const int pwmin = L - nq + (int)(cw0 / G);
     const int kend = L - nq + (int)(cwlast / G) + 1;                  // exclusive, <= L
     const int kfirst = pwmin >= 0 ? (lo_of(pwmin) / STEP) * STEP : 0;
     const int nsteps = kend > kfirst ? (kend - kfirst + STEP - 1) / STEP : 0;
-    const int64_t clast = wactive ? (c0 + kCols <= ncols ? c0 + kCols : ncols) - 1 : c0;
+    const int64_t clast = wactive ? (c0 + WCOLS <= ncols ? c0 + WCOLS : ncols) - 1 : c0;
     const int pmin = L - nq + (int)(c0 / G);
     const int pmax = L - nq + (int)(clast / G);
     const int lomax = lo_of(pmax);
     const int lomin = lo_of(pmin);
 
-    // query operand of S: slice kk = q[hq][grp*D/4 + 8kk .. +8)
-    bf16x8 qb[NK];
-    {
-        const uint16_t* qrow = p.query + ((int64_t)(q0 + tok) * p.num_q_heads + hq) * D + grp * (D / 4);
+    // query operand of S for tile j: slice kk = q[hq][grp*D/4 + 8kk .. +8), in registers
+    // (one tile) or in this wave's LDS region (two tiles; only this wave reads it back, and a
+    // wave's LDS accesses take effect in order, so no barrier is needed)
+    bf16x8 qb[kQLds ? 1 : CT][NK];
+    uint8_t* const sq = sm_q + (kQLds ? wave * (CT * NK * 64 * 16) : 0);
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+        const uint16_t* qrow = p.query + ((int64_t)(q0 + tok[j]) * p.num_q_heads + hq[j]) * D + grp * (D / 4);
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (cvalid && pos >= 0) v = *reinterpret_cast<const u32x4*>(qrow + 8 * kk);
-            qb[kk] = __builtin_bit_cast(bf16x8, v);
+            if (cvalid[j] && pos[j] >= 0) v = *reinterpret_cast<const u32x4*>(qrow + 8 * kk);
+            if constexpr (kQLds)
+                *reinterpret_cast<u32x4*>(sq + ((j * NK + kk) * 64 + lane) * 16) = v;
+            else
+                qb[kQLds ? 0 : j][kk] = __builtin_bit_cast(bf16x8, v);
         }
     }
+    auto read_q = [&](int j, int kk) {
+        return kQLds ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sq + ((j * NK + kk) * 64 + lane) * 16))
+                     : qb[kQLds ? 0 : j][kk];
+    };
 
     const float kscale = p.k_scales != nullptr
                              ? ((const __attribute__((address_space(4))) float*)p.k_scales)[h]
@@ -236,14 +272,20 @@ void prefill_kernel(PrefillParams p) {
     const float sscale = p.score_scale * kscale;
     const ConstI32Ptr bt = (ConstI32Ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
 
-    f32x4 oacc[NT], osum[NT];
+    f32x4 oacc[CT][NT], osum[CT][NT];
+    float mref[CT];                        // running reference maximum of this lane's columns
+    float l_hi[CT], l_lo[CT];              // sum of this lane's share of their probabilities
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        oacc[t] = f32x4{};
-        osum[t] = f32x4{};
+    for (int j = 0; j < CT; ++j) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            oacc[j][t] = f32x4{};
+            osum[j][t] = f32x4{};
+        }
+        mref[j] = -INFINITY;
+        l_hi[j] = 0.0f;
+        l_lo[j] = 0.0f;
     }
-    float mref = -INFINITY;                // running reference maximum of this column
-    float l_hi = 0.0f, l_lo = 0.0f;        // sum of this lane's share of the probabilities
 
     if (nsteps > 0) {   // (then L >= 1, so the table and the cache hold at least one block)
     // ---- block ids.  The NB ids of a step are read one step before the step is staged,
@@ -361,8 +403,8 @@ void prefill_kernel(PrefillParams p) {
     };
 
     int flush = 0;
-    // multiply the O rows (columns 4*grp + i) by their columns' factors
-    auto rescale_rows = [&](float f) __attribute__((always_inline)) {
+    // multiply the O rows of tile j (its columns 4*grp + i) by their columns' factors
+    auto rescale_rows = [&](int j, float f) __attribute__((always_inline)) {
         float fr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) fr[i] = __shfl(f, 4 * grp + i);
@@ -370,8 +412,8 @@ void prefill_kernel(PrefillParams p) {
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                oacc[t][i] *= fr[i];
-                osum[t][i] *= fr[i];
+                oacc[j][t][i] *= fr[i];
+                osum[j][t][i] *= fr[i];
             }
     };
 
@@ -382,13 +424,13 @@ void prefill_kernel(PrefillParams p) {
         const uint8_t* sk = sm_kv[buf];
 
         // ---- value operands of P.V (lane: slots 4*grp .. +3 of both blocks of a pair, channel
-        // 16t + col).  They do not depend on the scores: when they fit in 64 registers they
-        // are read first, so their LDS latency hides behind S and the softmax; otherwise each
-        // is read just before its products.
+        // 16t + col).  They do not depend on the scores: with one column tile, when they fit in
+        // 64 registers, they are read first, so their LDS latency hides behind S and the
+        // softmax; otherwise each is read just before its products.
         auto read_v = [&](int t, int r) {
             return *reinterpret_cast<const pv_t*>(sk + (NB + 2 * r) * TL + lds_value(16 * t + col, 4 * grp, 0));
         };
-        constexpr bool kEarlyV = D <= 128 && NT * (NB / 2) <= 16;
+        constexpr bool kEarlyV = CT == 1 && D <= 128 && NT * (NB / 2) <= 16;
         pv_t vb[kEarlyV ? NT : 1][NB / 2];
         if constexpr (kEarlyV) {
 #pragma unroll
@@ -397,18 +439,40 @@ void prefill_kernel(PrefillParams p) {
                 for (int r = 0; r < NB / 2; ++r) vb[t][r] = read_v(t, r);
         }
 
-        // ---- S = K.Q^T for each block: lane holds slots 4*grp + i of its column
-        f32x4 s[NB];
+        // ---- S = K.Q^T for each block and column tile: lane holds slots 4*grp + i of its
+        // column; each key operand read feeds the products of every tile
+        f32x4 s[CT][NB];
+        auto read_k = [&](int c, int kk) {
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                sk + c * TL + lds_key<D>(col, grp * (D / 4) + 8 * kk)));
+        };
+        if constexpr (CT == 2) {
+            // contraction slice outermost: the query operands of slice kk are read once per
+            // step, and the 2 NB accumulators are independent
 #pragma unroll
-        for (int c = 0; c < NB; ++c) {
-            f32x4 a = f32x4{};
+            for (int c = 0; c < NB; ++c)
+#pragma unroll
+                for (int j = 0; j < CT; ++j) s[j][c] = f32x4{};
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(
-                    sk + c * TL + lds_key<D>(col, grp * (D / 4) + 8 * kk));
-                a = mfma16(__builtin_bit_cast(bf16x8, v), qb[kk], a);
+                bf16x8 qk[CT];
+#pragma unroll
+                for (int j = 0; j < CT; ++j) qk[j] = read_q(j, kk);
+#pragma unroll
+                for (int c = 0; c < NB; ++c) {
+                    const bf16x8 kop = read_k(c, kk);
+#pragma unroll
+                    for (int j = 0; j < CT; ++j) s[j][c] = mfma16(kop, qk[j], s[j][c]);
+                }
             }
-            s[c] = a;
+        } else {
+#pragma unroll
+            for (int c = 0; c < NB; ++c) {
+                f32x4 a = f32x4{};
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) a = mfma16(read_k(c, kk), read_q(0, kk), a);
+                s[0][c] = a;
+            }
         }
 
         // ---- raw scores masked outside [clo, pos] and outside valid blocks; the base-2
@@ -416,65 +480,78 @@ void prefill_kernel(PrefillParams p) {
         if ((kb + STEP > pmin + 1) | (kb < lomax) | (okmask != kAllBlocks)) {
             const int k0 = kb + 4 * grp;
 #pragma unroll
+            for (int j = 0; j < CT; ++j)
+#pragma unroll
+                for (int c = 0; c < NB; ++c)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kp = k0 + c * kBlockSize + i;
+                        const bool ok = kp >= clo[j] && kp <= pos[j] && ((okmask >> c) & 1u);
+                        s[j][c][i] = ok ? s[j][c][i] : -INFINITY;
+                    }
+        }
+        float mu[CT];
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            float mx = -INFINITY;
+#pragma unroll
             for (int c = 0; c < NB; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int kp = k0 + c * kBlockSize + i;
-                    const bool ok = kp >= clo && kp <= pos && ((okmask >> c) & 1u);
-                    s[c][i] = ok ? s[c][i] : -INFINITY;
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][c][i]);
+            mx = max_over_groups(mx) * sscale;
+            // lazy reference move: only when a score exceeds it by 2^8 (or on the first keys)
+            const bool move = mx > mref[j] + kRescaleLog2;
+            if (__ballot(move) != 0) {
+                const float f = move ? (mref[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mref[j] - mx)) : 1.0f;
+                if (move) {
+                    mref[j] = mx;
+                    l_hi[j] *= f;
+                    l_lo[j] *= f;
                 }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int c = 0; c < NB; ++c)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[c][i]);
-        mx = max_over_groups(mx) * sscale;
-        // lazy reference move: only when a score exceeds it by 2^8 (or on the first keys)
-        const bool move = mx > mref + kRescaleLog2;
-        if (__ballot(move) != 0) {
-            const float f = move ? (mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mref - mx)) : 1.0f;
-            if (move) {
-                mref = mx;
-                l_hi *= f;
-                l_lo *= f;
+                rescale_rows(j, f);
             }
-            rescale_rows(f);
+            mu[j] = mref[j] == -INFINITY ? 0.0f : mref[j];
         }
-        const float mu = mref == -INFINITY ? 0.0f : mref;
 
         // ---- probabilities; pair r holds blocks 2r and 2r+1, element 4c' + i of it is slot
         // 4*grp + i of block 2r + c'.  One-byte caches: one fp16 term, every probability
         // (and the normaliser with it) scaled by 2^kPShift so that small ones stay normal
         // fp16 numbers.  bf16 cache: a high (pf truncated to bf16, so pf - hi is exact) and
         // a low bf16 term.
-        const float mus = kF16 ? mu - (float)kPShift : mu;
-        pv_t pa[NB / 2], pb[kF16 ? 1 : NB / 2];
-        float psum = 0.0f;
+        pv_t pa[CT][NB / 2], pb[CT][kF16 ? 1 : NB / 2];
 #pragma unroll
-        for (int c = 0; c < NB; ++c)
+        for (int j = 0; j < CT; ++j) {
+            const float mus = kF16 ? mu[j] - (float)kPShift : mu[j];
+            float psum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][i], sscale, -mus));
-                if constexpr (kF16) {
-                    pa[c / 2][4 * (c % 2) + i] = (_Float16)pf;   // round to nearest even
-                } else {
-                    const float hf = __uint_as_float(__float_as_uint(pf) & 0xFFFF0000u);
-                    pa[c / 2][4 * (c % 2) + i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(pf) >> 16));
-                    pb[c / 2][4 * (c % 2) + i] = (__bf16)(pf - hf);
+            for (int c = 0; c < NB; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][c][i], sscale, -mus));
+                    if constexpr (kF16) {
+                        pa[j][c / 2][4 * (c % 2) + i] = (_Float16)pf;   // round to nearest even
+                    } else {
+                        const float hf = __uint_as_float(__float_as_uint(pf) & 0xFFFF0000u);
+                        pa[j][c / 2][4 * (c % 2) + i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(pf) >> 16));
+                        pb[j][c / 2][4 * (c % 2) + i] = (__bf16)(pf - hf);
+                    }
+                    psum += pf;
                 }
-                psum += pf;
-            }
-        comp_add(l_hi, l_lo, psum);
+            comp_add(l_hi[j], l_lo[j], psum);
+        }
 
-        // ---- O += P.V per channel tile (value slots past the context were zeroed when staged)
+        // ---- O += P.V per channel tile (value slots past the context were zeroed when
+        // staged); each value operand read feeds the products of every column tile
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
             for (int r = 0; r < NB / 2; ++r) {
                 const pv_t v = kEarlyV ? vb[kEarlyV ? t : 0][r] : read_v(t, r);
-                oacc[t] = mfma16(pa[r], v, oacc[t]);
-                if constexpr (!kF16) oacc[t] = mfma16(pb[kF16 ? 0 : r], v, oacc[t]);
+#pragma unroll
+                for (int j = 0; j < CT; ++j) {
+                    oacc[j][t] = mfma16(pa[j][r], v, oacc[j][t]);
+                    if constexpr (!kF16) oacc[j][t] = mfma16(pb[j][kF16 ? 0 : r], v, oacc[j][t]);
+                }
             }
         }
 
@@ -482,10 +559,12 @@ void prefill_kernel(PrefillParams p) {
         if (++flush == S::FLUSH) {
             flush = 0;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                osum[t] += oacc[t];
-                oacc[t] = f32x4{};
-            }
+            for (int j = 0; j < CT; ++j)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    osum[j][t] += oacc[j][t];
+                    oacc[j][t] = f32x4{};
+                }
         }
     };
 
@@ -545,37 +624,42 @@ void prefill_kernel(PrefillParams p) {
         if (__any(bad) && lane == 0) report_error(p.err, kErrBlockId);
     }
     if (!wactive) return;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) osum[t] += oacc[t];
-
-    // ---- normalise: the column's probability sum over its four groups, then v_scale / l
-    float l_tot = l_hi + l_lo;
-    l_tot += __shfl_xor(l_tot, 16);
-    l_tot += __shfl_xor(l_tot, 32);
     const float vscale = p.v_scales != nullptr
                              ? ((const __attribute__((address_space(4))) float*)p.v_scales)[h]
                              : p.v_scale;
-    const float inv = l_tot > 0.0f ? vscale / l_tot : 0.0f;   // no attended key: zero row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int orow = 4 * grp + i;                          // the column this row holds
-        const float f = __shfl(inv, orow);
-        const int64_t oc = c0 + orow;
-        if (oc >= ncols) continue;
-        const int otok = (int)(oc / G);
-        const int ohq = h * G + (int)(oc % G);
-        const int64_t base = ((int64_t)(q0 + otok) * p.num_q_heads + ohq) * D;
+    for (int j = 0; j < CT; ++j) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) store_out(p.out, p.out_f32, base + 16 * t + col, osum[t][i] * f);
+        for (int t = 0; t < NT; ++t) osum[j][t] += oacc[j][t];
+
+        // ---- normalise: the column's probability sum over its four groups, then v_scale / l
+        float l_tot = l_hi[j] + l_lo[j];
+        l_tot += __shfl_xor(l_tot, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        const float inv = l_tot > 0.0f ? vscale / l_tot : 0.0f;   // no attended key: zero row
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int orow = 4 * grp + i;                          // the column this row holds
+            const float f = __shfl(inv, orow);
+            const int64_t oc = c0 + kCols * j + orow;
+            if (oc >= ncols) continue;
+            const int otok = (int)(oc / G);
+            const int ohq = h * G + (int)(oc % G);
+            const int64_t base = ((int64_t)(q0 + otok) * p.num_q_heads + ohq) * D;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) store_out(p.out, p.out_f32, base + 16 * t + col, osum[j][t][i] * f);
+        }
     }
 }
 
 template <int D>
 hipError_t launch_d(const PrefillParams& p, Codec codec, hipStream_t s) {
     const int G = p.num_q_heads / p.num_kv_heads;
-    const int64_t tiles = ((int64_t)p.max_query_len * G + kWaves * kCols - 1) / (kWaves * kCols);
+    constexpr int kWgCols = kWaves * kCols * col_tiles(D);   // query columns per workgroup
+    const int64_t tiles = ((int64_t)p.max_query_len * G + kWgCols - 1) / kWgCols;
     if (tiles <= 0 || p.num_seqs <= 0) return hipSuccess;
-    if (tiles > 0x7FFFFFFF || p.num_seqs > 65535 || p.num_kv_heads > 65535) return hipErrorInvalidValue;
+    const int64_t groups = (int64_t)p.num_seqs * p.num_kv_heads;   // (sequence, kv head) pairs
+    if (tiles * groups > 0x7FFFFFFF) return hipErrorInvalidValue;
     const void* fn;
     switch (codec) {
         case kCodecE4M3: fn = reinterpret_cast<const void*>(&prefill_kernel<D, kCodecE4M3>); break;
@@ -584,8 +668,7 @@ hipError_t launch_d(const PrefillParams& p, Codec codec, hipStream_t s) {
         case kCodecINT8: fn = reinterpret_cast<const void*>(&prefill_kernel<D, kCodecINT8>); break;
         default: return hipErrorInvalidValue;
     }
-    return launch_kernel(fn, dim3((unsigned)tiles, p.num_kv_heads, p.num_seqs), dim3(64 * kWaves),
-                         0, s, p);
+    return launch_kernel(fn, dim3((unsigned)(tiles * groups)), dim3(64 * kWaves), 0, s, p);
 }
 
 }  // namespace
