@@ -1,7 +1,9 @@
 """GPU parity at the measured workload sizes, in the launch configuration the benchmark uses
-(automatic split count unless stated), against the fp64 oracle on sampled (sequence, query
-head) outputs; cache bytes are compared in full.  Also the long-context checks: a planted
-needle key must be retrieved at 4K..256K, and the error must not grow with context length."""
+(automatic split count unless stated), against the fp64 oracle on every (sequence, query
+head) output of the multi-sequence batches (the oracle runs one pair per task on a thread
+pool) and on sampled ones elsewhere; cache bytes are compared in full.  Also the
+long-context checks: a planted needle key must be retrieved at 4K..256K, and the error must
+not grow with context length."""
 import numpy as np
 import pytest
 import torch
@@ -10,6 +12,11 @@ import synthetic as syn
 from gpu_util import (BF16, E4M3, DeviceInputs, assert_close, dev_caches, gpu_decode, gpu_decode_step,
                       gpu_write, new_counters, oracle_decode, oracle_decode_threaded, oracle_write,
                       sample_pairs, say, to_host_bits)
+
+
+def all_pairs(w):
+    """Every (sequence, query head) pair of the batch."""
+    return np.array([(b, h) for b in range(w.num_seqs) for h in range(w.num_q_heads)], np.int32)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +29,11 @@ def _layer_parity(w, layer, pairs, num_splits_list=(0,), out_f32=False, check_ca
     if check_cache:
         assert np.array_equal(to_host_bits(kc), okc), f"{w.name}/{layer.name}: key cache bytes differ"
         assert np.array_equal(to_host_bits(vc), ovc), f"{w.name}/{layer.name}: value cache bytes differ"
-    ref = oracle_decode(w, layer, okc, ovc, pairs=pairs)
+    if len(pairs) > 64:
+        say(f"oracle decode of {len(pairs)} (sequence, head) pairs on a thread pool")
+        ref = oracle_decode_threaded(w, layer, okc, ovc, pairs)
+    else:
+        ref = oracle_decode(w, layer, okc, ovc, pairs=pairs)
     dev = DeviceInputs(w)
     results = {}
     for ns in num_splits_list:
@@ -48,7 +59,7 @@ def test_tiny_all_heads():
 def test_llama8b_batch8_16k_24k(scale_mode):
     w = syn.llama8b_batch(scale_mode)
     say(f"workload {w.name} lens={w.context_lens.tolist()}")
-    _layer_parity(w, w.layers[0], sample_pairs(w, 2))
+    _layer_parity(w, w.layers[0], all_pairs(w))
 
 
 def test_llama8b_headline_128k():
@@ -78,7 +89,7 @@ def test_llama8b_headline_b8_128k():
     okc, ovc = oracle_write(w, layer)
     assert np.array_equal(to_host_bits(kc), okc), "key cache bytes differ"
     assert np.array_equal(to_host_bits(vc), ovc), "value cache bytes differ"
-    pairs = sample_pairs(w, 2)
+    pairs = all_pairs(w)
     say(f"oracle decode of {len(pairs)} (sequence, head) pairs")
     ref = oracle_decode_threaded(w, layer, okc, ovc, pairs)
     assert_close(got[pairs[:, 0], pairs[:, 1]], ref, what=f"{w.name} fused step")
@@ -93,14 +104,14 @@ def test_gptoss_mixed_layers(skip_sw):
     w = syn.gptoss_mixed(skip_sw=skip_sw)
     for layer in w.layers:
         say(f"workload {w.name} layer {layer.name} ({layer.cache_dtype}, window {layer.sliding_window})")
-        _layer_parity(w, layer, sample_pairs(w, 2))
+        _layer_parity(w, layer, all_pairs(w))
 
 
 def test_d256_global_and_window_layers():
     w = syn.gemma_d256()
     for layer in w.layers:
         say(f"workload {w.name} layer {layer.name} (window {layer.sliding_window})")
-        _layer_parity(w, layer, sample_pairs(w, 1), num_splits_list=(0, 4, 8, 16))
+        _layer_parity(w, layer, all_pairs(w), num_splits_list=(0, 4, 8, 16))
 
 
 def _needle_case(L, variant=0):
