@@ -73,6 +73,7 @@ def _bind(path: str) -> ctypes.CDLL:
         "oracle_paged_decode_pairs": [P, P, i32, P, P, P, i32, P, i32, P, i32, i32, i32,
                                       i32, f64, f64, i32],
         "oracle_cache_write_per_head": [P, P, P, P, i32, P, i32, i32, i32, i32, i32, P, P],
+        "oracle_cache_write_rotated_per_head": [P, P, P, P, i32, P, i32, i32, i32, i32, i32, P, P],
         "oracle_paged_decode_pairs_per_head": [P, P, i32, P, P, P, i32, P, i32, P, i32, i32, i32,
                                                i32, P, P, i32],
         "oracle_paged_prefill_pairs": [P, P, i32, P, P, i32, P, P, i32, P, i32, P, i32, i32, i32,
@@ -86,6 +87,8 @@ def _bind(path: str) -> ctypes.CDLL:
         "oracle_cache_write_rotated": [P, P, P, P, i32, P, i32, i32, i32, i32, i32, f32, f32],
         "oracle_paged_decode_rotated_pairs": [P, P, i32, P, P, P, i32, P, i32, P, i32, i32, i32,
                                               i32, f64, f64, i32],
+        "oracle_paged_decode_rotated_pairs_per_head": [P, P, i32, P, P, P, i32, P, i32, P, i32, i32,
+                                                       i32, i32, P, P, i32],
     }.items():
         fn = getattr(L, name)
         fn.restype = None
@@ -367,6 +370,61 @@ def paged_decode_rotated_pairs(pairs, q, key_cache, value_cache, cache_dtype: in
                                             num_kv_heads, head_dim, block_size, float(k_scale),
                                             float(v_scale), int(sliding_window))
     return out
+
+
+def cache_write_rotated_per_head(key, value, key_cache: np.ndarray, value_cache: np.ndarray,
+                                 cache_dtype: int, slot_mapping, num_kv_heads: int, head_dim: int,
+                                 block_size: int, num_blocks: int, k_scales, v_scales) -> None:
+    """cache_write_rotated with one (k, v) scale pair per kv head (float32 [num_kv_heads])."""
+    k = np.ascontiguousarray(key, dtype=np.uint16)
+    v = np.ascontiguousarray(value, dtype=np.uint16)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    ks = np.ascontiguousarray(k_scales, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scales, dtype=np.float32)
+    T = sm.shape[0]
+    assert k.size == T * num_kv_heads * head_dim and v.size == k.size
+    assert ks.shape == (num_kv_heads,) and vs.shape == (num_kv_heads,)
+    assert head_dim & (head_dim - 1) == 0 and block_size == 16
+    want = np.uint16 if cache_dtype == CACHE_BF16 else np.uint8
+    assert key_cache.dtype == want and value_cache.dtype == want
+    assert key_cache.flags["C_CONTIGUOUS"] and value_cache.flags["C_CONTIGUOUS"]
+    lib().oracle_cache_write_rotated_per_head(_ptr(k), _ptr(v), _ptr(key_cache), _ptr(value_cache),
+                                              cache_dtype, _ptr(sm), T, num_kv_heads, head_dim,
+                                              block_size, num_blocks, _ptr(ks), _ptr(vs))
+
+
+def paged_decode_rotated_pairs_per_head(pairs, q, key_cache, value_cache, cache_dtype: int,
+                                        block_tables, context_lens, num_q_heads: int,
+                                        num_kv_heads: int, head_dim: int, block_size: int,
+                                        k_scales, v_scales, sliding_window: int = 0) -> np.ndarray:
+    """paged_decode_rotated_pairs with one (k, v) scale pair per kv head: [n][D]."""
+    q, bt, cl = _decode_common(q, key_cache, value_cache, cache_dtype, block_tables, context_lens)
+    pr = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    ks = np.ascontiguousarray(np.asarray(k_scales, dtype=np.float32), dtype=np.float64)
+    vs = np.ascontiguousarray(np.asarray(v_scales, dtype=np.float32), dtype=np.float64)
+    assert ks.shape == (num_kv_heads,) and vs.shape == (num_kv_heads,)
+    out = np.empty((pr.shape[0], head_dim), dtype=np.float64)
+    lib().oracle_paged_decode_rotated_pairs_per_head(_ptr(out), _ptr(pr), pr.shape[0], _ptr(q),
+                                                     _ptr(key_cache), _ptr(value_cache),
+                                                     cache_dtype, _ptr(bt), bt.shape[1], _ptr(cl),
+                                                     num_q_heads, num_kv_heads, head_dim,
+                                                     block_size, _ptr(ks), _ptr(vs),
+                                                     int(sliding_window))
+    return out
+
+
+def paged_decode_rotated_per_head(q, key_cache, value_cache, cache_dtype: int, block_tables,
+                                  context_lens, num_q_heads: int, num_kv_heads: int,
+                                  head_dim: int, block_size: int, k_scales, v_scales,
+                                  sliding_window: int = 0) -> np.ndarray:
+    """Every (sequence, query head) over a rotated cache with per-kv-head scales: [B][Hq][D]."""
+    B = np.asarray(context_lens).shape[0]
+    pairs = np.array([(b, hq) for b in range(B) for hq in range(num_q_heads)], np.int32)
+    out = paged_decode_rotated_pairs_per_head(pairs, q, key_cache, value_cache, cache_dtype,
+                                              block_tables, context_lens, num_q_heads,
+                                              num_kv_heads, head_dim, block_size, k_scales,
+                                              v_scales, sliding_window)
+    return out.reshape(B, num_q_heads, head_dim)
 
 
 def paged_decode_rotated(q, key_cache, value_cache, cache_dtype: int, block_tables, context_lens,

@@ -588,12 +588,15 @@ static uint16_t f32_to_bf16(float f) {
 /*
  * Rotated cache write: each K and V row (d elements of one token and kv head) is widened
  * to f32, rotated by oracle_hadamard_f32, then quantised exactly as oracle_cache_write
- * quantises (e4m3 cache) or rounded to bf16 (bf16 cache).
+ * quantises (e4m3 cache) or rounded to bf16 (bf16 cache).  k_scales / v_scales: one scale
+ * per kv head (the per-attention-head granularity of "FP8 KV Cache Quantization: Capacity
+ * Gains and Accuracy Risk", "Scales and calibration"), or null for k_scale / v_scale.
  */
-void oracle_cache_write_rotated(const uint16_t* key, const uint16_t* value,
-                                void* key_cache, void* value_cache, int cache_dtype,
-                                const int64_t* slot_mapping, int T, int Hkv, int D, int bs,
-                                int NB, float k_scale, float v_scale) {
+static void cache_write_rotated_core(const uint16_t* key, const uint16_t* value,
+                                     void* key_cache, void* value_cache, int cache_dtype,
+                                     const int64_t* slot_mapping, int T, int Hkv, int D, int bs,
+                                     int NB, float k_scale, float v_scale, const float* k_scales,
+                                     const float* v_scales) {
     float* rk = (float*)malloc(sizeof(float) * (size_t)D);
     float* rv = (float*)malloc(sizeof(float) * (size_t)D);
     for (int t = 0; t < T; ++t) {
@@ -613,8 +616,8 @@ void oracle_cache_write_rotated(const uint16_t* key, const uint16_t* value,
                                        cache_dtype == ORACLE_CACHE_BF16 ? 2 : 1);
                 int64_t vi = value_index(blk, h, in_block, i, Hkv, bs, D);
                 if (cache_dtype == ORACLE_CACHE_E4M3) {
-                    ((uint8_t*)key_cache)[ki] = quantize_f32(rk[i], k_scale);
-                    ((uint8_t*)value_cache)[vi] = quantize_f32(rv[i], v_scale);
+                    ((uint8_t*)key_cache)[ki] = quantize_f32(rk[i], k_scales ? k_scales[h] : k_scale);
+                    ((uint8_t*)value_cache)[vi] = quantize_f32(rv[i], v_scales ? v_scales[h] : v_scale);
                 } else {
                     ((uint16_t*)key_cache)[ki] = f32_to_bf16(rk[i]);
                     ((uint16_t*)value_cache)[vi] = f32_to_bf16(rv[i]);
@@ -624,6 +627,23 @@ void oracle_cache_write_rotated(const uint16_t* key, const uint16_t* value,
     }
     free(rk);
     free(rv);
+}
+
+void oracle_cache_write_rotated(const uint16_t* key, const uint16_t* value,
+                                void* key_cache, void* value_cache, int cache_dtype,
+                                const int64_t* slot_mapping, int T, int Hkv, int D, int bs,
+                                int NB, float k_scale, float v_scale) {
+    cache_write_rotated_core(key, value, key_cache, value_cache, cache_dtype, slot_mapping, T,
+                             Hkv, D, bs, NB, k_scale, v_scale, NULL, NULL);
+}
+
+void oracle_cache_write_rotated_per_head(const uint16_t* key, const uint16_t* value,
+                                         void* key_cache, void* value_cache, int cache_dtype,
+                                         const int64_t* slot_mapping, int T, int Hkv, int D,
+                                         int bs, int NB, const float* k_scales,
+                                         const float* v_scales) {
+    cache_write_rotated_core(key, value, key_cache, value_cache, cache_dtype, slot_mapping, T,
+                             Hkv, D, bs, NB, 1.0f, 1.0f, k_scales, v_scales);
 }
 
 /*
@@ -671,4 +691,25 @@ void oracle_paged_decode_rotated_pairs(double* out, const int32_t* pairs, int np
         free(V);
     }
     free(qr);
+}
+
+/*
+ * Decode over a rotated cache with one (k, v) scale pair per kv head: each pair decoded as
+ * oracle_paged_decode_rotated_pairs decodes it, with its kv head's two scales.
+ */
+void oracle_paged_decode_rotated_pairs_per_head(double* out, const int32_t* pairs, int npairs,
+                                                const uint16_t* q, const void* key_cache,
+                                                const void* value_cache, int cache_dtype,
+                                                const int32_t* block_tables, int max_blocks,
+                                                const int32_t* context_lens, int Hq, int Hkv,
+                                                int D, int bs, const double* k_scales,
+                                                const double* v_scales, int window) {
+    int group = Hq / Hkv;
+    for (int p = 0; p < npairs; ++p) {
+        int kvh = pairs[2 * p + 1] / group;
+        oracle_paged_decode_rotated_pairs(out + (int64_t)p * D, pairs + 2 * p, 1, q, key_cache,
+                                          value_cache, cache_dtype, block_tables, max_blocks,
+                                          context_lens, Hq, Hkv, D, bs, k_scales[kvh],
+                                          v_scales[kvh], window);
+    }
 }

@@ -81,6 +81,13 @@ MUTANTS = {
         "(void)o;"),
     "rotated_decode_query_not_rotated": ("oracle_hadamard_f64(qr, D);", "(void)qr;"),
     "rotated_write_values_unrotated": ("oracle_hadamard_f32(rv, D);", "(void)rv;"),
+    "rotated_per_head_write_head0_scale": ("quantize_f32(rk[i], k_scales ? k_scales[h] : k_scale)",
+                                           "quantize_f32(rk[i], k_scales ? k_scales[0] : k_scale)"),
+    "rotated_per_head_values_with_key_scales": (
+        "quantize_f32(rv[i], v_scales ? v_scales[h] : v_scale)",
+        "quantize_f32(rv[i], k_scales ? k_scales[h] : v_scale)"),
+    "rotated_per_head_decode_interleaved_heads": ("int kvh = pairs[2 * p + 1] / group;",
+                                                  "int kvh = pairs[2 * p + 1] % Hkv;"),
     "e5m2_exponent_bias": ("mag = ldexp(1.0 + (double)M / 4.0, E - 15);",
                            "mag = ldexp(1.0 + (double)M / 4.0, E - 16);"),
     "e5m2_subnormal_step": ("mag = ldexp((double)M, -16);", "mag = ldexp((double)M, -15);"),

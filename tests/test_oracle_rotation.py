@@ -135,3 +135,55 @@ def test_rotation_spreads_outliers_and_lowers_the_fp8_error():
         e_plain = np.abs(plain - ref).max()
         e_rot = np.abs(rot - ref).max()
         assert e_rot < e_plain, (cid, e_rot, e_plain)
+
+
+# ---- per-kv-head scales on the rotated path
+
+def test_rotated_per_head_write_is_the_per_tensor_rotated_write_head_by_head():
+    w = syn.make_workload("rot-ph-write", 96, num_q_heads=12, num_kv_heads=3, head_dim=128,
+                          context_lens=[70, 300], outlier_frac=0.01)
+    L = w.layers[0]
+    ks = syn.spread_head_scales(w.num_kv_heads, 96)
+    vs = syn.spread_head_scales(w.num_kv_heads, 97)
+    assert len(set(ks.tolist())) == w.num_kv_heads        # distinct, so a wrong head shows
+    kc, vc = _caches(w, E4M3)
+    oracle.cache_write_rotated_per_head(L.k, L.v, kc, vc, E4M3, w.slot_mapping, w.num_kv_heads,
+                                        w.head_dim, 16, w.num_blocks, ks, vs)
+    tiles = lambda c: c.reshape(w.num_blocks, w.num_kv_heads, -1)
+    for h in range(w.num_kv_heads):
+        pk, pv = _caches(w, E4M3)
+        oracle.cache_write_rotated(L.k, L.v, pk, pv, E4M3, w.slot_mapping, w.num_kv_heads, w.head_dim,
+                                   16, w.num_blocks, float(ks[h]), float(vs[h]))
+        assert np.array_equal(tiles(kc)[:, h], tiles(pk)[:, h]), f"key head {h}"
+        assert np.array_equal(tiles(vc)[:, h], tiles(pv)[:, h]), f"value head {h}"
+
+
+def test_rotated_per_head_decode_equals_plain_decode_when_the_codes_are_exact():
+    """Rows x = H r (r in {-1, 0, 1}) rotate back to r exactly in f32; with power-of-two
+    scales that differ per kv head, r / s is an exact e4m3 code, so the rotated fp8 cache
+    dequantises to r with each head's own scales, and attention in the rotated space, rotated
+    back, is the plain attention over x held in a bf16 cache.  A scale taken from the wrong
+    head, or a scale applied twice, moves the result off it."""
+    w, xk, xv, rk, rv = _exact_workload(syn.E4M3, cid=98)
+    ks = np.array([0.25, 0.5], np.float32)
+    vs = np.array([0.125, 1.0], np.float32)
+    rot_k, rot_v = _caches(w, E4M3)
+    oracle.cache_write_rotated_per_head(xk, xv, rot_k, rot_v, E4M3, w.slot_mapping,
+                                        w.num_kv_heads, w.head_dim, 16, w.num_blocks, ks, vs)
+    pl_k, pl_v = _caches(w, BF16)
+    oracle.cache_write(xk, xv, pl_k, pl_v, BF16, w.slot_mapping, w.num_kv_heads, w.head_dim, 16,
+                       w.num_blocks, 1.0, 1.0)
+    for window in (0, 10):
+        got = oracle.paged_decode_rotated_per_head(w.q, rot_k, rot_v, E4M3, w.block_tables,
+                                                   w.context_lens, w.num_q_heads, w.num_kv_heads,
+                                                   w.head_dim, 16, ks, vs, window)
+        ref = oracle.paged_decode(w.q, pl_k, pl_v, BF16, w.block_tables, w.context_lens,
+                                  w.num_q_heads, w.num_kv_heads, w.head_dim, 16, 1.0, 1.0, window)
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+    # the same cache read with the heads' scales swapped is measurably different
+    ref0 = oracle.paged_decode(w.q, pl_k, pl_v, BF16, w.block_tables, w.context_lens,
+                               w.num_q_heads, w.num_kv_heads, w.head_dim, 16, 1.0, 1.0, 0)
+    bad = oracle.paged_decode_rotated_per_head(w.q, rot_k, rot_v, E4M3, w.block_tables,
+                                               w.context_lens, w.num_q_heads, w.num_kv_heads,
+                                               w.head_dim, 16, ks[::-1].copy(), vs[::-1].copy(), 0)
+    assert np.abs(bad - ref0).max() > 1e-3
