@@ -81,6 +81,13 @@ SIGNATURES = {
                                         _I, _F, _F, _I, _I, _P, _SZ, _P]),
     "fp8kv_decode_step_rotated": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
                                        _I, _I, _I, _F, _F, _I, _I, _P, _SZ, _P, _SZ, _P]),
+    "fp8kv_cache_write_rotated_per_head": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P,
+                                                _P]),
+    "fp8kv_paged_decode_rotated_per_head": (_I, [_P, _I, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
+                                                 _I, _I, _I, _P, _P, _I, _I, _P, _SZ, _P]),
+    "fp8kv_decode_step_rotated_per_head": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
+                                                _I, _I, _I, _I, _I, _P, _P, _I, _I, _P, _SZ, _P,
+                                                _SZ, _P]),
 }
 
 if not os.path.exists(LIBRARY_PATH):
@@ -403,3 +410,45 @@ def fp8kv_decode_step_rotated(out, out_dtype, query, key_new, value_new, key_cac
                                                 num_splits, _addr(counters), counters_bytes,
                                                 _addr(workspace), workspace_bytes, _stream(stream)),
                   "fp8kv_decode_step_rotated")
+
+
+def fp8kv_cache_write_rotated_per_head(key, value, key_cache, value_cache, cache_dtype, slot_mapping,
+                                       num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                                       k_scales, v_scales, stream=None) -> int:
+    return _check(lib.fp8kv_cache_write_rotated_per_head(_addr(key), _addr(value), _addr(key_cache),
+                                                         _addr(value_cache), cache_dtype,
+                                                         _addr(slot_mapping), num_tokens,
+                                                         num_kv_heads, head_dim, block_size,
+                                                         num_blocks, _addr(k_scales),
+                                                         _addr(v_scales), _stream(stream)),
+                  "fp8kv_cache_write_rotated_per_head")
+
+
+def fp8kv_paged_decode_rotated_per_head(out, out_dtype, query, key_cache, value_cache, cache_dtype,
+                                        block_tables, max_blocks_per_seq, context_lens,
+                                        max_context_len, num_seqs, num_q_heads, num_kv_heads,
+                                        head_dim, block_size, num_blocks, k_scales, v_scales,
+                                        sliding_window, num_splits, workspace, workspace_bytes,
+                                        stream=None) -> int:
+    return _check(lib.fp8kv_paged_decode_rotated_per_head(
+        _addr(out), out_dtype, _addr(query), _addr(key_cache), _addr(value_cache), cache_dtype,
+        _addr(block_tables), max_blocks_per_seq, _addr(context_lens), max_context_len, num_seqs,
+        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, _addr(k_scales),
+        _addr(v_scales), sliding_window, num_splits, _addr(workspace), workspace_bytes,
+        _stream(stream)), "fp8kv_paged_decode_rotated_per_head")
+
+
+def fp8kv_decode_step_rotated_per_head(out, out_dtype, query, key_new, value_new, key_cache,
+                                       value_cache, cache_dtype, block_tables, max_blocks_per_seq,
+                                       context_lens, max_context_len, num_seqs, num_q_heads,
+                                       num_kv_heads, head_dim, block_size, num_blocks, k_scales,
+                                       v_scales, sliding_window, num_splits, counters,
+                                       counters_bytes, workspace, workspace_bytes,
+                                       stream=None) -> int:
+    return _check(lib.fp8kv_decode_step_rotated_per_head(
+        _addr(out), out_dtype, _addr(query), _addr(key_new), _addr(value_new), _addr(key_cache),
+        _addr(value_cache), cache_dtype, _addr(block_tables), max_blocks_per_seq,
+        _addr(context_lens), max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+        block_size, num_blocks, _addr(k_scales), _addr(v_scales), sliding_window, num_splits,
+        _addr(counters), counters_bytes, _addr(workspace), workspace_bytes, _stream(stream)),
+        "fp8kv_decode_step_rotated_per_head")

@@ -722,15 +722,22 @@ int fp8kv_paged_prefill_per_head(void* out, int out_dtype, const void* query,
                               true, sliding_window, stream);
 }
 
-int fp8kv_cache_write_rotated(const void* key, const void* value, void* key_cache,
-                              void* value_cache, int cache_dtype, const int64_t* slot_mapping,
-                              int num_tokens, int num_kv_heads, int head_dim, int block_size,
-                              int num_blocks, float k_scale, float v_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int rotated_write_impl(const void* key, const void* value, void* key_cache, void* value_cache,
+                       int cache_dtype, const int64_t* slot_mapping, int num_tokens,
+                       int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                       const Scales& sc, bool per_head_call, void* stream) {
     if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return FP8KV_ERR_SHAPE;
     if (!head_dim_ok(head_dim) || block_size != kBlockSize) return FP8KV_ERR_UNSUPPORTED;
     if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
-    const bool fp8 = cache_dtype != FP8KV_BF16;   // one-byte codes (E4M3, E5M2, INT8)
-    if (fp8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return FP8KV_ERR_SCALE;
+    const bool fp8 = cache_dtype != FP8KV_BF16;   // one-byte codes (E4M3)
+    if (fp8) {
+        const int st = check_scales(sc, per_head_call);
+        if (st != FP8KV_OK) return st;
+    }
     if (num_tokens == 0) return FP8KV_OK;
     if (!key || !value || !key_cache || !value_cache || !slot_mapping) return FP8KV_ERR_NULL;
     if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
@@ -744,10 +751,37 @@ int fp8kv_cache_write_rotated(const void* key, const void* value, void* key_cach
     p.num_tokens = num_tokens;
     p.num_kv_heads = num_kv_heads;
     p.num_blocks = num_blocks;
-    p.k_scale = fp8 ? k_scale : 1.0f;
-    p.v_scale = fp8 ? v_scale : 1.0f;
+    const bool heads = fp8 && per_head_call;
+    p.k_scale = fp8 && !heads ? sc.k : 1.0f;
+    p.v_scale = fp8 && !heads ? sc.v : 1.0f;
+    p.k_scales = heads ? sc.ks : nullptr;
+    p.v_scales = heads ? sc.vs : nullptr;
     p.err = g_error_word;
     return hip_status(fp8kv::launch_rotate_write(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8kv_cache_write_rotated(const void* key, const void* value, void* key_cache,
+                              void* value_cache, int cache_dtype, const int64_t* slot_mapping,
+                              int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, float k_scale, float v_scale, void* stream) {
+    return rotated_write_impl(key, value, key_cache, value_cache, cache_dtype, slot_mapping,
+                              num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                              tensor_scales(k_scale, v_scale), false, stream);
+}
+
+int fp8kv_cache_write_rotated_per_head(const void* key, const void* value, void* key_cache,
+                                       void* value_cache, int cache_dtype,
+                                       const int64_t* slot_mapping, int num_tokens,
+                                       int num_kv_heads, int head_dim, int block_size,
+                                       int num_blocks, const float* k_scales,
+                                       const float* v_scales, void* stream) {
+    return rotated_write_impl(key, value, key_cache, value_cache, cache_dtype, slot_mapping,
+                              num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                              head_scales(k_scales, v_scales), true, stream);
 }
 
 size_t fp8kv_paged_decode_rotated_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
@@ -761,14 +795,17 @@ size_t fp8kv_paged_decode_rotated_workspace_size(int num_seqs, int num_q_heads, 
     return rotated_layout(dec, num_seqs, num_q_heads, head_dim).total;
 }
 
-int fp8kv_paged_decode_rotated(void* out, int out_dtype, const void* query, const void* key_cache,
-                               const void* value_cache, int cache_dtype,
-                               const int32_t* block_tables, int max_blocks_per_seq,
-                               const int32_t* context_lens, int max_context_len, int num_seqs,
-                               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                               int num_blocks, float k_scale, float v_scale, int sliding_window,
-                               int num_splits, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+}  // extern "C"
+
+namespace {
+
+int rotated_decode_impl(void* out, int out_dtype, const void* query, const void* key_cache,
+                        const void* value_cache, int cache_dtype, const int32_t* block_tables,
+                        int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                        int block_size, int num_blocks, const Scales& sc, bool per_head_call,
+                        int sliding_window, int num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream) {
     if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
     // the rotated path is defined for the E4M3 and BF16 caches
     if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
@@ -783,8 +820,8 @@ int fp8kv_paged_decode_rotated(void* out, int out_dtype, const void* query, cons
     // the decode's part of the workspace is checked by setup_decode; the rotation buffers here
     st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
-                      num_kv_heads, head_dim, block_size, num_blocks, tensor_scales(k_scale, v_scale),
-                      false, sliding_window, num_splits, workspace,
+                      num_kv_heads, head_dim, block_size, num_blocks, sc, per_head_call,
+                      sliding_window, num_splits, workspace,
                       workspace_bytes < dec ? workspace_bytes : dec, false);
     if (st != FP8KV_OK) return st;
     if (num_seqs == 0) return FP8KV_OK;
@@ -814,14 +851,14 @@ int fp8kv_paged_decode_rotated(void* out, int out_dtype, const void* query, cons
     return hip_status(fp8kv::launch_rotate_out(out_rot, out, out_dtype == FP8KV_F32, rows, head_dim, s));
 }
 
-int fp8kv_decode_step_rotated(void* out, int out_dtype, const void* query, const void* key_new,
-                              const void* value_new, void* key_cache, void* value_cache,
-                              int cache_dtype, const int32_t* block_tables, int max_blocks_per_seq,
-                              const int32_t* context_lens, int max_context_len, int num_seqs,
-                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                              int num_blocks, float k_scale, float v_scale, int sliding_window,
-                              int num_splits, void* counters, size_t counters_bytes,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+int rotated_step_impl(void* out, int out_dtype, const void* query, const void* key_new,
+                      const void* value_new, void* key_cache, void* value_cache, int cache_dtype,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int max_context_len, int num_seqs,
+                      int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, const Scales& sc, bool per_head_call, int sliding_window,
+                      int num_splits, void* counters, size_t counters_bytes, void* workspace,
+                      size_t workspace_bytes, void* stream) {
     if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
     // the rotated path is defined for the E4M3 and BF16 caches
     if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
@@ -835,8 +872,8 @@ int fp8kv_decode_step_rotated(void* out, int out_dtype, const void* query, const
     bool fp8 = true;
     st = setup_decode(p, fp8, query, key_cache, value_cache, cache_dtype, block_tables,
                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
-                      num_kv_heads, head_dim, block_size, num_blocks, tensor_scales(k_scale, v_scale),
-                      false, sliding_window, num_splits, workspace,
+                      num_kv_heads, head_dim, block_size, num_blocks, sc, per_head_call,
+                      sliding_window, num_splits, workspace,
                       workspace_bytes < dec ? workspace_bytes : dec, false);
     if (st != FP8KV_OK) return st;
     if (num_seqs == 0) return FP8KV_OK;
@@ -854,8 +891,8 @@ int fp8kv_decode_step_rotated(void* out, int out_dtype, const void* query, const
     p.out_f32 = one_launch ? (out_dtype == FP8KV_F32) : 1;
     p.k_new = static_cast<const uint16_t*>(key_new);
     p.v_new = static_cast<const uint16_t*>(value_new);
-    p.k_scale_q = fp8 ? k_scale : 1.0f;
-    p.v_scale_q = fp8 ? v_scale : 1.0f;
+    p.k_scale_q = fp8 && !per_head_call ? sc.k : 1.0f;
+    p.v_scale_q = fp8 && !per_head_call ? sc.v : 1.0f;
     p.rot_scale = (float)(1.0 / sqrt((double)head_dim));
     const hipStream_t s = static_cast<hipStream_t>(stream);
     st = hip_status(fp8kv::launch_decode_partial_rotated(p, codec_of(cache_dtype), head_dim, s));
@@ -864,6 +901,76 @@ int fp8kv_decode_step_rotated(void* out, int out_dtype, const void* query, const
     if (st != FP8KV_OK) return st;
     return hip_status(fp8kv::launch_rotate_out(out_rot, out, out_dtype == FP8KV_F32,
                                                (int64_t)num_seqs * num_q_heads, head_dim, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8kv_paged_decode_rotated(void* out, int out_dtype, const void* query, const void* key_cache,
+                               const void* value_cache, int cache_dtype,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int max_context_len, int num_seqs,
+                               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, float k_scale, float v_scale, int sliding_window,
+                               int num_splits, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return rotated_decode_impl(out, out_dtype, query, key_cache, value_cache, cache_dtype,
+                               block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, tensor_scales(k_scale, v_scale), false, sliding_window,
+                               num_splits, workspace, workspace_bytes, stream);
+}
+
+int fp8kv_paged_decode_rotated_per_head(void* out, int out_dtype, const void* query,
+                                        const void* key_cache, const void* value_cache,
+                                        int cache_dtype, const int32_t* block_tables,
+                                        int max_blocks_per_seq, const int32_t* context_lens,
+                                        int max_context_len, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, const float* k_scales,
+                                        const float* v_scales, int sliding_window, int num_splits,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    return rotated_decode_impl(out, out_dtype, query, key_cache, value_cache, cache_dtype,
+                               block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, head_scales(k_scales, v_scales), true, sliding_window,
+                               num_splits, workspace, workspace_bytes, stream);
+}
+
+int fp8kv_decode_step_rotated(void* out, int out_dtype, const void* query, const void* key_new,
+                              const void* value_new, void* key_cache, void* value_cache,
+                              int cache_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* context_lens, int max_context_len, int num_seqs,
+                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, float k_scale, float v_scale, int sliding_window,
+                              int num_splits, void* counters, size_t counters_bytes,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return rotated_step_impl(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
+                             cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                             max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                             block_size, num_blocks, tensor_scales(k_scale, v_scale), false,
+                             sliding_window, num_splits, counters, counters_bytes, workspace,
+                             workspace_bytes, stream);
+}
+
+int fp8kv_decode_step_rotated_per_head(void* out, int out_dtype, const void* query,
+                                       const void* key_new, const void* value_new,
+                                       void* key_cache, void* value_cache, int cache_dtype,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, int max_context_len,
+                                       int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks,
+                                       const float* k_scales, const float* v_scales,
+                                       int sliding_window, int num_splits, void* counters,
+                                       size_t counters_bytes, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    return rotated_step_impl(out, out_dtype, query, key_new, value_new, key_cache, value_cache,
+                             cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                             max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                             block_size, num_blocks, head_scales(k_scales, v_scales), true,
+                             sliding_window, num_splits, counters, counters_bytes, workspace,
+                             workspace_bytes, stream);
 }
 
 }  // extern "C"

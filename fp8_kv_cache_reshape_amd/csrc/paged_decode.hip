@@ -727,8 +727,9 @@ void decode_partial_kernel(DecodeParams p) {
                          + ((int64_t)tok_blk * p.num_kv_heads + h) * TILE_BYTES;
             if constexpr (ROT) {
                 if constexpr (FP8) {
-                    // IEEE f32 division by the scale, then the cast
-                    const float sc = val ? p.v_scale_q : p.k_scale_q;
+                    // IEEE f32 division by the head's scale, then the cast
+                    const float sc = val ? head_scale(p.v_scales, h, p.v_scale_q)
+                                         : head_scale(p.k_scales, h, p.k_scale_q);
                     uint32_t cw[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) cw[j] = pack2<C>(rv[2 * j] / sc, rv[2 * j + 1] / sc);

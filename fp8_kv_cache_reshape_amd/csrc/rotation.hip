@@ -46,10 +46,14 @@ __global__ __launch_bounds__(256) void rotate_write_kernel(CacheWriteParams p, f
         uint8_t* kc = static_cast<uint8_t*>(p.key_cache);
         uint8_t* vc = static_cast<uint8_t*>(p.value_cache);
         uint32_t ck[4], cv[4];
+        // the head's scales (per-kv-head arrays when given, else the per-tensor pair); h
+        // differs between the rows of a wave, so these are vector loads
+        const float ksc = p.k_scales != nullptr ? p.k_scales[h] : p.k_scale;
+        const float vsc = p.v_scales != nullptr ? p.v_scales[h] : p.v_scale;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {   // IEEE f32 division by the scale, then the cast
-            ck[j] = pack2<C>(k[2 * j] / p.k_scale, k[2 * j + 1] / p.k_scale);
-            cv[j] = pack2<C>(v[2 * j] / p.v_scale, v[2 * j + 1] / p.v_scale);
+            ck[j] = pack2<C>(k[2 * j] / ksc, k[2 * j + 1] / ksc);
+            cv[j] = pack2<C>(v[2 * j] / vsc, v[2 * j + 1] / vsc);
         }
         *reinterpret_cast<uint2*>(kc + tile + key_chunk_offset<D, 1>(off, c * 8)) =
             make_uint2(ck[0] | (ck[1] << 16), ck[2] | (ck[3] << 16));

@@ -583,6 +583,47 @@ int fp8kv_decode_step_rotated(void* out, int out_dtype, const void* query,
                               void* counters, size_t counters_bytes,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Per-kv-head scales on the rotated path (page "FP8 KV Cache Quantization: Capacity Gains
+ * and Accuracy Risk", "Scales and calibration", combined with the rotation above):
+ * fp8kv_cache_write_rotated_per_head, fp8kv_paged_decode_rotated_per_head and
+ * fp8kv_decode_step_rotated_per_head are the three rotated calls with k_scales / v_scales
+ * as for fp8kv_cache_write_per_head (device float32 [num_kv_heads] each, 4-byte aligned,
+ * caller-owned; null: FP8KV_ERR_NULL; read by the kernels, not validated on the host): kv
+ * head h's rotated rows are divided by k_scales[h] / v_scales[h] before the cast, and its
+ * codes are dequantised with the same two scales.  Calibrate them on the rotated rows of
+ * each head.  Everything else as for the per-tensor calls.
+ */
+int fp8kv_cache_write_rotated_per_head(const void* key, const void* value,
+                                       void* key_cache, void* value_cache, int cache_dtype,
+                                       const int64_t* slot_mapping, int num_tokens,
+                                       int num_kv_heads, int head_dim, int block_size,
+                                       int num_blocks, const float* k_scales,
+                                       const float* v_scales, void* stream);
+
+int fp8kv_paged_decode_rotated_per_head(void* out, int out_dtype, const void* query,
+                                        const void* key_cache, const void* value_cache,
+                                        int cache_dtype, const int32_t* block_tables,
+                                        int max_blocks_per_seq, const int32_t* context_lens,
+                                        int max_context_len, int num_seqs, int num_q_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, const float* k_scales,
+                                        const float* v_scales, int sliding_window,
+                                        int num_splits, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+int fp8kv_decode_step_rotated_per_head(void* out, int out_dtype, const void* query,
+                                       const void* key_new, const void* value_new,
+                                       void* key_cache, void* value_cache, int cache_dtype,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, int max_context_len,
+                                       int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks,
+                                       const float* k_scales, const float* v_scales,
+                                       int sliding_window, int num_splits, void* counters,
+                                       size_t counters_bytes, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

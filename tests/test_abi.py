@@ -289,3 +289,44 @@ def test_split_passes_per_head_reject():
     assert m(*bad) == F.FP8KV_ERR_WORKSPACE
     bad = list(margs); bad[0] = 0
     assert m(*bad) == F.FP8KV_ERR_NULL
+
+
+def _rot_ph(kind, **kw):
+    """The per-head rotated calls with plausible arguments (fake device addresses)."""
+    if kind == "write":
+        a = dict(key=FAKE, value=FAKE, key_cache=FAKE, value_cache=FAKE, cache_dtype=F.FP8KV_E4M3,
+                 slot_mapping=FAKE, num_tokens=4, num_kv_heads=8, head_dim=128, block_size=16,
+                 num_blocks=10, k_scales=FAKE, v_scales=FAKE, stream=0)
+        a.update(kw)
+        return F.lib.fp8kv_cache_write_rotated_per_head(*a.values())
+    a = dict(out=FAKE, out_dtype=F.FP8KV_BF16, query=FAKE, key_new=FAKE, value_new=FAKE,
+             key_cache=FAKE, value_cache=FAKE, cache_dtype=F.FP8KV_E4M3, block_tables=FAKE,
+             max_blocks_per_seq=64, context_lens=FAKE, max_context_len=1024, num_seqs=2,
+             num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=200,
+             k_scales=FAKE, v_scales=FAKE, sliding_window=0, num_splits=4, counters=FAKE,
+             counters_bytes=1 << 20, workspace=FAKE, workspace_bytes=0, stream=0)
+    a.update(kw)
+    if kind == "step":
+        return F.lib.fp8kv_decode_step_rotated_per_head(*a.values())
+    for k in ("key_new", "value_new", "counters", "counters_bytes"):
+        del a[k]
+    return F.lib.fp8kv_paged_decode_rotated_per_head(*a.values())
+
+
+@pytest.mark.parametrize("kind", ["write", "decode", "step"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_scales=0), F.FP8KV_ERR_NULL), (dict(v_scales=0), F.FP8KV_ERR_NULL),
+    (dict(k_scales=FAKE + 2), F.FP8KV_ERR_SHAPE), (dict(v_scales=FAKE + 1), F.FP8KV_ERR_SHAPE),
+    (dict(cache_dtype=F.FP8KV_E5M2), F.FP8KV_ERR_UNSUPPORTED),
+    (dict(head_dim=96), F.FP8KV_ERR_UNSUPPORTED),
+])
+def test_rotated_per_head_rejects(kind, kw, status):
+    assert _rot_ph(kind, **kw) == status
+
+
+def test_rotated_per_head_bf16_ignores_scale_arrays():
+    assert _rot_ph("write", cache_dtype=F.FP8KV_BF16, k_scales=0, v_scales=0, num_tokens=0) == F.FP8KV_OK
+    for kind in ("decode", "step"):
+        assert _rot_ph(kind, cache_dtype=F.FP8KV_BF16, k_scales=0, v_scales=0, workspace=0) == \
+            F.FP8KV_ERR_WORKSPACE
+        assert _rot_ph(kind, num_seqs=0, query=0, out=0, workspace=0) == F.FP8KV_OK

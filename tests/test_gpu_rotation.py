@@ -189,3 +189,102 @@ def test_rotated_step_fixed_splits_reproducible():
     a = _check_step(w, L, ks, vs, out_f32=True, num_splits=7)
     b = _check_step(w, L, ks, vs, out_f32=True, num_splits=7)
     assert np.array_equal(a, b)
+
+
+# ---- per-kv-head scales on the rotated path
+
+def _head_scales(w, L):
+    """Per-kv-head amax / 448 scales of the rotated rows (float32 [Hkv] each)."""
+    rk = oracle.hadamard_f32(syn.bf16_bits_to_f32(L.k)).reshape(w.num_tokens, w.num_kv_heads, -1)
+    rv = oracle.hadamard_f32(syn.bf16_bits_to_f32(L.v)).reshape(w.num_tokens, w.num_kv_heads, -1)
+    ks = (np.abs(rk).max(axis=(0, 2)).astype(np.float32) / np.float32(448.0)).astype(np.float32)
+    vs = (np.abs(rv).max(axis=(0, 2)).astype(np.float32) / np.float32(448.0)).astype(np.float32)
+    return ks, vs
+
+
+def _mk_ph(Hq, Hkv, D, lens, cid, window=0):
+    # outliers on some heads only, so the per-head scales differ widely
+    w = syn.make_workload(f"rotph-{Hq}-{Hkv}-{D}-w{window}", cid, num_q_heads=Hq, num_kv_heads=Hkv,
+                          head_dim=D, context_lens=lens, outlier_frac=0.02,
+                          layers=(("l0", window, syn.E4M3),))
+    L = w.layers[0]
+    ks, vs = _head_scales(w, L)
+    return w, L, ks, vs
+
+
+def _write_ph_both(w, L, ks, vs, rows=None):
+    kc, vc = dev_caches(w, E4M3)
+    rows = np.arange(w.num_tokens) if rows is None else rows
+    slots = torch.from_numpy(np.ascontiguousarray(w.slot_mapping[rows])).to(DEV)
+    kd, vd = u16_dev(L.k[rows]), u16_dev(L.v[rows])
+    ksd, vsd = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+    F.fp8kv_cache_write_rotated_per_head(kd, vd, kc, vc, E4M3, slots, len(rows), w.num_kv_heads,
+                                         w.head_dim, 16, w.num_blocks, ksd, vsd)
+    torch.cuda.synchronize()
+    okc, ovc = host_caches(w, E4M3)
+    oracle.cache_write_rotated_per_head(L.k, L.v, okc, ovc, E4M3, w.slot_mapping, w.num_kv_heads,
+                                        w.head_dim, 16, w.num_blocks, ks, vs)
+    return kc, vc, okc, ovc, ksd, vsd
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rotated_per_head_write_bit_exact(D):
+    w, L, ks, vs = _mk_ph(4 * 4, 4, D, [37, 300, 1027, 16], cid=230 + D)
+    assert len(set(ks.tolist())) > 1
+    say(f"cache_write_rotated_per_head {w.name} k_scales={ks.tolist()}")
+    kc, vc, okc, ovc, _, _ = _write_ph_both(w, L, ks, vs)
+    assert np.array_equal(to_host_bits(kc), okc), "key cache bytes differ"
+    assert np.array_equal(to_host_bits(vc), ovc), "value cache bytes differ"
+
+
+def _ref_ph(w, L, ks, vs, okc, ovc):
+    return oracle.paged_decode_rotated_per_head(w.q, okc, ovc, E4M3, w.block_tables, w.context_lens,
+                                                w.num_q_heads, w.num_kv_heads, w.head_dim, 16, ks, vs,
+                                                L.sliding_window)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (64, 8, 64), (16, 2, 256)])
+def test_rotated_per_head_decode_matches_oracle(Hq, Hkv, D):
+    w, L, ks, vs = _mk_ph(Hq, Hkv, D, [1, 17, 300, 1027, 0], cid=240 + D)
+    say(f"paged_decode_rotated_per_head {w.name}")
+    kc, vc, okc, ovc, ksd, vsd = _write_ph_both(w, L, ks, vs)
+    dev = DeviceInputs(w)
+    B = w.num_seqs
+    nbytes = F.fp8kv_paged_decode_rotated_workspace_size(B, Hq, Hkv, D, 16, w.max_context_len, 0, 0)
+    ws = torch.full((max(nbytes, 256),), 0xFF, dtype=torch.uint8, device=DEV)
+    out = torch.empty(B * Hq * D, dtype=torch.bfloat16, device=DEV)
+    F.fp8kv_paged_decode_rotated_per_head(out, F.FP8KV_BF16, dev.q, kc, vc, E4M3, dev.bt,
+                                          w.max_blocks_per_seq, dev.cl, w.max_context_len, B, Hq, Hkv,
+                                          D, 16, w.num_blocks, ksd, vsd, 0, 0, ws, ws.numel())
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64).reshape(B, Hq, D)
+    assert_close(got, _ref_ph(w, L, ks, vs, okc, ovc), what=w.name)
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 129])
+def test_rotated_per_head_step_matches_oracle(num_splits):
+    w, L, ks, vs = _mk_ph(32, 8, 128, [5, 700, 2049, 16], cid=250)
+    say(f"decode_step_rotated_per_head splits={num_splits}")
+    kc, vc, _, _, ksd, vsd = _write_ph_both(w, L, ks, vs, rows=w.prefix_token_rows())
+    dev = DeviceInputs(w)
+    B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+    cnt = new_counters(B, Hkv)
+    nbytes = F.fp8kv_paged_decode_rotated_workspace_size(B, Hq, Hkv, D, 16, w.max_context_len, 0,
+                                                        num_splits)
+    ws = torch.full((max(nbytes, 256),), 0xFF, dtype=torch.uint8, device=DEV)
+    kn, vn = step_rows_by_seq(w, L)
+    kd, vd = u16_dev(kn), u16_dev(vn)
+    out = torch.empty(B * Hq * D, dtype=torch.float32, device=DEV)
+    F.fp8kv_decode_step_rotated_per_head(out, F.FP8KV_F32, dev.q, kd, vd, kc, vc, E4M3, dev.bt,
+                                         w.max_blocks_per_seq, dev.cl, w.max_context_len, B, Hq, Hkv,
+                                         D, 16, w.num_blocks, ksd, vsd, 0, num_splits, cnt,
+                                         cnt.numel(), ws, ws.numel())
+    torch.cuda.synchronize()
+    okc, ovc = host_caches(w, E4M3)
+    oracle.cache_write_rotated_per_head(L.k, L.v, okc, ovc, E4M3, w.slot_mapping, w.num_kv_heads,
+                                        w.head_dim, 16, w.num_blocks, ks, vs)
+    assert np.array_equal(to_host_bits(kc), okc), "key cache bytes differ after the step"
+    assert np.array_equal(to_host_bits(vc), ovc), "value cache bytes differ after the step"
+    got = out.cpu().numpy().astype(np.float64).reshape(B, Hq, D)
+    assert_close(got, _ref_ph(w, L, ks, vs, okc, ovc), atol=2e-4, rtol=2e-3, what=w.name)
+    assert not cnt.cpu().numpy().any(), "counters were not returned to zero"
