@@ -78,6 +78,8 @@ def _bind(path: str) -> ctypes.CDLL:
                                                i32, P, P, i32],
         "oracle_paged_prefill_pairs": [P, P, i32, P, P, i32, P, P, i32, P, i32, P, i32, i32, i32,
                                        i32, f64, f64, i32],
+        "oracle_paged_prefill_rotated_pairs": [P, P, i32, P, P, i32, P, P, i32, P, i32, P, i32, i32,
+                                               i32, i32, f64, f64, i32],
         "oracle_hadamard_f32": [P, i32],
         "oracle_e5m2_decode_n": [P, P, i64],
         "oracle_e5m2_encode_n": [P, P, i64],
@@ -294,6 +296,42 @@ def paged_prefill_pairs(pairs, q, query_start_loc, key_cache, value_cache, cache
                                      block_size, float(k_scale), float(v_scale),
                                      int(sliding_window))
     return out
+
+
+def paged_prefill_rotated_pairs(pairs, q, query_start_loc, key_cache, value_cache,
+                                cache_dtype: int, block_tables, context_lens, num_q_heads: int,
+                                num_kv_heads: int, head_dim: int, block_size: int, k_scale: float,
+                                v_scale: float, sliding_window: int = 0) -> np.ndarray:
+    """paged_prefill_pairs over a rotated cache: each query row rotated, attention in the
+    rotated space, each output row rotated back (fp64): [n][D]."""
+    q, bt, cl = _decode_common(q, key_cache, value_cache, cache_dtype, block_tables, context_lens)
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    B = cl.shape[0]
+    assert qsl.shape == (B + 1,) and qsl[0] == 0 and np.all(np.diff(qsl) >= 0)
+    assert q.shape[0] == qsl[-1] and head_dim & (head_dim - 1) == 0
+    pr = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    assert np.all((pr[:, 0] >= 0) & (pr[:, 0] < qsl[-1]))
+    out = np.empty((pr.shape[0], head_dim), dtype=np.float64)
+    lib().oracle_paged_prefill_rotated_pairs(_ptr(out), _ptr(pr), pr.shape[0], _ptr(q), _ptr(qsl), B,
+                                             _ptr(key_cache), _ptr(value_cache), cache_dtype,
+                                             _ptr(bt), bt.shape[1], _ptr(cl), num_q_heads,
+                                             num_kv_heads, head_dim, block_size, float(k_scale),
+                                             float(v_scale), int(sliding_window))
+    return out
+
+
+def paged_prefill_rotated(q, query_start_loc, key_cache, value_cache, cache_dtype: int,
+                          block_tables, context_lens, num_q_heads: int, num_kv_heads: int,
+                          head_dim: int, block_size: int, k_scale: float, v_scale: float,
+                          sliding_window: int = 0) -> np.ndarray:
+    """Every (query row, query head) over a rotated cache: [Tq][Hq][D]."""
+    Tq = int(np.asarray(query_start_loc)[-1])
+    pairs = np.array([(r, hq) for r in range(Tq) for hq in range(num_q_heads)], np.int32)
+    out = paged_prefill_rotated_pairs(pairs, q, query_start_loc, key_cache, value_cache,
+                                      cache_dtype, block_tables, context_lens, num_q_heads,
+                                      num_kv_heads, head_dim, block_size, k_scale, v_scale,
+                                      sliding_window)
+    return out.reshape(Tq, num_q_heads, head_dim)
 
 
 def paged_prefill(q, query_start_loc, key_cache, value_cache, cache_dtype: int, block_tables,

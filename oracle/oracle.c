@@ -486,12 +486,18 @@ void oracle_paged_decode_pairs_per_head(double* out, const int32_t* pairs, int n
  *   q      bf16 [Tq][Hq][D]
  *   pairs  int32 [n][2]: (query row, query head) to compute;  out double [n][D]
  */
-void oracle_paged_prefill_pairs(double* out, const int32_t* pairs, int npairs,
-                                const uint16_t* q, const int32_t* qsl, int B,
-                                const void* key_cache, const void* value_cache,
-                                int cache_dtype, const int32_t* block_tables, int max_blocks,
-                                const int32_t* context_lens, int Hq, int Hkv, int D, int bs,
-                                double k_scale, double v_scale, int window) {
+void oracle_hadamard_f64(double* x, int d);
+
+/* rotate != 0: the rotated-cache form (page "KV Cache Quantization: What FP8 and q8_0 Cost
+ * in Accuracy", paragraph on the llama.cpp rotation): each query row is rotated (fp64)
+ * before the attention and each output row rotated back, as oracle_paged_decode_rotated_pairs
+ * does for one decode token. */
+static void prefill_pairs_core(double* out, const int32_t* pairs, int npairs,
+                               const uint16_t* q, const int32_t* qsl, int B,
+                               const void* key_cache, const void* value_cache,
+                               int cache_dtype, const int32_t* block_tables, int max_blocks,
+                               const int32_t* context_lens, int Hq, int Hkv, int D, int bs,
+                               double k_scale, double v_scale, int window, int rotate) {
     int group = Hq / Hkv;
     int eb = cache_dtype == ORACLE_CACHE_BF16 ? 2 : 1;
     for (int p = 0; p < npairs; ++p) {
@@ -510,6 +516,7 @@ void oracle_paged_prefill_pairs(double* out, const int32_t* pairs, int npairs,
         double* V = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
         for (int i = 0; i < D; ++i)
             qv[i] = (double)oracle_bf16_to_f32(q[(row * Hq + hq) * D + i]);
+        if (rotate) oracle_hadamard_f64(qv, D);
         for (int64_t j = start; j < end; ++j) {
             int64_t phys = block_tables[(int64_t)b * max_blocks + j / bs];
             int slot = (int)(j % bs);
@@ -523,10 +530,35 @@ void oracle_paged_prefill_pairs(double* out, const int32_t* pairs, int npairs,
             }
         }
         oracle_attention_rows(out + (int64_t)p * D, qv, K, V, n, D);
+        if (rotate) oracle_hadamard_f64(out + (int64_t)p * D, D);   /* back to the original coordinates */
         free(qv);
         free(K);
         free(V);
     }
+}
+
+void oracle_paged_prefill_pairs(double* out, const int32_t* pairs, int npairs,
+                                const uint16_t* q, const int32_t* qsl, int B,
+                                const void* key_cache, const void* value_cache,
+                                int cache_dtype, const int32_t* block_tables, int max_blocks,
+                                const int32_t* context_lens, int Hq, int Hkv, int D, int bs,
+                                double k_scale, double v_scale, int window) {
+    prefill_pairs_core(out, pairs, npairs, q, qsl, B, key_cache, value_cache, cache_dtype,
+                       block_tables, max_blocks, context_lens, Hq, Hkv, D, bs, k_scale, v_scale,
+                       window, 0);
+}
+
+/* Prefill over a rotated cache (fp8kv-style rotated rows, per-tensor scales). */
+void oracle_paged_prefill_rotated_pairs(double* out, const int32_t* pairs, int npairs,
+                                        const uint16_t* q, const int32_t* qsl, int B,
+                                        const void* key_cache, const void* value_cache,
+                                        int cache_dtype, const int32_t* block_tables,
+                                        int max_blocks, const int32_t* context_lens, int Hq,
+                                        int Hkv, int D, int bs, double k_scale, double v_scale,
+                                        int window) {
+    prefill_pairs_core(out, pairs, npairs, q, qsl, B, key_cache, value_cache, cache_dtype,
+                       block_tables, max_blocks, context_lens, Hq, Hkv, D, bs, k_scale, v_scale,
+                       window, 1);
 }
 
 /* --------------------------------------------------- Hadamard rotation --- */

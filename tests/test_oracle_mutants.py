@@ -88,6 +88,9 @@ MUTANTS = {
         "quantize_f32(rv[i], k_scales ? k_scales[h] : v_scale)"),
     "rotated_per_head_decode_interleaved_heads": ("int kvh = pairs[2 * p + 1] / group;",
                                                   "int kvh = pairs[2 * p + 1] % Hkv;"),
+    "rotated_prefill_query_not_rotated": ("if (rotate) oracle_hadamard_f64(qv, D);", "(void)rotate;"),
+    "rotated_prefill_output_not_rotated_back": (
+        "if (rotate) oracle_hadamard_f64(out + (int64_t)p * D, D);", "(void)rotate;"),
     "e5m2_exponent_bias": ("mag = ldexp(1.0 + (double)M / 4.0, E - 15);",
                            "mag = ldexp(1.0 + (double)M / 4.0, E - 16);"),
     "e5m2_subnormal_step": ("mag = ldexp((double)M, -16);", "mag = ldexp((double)M, -15);"),

@@ -187,3 +187,47 @@ def test_rotated_per_head_decode_equals_plain_decode_when_the_codes_are_exact():
                                                w.context_lens, w.num_q_heads, w.num_kv_heads,
                                                w.head_dim, 16, ks[::-1].copy(), vs[::-1].copy(), 0)
     assert np.abs(bad - ref0).max() > 1e-3
+
+
+# ---- prefill over a rotated cache
+
+def test_rotated_prefill_equals_plain_prefill_when_the_rotation_is_exact():
+    """bf16 cache holding r = H x exactly: every chunk row's rotated prefill, rotated back,
+    is the plain prefill over x (up to fp64 rounding), with and without a window."""
+    w, xk, xv, rk, rv = _exact_workload(syn.BF16, cid=99)
+    rot_k, rot_v = _caches(w, BF16)
+    oracle.cache_write_rotated(xk, xv, rot_k, rot_v, BF16, w.slot_mapping, w.num_kv_heads,
+                               w.head_dim, 16, w.num_blocks, 1.0, 1.0)
+    pl_k, pl_v = _caches(w, BF16)
+    oracle.cache_write(xk, xv, pl_k, pl_v, BF16, w.slot_mapping, w.num_kv_heads, w.head_dim, 16,
+                       w.num_blocks, 1.0, 1.0)
+    pq = syn.prefill_queries(w, [9, 40], 99)
+    for window in (0, 10):
+        args = (w.block_tables, w.context_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, 16,
+                1.0, 1.0, window)
+        got = oracle.paged_prefill_rotated(pq.q, pq.query_start_loc, rot_k, rot_v, BF16, *args)
+        ref = oracle.paged_prefill(pq.q, pq.query_start_loc, pl_k, pl_v, BF16, *args)
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_rotated_prefill_last_row_is_the_rotated_decode():
+    """A chunk's last row sits at the context's last position, so its rotated prefill is
+    the rotated decode of that token, bit for bit (the same fp64 steps)."""
+    w = syn.make_workload("rot-pf-dec", 100, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                          context_lens=[70, 300], outlier_frac=0.01)
+    L = w.layers[0]
+    kc, vc = _caches(w, E4M3)
+    oracle.cache_write_rotated(L.k, L.v, kc, vc, E4M3, w.slot_mapping, 2, 128, 16, w.num_blocks,
+                               0.02, 0.03)
+    pq = syn.prefill_queries(w, [5, 12], 100)
+    q = w.q.copy()
+    last = pq.query_start_loc[1:] - 1
+    q[0], q[1] = pq.q[last[0]], pq.q[last[1]]
+    for window in (0, 33):
+        pf = oracle.paged_prefill_rotated_pairs(
+            np.array([(r, hq) for r in last for hq in range(8)], np.int32), pq.q,
+            pq.query_start_loc, kc, vc, E4M3, w.block_tables, w.context_lens, 8, 2, 128, 16, 0.02,
+            0.03, window)
+        dec = oracle.paged_decode_rotated(q, kc, vc, E4M3, w.block_tables, w.context_lens, 8, 2, 128,
+                                          16, 0.02, 0.03, window)
+        assert np.array_equal(pf, dec.reshape(-1, 128))
