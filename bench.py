@@ -488,6 +488,8 @@ def main(argv=None):
     ap.add_argument("--prefill-workload", default="llama8b-8k,d256-8k",
                     help="comma-separated: " + ", ".join(sorted(PREFILL_WORKLOADS)))
     ap.add_argument("--prefill-caches", default="e4m3,bf16", help="cache dtypes to time")
+    ap.add_argument("--prefill-rotated", action="store_true",
+                    help="with --prefill: also time the prefill over rotated caches (head_dim <= 128)")
     ap.add_argument("--codec", choices=["e4m3", "e5m2", "int8"], default="e4m3",
                     help="one-byte cache codec of the timed fp8 layer (default e4m3)")
     ap.add_argument("--rotated", action="store_true",
@@ -737,16 +739,33 @@ def prefill_bench(F, torch, syn, name: str, args) -> dict:
                        f"window {layer.sliding_window}",
            "flops_per_call": flops}
     launches = 20
-    for cache in args.prefill_caches.split(","):
+    # with --prefill-rotated, the e4m3 and bf16 caches are also timed as rotated caches
+    # (fp8kv_cache_write_rotated, then fp8kv_paged_prefill_rotated: query rotation, prefill
+    # with the two-term query, output rotation); head_dim 256 has no rotated prefill
+    kinds = [(c, False) for c in args.prefill_caches.split(",")]
+    if args.prefill_rotated and D <= 128:
+        kinds += [(c, True) for c in args.prefill_caches.split(",")]
+    rws = None
+    for cache, rot in kinds:
         cdt = F.FP8KV_E4M3 if cache == "e4m3" else F.FP8KV_BF16
         dt = torch.uint8 if cache == "e4m3" else torch.int16
         kc, vc = torch.zeros(n, dtype=dt, device=dev), torch.zeros(n, dtype=dt, device=dev)
         ks = layer.k_scale if cache == "e4m3" else 1.0
         vs = layer.v_scale if cache == "e4m3" else 1.0
-        F.fp8kv_cache_write(k_all, v_all, kc, vc, cdt, slots, w.num_tokens, Hkv, D, BLOCK,
-                            w.num_blocks, ks, vs)
+        write = F.fp8kv_cache_write_rotated if rot else F.fp8kv_cache_write
+        write(k_all, v_all, kc, vc, cdt, slots, w.num_tokens, Hkv, D, BLOCK, w.num_blocks, ks, vs)
+        if rot and rws is None:
+            rws_bytes = F.fp8kv_paged_prefill_rotated_workspace_size(pq.num_tokens, Hq, D)
+            rws = torch.empty(rws_bytes, dtype=torch.uint8, device=dev)
 
         def call():
+            if rot:
+                F.fp8kv_paged_prefill_rotated(out, F.FP8KV_BF16, q, qsl, kc, vc, cdt, bt,
+                                              w.max_blocks_per_seq, cl, w.max_context_len,
+                                              w.num_seqs, pq.max_query_len, pq.num_tokens, Hq, Hkv,
+                                              D, BLOCK, w.num_blocks, ks, vs, layer.sliding_window,
+                                              rws, rws.numel())
+                return
             F.fp8kv_paged_prefill(out, F.FP8KV_BF16, q, qsl, kc, vc, cdt, bt, w.max_blocks_per_seq,
                                   cl, w.max_context_len, w.num_seqs, pq.max_query_len, Hq, Hkv, D,
                                   BLOCK, w.num_blocks, ks, vs, layer.sliding_window)
@@ -761,12 +780,15 @@ def prefill_bench(F, torch, syn, name: str, args) -> dict:
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / launches
         tf = flops / (ms * 1e-3) / 1e12
-        res[cache] = {"us_per_call": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
-                      "pct_of_bf16_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2)}
+        res[cache + ("_rotated" if rot else "")] = {
+            "us_per_call": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+            "pct_of_bf16_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2)}
         del kc, vc
         torch.cuda.empty_cache()
     if "e4m3" in res and "bf16" in res:
         res["fp8_over_bf16_time"] = round(res["e4m3"]["us_per_call"] / res["bf16"]["us_per_call"], 4)
+    if "e4m3" in res and "e4m3_rotated" in res:
+        res["rotated_over_plain_time"] = round(res["e4m3_rotated"]["us_per_call"] / res["e4m3"]["us_per_call"], 4)
     if "e4m3" in res:
         res["roofline"] = {"bound": "mfma", "achieved": res["e4m3"]["TFLOPs"],
                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

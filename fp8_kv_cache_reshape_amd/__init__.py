@@ -83,6 +83,9 @@ SIGNATURES = {
                                        _I, _I, _I, _F, _F, _I, _I, _P, _SZ, _P, _SZ, _P]),
     "fp8kv_cache_write_rotated_per_head": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P,
                                                 _P]),
+    "fp8kv_paged_prefill_rotated_workspace_size": (_SZ, [_I, _I, _I]),
+    "fp8kv_paged_prefill_rotated": (_I, [_P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I,
+                                         _I, _I, _I, _I, _F, _F, _I, _P, _SZ, _P]),
     "fp8kv_paged_decode_rotated_per_head": (_I, [_P, _I, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
                                                  _I, _I, _I, _P, _P, _I, _I, _P, _SZ, _P]),
     "fp8kv_decode_step_rotated_per_head": (_I, [_P, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
@@ -452,3 +455,22 @@ def fp8kv_decode_step_rotated_per_head(out, out_dtype, query, key_new, value_new
         block_size, num_blocks, _addr(k_scales), _addr(v_scales), sliding_window, num_splits,
         _addr(counters), counters_bytes, _addr(workspace), workspace_bytes, _stream(stream)),
         "fp8kv_decode_step_rotated_per_head")
+
+
+def fp8kv_paged_prefill_rotated_workspace_size(num_query_tokens, num_q_heads, head_dim) -> int:
+    return int(lib.fp8kv_paged_prefill_rotated_workspace_size(num_query_tokens, num_q_heads, head_dim))
+
+
+def fp8kv_paged_prefill_rotated(out, out_dtype, query, query_start_loc, key_cache, value_cache,
+                                cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                                max_context_len, num_seqs, max_query_len, num_query_tokens,
+                                num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                k_scale, v_scale, sliding_window, workspace, workspace_bytes,
+                                stream=None) -> int:
+    return _check(lib.fp8kv_paged_prefill_rotated(
+        _addr(out), out_dtype, _addr(query), _addr(query_start_loc), _addr(key_cache),
+        _addr(value_cache), cache_dtype, _addr(block_tables), max_blocks_per_seq,
+        _addr(context_lens), max_context_len, num_seqs, max_query_len, num_query_tokens,
+        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, k_scale, v_scale,
+        sliding_window, _addr(workspace), workspace_bytes, _stream(stream)),
+        "fp8kv_paged_prefill_rotated")

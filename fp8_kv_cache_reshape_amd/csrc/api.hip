@@ -1,6 +1,7 @@
 // api.hip -- the extern "C" entry points of libfp8kv (declared in include/fp8kv.h):
 // host-side validation (before any HIP call), split planning, workspace layout, and the
 // kernel launches on the caller's stream.
+#include <limits.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -350,14 +351,46 @@ int decode_step_impl(void* out, int out_dtype, const void* query, const void* ke
     return hip_status(fp8kv::launch_decode_merge(p, head_dim, s));
 }
 
+// Workspace of the rotated prefill: the rotated query's two bf16 terms and the f32 output
+// before it is rotated back, each 256-byte aligned.
+struct PrefillRotLayout {
+    size_t q_hi, q_lo, out, total;
+};
+
+PrefillRotLayout prefill_rot_layout(int64_t rows, int head_dim) {
+    const auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    PrefillRotLayout l;
+    const size_t n = (size_t)rows * head_dim;
+    l.q_hi = 0;
+    l.q_lo = up(n * 2);
+    l.out = l.q_lo + up(n * 2);
+    l.total = l.out + up(n * 4);
+    return l;
+}
+
+// The rotated prefill's extra arguments: the caller's row count and workspace.
+struct PrefillRot {
+    int num_query_tokens;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
 int paged_prefill_impl(void* out, int out_dtype, const void* query,
                        const int32_t* query_start_loc, const void* key_cache,
                        const void* value_cache, int cache_dtype, const int32_t* block_tables,
                        int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
                        int num_seqs, int max_query_len, int num_q_heads, int num_kv_heads,
                        int head_dim, int block_size, int num_blocks, const Scales& sc,
-                       bool per_head_call, int sliding_window, void* stream) {
+                       bool per_head_call, int sliding_window, void* stream,
+                       const PrefillRot* rot = nullptr) {
     if (out_dtype != FP8KV_BF16 && out_dtype != FP8KV_F32) return FP8KV_ERR_UNSUPPORTED;
+    if (rot != nullptr) {
+        // the rotated path is defined for the E4M3 and BF16 caches; its low query term lives
+        // in the two-tile kernel's LDS, which head_dim 256 does not use
+        if (cache_dtype != FP8KV_E4M3 && cache_dtype != FP8KV_BF16) return FP8KV_ERR_UNSUPPORTED;
+        if (head_dim == 256) return FP8KV_ERR_UNSUPPORTED;
+        if (rot->num_query_tokens < 0) return FP8KV_ERR_SHAPE;
+    }
     int st = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_context_len, sliding_window, 0);
     if (st != FP8KV_OK) return st;
@@ -400,7 +433,32 @@ int paged_prefill_impl(void* out, int out_dtype, const void* query,
     p.k_scales = heads ? sc.ks : nullptr;
     p.v_scales = heads ? sc.vs : nullptr;
     p.err = g_error_word;
-    return hip_status(fp8kv::launch_prefill(p, codec_of(cache_dtype), head_dim, static_cast<hipStream_t>(stream)));
+    p.query_lo = nullptr;
+    p.num_rows = INT_MAX;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (rot == nullptr) return hip_status(fp8kv::launch_prefill(p, codec_of(cache_dtype), head_dim, s));
+    // rotated: query rotation into two bf16 terms, the prefill in the rotated space into f32
+    // rows, then the rotation back into `out`
+    if (rot->num_query_tokens == 0) return FP8KV_OK;
+    const int64_t rows = (int64_t)rot->num_query_tokens * num_q_heads;
+    const PrefillRotLayout rl = prefill_rot_layout(rows, head_dim);
+    if (!rot->workspace || rot->workspace_bytes < rl.total) return FP8KV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(rot->workspace) & 255u) != 0) return FP8KV_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(rot->workspace);
+    uint16_t* q_hi = reinterpret_cast<uint16_t*>(ws + rl.q_hi);
+    uint16_t* q_lo = reinterpret_cast<uint16_t*>(ws + rl.q_lo);
+    float* out_rot = reinterpret_cast<float*>(ws + rl.out);
+    int st2 = hip_status(fp8kv::launch_rotate_query(static_cast<const uint16_t*>(query), q_hi, q_lo,
+                                                    rows, head_dim, s));
+    if (st2 != FP8KV_OK) return st2;
+    p.query = q_hi;
+    p.query_lo = q_lo;
+    p.num_rows = rot->num_query_tokens;
+    p.out = out_rot;
+    p.out_f32 = 1;
+    st2 = hip_status(fp8kv::launch_prefill(p, codec_of(cache_dtype), head_dim, s));
+    if (st2 != FP8KV_OK) return st2;
+    return hip_status(fp8kv::launch_rotate_out(out_rot, out, out_dtype == FP8KV_F32, rows, head_dim, s));
 }
 
 int partial_impl(const void* query, const void* key_cache, const void* value_cache,
@@ -720,6 +778,29 @@ int fp8kv_paged_prefill_per_head(void* out, int out_dtype, const void* query,
                               max_context_len, num_seqs, max_query_len, num_q_heads, num_kv_heads,
                               head_dim, block_size, num_blocks, head_scales(k_scales, v_scales),
                               true, sliding_window, stream);
+}
+
+size_t fp8kv_paged_prefill_rotated_workspace_size(int num_query_tokens, int num_q_heads,
+                                                  int head_dim) {
+    if (num_query_tokens < 0 || num_q_heads <= 0 || !head_dim_ok(head_dim)) return 0;
+    return prefill_rot_layout((int64_t)num_query_tokens * num_q_heads, head_dim).total;
+}
+
+int fp8kv_paged_prefill_rotated(void* out, int out_dtype, const void* query,
+                                const int32_t* query_start_loc, const void* key_cache,
+                                const void* value_cache, int cache_dtype,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int max_context_len, int num_seqs,
+                                int max_query_len, int num_query_tokens, int num_q_heads,
+                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                float k_scale, float v_scale, int sliding_window,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    const PrefillRot rot{num_query_tokens, workspace, workspace_bytes};
+    return paged_prefill_impl(out, out_dtype, query, query_start_loc, key_cache, value_cache,
+                              cache_dtype, block_tables, max_blocks_per_seq, context_lens,
+                              max_context_len, num_seqs, max_query_len, num_q_heads, num_kv_heads,
+                              head_dim, block_size, num_blocks, tensor_scales(k_scale, v_scale),
+                              false, sliding_window, stream, &rot);
 }
 
 }  // extern "C"

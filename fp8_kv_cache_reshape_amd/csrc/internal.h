@@ -103,6 +103,11 @@ struct PrefillParams {
     const float* k_scales;         // per-kv-head scales [Hkv] (device), or null
     const float* v_scales;
     unsigned int* err;             // device error word (FP8KV_DEVERR_* bits), or null
+    // prefill over a rotated cache: the rotated query's low bf16 term (query holds the high
+    // one), or null; and the number of query rows the caller's buffers hold (rows at or past
+    // it are neither read nor written; INT_MAX for the plain prefill)
+    const uint16_t* query_lo;
+    int num_rows;
 };
 
 // Bits of the device error word (the public FP8KV_DEVERR_* values).

@@ -135,13 +135,15 @@ __device__ constexpr int lds_value(int ch, int slot, int cb) {
 // registers of two waves per SIMD.
 __host__ __device__ constexpr int col_tiles(int d) { return d <= 128 && FP8KV_PREFILL_TILES >= 2 ? 2 : 1; }
 
-template <int D, int C>
+template <int D, int C, bool QLO = false>
 struct Stage {
     static constexpr int CT = col_tiles(D);
     static constexpr bool WIDE = D == 64 || (D == 128 && C != kCodecBF16);
     // blocks per step (a two-byte cache stages twice the bytes and needs the low P term, so
     // its steps are half as long at two column tiles)
-    static constexpr int NB = CT == 2 ? (D == 64 ? 8 : 4) / (C == kCodecBF16 ? 2 : 1)
+    // (with the low query term the query operands take twice the LDS, so head_dim 128 steps
+    // are 32 keys)
+    static constexpr int NB = CT == 2 ? (QLO && D == 128 ? 2 : (D == 64 ? 8 : 4) / (C == kCodecBF16 ? 2 : 1))
                                       : (D <= 128 ? 4 : 2) * (WIDE ? 2 : 1);
     static constexpr int STEP = NB * kBlockSize;              // keys per step
     static constexpr int ES = C == kCodecBF16 ? 2 : 1;       // source bytes per element
@@ -157,11 +159,12 @@ struct Stage {
     static_assert(PER % 16 == 0 && FLUSH >= 1, "staging geometry");
 };
 
-template <int D, int C>
+// QLO: the rotated prefill, whose query enters S as two bf16 terms (query, query_lo).
+template <int D, int C, bool QLO = false>
 __global__ __launch_bounds__(64 * kWaves)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams p) {
-    using S = Stage<D, C>;
+    using S = Stage<D, C, QLO>;
     constexpr int CT = S::CT;
     constexpr int WCOLS = kCols * CT;      // query columns per wave
     constexpr int NB = S::NB;
@@ -180,7 +183,9 @@ void prefill_kernel(PrefillParams p) {
     // pieces [tile][slice][lane]), read again for every step: registers are what bounds
     // this kernel
     constexpr bool kQLds = CT == 2;
-    __shared__ __attribute__((aligned(16))) uint8_t sm_q[kQLds ? kWaves * CT * NK * 64 * 16 : 16];
+    static_assert(!QLO || kQLds, "the low query term lives in LDS");
+    constexpr int kQTerms = QLO ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) uint8_t sm_q[kQLds ? kWaves * kQTerms * CT * NK * 64 * 16 : 16];
 
     const int lane = threadIdx.x & 63;
     // wave-uniform (a scalar register, so that the staging addresses stay scalar)
@@ -223,7 +228,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int j = 0; j < CT; ++j) {
         const int64_t cg = c0 + kCols * j + col;
-        cvalid[j] = cg < ncols;
+        cvalid[j] = cg < ncols && q0 + (int)(cg / G) < p.num_rows;
         tok[j] = cvalid[j] ? (int)(cg / G) : 0;
         hq[j] = h * G + (cvalid[j] ? (int)(cg % G) : 0);
         pos[j] = L - nq + tok[j];          // < 0: the column attends to nothing
@@ -247,23 +252,31 @@ void prefill_kernel(PrefillParams p) {
     // (one tile) or in this wave's LDS region (two tiles; only this wave reads it back, and a
     // wave's LDS accesses take effect in order, so no barrier is needed)
     bf16x8 qb[kQLds ? 1 : CT][NK];
-    uint8_t* const sq = sm_q + (kQLds ? wave * (CT * NK * 64 * 16) : 0);
+    uint8_t* const sq = sm_q + (kQLds ? wave * (kQTerms * CT * NK * 64 * 16) : 0);
 #pragma unroll
     for (int j = 0; j < CT; ++j) {
-        const uint16_t* qrow = p.query + ((int64_t)(q0 + tok[j]) * p.num_q_heads + hq[j]) * D + grp * (D / 4);
+        const int64_t qoff = ((int64_t)(q0 + tok[j]) * p.num_q_heads + hq[j]) * D + grp * (D / 4);
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (cvalid[j] && pos[j] >= 0) v = *reinterpret_cast<const u32x4*>(qrow + 8 * kk);
+            if (cvalid[j] && pos[j] >= 0) v = *reinterpret_cast<const u32x4*>(p.query + qoff + 8 * kk);
             if constexpr (kQLds)
                 *reinterpret_cast<u32x4*>(sq + ((j * NK + kk) * 64 + lane) * 16) = v;
             else
                 qb[kQLds ? 0 : j][kk] = __builtin_bit_cast(bf16x8, v);
+            if constexpr (QLO) {   // the low term, in the second half of the region
+                u32x4 u = {0u, 0u, 0u, 0u};
+                if (cvalid[j] && pos[j] >= 0) u = *reinterpret_cast<const u32x4*>(p.query_lo + qoff + 8 * kk);
+                *reinterpret_cast<u32x4*>(sq + (((CT + j) * NK + kk) * 64 + lane) * 16) = u;
+            }
         }
     }
     auto read_q = [&](int j, int kk) {
         return kQLds ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sq + ((j * NK + kk) * 64 + lane) * 16))
                      : qb[kQLds ? 0 : j][kk];
+    };
+    auto read_qlo = [&](int j, int kk) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sq + (((CT + j) * NK + kk) * 64 + lane) * 16));
     };
 
     const float kscale = p.k_scales != nullptr
@@ -455,14 +468,20 @@ void prefill_kernel(PrefillParams p) {
                 for (int j = 0; j < CT; ++j) s[j][c] = f32x4{};
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
-                bf16x8 qk[CT];
+                bf16x8 qk[CT], ql[QLO ? CT : 1];
 #pragma unroll
-                for (int j = 0; j < CT; ++j) qk[j] = read_q(j, kk);
+                for (int j = 0; j < CT; ++j) {
+                    qk[j] = read_q(j, kk);
+                    if constexpr (QLO) ql[j] = read_qlo(j, kk);
+                }
 #pragma unroll
                 for (int c = 0; c < NB; ++c) {
                     const bf16x8 kop = read_k(c, kk);
 #pragma unroll
-                    for (int j = 0; j < CT; ++j) s[j][c] = mfma16(kop, qk[j], s[j][c]);
+                    for (int j = 0; j < CT; ++j) {
+                        s[j][c] = mfma16(kop, qk[j], s[j][c]);
+                        if constexpr (QLO) s[j][c] = mfma16(kop, ql[QLO ? j : 0], s[j][c]);
+                    }
                 }
             }
         } else {
@@ -644,12 +663,25 @@ void prefill_kernel(PrefillParams p) {
             const int64_t oc = c0 + kCols * j + orow;
             if (oc >= ncols) continue;
             const int otok = (int)(oc / G);
+            if (q0 + otok >= p.num_rows) continue;
             const int ohq = h * G + (int)(oc % G);
             const int64_t base = ((int64_t)(q0 + otok) * p.num_q_heads + ohq) * D;
 #pragma unroll
             for (int t = 0; t < NT; ++t) store_out(p.out, p.out_f32, base + 16 * t + col, osum[j][t][i] * f);
         }
     }
+}
+
+template <int D>
+const void* rotated_kernel(Codec codec) {
+    if constexpr (col_tiles(D) == 2) {
+        switch (codec) {
+            case kCodecE4M3: return reinterpret_cast<const void*>(&prefill_kernel<D, kCodecE4M3, true>);
+            case kCodecBF16: return reinterpret_cast<const void*>(&prefill_kernel<D, kCodecBF16, true>);
+            default: return nullptr;
+        }
+    }
+    return nullptr;   // the low query term needs the two-tile kernel's LDS query operands
 }
 
 template <int D>
@@ -661,6 +693,11 @@ hipError_t launch_d(const PrefillParams& p, Codec codec, hipStream_t s) {
     const int64_t groups = (int64_t)p.num_seqs * p.num_kv_heads;   // (sequence, kv head) pairs
     if (tiles * groups > 0x7FFFFFFF) return hipErrorInvalidValue;
     const void* fn;
+    if (p.query_lo != nullptr) {
+        fn = rotated_kernel<D>(codec);
+        if (fn == nullptr) return hipErrorInvalidValue;
+        return launch_kernel(fn, dim3((unsigned)(tiles * groups)), dim3(64 * kWaves), 0, s, p);
+    }
     switch (codec) {
         case kCodecE4M3: fn = reinterpret_cast<const void*>(&prefill_kernel<D, kCodecE4M3>); break;
         case kCodecBF16: fn = reinterpret_cast<const void*>(&prefill_kernel<D, kCodecBF16>); break;

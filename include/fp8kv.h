@@ -584,6 +584,43 @@ int fp8kv_decode_step_rotated(void* out, int out_dtype, const void* query,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fp8kv_paged_prefill_rotated_workspace_size -- bytes of device workspace
+ * fp8kv_paged_prefill_rotated needs for num_query_tokens query rows (0 on invalid
+ * arguments): the rotated query (two bf16 terms) and the f32 output before it is rotated
+ * back.
+ */
+size_t fp8kv_paged_prefill_rotated_workspace_size(int num_query_tokens, int num_q_heads,
+                                                  int head_dim);
+
+/*
+ * fp8kv_paged_prefill_rotated -- fp8kv_paged_prefill over a rotated cache: every chunk row
+ *   out = H/sqrt(d) . Attention(H/sqrt(d) . q, K_rot, V_rot)
+ * over its causal prefix, as fp8kv_paged_decode_rotated computes it for one token: the
+ * query rotated in f32 and split into two bf16 terms that both enter S = K.q^T, the
+ * output rotated back from f32.  Three launches on `stream` (query rotation, prefill,
+ * output rotation).
+ *
+ *   num_query_tokens  host count of query rows, query_start_loc[num_seqs]; rows at or past
+ *                     it are neither read nor written
+ *   workspace         at least fp8kv_paged_prefill_rotated_workspace_size(num_query_tokens,
+ *                     num_q_heads, head_dim) bytes, 256-byte aligned, contents on entry
+ *                     irrelevant (else FP8KV_ERR_WORKSPACE)
+ *
+ * Cache dtypes FP8KV_E4M3 and FP8KV_BF16, head_dim 64 or 128 (the low query term lives in
+ * the LDS query operands of the kernel's two-column-tile form; head_dim 256:
+ * FP8KV_ERR_UNSUPPORTED).  Per-tensor scales; everything else as for fp8kv_paged_prefill.
+ */
+int fp8kv_paged_prefill_rotated(void* out, int out_dtype, const void* query,
+                                const int32_t* query_start_loc,
+                                const void* key_cache, const void* value_cache, int cache_dtype,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int max_context_len,
+                                int num_seqs, int max_query_len, int num_query_tokens,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int num_blocks, float k_scale, float v_scale, int sliding_window,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Per-kv-head scales on the rotated path (page "FP8 KV Cache Quantization: Capacity Gains
  * and Accuracy Risk", "Scales and calibration", combined with the rotation above):
  * fp8kv_cache_write_rotated_per_head, fp8kv_paged_decode_rotated_per_head and

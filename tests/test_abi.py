@@ -330,3 +330,34 @@ def test_rotated_per_head_bf16_ignores_scale_arrays():
         assert _rot_ph(kind, cache_dtype=F.FP8KV_BF16, k_scales=0, v_scales=0, workspace=0) == \
             F.FP8KV_ERR_WORKSPACE
         assert _rot_ph(kind, num_seqs=0, query=0, out=0, workspace=0) == F.FP8KV_OK
+
+
+def _prefill_rot(**kw):
+    a = dict(out=FAKE, out_dtype=F.FP8KV_BF16, query=FAKE, query_start_loc=FAKE, key_cache=FAKE,
+             value_cache=FAKE, cache_dtype=F.FP8KV_E4M3, block_tables=FAKE, max_blocks_per_seq=64,
+             context_lens=FAKE, max_context_len=1024, num_seqs=2, max_query_len=64,
+             num_query_tokens=100, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+             num_blocks=200, k_scale=1.0, v_scale=1.0, sliding_window=0, workspace=FAKE,
+             workspace_bytes=0, stream=0)
+    a.update(kw)
+    return F.lib.fp8kv_paged_prefill_rotated(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=256), F.FP8KV_ERR_UNSUPPORTED), (dict(cache_dtype=F.FP8KV_E5M2), F.FP8KV_ERR_UNSUPPORTED),
+    (dict(cache_dtype=F.FP8KV_INT8), F.FP8KV_ERR_UNSUPPORTED), (dict(num_query_tokens=-1), F.FP8KV_ERR_SHAPE),
+    (dict(workspace=0), F.FP8KV_ERR_WORKSPACE), (dict(workspace=FAKE + 16, workspace_bytes=1 << 30), F.FP8KV_ERR_WORKSPACE),
+    (dict(k_scale=0.0), F.FP8KV_ERR_SCALE), (dict(query=0), F.FP8KV_ERR_NULL),
+    (dict(out_dtype=7), F.FP8KV_ERR_UNSUPPORTED), (dict(num_q_heads=30), F.FP8KV_ERR_SHAPE),
+])
+def test_prefill_rotated_rejects(kw, status):
+    assert _prefill_rot(**kw) == status
+
+
+def test_prefill_rotated_no_work_and_workspace_size():
+    assert _prefill_rot(num_query_tokens=0) == F.FP8KV_OK
+    assert _prefill_rot(num_seqs=0, query=0, out=0) == F.FP8KV_OK
+    ws = F.fp8kv_paged_prefill_rotated_workspace_size
+    assert ws(100, 32, 128) == 2 * 100 * 32 * 128 * 2 + 100 * 32 * 128 * 4
+    assert ws(1, 1, 64) == 256 + 256 + 256
+    assert ws(-1, 32, 128) == 0 and ws(10, 32, 96) == 0 and ws(10, 0, 128) == 0

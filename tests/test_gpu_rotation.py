@@ -288,3 +288,94 @@ def test_rotated_per_head_step_matches_oracle(num_splits):
     got = out.cpu().numpy().astype(np.float64).reshape(B, Hq, D)
     assert_close(got, _ref_ph(w, L, ks, vs, okc, ovc), atol=2e-4, rtol=2e-3, what=w.name)
     assert not cnt.cpu().numpy().any(), "counters were not returned to zero"
+
+
+# ---- prefill over a rotated cache
+
+PF_LENS, PF_CHUNKS = [37, 300, 1027, 16, 5, 40], [37, 64, 200, 1, 5, 0]
+
+
+def _prefill_rot(w, L, ks, vs, kc, vc, cdt, pq, out_f32=False, num_query_tokens=None):
+    dev = DeviceInputs(w)
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    T = pq.num_tokens if num_query_tokens is None else num_query_tokens
+    nbytes = F.fp8kv_paged_prefill_rotated_workspace_size(T, Hq, D)
+    ws = torch.full((max(nbytes, 256),), 0xFF, dtype=torch.uint8, device=DEV)
+    out = torch.full((max(pq.num_tokens, 1) * Hq * D,), float("nan"),
+                     dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
+    q = u16_dev(pq.q)
+    qsl = torch.from_numpy(np.ascontiguousarray(pq.query_start_loc)).to(DEV)
+    F.fp8kv_paged_prefill_rotated(out, F.FP8KV_F32 if out_f32 else F.FP8KV_BF16, q, qsl, kc, vc, cdt,
+                                  dev.bt, w.max_blocks_per_seq, dev.cl, w.max_context_len,
+                                  w.num_seqs, pq.max_query_len, T, Hq, Hkv, D, 16, w.num_blocks, ks,
+                                  vs, L.sliding_window, ws, ws.numel())
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)[: pq.num_tokens * Hq * D].reshape(
+        pq.num_tokens, Hq, D)
+
+
+def _pf_pairs(w, pq, seed=280):
+    """Every row for the first and the last query head (all tiles and tails), and every
+    head for the first, the last and three random rows of each sequence."""
+    rng = np.random.default_rng(seed)
+    Hq = w.num_q_heads
+    pairs = {(r, hq) for r in range(pq.num_tokens) for hq in (0, Hq - 1)}
+    for b in range(w.num_seqs):
+        a, e = int(pq.query_start_loc[b]), int(pq.query_start_loc[b + 1])
+        if e > a:
+            for r in {a, e - 1, *rng.integers(a, e, 3).tolist()}:
+                pairs |= {(r, hq) for hq in range(Hq)}
+    return np.array(sorted(pairs), np.int32)
+
+
+def _check_prefill_rot(w, L, ks, vs, pq, out_f32=False):
+    cdt, kc, vc, okc, ovc = _write_both(w, L, ks, vs)
+    got = _prefill_rot(w, L, ks, vs, kc, vc, cdt, pq, out_f32=out_f32)
+    pairs = _pf_pairs(w, pq)
+    ref = oracle.paged_prefill_rotated_pairs(pairs, pq.q, pq.query_start_loc, okc, ovc, cdt,
+                                             w.block_tables, w.context_lens, w.num_q_heads,
+                                             w.num_kv_heads, w.head_dim, 16, ks, vs, L.sliding_window)
+    tol = dict(atol=2e-4, rtol=2e-3) if out_f32 else {}
+    assert_close(got[pairs[:, 0], pairs[:, 1]], ref, what=f"{w.name} rotated prefill", **tol)
+    assert np.all(np.isfinite(got)), "non-finite rows"
+    return got, ref
+
+
+@pytest.mark.parametrize("cache", [syn.E4M3, syn.BF16])
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 1, 64), (32, 8, 128), (64, 8, 64), (12, 2, 128)])
+def test_rotated_prefill_matches_oracle(Hq, Hkv, D, cache):
+    w, L, ks, vs = _mk(Hq, Hkv, D, PF_LENS, cid=260 + Hq + D, cache=cache)
+    pq = syn.prefill_queries(w, PF_CHUNKS, 260 + Hq + D)
+    say(f"paged_prefill_rotated {w.name}")
+    _check_prefill_rot(w, L, ks, vs, pq)
+
+
+def test_rotated_prefill_f32_output():
+    w, L, ks, vs = _mk(32, 8, 128, [700, 2049, 90], cid=270)
+    pq = syn.prefill_queries(w, [200, 333, 17], 270)
+    say(f"paged_prefill_rotated f32 {w.name}")
+    _check_prefill_rot(w, L, ks, vs, pq, out_f32=True)
+
+
+@pytest.mark.parametrize("window", [17, 512])
+def test_rotated_prefill_windows(window):
+    w, L, ks, vs = _mk(64, 8, 64, [1, 20, 200, 1100], cid=271, window=window)
+    pq = syn.prefill_queries(w, [1, 20, 150, 300], 271)
+    say(f"paged_prefill_rotated window={window}")
+    _check_prefill_rot(w, L, ks, vs, pq)
+
+
+def test_rotated_prefill_rows_past_num_query_tokens_are_untouched():
+    """num_query_tokens below query_start_loc[B]: the rows before it match the oracle, the
+    rows past it keep their NaN fill (neither read nor written)."""
+    w, L, ks, vs = _mk(32, 8, 128, [300, 500], cid=272)
+    pq = syn.prefill_queries(w, [100, 60], 272)
+    cdt, kc, vc, okc, ovc = _write_both(w, L, ks, vs)
+    got = _prefill_rot(w, L, ks, vs, kc, vc, cdt, pq, num_query_tokens=130)
+    pairs = np.array([(r, hq) for r in (0, 59, 99, 100, 129) for hq in range(w.num_q_heads)], np.int32)
+    ref = oracle.paged_prefill_rotated_pairs(pairs, pq.q, pq.query_start_loc, okc, ovc, cdt,
+                                             w.block_tables, w.context_lens, w.num_q_heads,
+                                             w.num_kv_heads, w.head_dim, 16, ks, vs)
+    assert_close(got[pairs[:, 0], pairs[:, 1]], ref, what="rows before num_query_tokens")
+    assert np.all(np.isfinite(got[:130]))
+    assert np.all(np.isnan(got[130:]))
