@@ -372,13 +372,38 @@ def read_ceiling(torch, root: str, gib: int = 2, launches: int = 20) -> dict:
     best = max(rates, key=rates.get)
     half = (best[0], best[1] // 2, best[2])
     converged = half in rates and rates[half] >= 0.99 * rates[best]
-    names = ("stride", "chunk")
+    # paged reads: 1 and 2 KiB pieces at scattered places over a power-of-two buffer, the
+    # granule of a paged cache's reads (one 16-token block of one kv head: 1 KiB of keys or
+    # values at head_dim 64 in one-byte codes, 2 KiB at 128)
+    pn = 1 << 31
+    pbuf = torch.ones(pn, dtype=torch.uint8, device="cuda")
+    paged = {}
+    for pat in (2, 3):
+        for u in unrolls:
+            for grid in (2048, 4096, 8192, 16384):
+                call = lambda: lib.fp8kv_probe_read(pbuf.data_ptr(), pn, grid, u, pat, sink.data_ptr(), stream)
+                for _ in range(2):
+                    assert call() == 0, "paged read probe launch failed"
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(launches):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
+                paged[(pat, grid, u)] = pn / (e0.elapsed_time(e1) / launches * 1e-3) / 1e9
+    del pbuf
+    names = ("stride", "chunk", "paged1k", "paged2k")
     return {"GBps": round(rates[best], 1), "bytes": n, "pattern": names[best[0]], "grid": best[1],
             "loads_in_flight": best[2],
             "GBps_by_config": {f"{names[p]}-{grd}x{u}": round(r, 1) for (p, grd, u), r in rates.items()},
             "converged": bool(converged),
+            "paged_GBps": {"1KiB": round(max(r for (p, _, _), r in paged.items() if p == 2), 1),
+                           "2KiB": round(max(r for (p, _, _), r in paged.items() if p == 3), 1)},
+            "paged_GBps_by_config": {f"{names[p]}-{grd}x{u}": round(r, 1) for (p, grd, u), r in paged.items()},
             "kernel": "16-byte nontemporal reads, 256 threads per workgroup; keys are pattern (grid-"
-                      "stride or contiguous runs per workgroup), grid x loads in flight per thread"}
+                      "stride or contiguous runs per workgroup; paged: 1 or 2 KiB pieces at "
+                      "scattered places), grid x loads in flight per thread"}
 
 
 def _oracle_threads() -> int:
@@ -617,6 +642,12 @@ def main(argv=None):
         rc = read_ceiling(torch, root)
         result["read_ceiling"] = rc
         result["pct_of_read_ceiling"] = round(100 * value / rc["GBps"], 2)
+        # the paged ceiling at this layer's read granule (one block of one kv head)
+        granule = BLOCK * w.head_dim * (1 if layer.cache_dtype == "e4m3" else 2)
+        key = {1024: "1KiB", 2048: "2KiB"}.get(granule)
+        if key is not None:
+            result["pct_of_paged_read_ceiling"] = {"granule": key,
+                                                   "pct": round(100 * value / rc["paged_GBps"][key], 2)}
         torch.cuda.empty_cache()
 
     if not (args.no_bf16 or args.profile or heads is not None or codec is not None) \
