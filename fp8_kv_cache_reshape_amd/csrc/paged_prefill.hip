@@ -15,8 +15,11 @@
 // Work mapping.  A query "column" is one (chunk token, query head of the group) pair; the
 // columns of a (sequence, kv head) are numbered token-major, head fastest, so the g heads
 // of one token -- which read the same keys -- sit side by side.  A workgroup of 8 waves
-// owns 128 consecutive columns of one (sequence, kv head), 16 per wave, and walks the keys
-// they need one step at a time: 64 tokens (four cache blocks) for d <= 128, 32 for d = 256.
+// owns consecutive columns of one (sequence, kv head): two 16-column tiles per wave at
+// d <= 128 (256 per workgroup), whose products share every key and value operand read, and
+// one at d = 256 (128 per workgroup), whose accumulators would not fit twice.  It walks the
+// keys its columns need one step at a time (Stage: 32 to 128 keys).  The grid is ordered
+// longest first over every (sequence, kv head).
 //
 // Staging.  Each step's K and V tiles are loaded once per workgroup (spread over the waves),
 // widened on the way -- keys to bf16, values to fp16 (bf16 for the bf16 cache); one-byte
@@ -25,10 +28,11 @@
 // LDS, so no wave converts codes itself.  The LDS
 // tiles have their own order, chosen so that every operand read instruction covers
 // contiguous 256-byte runs (no bank conflicts): keys [group][slice][slot][8 channels],
-// values of a block pair [16-channel tile][group][channel][block][4 slots].
+// values of a block pair [16-channel tile][group][channel][block][4 slots].  With two
+// column tiles the query operands sit in LDS too, in each wave's own region.
 //
-// Both products run on 16x16x32 matrix-core tiles (16 columns per wave keeps the two
-// accumulator levels and the query operand small enough for two waves per SIMD):
+// Both products run on 16x16x32 matrix-core tiles (per 16-column tile; 16 columns keep
+// the layout in which the scores feed P.V straight from registers):
 //   S = K.Q^T per block : A = 16 key slots x 32 channels, B = 32 channels x 16 columns.
 //               Lane l (column l%16, group g = l/16) gets slots 4g..4g+3 of the block; the
 //               32-channel slice kk of group g is channels [g*d/4 + 8kk, +8) -- one 16-byte
